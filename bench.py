@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Throughput of the latent-MoE layer on one MI355X.
+
+A step is one lmoe_forward over one batch of T tokens (router, top-K,
+permutation, D, routed experts, combine + U, shared expert). The default
+workload is the Edge0-145B-shaped decode / speculative-verify layer: H 2560,
+latent 1792, 512 NVFP4 experts, top-10, 8 Q8 D/U groups, shared expert 640,
+T = 4. Weights are synthetic (seeded N(0, 0.02) masters quantized on the GPU
+by the library's packers; router N(0, 1/sqrt(H)) and x ~ N(0, 1) from the
+same seeded generator as the tests). Steps rotate over --copies independently
+seeded layers so that the 256 MB Infinity Cache cannot hold the weights a
+step reads; inputs are resident in HBM before the timed region.
+
+Prints one JSON line (rank 0). --gpus above 1 is refused: this build runs on
+one GPU.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_layer(lm, wl, w, seed, layer_idx, torch):
+    """One layer's weights, drawn and packed on the device."""
+    dev = "cuda"
+    E, H, L, G, F, Fs = w.n_experts, w.hidden, w.latent, w.n_groups, w.expert_ffn, w.shared_ffn
+    layer = lm.Layer(H, L, E, w.top_k, G, F, Fs, w.du_bits, max(w.tokens, 1),
+                     has_router_bias=w.router_bias)
+    router = torch.from_numpy(wl.router(w, seed, layer_idx)).to(dev)
+    router_bf16 = torch.empty(E, H, dtype=torch.int16, device=dev)
+    lm.pack_bf16(router, router_bf16)
+    bias = wl.router_bias(w, seed, layer_idx)
+    labels = wl.labels(w, seed, layer_idx)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed * 1000003 + layer_idx * 7919 + 17)
+    rnd = lambda *s: torch.randn(*s, generator=gen, device=dev) * wl.WEIGHT_STD
+    dg = lm.du_matrix_bytes(L, H, w.du_bits)
+    ug = lm.du_matrix_bytes(H, L, w.du_bits)
+    d_blob = torch.empty(G * dg, dtype=torch.uint8, device=dev)
+    u_blob = torch.empty(G * ug, dtype=torch.uint8, device=dev)
+    for g in range(G):
+        lm.pack_blocks(rnd(L, H), w.du_bits, d_blob[g * dg:(g + 1) * dg])
+        lm.pack_blocks(rnd(H, L), w.du_bits, u_blob[g * ug:(g + 1) * ug])
+    shared = []
+    for shp in ((Fs, H), (Fs, H), (H, Fs)):
+        t = torch.empty(*shp, dtype=torch.int16, device=dev)
+        lm.pack_bf16(rnd(*shp), t)
+        shared.append(t)
+    rec = lm.expert_record_bytes(L, F)
+    experts = torch.empty(E, rec, dtype=torch.uint8, device=dev)
+    chunk = 64
+    for e0 in range(0, E, chunk):
+        n = min(chunk, E - e0)
+        g_, u_, d_ = wl.torch_expert_masters(w, seed, layer_idx, e0, n, dev)
+        lm.pack_expert_records(g_, u_, d_, experts[e0:e0 + n])
+        del g_, u_, d_
+    layer.load(dict(router_bf16=router_bf16,
+                    router_bias=None if bias is None else torch.from_numpy(bias).to(dev),
+                    labels=torch.from_numpy(labels).to(dev), d_blob=d_blob, u_blob=u_blob,
+                    experts=experts, shared=tuple(shared)))
+    torch.cuda.synchronize()
+    return layer, labels
+
+
+def phase_bytes(w, idx, labels):
+    """Algorithmic HBM bytes of each of the four decode kernels for one
+    forward with routing idx [T][K]: every weight the step must read once,
+    plus the activations it must read and write."""
+    T, H, L, E, K, G, F, Fs = (w.tokens, w.hidden, w.latent, w.n_experts, w.top_k, w.n_groups,
+                               w.expert_ffn, w.shared_ffn)
+    du = (w.du_bits / 8.0) * (34.0 / 32.0 if w.du_bits == 8 else 18.0 / 16.0)  # bytes / weight
+    distinct = len(set(idx.ravel().tolist()))
+    used_groups = len(set(labels[idx.ravel()].tolist()))
+    fp4 = 0.5 + 1.0 / 16.0
+    p1 = E * H * 2 + G * L * H * du + 2 * Fs * H * 2 + T * H * 4 + T * G * L * 4 + T * Fs * 4
+    p2 = distinct * 2 * F * L * fp4 + T * K * (L + F) * 4
+    p3 = distinct * L * F * fp4 + T * K * (F + L) * 4
+    p4 = used_groups * H * L * du + H * Fs * 2 + T * (G * L + Fs + H) * 4
+    return [p1, p2, p3, p4], distinct, used_groups
+
+
+def cpu_baseline(w, seed, tokens):
+    """The fp64 oracle timed on the host on a bounded sample: one forward of
+    `tokens` tokens of layer 0 (including its on-the-fly dequantization of
+    D, U and the experts it touches; excluding weight drawing and packing)."""
+    import oracle
+    from latent_mixture_experts_amd import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    d = oracle.LayerDims(w.hidden, w.latent, w.n_experts, w.top_k, w.n_groups, w.expert_ffn,
+                         w.shared_ffn, w.du_bits)
+    x = wl.x(w, seed, 0, tokens=tokens)
+    m = wl.masters(w, seed, 0)
+    lg = oracle.router_logits(x, oracle.f32_to_bf16_bits(m["router"]), m["router_bias"])
+    idx, _ = oracle.select_topk(lg, w.top_k)
+    m["expert_ids"] = sorted(set(idx.ravel().tolist()))
+    blobs = oracle.pack_layer(d, m)
+    t0 = time.perf_counter()
+    oracle.layer_forward(d, blobs, x)
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
+            "sample": "one fp64 NumPy forward of %d tokens of the %s layer (seed %d), including "
+                      "dequantization of D, U and the %d experts it touches; %.1f s" % (
+                          tokens, w.name, seed, len(m["expert_ids"]), dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="145b_decode")
+    ap.add_argument("--copies", type=int, default=8)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d refused)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from latent_mixture_experts_amd import lmoe as lm
+    from latent_mixture_experts_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    if w.tokens > 8:
+        print("workload %s needs the prefill path, which bench.py does not time yet" % w.name,
+              file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    t_build = time.time()
+    layers, labels = [], []
+    for r in range(args.copies):
+        L_, lab = build_layer(lm, wl, w, args.seed, r, torch)
+        layers.append(L_)
+        labels.append(lab)
+    log("built %d layer copies in %.1f s" % (args.copies, time.time() - t_build))
+
+    T = w.tokens
+    x = torch.from_numpy(wl.x(w, args.seed, 0)).cuda()
+    y = torch.empty(T, w.hidden, device="cuda")
+
+    # routing of each copy, for the algorithmic byte counts
+    bytes_per_copy, distinct, groups = [], [], []
+    for r, L_ in enumerate(layers):
+        idx = torch.empty(T, w.top_k, dtype=torch.int32, device="cuda")
+        L_.forward(x, y, debug=dict(topk_idx=idx))
+        torch.cuda.synchronize()
+        pb, dn, ug = phase_bytes(w, idx.cpu().numpy(), labels[r])
+        bytes_per_copy.append(pb)
+        distinct.append(dn)
+        groups.append(ug)
+    pbytes = np.mean(np.array(bytes_per_copy), axis=0)
+
+    for i in range(args.warmup):
+        layers[i % args.copies].forward(x, y)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        layers[i % args.copies].forward(x, y)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+
+    # per-kernel durations with HIP events recorded on the forward's stream
+    nph = lm.lib().lmoe_phase_count()
+    nprof = max(args.copies * 4, 32)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)] for _ in range(nprof)]
+    for row in evs:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    for i in range(nprof):
+        L_ = layers[i % args.copies]
+        L_.set_phase_events([e.cuda_event for e in evs[i]])
+        L_.forward(x, y)
+    for L_ in layers:
+        L_.set_phase_events(None)
+    torch.cuda.synchronize()
+    phase_ms = np.array([[row[k].elapsed_time(row[k + 1]) for k in range(nph)] for row in evs])
+    phase_avg = phase_ms.mean(axis=0)
+    dom = int(np.argmax(phase_avg))
+    achieved = pbytes[dom] / (phase_avg[dom] * 1e-3) / 1e9
+    total_bytes = float(np.sum(pbytes))
+    log("step %.2f us; phases (us): %s; phase GB/s: %s; whole-forward %.0f GB/s over %.1f MB" % (
+        ms * 1e3, " ".join("%.2f" % (p * 1e3) for p in phase_avg),
+        " ".join("%.0f" % (b / (p * 1e-3) / 1e9) for b, p in zip(pbytes, phase_avg)),
+        total_bytes / (ms * 1e-3) / 1e9, total_bytes / 1e6))
+    log("distinct experts per step %.1f, groups used %.1f" % (np.mean(distinct), np.mean(groups)))
+
+    out = {
+        "metric": "latent-MoE layer tokens/s (decode; HBM roofline)",
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": T, "hidden": w.hidden, "latent": w.latent,
+                   "experts": w.n_experts, "top_k": w.top_k, "groups": w.n_groups,
+                   "expert_ffn": w.expert_ffn, "shared_ffn": w.shared_ffn,
+                   "du_format": "Q%d" % w.du_bits, "expert_format": "NVFP4",
+                   "weight_copies": args.copies,
+                   "forward_algorithmic_bytes": total_bytes,
+                   "forward_GBps": total_bytes / (ms * 1e-3) / 1e9},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "k_phase%d" % (dom + 1),
+                     "kernel_us": phase_avg[dom] * 1e3,
+                     "kernel_algorithmic_bytes": pbytes[dom]},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.seed, T)
+    print(json.dumps(out), flush=True)
+    for L_ in layers:
+        L_.close()
+
+
+if __name__ == "__main__":
+    main()

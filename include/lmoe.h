@@ -1,0 +1,186 @@
+/*
+ * lmoe.h -- C ABI of liblmoe.so, the latent mixture-of-experts layer of the
+ * Edge0 145B / 120B models on AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (by title, then section / equation / table):
+ *   LAYER    = "Edge0 145B and Edge0 120B" model page: "Model profile" table
+ *              (512 routed experts plus one shared expert, top_k 10, latent
+ *              compression with 8 groups of D/U chosen by each expert's group
+ *              label, expert formats, D/U formats) and the "Edge0-145B
+ *              architecture" / "Edge0-120B architecture" tables and text
+ *              (SwiGLU width 640; D projects to ell per routing group; only
+ *              the experts work at ell; U projects the combined result back).
+ *   TEARDOWN = "Edge0-145B: a Qwen MoE with its experts squeezed, and a 51B
+ *              table left on the SSD": "A latent in front of the experts"
+ *              (the layer equation y = U_g(sum_e w_e E_e(D_g x)); D runs over
+ *              all groups, U once per group a token routed into; the router
+ *              reads the full-width hidden state), "What is 4-bit" (NVFP4
+ *              record: FP4 values, an E4M3 scale per 16, a 16-byte tail; Q8_0
+ *              / Q4_0 D/U), "The base, byte for byte" (bf16 router weights).
+ *
+ * The layer, per token x (fp32, width H):
+ *   l      = Wr x (+ b)                 router logits over E experts
+ *   idx, w = top K of l (descending, ties to the lower index) and the
+ *            softmax of the kept logits (= softmax over E, keep K, renormalize)
+ *   for each kept expert e with group g = label[e]:
+ *            h = silu(Wg_e (D_g x)) * (Wu_e (D_g x));   o = w * Wd_e h
+ *   y      = sum over groups g used by x of U_g (sum of that group's o)
+ *          + Ws_down (silu(Ws_gate x) * (Ws_up x))
+ *
+ * Packed input formats (host or device memory; the library copies them):
+ *   router      bf16 [E][H] (uint16 bit patterns)
+ *   router bias fp32 [E], optional
+ *   labels      uint8 [E], each < G
+ *   D blob      G matrices D_g [ell][H], one after another; each = codes then
+ *               fp16 scales [ell][H/32]. Q8 codes: int8 [ell][H]; Q4 codes:
+ *               bytes [ell][H/2] holding q+8, element 2i in the low nibble.
+ *               Q8: x ~ q * d; Q4: x ~ (nibble - 8) * d. Blocks of 32 run
+ *               along the row (the input dimension).
+ *   U blob      G matrices U_g [H][ell], same block layout.
+ *   experts     E fixed-size NVFP4 records, each: gate codes [F][ell/2],
+ *               up codes [F][ell/2], down codes [ell][F/2] (E2M1, element 2i
+ *               in the low nibble), gate scales [F][ell/16], up scales
+ *               [F][ell/16], down scales [ell][F/16] (E4M3, one per 16 along
+ *               the row), tail: fp32 ts_gate, ts_up, ts_down, uint32 0.
+ *               Weight = e2m1 * e4m3 * ts. Record = 3*ell*F*9/16 + 16 bytes
+ *               (1,935,376 B at ell 1792, F 640).
+ *   shared      bf16 gate [Fs][H], up [Fs][H], down [H][Fs].
+ *
+ * Errors: every entry point returns 0 or a negative LMOE_E* code; argument
+ * errors are found on the host before any launch. Device-side faults surface
+ * as LMOE_EHIP at a later call. lmoe_last_error() gives the last message of
+ * the calling thread.
+ *
+ * Threads and streams: a handle is not thread-safe. Forward calls on one
+ * handle must be ordered (one stream, or explicit events): they share the
+ * handle's workspace.
+ */
+#ifndef LMOE_H
+#define LMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LMOE_OK            0
+#define LMOE_EINVAL       -1   /* bad argument: NULL, size, T out of range, label >= G */
+#define LMOE_ENOMEM       -2   /* device allocation failed */
+#define LMOE_EHIP         -3   /* a HIP runtime call failed */
+#define LMOE_ESTATE       -4   /* forward before load_weights */
+#define LMOE_EUNSUPPORTED -5   /* dimensions the kernels do not cover */
+
+/* Layer dimensions, validated by lmoe_create.
+ * Constraints: hidden % 256 == 0, latent % 64 == 0, expert_ffn % 32 == 0,
+ * shared_ffn % 32 == 0, hidden <= 4096, latent <= 4096, expert_ffn <= 4096,
+ * shared_ffn <= 4096, 1 <= top_k <= min(n_experts, 64), n_experts <= 1024,
+ * 1 <= n_groups <= 64, du_bits in {8, 4}, max_tokens >= 1. */
+typedef struct lmoe_dims {
+  int32_t hidden;          /* H */
+  int32_t latent;          /* ell */
+  int32_t n_experts;       /* E */
+  int32_t top_k;           /* K */
+  int32_t n_groups;        /* G */
+  int32_t expert_ffn;      /* F, SwiGLU width of a routed expert */
+  int32_t shared_ffn;      /* Fs, SwiGLU width of the shared expert */
+  int32_t du_bits;         /* 8 = Q8, 4 = Q4 ("D/U formats", LAYER) */
+  int32_t max_tokens;      /* largest T a forward may take; sizes the workspace */
+  int32_t has_router_bias; /* 1: lmoe_weights.router_bias is read */
+} lmoe_dims;
+
+/* Packed weights (layouts above). Pointers may be host or device memory;
+ * lmoe_load_weights copies what it needs and keeps no pointer. */
+typedef struct lmoe_weights {
+  const uint16_t* router_bf16;
+  const float*    router_bias;          /* NULL unless has_router_bias */
+  const uint8_t*  group_labels;
+  const uint8_t*  d_blob;  size_t d_bytes;
+  const uint8_t*  u_blob;  size_t u_bytes;
+  const uint8_t*  experts; size_t expert_record_bytes;   /* E records */
+  const uint16_t* shared_gate_bf16;
+  const uint16_t* shared_up_bf16;
+  const uint16_t* shared_down_bf16;
+} lmoe_weights;
+
+/* Optional intermediate outputs of lmoe_forward; DEVICE pointers, each may
+ * be NULL. Written on the forward's stream. */
+typedef struct lmoe_debug {
+  int32_t* topk_idx;       /* [T][K] expert ids, descending logit, ties to lower id */
+  float*   topk_w;         /* [T][K] renormalized softmax weights */
+  int32_t* perm;           /* [T*K]: stable sort of a = t*K+k by (label, expert) */
+  int32_t* expert_count;   /* [E] assignments per expert */
+  int32_t* group_off;      /* [G+1] start of each group's segment in perm */
+  float*   latent;         /* [T][G][ell] D_g x; entries of (t, g) pairs that
+                              token t does not use are unspecified */
+} lmoe_debug;
+
+typedef struct lmoe lmoe_t;
+
+/* Create a handle on HIP device `hip_device`: validates dims, allocates the
+ * workspace for max_tokens. *out is set only on success. */
+int lmoe_create(const lmoe_dims* dims, int hip_device, lmoe_t** out);
+
+/* Copy and re-lay the packed weights into device memory owned by the handle
+ * (the device layout is internal). Synchronous with respect to the host: the
+ * source buffers may be reused when it returns. `hip_stream` orders the
+ * copies (NULL = default stream). EINVAL on a size mismatch or a label >= G. */
+int lmoe_load_weights(lmoe_t* h, const lmoe_weights* w, void* hip_stream);
+
+/* y[T][H] = layer(x[T][H]); x and y are device fp32, row-major, not
+ * aliased. 1 <= T <= max_tokens. Asynchronous on `hip_stream`. `dbg` may be
+ * NULL. */
+int lmoe_forward(lmoe_t* h, const float* x_dev, int32_t T, float* y_dev,
+                 const lmoe_debug* dbg, void* hip_stream);
+
+/* One block of a pre-norm residual stack, in place on device memory:
+ *   x += layer(RMSNorm(x)),  RMSNorm(v) = v / sqrt(mean(v^2) + eps), unit gain.
+ * (The stack arrangement is this library's reading; the pages give none.) */
+int lmoe_forward_block(lmoe_t* h, float* x_inout_dev, int32_t T, float rms_eps,
+                       void* hip_stream);
+
+/* Profiling hook: when `events` is non-NULL, each following lmoe_forward /
+ * lmoe_forward_block records events[0] on its stream before its first kernel
+ * and events[i] after the i-th of its `n` kernels (hipEvent_t handles owned by
+ * the caller; the decode path has lmoe_phase_count() kernels, so n must equal
+ * lmoe_phase_count() + 1). NULL switches it off. EINVAL on a wrong n. */
+int lmoe_set_phase_events(lmoe_t* h, void* const* events, int32_t n);
+int32_t lmoe_phase_count(void);
+
+void lmoe_destroy(lmoe_t* h);
+
+const char* lmoe_strerror(int code);
+const char* lmoe_last_error(void);
+
+/* Bytes of one packed NVFP4 expert record and of one packed D_g / U_g. */
+size_t lmoe_expert_record_bytes(int32_t latent, int32_t expert_ffn);
+size_t lmoe_du_matrix_bytes(int32_t rows, int32_t cols, int32_t du_bits);
+
+/* ---- Device-side packing of fp32 masters into the formats above ----------
+ * For callers holding unquantized weights on the GPU. All pointers are
+ * DEVICE memory; asynchronous on `hip_stream`. Rounding is to nearest, ties
+ * to even, saturating:
+ *   bf16:  RNE of each fp32 value.
+ *   Q8/Q4: per 32 along the row, d = fp16(amax/127) (Q4: amax/7),
+ *          q = clamp(round(x/d), -127, 127) (Q4: [-8, 7]); d == 0 -> q = 0.
+ *   NVFP4: per matrix ts = fp32(amax/(6*448)) (1 for an all-zero matrix); per
+ *          16 along the row s = E4M3(amax16/(6*ts)) saturating at 448;
+ *          q = E2M1(x/(s*ts)) saturating at 6, magnitude 0 stored as +0.
+ * These readings of the formats are this library's; the pages give only the
+ * element and scale types and the block sizes. */
+int lmoe_pack_bf16(const float* src, size_t n, uint16_t* dst, void* hip_stream);
+/* One matrix [rows][cols] (cols % 32 == 0) into codes then fp16 scales, i.e.
+ * lmoe_du_matrix_bytes(rows, cols, bits) bytes at dst. */
+int lmoe_pack_blocks(const float* src, int32_t rows, int32_t cols, int32_t du_bits,
+                     uint8_t* dst, void* hip_stream);
+/* n expert records from gate [n][F][ell], up [n][F][ell], down [n][ell][F]
+ * into dst (n * lmoe_expert_record_bytes(ell, F) bytes). */
+int lmoe_pack_expert_records(const float* gate, const float* up, const float* down,
+                             int32_t n, int32_t latent, int32_t expert_ffn,
+                             uint8_t* dst, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LMOE_H */

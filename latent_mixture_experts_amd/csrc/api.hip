@@ -1,0 +1,330 @@
+// C ABI of liblmoe (declared and documented in include/lmoe.h): argument
+// validation, device memory, and dispatch to the decode path.
+#include <hip/hip_runtime.h>
+
+#include <new>
+#include <string>
+
+#include "internal.h"
+
+namespace lm {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+int hip_fail(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return LMOE_EHIP;
+}
+
+namespace {
+
+int check_dims(const lmoe_dims& d) {
+  auto bad = [](const char* m) {
+    set_error(std::string("lmoe_create: ") + m);
+    return LMOE_EINVAL;
+  };
+  auto unsup = [](const char* m) {
+    set_error(std::string("lmoe_create: ") + m);
+    return LMOE_EUNSUPPORTED;
+  };
+  if (d.hidden <= 0 || d.latent <= 0 || d.n_experts <= 0 || d.top_k <= 0 || d.n_groups <= 0 ||
+      d.expert_ffn <= 0 || d.shared_ffn <= 0 || d.max_tokens <= 0)
+    return bad("every dimension must be positive");
+  if (d.du_bits != 8 && d.du_bits != 4) return bad("du_bits must be 8 or 4");
+  if (d.top_k > d.n_experts) return bad("top_k exceeds n_experts");
+  if (d.has_router_bias != 0 && d.has_router_bias != 1) return bad("has_router_bias must be 0 or 1");
+  if (d.hidden % 256) return unsup("hidden must be a multiple of 256");
+  if (d.latent % 64) return unsup("latent must be a multiple of 64");
+  if (d.expert_ffn % 32 || d.shared_ffn % 32) return unsup("expert_ffn and shared_ffn must be multiples of 32");
+  if (d.hidden > 4096 || d.latent > 4096 || d.expert_ffn > 4096 || d.shared_ffn > 4096)
+    return unsup("widths above 4096");
+  if (d.n_experts > 1024 || d.top_k > 64 || d.n_groups > 64)
+    return unsup("n_experts <= 1024, top_k <= 64, n_groups <= 64");
+  return 0;
+}
+
+template <typename P>
+int dalloc(lmoe_t* h, P** p, size_t bytes) {
+  void* q = nullptr;
+  hipError_t e = hipMalloc(&q, bytes ? bytes : 1);
+  if (e != hipSuccess) {
+    set_error(std::string("hipMalloc of ") + std::to_string(bytes) + " bytes: " + hipGetErrorString(e));
+    return LMOE_ENOMEM;
+  }
+  h->allocations.push_back(q);
+  *p = (P*)q;
+  return 0;
+}
+
+void free_all(lmoe_t* h) {
+  for (void* p : h->allocations) (void)hipFree(p);
+  h->allocations.clear();
+}
+
+int create_impl(lmoe_t* h) {
+  const lmoe_dims& d = h->d;
+  const int E = d.n_experts, H = d.hidden, L = d.latent, G = d.n_groups, F = d.expert_ffn,
+            Fs = d.shared_ffn, K = d.top_k;
+  const int du = d.du_bits == 8 ? kQ8 : kQ4;
+  h->g_router = make_geom(kBF16, E, H);
+  h->g_d = make_geom(du, L, H);
+  h->g_u = make_geom(du, H, L);
+  h->g_gu = make_geom(kFP4, 2 * F, L);   // tiles of 32 gate + 32 up rows
+  h->g_dn = make_geom(kFP4, L, F);
+  h->g_sgu = make_geom(kBF16, 2 * Fs, H);
+  h->g_sdn = make_geom(kBF16, H, Fs);
+  h->ts_off = h->g_gu.bytes() + h->g_dn.bytes();
+  h->expert_stride = (h->ts_off + 16 + 255) / 256 * 256;
+
+  int rc;
+#define A(p, n) if ((rc = dalloc(h, &(p), (n)))) return rc
+  A(h->router, h->g_router.bytes());
+  A(h->bias, sizeof(float) * E);
+  A(h->labels, (size_t)E);
+  A(h->dmat, h->g_d.bytes() * G);
+  A(h->umat, h->g_u.bytes() * G);
+  A(h->experts, h->expert_stride * E);
+  A(h->sgu, h->g_sgu.bytes());
+  A(h->sdn, h->g_sdn.bytes());
+
+  Workspace& w = h->ws;
+  const int T = d.max_tokens < kMaxDecodeT ? d.max_tokens : kMaxDecodeT;
+  w.tmax = T;
+  w.nch = (H + 64 * h->g_d.nss - 1) / (64 * h->g_d.nss);
+  const int Epad = h->g_router.tiles * 64;
+  const int n = T * K;
+  A(w.part64, sizeof(double) * w.nch * T * Epad);
+  A(w.logits, sizeof(double) * T * E);
+  A(w.topk_idx, sizeof(int) * n);
+  A(w.topk_w, sizeof(float) * n);
+  A(w.perm, sizeof(int) * n);
+  A(w.inv, sizeof(int) * n);
+  A(w.slot_expert, sizeof(int) * n);
+  A(w.slot_start, sizeof(int) * n);
+  A(w.slot_count, sizeof(int) * n);
+  A(w.n_slots, sizeof(int));
+  A(w.gslot_off, sizeof(int) * (G + 1));
+  A(w.group_off, sizeof(int) * (G + 1));
+  A(w.expert_count, sizeof(int) * E);
+  A(w.rms, sizeof(float) * T);
+  A(w.xl, sizeof(float) * T * G * L);
+  A(w.hs, sizeof(float) * T * Fs);
+  A(w.hbuf, sizeof(float) * n * F);
+  A(w.obuf, sizeof(float) * n * L);
+  A(w.s, sizeof(float) * T * G * L);
+  A(w.ypart, sizeof(float) * (G + 1) * T * H);
+  A(w.ctr_router, sizeof(unsigned));
+  A(w.ctr_s, sizeof(unsigned) * G * (L / 64));
+  A(w.ctr_y, sizeof(unsigned) * (H / 64));
+#undef A
+  LMOE_HIP(hipMemset(w.ctr_router, 0, sizeof(unsigned)));
+  LMOE_HIP(hipMemset(w.ctr_s, 0, sizeof(unsigned) * G * (L / 64)));
+  LMOE_HIP(hipMemset(w.ctr_y, 0, sizeof(unsigned) * (H / 64)));
+  LMOE_HIP(hipDeviceSynchronize());
+  return 0;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) (void)hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+int copy_debug(lmoe_t* h, const lmoe_debug* dbg, int T, hipStream_t st) {
+  const lmoe_dims& d = h->d;
+  const Workspace& w = h->ws;
+  const size_t n = (size_t)T * d.top_k;
+  if (dbg->topk_idx) LMOE_HIP(hipMemcpyAsync(dbg->topk_idx, w.topk_idx, 4 * n, hipMemcpyDeviceToDevice, st));
+  if (dbg->topk_w) LMOE_HIP(hipMemcpyAsync(dbg->topk_w, w.topk_w, 4 * n, hipMemcpyDeviceToDevice, st));
+  if (dbg->perm) LMOE_HIP(hipMemcpyAsync(dbg->perm, w.perm, 4 * n, hipMemcpyDeviceToDevice, st));
+  if (dbg->expert_count)
+    LMOE_HIP(hipMemcpyAsync(dbg->expert_count, w.expert_count, 4 * (size_t)d.n_experts,
+                            hipMemcpyDeviceToDevice, st));
+  if (dbg->group_off)
+    LMOE_HIP(hipMemcpyAsync(dbg->group_off, w.group_off, 4 * (size_t)(d.n_groups + 1),
+                            hipMemcpyDeviceToDevice, st));
+  if (dbg->latent)
+    LMOE_HIP(hipMemcpyAsync(dbg->latent, w.xl, 4 * (size_t)T * d.n_groups * d.latent,
+                            hipMemcpyDeviceToDevice, st));
+  return 0;
+}
+
+int check_forward(lmoe_t* h, const void* x, int T, const void* y) {
+  if (!h) {
+    set_error("NULL handle");
+    return LMOE_EINVAL;
+  }
+  if (!h->loaded) {
+    set_error("forward before lmoe_load_weights");
+    return LMOE_ESTATE;
+  }
+  if (!x || !y) {
+    set_error("NULL x or y");
+    return LMOE_EINVAL;
+  }
+  if (T <= 0 || T > h->d.max_tokens) {
+    set_error("T must be in [1, max_tokens]");
+    return LMOE_EINVAL;
+  }
+  if (T > kMaxDecodeT) {
+    set_error("T above the decode path's limit of 8 tokens");
+    return LMOE_EUNSUPPORTED;
+  }
+  return 0;
+}
+
+}  // namespace
+}  // namespace lm
+
+using namespace lm;
+
+extern "C" {
+
+int lmoe_create(const lmoe_dims* dims, int hip_device, lmoe_t** out) {
+  if (!dims || !out) {
+    set_error("lmoe_create: NULL argument");
+    return LMOE_EINVAL;
+  }
+  if (int rc = check_dims(*dims)) return rc;
+  int ndev = 0;
+  LMOE_HIP(hipGetDeviceCount(&ndev));
+  if (hip_device < 0 || hip_device >= ndev) {
+    set_error("lmoe_create: no such HIP device");
+    return LMOE_EINVAL;
+  }
+  DeviceGuard g(hip_device);
+  lmoe_t* h = new (std::nothrow) lmoe_t();
+  if (!h) return LMOE_ENOMEM;
+  h->d = *dims;
+  h->device = hip_device;
+  if (int rc = create_impl(h)) {
+    free_all(h);
+    delete h;
+    return rc;
+  }
+  *out = h;
+  return 0;
+}
+
+int lmoe_load_weights(lmoe_t* h, const lmoe_weights* w, void* stream) {
+  if (!h || !w) {
+    set_error("lmoe_load_weights: NULL argument");
+    return LMOE_EINVAL;
+  }
+  DeviceGuard g(h->device);
+  return load_weights_impl(h, w, (hipStream_t)stream);
+}
+
+int lmoe_forward(lmoe_t* h, const float* x, int32_t T, float* y, const lmoe_debug* dbg,
+                 void* stream) {
+  if (int rc = check_forward(h, x, T, y)) return rc;
+  if (x == y) {
+    set_error("lmoe_forward: x and y alias");
+    return LMOE_EINVAL;
+  }
+  DeviceGuard g(h->device);
+  hipStream_t st = (hipStream_t)stream;
+  if (int rc = forward_decode(h, x, T, y, false, st)) return rc;
+  if (dbg) return copy_debug(h, dbg, T, st);
+  return 0;
+}
+
+int lmoe_forward_block(lmoe_t* h, float* x, int32_t T, float eps, void* stream) {
+  if (int rc = check_forward(h, x, T, x)) return rc;
+  if (!(eps >= 0.0f)) {
+    set_error("lmoe_forward_block: rms_eps must be >= 0");
+    return LMOE_EINVAL;
+  }
+  DeviceGuard g(h->device);
+  hipStream_t st = (hipStream_t)stream;
+  if (int rc = rms_rows(h, x, T, eps, st)) return rc;
+  return forward_decode(h, x, T, x, true, st);
+}
+
+int lmoe_set_phase_events(lmoe_t* h, void* const* events, int32_t n) {
+  if (!h) {
+    set_error("lmoe_set_phase_events: NULL handle");
+    return LMOE_EINVAL;
+  }
+  if (!events) {
+    h->phase_events.clear();
+    return 0;
+  }
+  if (n != kDecodePhases + 1) {
+    set_error("lmoe_set_phase_events: n must be lmoe_phase_count() + 1");
+    return LMOE_EINVAL;
+  }
+  h->phase_events.assign((hipEvent_t*)events, (hipEvent_t*)events + n);
+  return 0;
+}
+
+int32_t lmoe_phase_count(void) { return kDecodePhases; }
+
+void lmoe_destroy(lmoe_t* h) {
+  if (!h) return;
+  {
+    DeviceGuard g(h->device);
+    (void)hipDeviceSynchronize();
+    free_all(h);
+  }
+  delete h;
+}
+
+const char* lmoe_strerror(int code) {
+  switch (code) {
+    case LMOE_OK: return "success";
+    case LMOE_EINVAL: return "invalid argument";
+    case LMOE_ENOMEM: return "out of device memory";
+    case LMOE_EHIP: return "HIP runtime error";
+    case LMOE_ESTATE: return "handle not ready (weights not loaded)";
+    case LMOE_EUNSUPPORTED: return "dimensions not supported";
+    default: return "unknown error code";
+  }
+}
+
+const char* lmoe_last_error(void) { return g_last_error.c_str(); }
+
+size_t lmoe_expert_record_bytes(int32_t latent, int32_t expert_ffn) {
+  size_t n = (size_t)latent * expert_ffn;
+  return 3 * (n / 2) + 3 * (n / 16) + 16;
+}
+
+size_t lmoe_du_matrix_bytes(int32_t rows, int32_t cols, int32_t du_bits) {
+  return (size_t)rows * cols * du_bits / 8 + (size_t)rows * (cols / 32) * 2;
+}
+
+int lmoe_pack_bf16(const float* src, size_t n, uint16_t* dst, void* stream) {
+  if ((!src || !dst) && n) {
+    set_error("lmoe_pack_bf16: NULL pointer");
+    return LMOE_EINVAL;
+  }
+  return pack_bf16_impl(src, n, dst, (hipStream_t)stream);
+}
+
+int lmoe_pack_blocks(const float* src, int32_t rows, int32_t cols, int32_t bits, uint8_t* dst,
+                     void* stream) {
+  if (!src || !dst || rows < 0 || cols < 0 || cols % 32 || (bits != 8 && bits != 4)) {
+    set_error("lmoe_pack_blocks: bad argument (cols % 32 == 0, bits 8 or 4)");
+    return LMOE_EINVAL;
+  }
+  return pack_blocks_impl(src, rows, cols, bits, dst, (hipStream_t)stream);
+}
+
+int lmoe_pack_expert_records(const float* gate, const float* up, const float* down, int32_t n,
+                             int32_t latent, int32_t ffn, uint8_t* dst, void* stream) {
+  if (!gate || !up || !down || !dst || n < 0 || latent <= 0 || ffn <= 0 ||
+      ((size_t)latent * ffn) % 256) {
+    set_error("lmoe_pack_expert_records: bad argument (latent*ffn % 256 == 0)");
+    return LMOE_EINVAL;
+  }
+  return pack_experts_impl(gate, up, down, n, latent, ffn, dst, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,164 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Bit-exact: top-K indices, the group permutation, expert counts and group
+offsets. Within the spec bar: y (relative L2 <= 1e-3 and max-abs <=
+1e-2 * rms(y)); routing weights and latents are held to a far tighter bound
+because the path computes in fp32 / fp64 throughout."""
+
+import sys
+
+import numpy as np
+import pytest
+
+from cases import Case, assert_close, rel_errors
+from latent_mixture_experts_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _lmoe():
+    from latent_mixture_experts_amd import lmoe
+    return lmoe
+
+
+def make_layer(case, max_tokens=8):
+    lm = _lmoe()
+    w = case.w
+    layer = lm.Layer(w.hidden, w.latent, w.n_experts, w.top_k, w.n_groups, w.expert_ffn,
+                     w.shared_ffn, w.du_bits, max_tokens, has_router_bias=w.router_bias)
+    layer.load(case.blobs)
+    return layer
+
+
+def run(layer, case, T):
+    w = case.w
+    dev = "cuda"
+    x = torch.from_numpy(np.ascontiguousarray(case.x[:T])).to(dev)
+    y = torch.empty(T, w.hidden, device=dev, dtype=torch.float32)
+    dbg = dict(
+        topk_idx=torch.empty(T, w.top_k, dtype=torch.int32, device=dev),
+        topk_w=torch.empty(T, w.top_k, dtype=torch.float32, device=dev),
+        perm=torch.empty(T * w.top_k, dtype=torch.int32, device=dev),
+        expert_count=torch.empty(w.n_experts, dtype=torch.int32, device=dev),
+        group_off=torch.empty(w.n_groups + 1, dtype=torch.int32, device=dev),
+        latent=torch.full((T, w.n_groups, w.latent), float("nan"), device=dev),
+    )
+    layer.forward(x, y, debug=dbg)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), {k: v.cpu().numpy() for k, v in dbg.items()}
+
+
+def check(case, layer, T, label):
+    print("case", label, "T", T, flush=True)
+    got, dbg = run(layer, case, T)
+    r = case.expect(T)
+    assert np.array_equal(dbg["topk_idx"], r["idx"]), "top-K indices differ"
+    assert np.array_equal(dbg["perm"], r["perm"]), "permutation differs"
+    assert np.array_equal(dbg["expert_count"], r["expert_count"])
+    assert np.array_equal(dbg["group_off"], r["group_off"])
+    assert np.max(np.abs(dbg["topk_w"] - r["w"])) <= 1e-6
+    used = r["used"]
+    rel, _ = rel_errors(dbg["latent"][used], r["xl"][used])
+    assert rel <= 1e-5, "latent D x relative error %.3g" % rel
+    rel, mx = assert_close(got, r["y"], "y")
+    rel_r, _ = rel_errors(got - r["y_shared"], r["y_routed"])
+    print("  y rel L2 %.3g max/rms %.3g; routed part rel L2 %.3g" % (rel, mx, rel_r), flush=True)
+    assert rel_r <= 1e-4, "routed part relative error %.3g" % rel_r
+    return got
+
+
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def tiny():
+    c = Case(wl.WORKLOADS["tiny"], tokens=8)
+    return c, make_layer(c)
+
+
+@pytest.mark.parametrize("T", range(1, 9))
+def test_tiny_all_token_counts(tiny, T):
+    case, layer = tiny
+    check(case, layer, T, "tiny")
+
+
+def test_tiny_repeatable_bitwise(tiny):
+    case, layer = tiny
+    a, da = run(layer, case, 4)
+    b, db = run(layer, case, 4)
+    assert np.array_equal(a, b) and all(np.array_equal(da[k], db[k]) for k in da if k != "latent")
+
+
+@pytest.fixture(scope="module")
+def l145():
+    c = Case(wl.WORKLOADS["145b_decode"], tokens=8)
+    return c, make_layer(c)
+
+
+@pytest.mark.parametrize("T", [4, 1, 5, 8])
+def test_145b_decode(l145, T):
+    case, layer = l145
+    check(case, layer, T, "145b_decode")
+
+
+@pytest.fixture(scope="module")
+def l120():
+    c = Case(wl.WORKLOADS["120b_decode"], tokens=8)
+    return c, make_layer(c)
+
+
+@pytest.mark.parametrize("T", [5, 2, 7])
+def test_120b_decode(l120, T):
+    case, layer = l120
+    check(case, layer, T, "120b_decode")
+
+
+def test_same_token_repeated_shares_experts():
+    """All tokens identical: every routed expert serves T tokens at once."""
+    w = wl.WORKLOADS["tiny"]
+    x = np.repeat(wl.x(w, 3, tokens=1), 8, axis=0)
+    c = Case(w, seed=3, x=x)
+    layer = make_layer(c)
+    check(c, layer, 8, "tiny repeated token")
+
+
+def test_exact_ties_break_to_lower_index():
+    """Integer-valued x and router rows make every logit an exact integer, so
+    ties are exact on both sides; the lower expert index must win."""
+    w = wl.WORKLOADS["tiny"]
+    m = wl.masters(w, seed=5)
+    rng = np.random.default_rng(5)
+    m["router"] = rng.integers(-1, 2, (w.n_experts, w.hidden)).astype(np.float32)
+    m["router"][8:] = m["router"][:8]                  # duplicate rows: exact ties
+    x = rng.integers(-1, 2, (6, w.hidden)).astype(np.float32)
+    x[5] = 0.0                                         # all logits tie at zero
+    c = Case(w, seed=5, x=x, masters=m)
+    layer = make_layer(c)
+    check(c, layer, 6, "tiny exact ties")
+
+
+def test_argument_errors_on_device():
+    lm = _lmoe()
+    c = Case(wl.WORKLOADS["tiny"], tokens=4)
+    layer = make_layer(c, max_tokens=4)
+    x = torch.zeros(8, 256, device="cuda")
+    y = torch.zeros(8, 256, device="cuda")
+    with pytest.raises(lm.LmoeError) as e:
+        layer.forward(x, y, T=5)
+    assert e.value.code == lm.EINVAL
+    with pytest.raises(lm.LmoeError) as e:
+        layer.forward(x, y, T=0)
+    assert e.value.code == lm.EINVAL
+    with pytest.raises(lm.LmoeError) as e:
+        layer.forward(x, x, T=2)
+    assert e.value.code == lm.EINVAL
+    fresh = lm.Layer(256, 128, 16, 2, 2, 64, 64, 8, 4)
+    with pytest.raises(lm.LmoeError) as e:
+        fresh.forward(x, y, T=1)
+    assert e.value.code == lm.ESTATE
+    bad = dict(c.blobs)
+    bad["labels"] = np.full(16, 2, np.uint8)
+    with pytest.raises(lm.LmoeError) as e:
+        fresh.load(bad)
+    assert e.value.code == lm.EINVAL
