@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_145b_t4_traffic.json")
 
 
 def log(*a):
@@ -90,6 +91,23 @@ def phase_bytes(w, idx, labels):
     p3 = distinct * L * F * fp4 + T * K * (F + L) * 4
     p4 = used_groups * H * L * du + H * Fs * 2 + T * (G * L + Fs + H) * 4
     return [p1, p2, p3, p4], distinct, used_groups
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when there is none or the kernel source has changed
+    since the counters were taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        src = open(os.path.join(ROOT, t["source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if t.get("workload") != workload or hashlib.sha256(src).hexdigest() != t["source_sha256"]:
+        return None
+    k = t["kernels"].get(kernel)
+    return None if k is None else k["traffic_bytes"]
 
 
 def cpu_baseline(w, seed, tokens):
@@ -227,7 +245,8 @@ def main():
                    "forward_algorithmic_bytes": total_bytes,
                    "forward_GBps": total_bytes / (ms * 1e-3) / 1e9},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("k_phase%d" % (dom + 1), w.name),
                      "kernel": "k_phase%d" % (dom + 1),
                      "kernel_us": phase_avg[dom] * 1e3,
                      "kernel_algorithmic_bytes": pbytes[dom]},

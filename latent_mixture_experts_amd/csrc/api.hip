@@ -38,6 +38,7 @@ int check_dims(const lmoe_dims& d) {
   if (d.hidden % 256) return unsup("hidden must be a multiple of 256");
   if (d.latent % 64) return unsup("latent must be a multiple of 64");
   if (d.expert_ffn % 32 || d.shared_ffn % 32) return unsup("expert_ffn and shared_ffn must be multiples of 32");
+  if (d.du_bits == 4 && d.latent % 128) return unsup("Q4 D/U needs latent % 128 == 0");
   if (d.hidden > 4096 || d.latent > 4096 || d.expert_ffn > 4096 || d.shared_ffn > 4096)
     return unsup("widths above 4096");
   if (d.n_experts > 1024 || d.top_k > 64 || d.n_groups > 64)
@@ -68,7 +69,7 @@ int create_impl(lmoe_t* h) {
   const int E = d.n_experts, H = d.hidden, L = d.latent, G = d.n_groups, F = d.expert_ffn,
             Fs = d.shared_ffn, K = d.top_k;
   const int du = d.du_bits == 8 ? kQ8 : kQ4;
-  h->g_router = make_geom(kBF16, E, H);
+  h->g_router = make_geom(kBF16R, E, H);
   h->g_d = make_geom(du, L, H);
   h->g_u = make_geom(du, H, L);
   h->g_gu = make_geom(kFP4, 2 * F, L);   // tiles of 32 gate + 32 up rows
@@ -96,11 +97,11 @@ int create_impl(lmoe_t* h) {
   const int Epad = h->g_router.tiles * 64;
   const int n = T * K;
   A(w.part64, sizeof(double) * w.nch * T * Epad);
-  A(w.logits, sizeof(double) * T * E);
   A(w.topk_idx, sizeof(int) * n);
   A(w.topk_w, sizeof(float) * n);
   A(w.perm, sizeof(int) * n);
-  A(w.inv, sizeof(int) * n);
+  A(w.tg_cnt, sizeof(int) * T * G);
+  A(w.tg_pos, sizeof(int) * T * G * K);
   A(w.slot_expert, sizeof(int) * n);
   A(w.slot_start, sizeof(int) * n);
   A(w.slot_count, sizeof(int) * n);

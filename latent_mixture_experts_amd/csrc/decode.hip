@@ -1,5 +1,5 @@
-// Decode / speculative-verify forward (T <= 8 tokens): four launches of
-// dequant-in-register GEMVs over the tiled weight streams.
+// Decode / speculative-verify forward (T <= 8 tokens): four launches built on
+// a small-batch GEMV that runs its multiply-adds on the matrix cores.
 //
 // Layer ("Edge0-145B: a Qwen MoE with its experts squeezed, and a 51B table
 // left on the SSD", section "A latent in front of the experts", the layer
@@ -18,12 +18,16 @@
 //   phase 4  U_g over the per-group sums and the shared-expert down; the last
 //            block of each 64-row tile of y adds the partials in a fixed order
 //
-// Every weight byte is read once per forward with 16-byte lane loads that
-// form 1 KiB coalesced requests; activations are read through the scalar
-// data path (uniform addresses), so the vector ALUs only decode and multiply.
-// Cross-block steps use the "last block" pattern (release fence, counter,
-// acquire fence); counters are reset by the block that consumes them, so
-// forwards need no memset and the result is bit-reproducible.
+// GEMV core: a wavefront takes one super-step (256 columns) of one 64-row
+// tile. It reads the weights once with nontemporal 16-byte lane loads
+// (1 KiB coalesced per slot), decodes them in registers to fp16 (Q8, Q4,
+// NVFP4 with its E4M3 block scale folded in exactly) or uses bf16 as is, and
+// multiplies them on v_mfma_f32_16x16x32_{f16,bf16} with the tokens on the
+// M side (up to 16 tokens cost the same). Activations are split exactly
+// enough to keep fp32 accuracy: fp16 hi + lo (22 bits) against fp16
+// weights, three bf16 parts (exact) against bf16 weights. At T = 4 this
+// leaves the vector ALUs about 24 instructions per KiB of weights, so the
+// kernels are bound by HBM, not by decode arithmetic.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -35,11 +39,21 @@ namespace {
 typedef const __attribute__((address_space(4))) float* cf_t;     // uniform, read-only
 typedef const __attribute__((address_space(4))) int* ci_t;
 typedef const __attribute__((address_space(4))) uint8_t* cu8_t;
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ cf_t cf(const float* p) { return (cf_t)p; }
 __device__ __forceinline__ ci_t ci(const int* p) { return (ci_t)p; }
 
 __device__ __forceinline__ uint4 ldw(const uint8_t* p) { return *(const uint4*)p; }
+// weights are read once per forward: stream them past the caches
+__device__ __forceinline__ uint4 ldnt(const uint8_t* p) {
+  const u4v v = __builtin_nontemporal_load((const u4v*)p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 __device__ __forceinline__ float h2f(uint32_t bits) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFFFu));
@@ -49,169 +63,272 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
 
+constexpr int kXStr = 264;        // staged activation row: 256 columns + 8 pad (halves)
+
 // ---------------------------------------------------------------------------
-// One wavefront, one super-step (up to 256 columns) of one 64-row tile.
-// p points at the lane's 16 bytes of the super-step's first slot; xv[t] at
-// column 0 of the super-step in input vector t; ncs = code slots present.
-// acc[t] += sum over the super-step of row(lane) . xv[t].
+// MFMA A operand: the token vectors of one super-step, staged per wavefront.
 
 template <int NT>
-__device__ __forceinline__ void ss_q8(const uint8_t* p, int ncs, const cf_t (&xv)[NT],
-                                      float (&acc)[NT]) {
-  uint4 q[16];
+struct XRegs {
+  float4 v[NT];
+};
+
+// Lane l loads columns 4l..4l+3 of each of the n valid vectors (0 beyond).
+template <int NT>
+__device__ __forceinline__ void x_load(XRegs<NT>& r, const float* const (&src)[NT], int n,
+                                       int cols, int lane) {
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
-    if (j < ncs) q[j] = ldw(p + j * kSlot);
-  const uint4 sc = ldw(p + ncs * kSlot);
-  const uint32_t s4[4] = {sc.x, sc.y, sc.z, sc.w};
+  for (int i = 0; i < NT; ++i) {
+    r.v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < n && 4 * lane < cols) r.v[i] = *(const float4*)(src[i] + 4 * lane);
+  }
+}
+
+// fp16 hi/lo parts: xs[part][i][col], part 0 = hi, 1 = lo.
+template <int NT>
+__device__ __forceinline__ void x_stage_f16(const XRegs<NT>& r, _Float16* xs, int lane) {
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    if (2 * b < ncs) {
-      float blk[NT];
+  for (int i = 0; i < NT; ++i) {
+    const float v[4] = {r.v[i].x, r.v[i].y, r.v[i].z, r.v[i].w};
 #pragma unroll
-      for (int t = 0; t < NT; ++t) blk[t] = 0.f;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const uint4 w = q[2 * b + hh];
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float v = (float)(int8_t)(ww[i] >> (8 * j));
-            const int c = 32 * b + 16 * hh + 4 * i + j;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) blk[t] = __builtin_fmaf(v, xv[t][c], blk[t]);
-          }
-      }
-      const float d = h2f(s4[b >> 1] >> (16 * (b & 1)));
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t] = __builtin_fmaf(d, blk[t], acc[t]);
+    for (int j = 0; j < 4; ++j) {
+      const _Float16 hi = (_Float16)v[j];
+      xs[(0 * NT + i) * kXStr + 4 * lane + j] = hi;
+      xs[(1 * NT + i) * kXStr + 4 * lane + j] = (_Float16)(v[j] - (float)hi);
     }
   }
 }
 
-// Q4: each code slot is one block of 32 signed 4-bit codes (element 2m in the
-// low nibble of byte m). Shifting a nibble into the top of a byte gives 16*q
-// as an int8; the 1/16 folds into the block scale.
+// Three bf16 parts whose sum is the fp32 value exactly.
 template <int NT>
-__device__ __forceinline__ void ss_q4(const uint8_t* p, int ncs, const cf_t (&xv)[NT],
-                                      float (&acc)[NT]) {
-  uint4 q[8];
+__device__ __forceinline__ void x_stage_bf16(const XRegs<NT>& r, __bf16* xs, int lane) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (j < ncs) q[j] = ldw(p + j * kSlot);
-  const uint4 sc = ldw(p + ncs * kSlot);
-  const uint32_t s4[4] = {sc.x, sc.y, sc.z, sc.w};
+  for (int i = 0; i < NT; ++i) {
+    const float v[4] = {r.v[i].x, r.v[i].y, r.v[i].z, r.v[i].w};
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    if (b < ncs) {
-      float blk[NT];
+    for (int j = 0; j < 4; ++j) {
+      const __bf16 b1 = (__bf16)v[j];
+      const float r1 = v[j] - (float)b1;
+      const __bf16 b2 = (__bf16)r1;
+      const __bf16 b3 = (__bf16)(r1 - (float)b2);
+      xs[(0 * NT + i) * kXStr + 4 * lane + j] = b1;
+      xs[(1 * NT + i) * kXStr + 4 * lane + j] = b2;
+      xs[(2 * NT + i) * kXStr + 4 * lane + j] = b3;
+    }
+  }
+}
+
+template <int NT, typename E, typename V>
+__device__ __forceinline__ V a_read(const E* xs, int part, int tok, int n, int col) {
+  V z = {};
+  return tok < n ? *(const V*)(xs + (part * NT + tok) * kXStr + col) : z;
+}
+
+// ---------------------------------------------------------------------------
+// Weight decoding to MFMA B operands (8 values of one row).
+
+// Q8 codes held offset-binary (q + 128): fp16 bits 0x6400 | u = 1024 + u,
+// then minus 1152 gives q exactly.
+__device__ __forceinline__ half8 dec_q8(uint32_t w0, uint32_t w1) {
+  const half2v off = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const uint32_t d[4] = {__builtin_amdgcn_perm(0x64646464u, w0, 0x05010400u),
+                         __builtin_amdgcn_perm(0x64646464u, w0, 0x05030402u),
+                         __builtin_amdgcn_perm(0x64646464u, w1, 0x05010400u),
+                         __builtin_amdgcn_perm(0x64646464u, w1, 0x05030402u)};
+  half8 r;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) blk[t] = 0.f;
-      const uint32_t ww[4] = {q[b].x, q[b].y, q[b].z, q[b].w};
+  for (int i = 0; i < 4; ++i) {
+    const half2v h = __builtin_bit_cast(half2v, d[i]) - off;
+    r[2 * i] = h[0];
+    r[2 * i + 1] = h[1];
+  }
+  return r;
+}
+
+// Q4: 8 offset-binary nibbles (q + 8); the device keeps element i in the low
+// nibble of byte i and element i + 4 in its high nibble.
+__device__ __forceinline__ half8 dec_q4(uint32_t w) {
+  const half2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  const uint32_t d[4] = {__builtin_amdgcn_perm(0x64646464u, lo, 0x05010400u),
+                         __builtin_amdgcn_perm(0x64646464u, lo, 0x05030402u),
+                         __builtin_amdgcn_perm(0x64646464u, hi, 0x05010400u),
+                         __builtin_amdgcn_perm(0x64646464u, hi, 0x05030402u)};
+  half8 r;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = (ww[i] << 4) & 0xF0F0F0F0u;   // elements 8i + 0, 2, 4, 6
-        const uint32_t hi = ww[i] & 0xF0F0F0F0u;          // elements 8i + 1, 3, 5, 7
+  for (int i = 0; i < 4; ++i) {
+    const half2v h = __builtin_bit_cast(half2v, d[i]) - off;
+    r[2 * i] = h[0];
+    r[2 * i + 1] = h[1];
+  }
+  return r;
+}
+
+// NVFP4: 8 E2M1 codes (element 2i in the low nibble of byte i) times their
+// E4M3 block scale; e2m1 * e4m3 needs at most 6 significant bits and lies in
+// [2^-10, 2688], so the fp16 product is exact.
+__device__ __forceinline__ half8 dec_fp4(uint32_t w, _Float16 s) {
+  const half2v ss = {s, s};
+  const half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
+  const half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
+  const half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
+  const half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
+  half8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// ---------------------------------------------------------------------------
+// One wavefront, one super-step of one 64-row tile (4 row groups of 16).
+//
+// Slot j of the super-step holds chunk j/4 of row group j%4; lane l owns row
+// l%16 of the group and k-group l/16 of each 32-column block. The scale slot
+// (scaled formats) holds, at lane-chunk 16*rg + r, the scales of row r of
+// group rg. On return acc[rg] holds, in lane l, rows 16rg + l%16 for tokens
+// 4(l/16) + 0..3 (the MFMA D layout).
+//
+// xs: this wave's staging area; src[i]: vector i at the super-step's first
+// column; n: valid vectors; ncs: code slots present.
+template <int FMT, int NT>
+__device__ __forceinline__ void wave_ss(const uint8_t* p, int ncs, int cols,
+                                        const float* const (&src)[NT], int n, void* xs,
+                                        int lane, f4 (&acc)[4]) {
+  constexpr int CC = FMT == kQ8 ? 64 : (FMT == kBF16 ? 32 : 128);   // columns per chunk
+  constexpr int MAXCH = kSSCols / CC;
+  constexpr int NSL = 4 * MAXCH;
+  const int tok = lane & 15, qg = lane >> 4;
+
+  // activations first, then scales, then the weight stream: loads are
+  // counted in order, so the staging waits only for its own data
+  XRegs<NT> xr;
+  x_load<NT>(xr, src, n, cols, lane);
+  uint4 sc[4];
+  if (FMT != kBF16) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float v0 = (float)(int8_t)(lo >> (8 * j));
-          const float v1 = (float)(int8_t)(hi >> (8 * j));
-          const int c = 32 * b + 8 * i + 2 * j;
+    for (int rg = 0; rg < 4; ++rg) sc[rg] = ldw(p + ncs * kSlot + (rg * 16 + tok) * 16);
+  }
+  uint4 q[NSL];
 #pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            blk[t] = __builtin_fmaf(v0, xv[t][c], blk[t]);
-            blk[t] = __builtin_fmaf(v1, xv[t][c + 1], blk[t]);
+  for (int j = 0; j < NSL; ++j)
+    if (j < ncs) q[j] = ldnt(p + j * kSlot + lane * 16);
+
+  if (FMT == kBF16) x_stage_bf16<NT>(xr, (__bf16*)xs, lane);
+  else x_stage_f16<NT>(xr, (_Float16*)xs, lane);
+  __builtin_amdgcn_wave_barrier();
+
+  const int nch = ncs / 4;
+#pragma unroll
+  for (int c = 0; c < MAXCH; ++c) {
+    if (c >= nch) break;
+    if constexpr (FMT == kBF16) {
+      const __bf16* x = (const __bf16*)xs;
+      const int col = CC * c + 8 * qg;
+      const bf16x8 a0 = a_read<NT, __bf16, bf16x8>(x, 0, tok, n, col);
+      const bf16x8 a1 = a_read<NT, __bf16, bf16x8>(x, 1, tok, n, col);
+      const bf16x8 a2 = a_read<NT, __bf16, bf16x8>(x, 2, tok, n, col);
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, q[4 * c + rg]);
+        acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc[rg], 0, 0, 0);
+        acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc[rg], 0, 0, 0);
+        acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, b, acc[rg], 0, 0, 0);
+      }
+    } else {
+      constexpr int NB = CC / 32;                      // 32-column blocks per chunk
+      const _Float16* x = (const _Float16*)xs;
+      half8 ah[NB], al[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int col = CC * c + 32 * b + 8 * qg;
+        ah[b] = a_read<NT, _Float16, half8>(x, 0, tok, n, col);
+        al[b] = a_read<NT, _Float16, half8>(x, 1, tok, n, col);
+      }
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const uint4 w = q[4 * c + rg];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          if constexpr (FMT == kFP4) {
+            // block of 16 columns holding this lane's 8: 8c + 2b + qg/2
+            const int k = 4 * c + b;                     // scale half-word index
+            const uint32_t sb = (word(sc[rg], k >> 1) >> (16 * (k & 1) + 8 * (qg >> 1))) & 0xFFu;
+            const _Float16 s = (_Float16)__builtin_amdgcn_cvt_f32_fp8(sb, 0);
+            const half8 bw = dec_fp4(word(w, b), s);
+            acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[b], bw, acc[rg], 0, 0, 0);
+            acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[b], bw, acc[rg], 0, 0, 0);
+          } else {
+            const half8 bw = FMT == kQ8 ? dec_q8(word(w, 2 * b), word(w, 2 * b + 1))
+                                        : dec_q4(word(w, b));
+            f4 d = {0.f, 0.f, 0.f, 0.f};
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[b], bw, d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[b], bw, d, 0, 0, 0);
+            const int blk = NB * c + b;                  // fp16 scale of this 32-column block
+            const float s = h2f(word(sc[rg], blk >> 1) >> (16 * (blk & 1)));
+            acc[rg] += s * d;
           }
         }
       }
-      const float d = h2f(s4[b >> 1] >> (16 * (b & 1))) * 0.0625f;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t] = __builtin_fmaf(d, blk[t], acc[t]);
     }
   }
 }
 
-// NVFP4: each code slot is 32 E2M1 codes = two scale blocks of 16; the scale
-// slot holds 16 E4M3 bytes. The gfx950 converters decode two E2M1 values of
-// one byte (low nibble first) and two E4M3 values of one half-word.
+// Sum the per-wave MFMA accumulators of the block in wave order into wave 0.
+// Only lane groups holding tokens < NT are exchanged. Returns true on wave 0.
 template <int NT>
-__device__ __forceinline__ void ss_fp4(const uint8_t* p, int ncs, const cf_t (&xv)[NT],
-                                       float (&acc)[NT]) {
-  uint4 q[8];
+__device__ __forceinline__ bool block_reduce_mf(f4 (&acc)[4], f4* red, int wave, int lane, int nw) {
+  constexpr int LN = 16 * ((NT + 3) / 4);
+  if (lane < LN) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (j < ncs) q[j] = ldw(p + j * kSlot);
-  const uint4 sc = ldw(p + ncs * kSlot);
-  const uint32_t s4[4] = {sc.x, sc.y, sc.z, sc.w};
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j < ncs) {
-      const uint32_t ww[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
-      // scale bytes 2j and 2j+1 live in word j/2, half (j&1)
-      const auto sf = (j & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(s4[j >> 1], true)
-                              : __builtin_amdgcn_cvt_pk_f32_fp8(s4[j >> 1], false);
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        float blk[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) blk[t] = 0.f;
-#pragma unroll
-        for (int i = 2 * hb; i < 2 * hb + 2; ++i) {
-#define LMOE_FP4_BYTE(m)                                                               \
-  {                                                                                    \
-    const auto f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ww[i], 1.0f, m);          \
-    const int c = 32 * j + 8 * i + 2 * (m);                                            \
-    _Pragma("unroll") for (int t = 0; t < NT; ++t) {                                   \
-      blk[t] = __builtin_fmaf(f2[0], xv[t][c], blk[t]);                                \
-      blk[t] = __builtin_fmaf(f2[1], xv[t][c + 1], blk[t]);                            \
-    }                                                                                  \
+    for (int rg = 0; rg < 4; ++rg) red[(wave * 4 + rg) * LN + lane] = acc[rg];
   }
-          LMOE_FP4_BYTE(0)
-          LMOE_FP4_BYTE(1)
-          LMOE_FP4_BYTE(2)
-          LMOE_FP4_BYTE(3)
-#undef LMOE_FP4_BYTE
-        }
-        const float s = hb ? sf[1] : sf[0];
+  __syncthreads();
+  if (wave != 0) return false;
+  if (lane < LN) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = __builtin_fmaf(s, blk[t], acc[t]);
-      }
+    for (int rg = 0; rg < 4; ++rg) {
+      f4 s = red[rg * LN + lane];
+      for (int w = 1; w < nw; ++w) s += red[(w * 4 + rg) * LN + lane];
+      acc[rg] = s;
     }
   }
+  return true;
 }
 
-// bf16 rows, fp32 accumulation; a super-step has up to 32 code slots, taken
-// in two halves of 16 to bound live registers.
-template <int NT>
-__device__ __forceinline__ void ss_bf16(const uint8_t* p, int ncs, const cf_t (&xv)[NT],
-                                        float (&acc)[NT]) {
+template <int NT, typename V>
+__device__ __forceinline__ bool block_reduce(V (&acc)[NT], V* red, int wave, int lane, int nwaves) {
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    uint4 q[16];
+  for (int t = 0; t < NT; ++t) red[(wave * NT + t) * 64 + lane] = acc[t];
+  __syncthreads();
+  if (wave != 0) return false;
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (16 * half + j < ncs) q[j] = ldw(p + (16 * half + j) * kSlot);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (16 * half + j < ncs) {
-        const uint32_t ww[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v0 = __uint_as_float(ww[i] << 16);
-          const float v1 = __uint_as_float(ww[i] & 0xFFFF0000u);
-          const int c = 8 * (16 * half + j) + 2 * i;
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            acc[t] = __builtin_fmaf(v0, xv[t][c], acc[t]);
-            acc[t] = __builtin_fmaf(v1, xv[t][c + 1], acc[t]);
-          }
-        }
-      }
-    }
+  for (int t = 0; t < NT; ++t) {
+    V s = red[t * 64 + lane];
+    for (int w = 1; w < nwaves; ++w) s += red[(w * NT + t) * 64 + lane];
+    acc[t] = s;
   }
+  return true;
 }
+
+// Pointer to super-step `ss` of tile `tile` (lane offset not included).
+__device__ __forceinline__ const uint8_t* ss_ptr(const uint8_t* base, const Geom& g, int tile,
+                                                 int ss) {
+  return base + ((size_t)tile * g.tile_slots + (size_t)ss * g.full) * kSlot;
+}
+__device__ __forceinline__ int ss_cols(const Geom& g, int ss) { return min(kSSCols, g.k - ss * kSSCols); }
+__device__ __forceinline__ int ss_codes(int fmt, const Geom& g, int ss) {
+  return ss_code_slots(fmt, ss_cols(g, ss));
+}
+
+// LDS bytes of one wave's staging area, and of the MFMA reduction.
+template <int NT>
+constexpr int stage_bytes() { return 3 * NT * kXStr * 2; }
+template <int NT>
+constexpr int red_bytes_per_wave() { return 4 * 16 * ((NT + 3) / 4) * 16; }
 
 // Router: bf16 rows, fp64 products and sums, over a chunk of `nslot` (<= 8)
 // slots of 8 columns.
@@ -242,54 +359,33 @@ __device__ __forceinline__ void chunk_bf16_f64(const uint8_t* p, int nslot, cons
 }
 
 // D/U matrices: Q8 or Q4 (uniform branch on the handle's format).
-template <int NT>
-__device__ __forceinline__ void ss_du(int fmt, const uint8_t* p, int ncs, const cf_t (&xv)[NT],
-                                      float (&acc)[NT]) {
-  if (fmt == kQ8) ss_q8<NT>(p, ncs, xv, acc);
-  else ss_q4<NT>(p, ncs, xv, acc);
+// Data handed from one block to another inside a kernel goes through
+// coherent agent-scope accesses (they bypass the non-coherent cache levels
+// of the XCDs), so no cache writeback or invalidation is needed.
+template <typename V>
+__device__ __forceinline__ void st_co(V* p, V v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename V>
+__device__ __forceinline__ V ld_co(const V* p) {
+  return __hip_atomic_load((V*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Pointer to lane `lane`'s bytes of super-step `ss` of tile `tile`.
-__device__ __forceinline__ const uint8_t* tile_ptr(const uint8_t* base, const Geom& g, int tile,
-                                                   int ss, int lane) {
-  return base + ((size_t)tile * g.tile_slots + (size_t)ss * g.full) * kSlot + lane * 16;
-}
-__device__ __forceinline__ int ss_codes(int fmt, const Geom& g, int ss) {
-  return min(kSSCols, g.k - ss * kSSCols) / cols_per_slot(fmt);
-}
-
-// Sum the per-wave partials acc[t] of the block in wave order into wave 0.
-// red: nwaves * NT * 64 floats of LDS. Returns true on wave 0.
-template <int NT, typename V>
-__device__ __forceinline__ bool block_reduce(V (&acc)[NT], V* red, int wave, int lane, int nwaves) {
-#pragma unroll
-  for (int t = 0; t < NT; ++t) red[(wave * NT + t) * 64 + lane] = acc[t];
-  __syncthreads();
-  if (wave != 0) return false;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    V s = red[t * 64 + lane];
-    for (int w = 1; w < nwaves; ++w) s += red[(w * NT + t) * 64 + lane];
-    acc[t] = s;
-  }
-  return true;
-}
-
-// Last-block protocol: every thread's global writes are released before one
-// thread bumps the counter; the block that brings it to `expect` acquires and
-// resets it.
+// Last-block protocol: each block waits until its coherent stores have
+// completed, then one thread bumps the counter; the block that brings it to
+// `expect` goes on (and resets the counter for the next forward).
 __device__ __forceinline__ bool arrive_last(unsigned* ctr, unsigned expect, int* flag) {
-  __threadfence();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    unsigned old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = (old + 1 == expect);
-    if (old + 1 == expect) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old + 1 == expect;
+    *flag = last;
+    if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  bool last = *flag != 0;
-  if (last) __threadfence();
-  return last;
+  return *flag != 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -297,7 +393,6 @@ __device__ __forceinline__ bool arrive_last(unsigned* ctr, unsigned expect, int*
 
 struct Dims {
   int T, H, L, E, K, G, F, Fs;
-  int du_fmt;
 };
 
 struct P1 {
@@ -347,41 +442,68 @@ __device__ void routing(const P1& a, char* smem) {
   const int tid = threadIdx.x, nth = blockDim.x, lane = tid & 63, wave = tid >> 6;
   const int nw = nth >> 6;
   const int Epad = a.gr.tiles * 64;
+  const int n = T * d.K;
+  double* lg = (double*)smem;      // [T][E] logits
+  int* key = (int*)(lg + T * d.E); // [n] label * E + expert, assignment order
+  int* sperm = key + n;            // [n]
+  int* start = sperm + n;          // [n]
+  int* inv = start + n;            // [n]
+  int* slab = inv + n;             // [n] label at each sorted position
 
-  // logits = sum of chunk partials in chunk order (+ bias)
-  for (int i = tid; i < T * d.E; i += nth) {
-    int t = i / d.E, e = i % d.E;
-    double s = 0.0;
-    for (int c = 0; c < a.nch; ++c) s += ws.part64[((size_t)c * T + t) * Epad + e];
-    if (a.rms) s *= (double)a.rms[t];
-    s += (double)a.bias[e];
-    ws.logits[i] = s;
+  // logits = the chunk partials summed in chunk order (scaled by 1/rms in the
+  // block forward) + bias; every thread issues all its loads before summing
+  {
+    constexpr int U = 4;
+    const int total = T * d.E;
+    for (int base = 0; base < total; base += U * nth) {
+      double part[U][kRouterChunks];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = min(base + tid + u * nth, total - 1);
+        const int t = i / d.E, e = i % d.E;
+#pragma unroll
+        for (int c = 0; c < kRouterChunks; ++c)
+          part[u][c] = ld_co(ws.part64 + ((size_t)c * T + t) * Epad + e);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = base + tid + u * nth;
+        if (i < total) {
+          const int t = i / d.E, e = i % d.E;
+          double l = 0.0;
+#pragma unroll
+          for (int c = 0; c < kRouterChunks; ++c) l += part[u][c];
+          if (a.rms) l *= (double)a.rms[t];
+          lg[i] = l + (double)a.bias[e];
+        }
+      }
+    }
   }
   __syncthreads();
 
-  // top K per token, one wavefront per token: K rounds of a wave arg-max over
-  // (logit desc, expert asc); then the softmax of the kept logits
+  // Top K per token, one wavefront per token: K rounds of a wave arg-max over
+  // (logit desc, expert asc); lane k keeps the k-th winner; then the softmax
+  // of the kept logits.
   for (int t = wave; t < T; t += nw) {
     double v[16];
-    const int per = (d.E + 63) / 64;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      int e = lane + 64 * i;
-      v[i] = (i < per && e < d.E) ? ws.logits[t * d.E + e] : -INFINITY;
+      const int e = lane + 64 * i;
+      v[i] = e < d.E ? lg[t * d.E + e] : -INFINITY;
     }
-    double kept[64];
-    double l0 = 0.0;
+    double kv = -INFINITY, l0 = 0.0;
+    int ki = 0;
     for (int k = 0; k < d.K; ++k) {
       double bv = -INFINITY;
       int bi = 0x7FFFFFFF;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        int e = lane + 64 * i;
+        const int e = lane + 64 * i;
         if (v[i] > bv || (v[i] == bv && e < bi)) { bv = v[i]; bi = e; }
       }
       for (int o = 32; o > 0; o >>= 1) {
-        double ov = __shfl_xor(bv, o);
-        int oi = __shfl_xor(bi, o);
+        const double ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
         if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
       }
       if ((bi & 63) == lane) {
@@ -390,41 +512,38 @@ __device__ void routing(const P1& a, char* smem) {
           if (i == (bi >> 6)) v[i] = -INFINITY;
       }
       if (k == 0) l0 = bv;
-      if (lane == 0) ws.topk_idx[t * d.K + k] = bi;
-      if (k < 64) kept[k] = bv;
+      if (lane == k) { kv = bv; ki = bi; }
     }
-    if (lane == 0) {
-      double z = 0.0;
-      for (int k = 0; k < d.K; ++k) z += exp(kept[k] - l0);
-      for (int k = 0; k < d.K; ++k) ws.topk_w[t * d.K + k] = (float)(exp(kept[k] - l0) / z);
+    const double ex = lane < d.K ? exp(kv - l0) : 0.0;
+    double z = ex;
+    for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
+    if (lane < d.K) {
+      ws.topk_idx[t * d.K + lane] = ki;
+      ws.topk_w[t * d.K + lane] = (float)(ex / z);
+      key[t * d.K + lane] = (int)a.labels[ki] * d.E + ki;
     }
   }
   __syncthreads();
 
   // stable rank of each assignment by key (label, expert)
-  const int n = T * d.K;
-  int* key = (int*)smem;           // [n]
-  int* sperm = key + n;            // [n]
-  int* start = sperm + n;          // [n] slot start flags, then slot ids
   for (int i = tid; i < n; i += nth) {
-    int e = ws.topk_idx[i];
-    key[i] = (int)a.labels[e] * d.E + e;
-  }
-  __syncthreads();
-  for (int i = tid; i < n; i += nth) {
-    int ki = key[i], r = 0;
+    const int ki = key[i];
+    int r = 0;
     for (int j = 0; j < n; ++j) {
-      int kj = key[j];
+      const int kj = key[j];
       r += (kj < ki) || (kj == ki && j < i);
     }
     sperm[r] = i;
+    inv[i] = r;
     ws.perm[r] = i;
-    ws.inv[i] = r;
   }
   __syncthreads();
-  for (int j = tid; j < n; j += nth)
+  for (int j = tid; j < n; j += nth) {
     start[j] = (j == 0 || key[sperm[j]] != key[sperm[j - 1]]) ? 1 : 0;
+    slab[j] = key[sperm[j]] / d.E;
+  }
   __syncthreads();
+  // one slot per distinct expert, in (label, expert) order
   for (int j = tid; j < n; j += nth) {
     if (!start[j]) continue;
     int sid = 0;
@@ -435,7 +554,6 @@ __device__ void routing(const P1& a, char* smem) {
     ws.slot_start[sid] = j;
     ws.slot_count[sid] = end - j;
   }
-  __syncthreads();
   if (tid == 0) {
     int ns = 0;
     for (int j = 0; j < n; ++j) ns += start[j];
@@ -444,8 +562,7 @@ __device__ void routing(const P1& a, char* smem) {
   for (int g = tid; g <= d.G; g += nth) {
     int gs = 0, ga = 0;
     for (int j = 0; j < n; ++j) {
-      int lab = key[sperm[j]] / d.E;
-      if (lab < g) {
+      if (slab[j] < g) {
         ga += 1;
         gs += start[j];
       }
@@ -458,14 +575,24 @@ __device__ void routing(const P1& a, char* smem) {
     for (int j = 0; j < n; ++j) c += (key[j] % d.E) == e;
     ws.expert_count[e] = c;
   }
+  // for each (token, group): the sorted positions of its assignments, in
+  // ascending k (the order the per-group sum takes)
+  for (int q = tid; q < T * d.G; q += nth) {
+    const int t = q / d.G, g = q % d.G;
+    int c = 0;
+    for (int k = 0; k < d.K; ++k)
+      if (key[t * d.K + k] / d.E == g) ws.tg_pos[q * d.K + c++] = inv[t * d.K + k];
+    ws.tg_cnt[q] = c;
+  }
 }
+
 
 // ---------------------------------------------------------------------------
 // Phase 1: router | D_g | shared gate/up, by block index range.
 
-template <int T>
+template <int T, int DU>
 __global__ __launch_bounds__(1024) void k_phase1(P1 a) {
-  extern __shared__ char smem[];
+  extern __shared__ __align__(16) char smem[];
   const Dims& d = a.d;
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -474,7 +601,7 @@ __global__ __launch_bounds__(1024) void k_phase1(P1 a) {
   __shared__ int flag;
 
   if (b < a.nrb) {
-    // router: tile r, column chunk c; wave w covers 64 columns
+    // router: tile r, column chunk c; wave w covers 64 columns (fp64)
     const int r = b / a.nch, c = b % a.nch;
     const int col0 = c * a.cw + wave * 64;
     double acc[T];
@@ -488,100 +615,78 @@ __global__ __launch_bounds__(1024) void k_phase1(P1 a) {
       for (int t = 0; t < T; ++t) xv[t] = cf(a.x + (size_t)t * d.H + col0);
       chunk_bf16_f64<T>(p, nslot, xv, acc);
     }
-    double* red = (double*)smem;
-    if (block_reduce<T>(acc, red, wave, lane, nw)) {
+    if (block_reduce<T>(acc, (double*)smem, wave, lane, nw)) {
       const int Epad = a.gr.tiles * 64;
 #pragma unroll
-      for (int t = 0; t < T; ++t) a.ws.part64[((size_t)c * T + t) * Epad + r * 64 + lane] = acc[t];
+      for (int t = 0; t < T; ++t)
+        st_co(a.ws.part64 + ((size_t)c * T + t) * Epad + r * 64 + lane, acc[t]);
     }
     if (arrive_last(a.ws.ctr_router, (unsigned)a.nrb, &flag)) routing<T>(a, smem);
     return;
   }
 
-  float acc[T];
+  f4 acc[4];
 #pragma unroll
-  for (int t = 0; t < T; ++t) acc[t] = 0.f;
-  float* red = (float*)smem;
+  for (int rg = 0; rg < 4; ++rg) acc[rg] = (f4){0.f, 0.f, 0.f, 0.f};
+  char* xs = smem + wave * stage_bytes<T>();
+  f4* red = (f4*)(smem + nw * stage_bytes<T>());
+  const float* src[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) src[t] = a.x + (size_t)t * d.H + wave * kSSCols;
+
   if (b < a.nrb + a.ndb) {
     // D_g, tile r; wave = super-step
     const int i = b - a.nrb;
-    const int tiles = a.gd.tiles;
-    const int g = i / tiles, r = i % tiles;
-    if (wave < a.gd.nss) {
-      const uint8_t* base = a.dmat + (size_t)g * a.gd.bytes();
-      cf_t xv[T];
+    const int g = i / a.gd.tiles, r = i % a.gd.tiles;
+    if (wave < a.gd.nss)
+      wave_ss<DU, T>(ss_ptr(a.dmat + (size_t)g * a.gd.bytes(), a.gd, r, wave),
+                     ss_codes(DU, a.gd, wave), ss_cols(a.gd, wave), src, T, xs, lane, acc);
+    if (block_reduce_mf<T>(acc, red, wave, lane, nw)) {
 #pragma unroll
-      for (int t = 0; t < T; ++t) xv[t] = cf(a.x + (size_t)t * d.H + wave * kSSCols);
-      ss_du<T>(d.du_fmt, tile_ptr(base, a.gd, r, wave, lane), ss_codes(d.du_fmt, a.gd, wave),
-                     xv, acc);
-    }
-    if (block_reduce<T>(acc, red, wave, lane, nw)) {
+      for (int rg = 0; rg < 4; ++rg)
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        float v = acc[t];
-        if (a.rms) v *= a.rms[t];
-        a.ws.xl[((size_t)t * d.G + g) * d.L + r * 64 + lane] = v;
-      }
+        for (int v = 0; v < 4; ++v) {
+          const int t = 4 * (lane >> 4) + v;
+          if (t < T) {
+            float y = acc[rg][v];
+            if (a.rms) y *= a.rms[t];
+            a.ws.xl[((size_t)t * d.G + g) * d.L + r * 64 + rg * 16 + (lane & 15)] = y;
+          }
+        }
     }
     return;
   }
-  // shared gate/up pairs, tile r: lanes 0..31 gate rows, 32..63 up rows
+  // shared gate/up: row groups 0,1 hold gate rows, 2,3 the matching up rows
   const int r = b - a.nrb - a.ndb;
-  if (wave < a.gs.nss) {
-    cf_t xv[T];
+  if (wave < a.gs.nss)
+    wave_ss<kBF16, T>(ss_ptr(a.sgu, a.gs, r, wave), ss_codes(kBF16, a.gs, wave),
+                      ss_cols(a.gs, wave), src, T, xs, lane, acc);
+  if (block_reduce_mf<T>(acc, red, wave, lane, nw)) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) xv[t] = cf(a.x + (size_t)t * d.H + wave * kSSCols);
-    ss_bf16<T>(tile_ptr(a.sgu, a.gs, r, wave, lane), ss_codes(kBF16, a.gs, wave), xv, acc);
-  }
-  if (block_reduce<T>(acc, red, wave, lane, nw)) {
+    for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      float v = acc[t];
-      if (a.rms) v *= a.rms[t];
-      const float other = __shfl_xor(v, 32);
-      const int f = r * 32 + lane;
-      if (lane < 32 && f < d.Fs) a.ws.hs[(size_t)t * d.Fs + f] = silu(v) * other;
-    }
+      for (int v = 0; v < 4; ++v) {
+        const int t = 4 * (lane >> 4) + v;
+        const int f = r * 32 + rg * 16 + (lane & 15);
+        if (t < T && f < d.Fs) {
+          float gv = acc[rg][v], uv = acc[rg + 2][v];
+          if (a.rms) {
+            gv *= a.rms[t];
+            uv *= a.rms[t];
+          }
+          a.ws.hs[(size_t)t * d.Fs + f] = silu(gv) * uv;
+        }
+      }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Phase 2: routed-expert gate/up + SwiGLU.
-
-template <int NA>
-__device__ __forceinline__ void expert_gateup(const P2& a, int e, int g, int start, int r,
-                                              int wave, int lane, int nw, char* smem) {
-  const Dims& d = a.d;
-  float acc[NA];
-#pragma unroll
-  for (int i = 0; i < NA; ++i) acc[i] = 0.f;
-  const uint8_t* base = a.experts + (size_t)e * a.stride;
-  if (wave < a.ggu.nss) {
-    cf_t xv[NA];
-    ci_t perm = ci(a.ws.perm);
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int t = perm[start + i] / d.K;
-      xv[i] = cf(a.ws.xl + ((size_t)t * d.G + g) * d.L + wave * kSSCols);
-    }
-    ss_fp4<NA>(tile_ptr(base, a.ggu, r, wave, lane), ss_codes(kFP4, a.ggu, wave), xv, acc);
-  }
-  if (block_reduce<NA>(acc, (float*)smem, wave, lane, nw)) {
-    cf_t ts = cf((const float*)(base + a.ts_off));
-    const float s = lane < 32 ? ts[0] : ts[1];
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const float v = acc[i] * s;
-      const float other = __shfl_xor(v, 32);
-      const int f = r * 32 + lane;
-      if (lane < 32 && f < d.F) a.ws.hbuf[(size_t)(start + i) * d.F + f] = silu(v) * other;
-    }
-  }
-}
+// Phase 2: routed-expert gate/up + SwiGLU, one block per (slot, tile).
 
 template <int T>
 __global__ __launch_bounds__(1024) void k_phase2(P2 a) {
-  extern __shared__ char smem[];
+  extern __shared__ __align__(16) char smem[];
+  const Dims& d = a.d;
   const int tiles = a.ggu.tiles;
   const int j = blockIdx.x / tiles, r = blockIdx.x % tiles;
   ci_t ns = ci(a.ws.n_slots);
@@ -590,50 +695,42 @@ __global__ __launch_bounds__(1024) void k_phase2(P2 a) {
   const int e = ci(a.ws.slot_expert)[j], start = ci(a.ws.slot_start)[j];
   const int cnt = ci(a.ws.slot_count)[j];
   const int g = ((cu8_t)a.labels)[e];
-  switch (cnt) {
-    case 1: expert_gateup<1>(a, e, g, start, r, wave, lane, nw, smem); break;
-    case 2: if constexpr (T >= 2) expert_gateup<2>(a, e, g, start, r, wave, lane, nw, smem); break;
-    case 3: if constexpr (T >= 3) expert_gateup<3>(a, e, g, start, r, wave, lane, nw, smem); break;
-    case 4: if constexpr (T >= 4) expert_gateup<4>(a, e, g, start, r, wave, lane, nw, smem); break;
-    case 5: if constexpr (T >= 5) expert_gateup<5>(a, e, g, start, r, wave, lane, nw, smem); break;
-    case 6: if constexpr (T >= 6) expert_gateup<6>(a, e, g, start, r, wave, lane, nw, smem); break;
-    case 7: if constexpr (T >= 7) expert_gateup<7>(a, e, g, start, r, wave, lane, nw, smem); break;
-    default: if constexpr (T >= 8) expert_gateup<8>(a, e, g, start, r, wave, lane, nw, smem); break;
+  const uint8_t* base = a.experts + (size_t)e * a.stride;
+  ci_t perm = ci(a.ws.perm);
+  const float* src[T];
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    const int t = i < cnt ? perm[start + i] / d.K : 0;
+    src[i] = a.ws.xl + ((size_t)t * d.G + g) * d.L + wave * kSSCols;
+  }
+  f4 acc[4];
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg) acc[rg] = (f4){0.f, 0.f, 0.f, 0.f};
+  char* xs = smem + wave * stage_bytes<T>();
+  f4* red = (f4*)(smem + nw * stage_bytes<T>());
+  if (wave < a.ggu.nss)
+    wave_ss<kFP4, T>(ss_ptr(base, a.ggu, r, wave), ss_codes(kFP4, a.ggu, wave),
+                     ss_cols(a.ggu, wave), src, cnt, xs, lane, acc);
+  if (block_reduce_mf<T>(acc, red, wave, lane, nw)) {
+    cf_t ts = cf((const float*)(base + a.ts_off));
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int i = 4 * (lane >> 4) + v;
+        const int f = r * 32 + rg * 16 + (lane & 15);
+        if (i < cnt && f < d.F)
+          a.ws.hbuf[(size_t)(start + i) * d.F + f] = silu(acc[rg][v] * ts[0]) * (acc[rg + 2][v] * ts[1]);
+      }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Phase 3: routed-expert down, scaled by the routing weight; per-group sums.
 
-template <int NA>
-__device__ __forceinline__ void expert_down(const P3& a, int e, int start, int r, int wave,
-                                            int lane, int nw, char* smem) {
-  const Dims& d = a.d;
-  float acc[NA];
-#pragma unroll
-  for (int i = 0; i < NA; ++i) acc[i] = 0.f;
-  const uint8_t* base = a.experts + (size_t)e * a.stride;
-  if (wave < a.gdn.nss) {
-    cf_t xv[NA];
-#pragma unroll
-    for (int i = 0; i < NA; ++i) xv[i] = cf(a.ws.hbuf + (size_t)(start + i) * d.F + wave * kSSCols);
-    ss_fp4<NA>(tile_ptr(base + a.gu_bytes, a.gdn, r, wave, lane), ss_codes(kFP4, a.gdn, wave), xv,
-               acc);
-  }
-  if (block_reduce<NA>(acc, (float*)smem, wave, lane, nw)) {
-    cf_t ts = cf((const float*)(base + a.ts_off));
-    ci_t perm = ci(a.ws.perm);
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const float w = a.ws.topk_w[perm[start + i]];
-      a.ws.obuf[(size_t)(start + i) * d.L + r * 64 + lane] = acc[i] * ts[2] * w;
-    }
-  }
-}
-
 template <int T>
 __global__ __launch_bounds__(1024) void k_phase3(P3 a) {
-  extern __shared__ char smem[];
+  extern __shared__ __align__(16) char smem[];
   __shared__ int flag;
   const Dims& d = a.d;
   const int tiles = a.gdn.tiles;
@@ -644,29 +741,64 @@ __global__ __launch_bounds__(1024) void k_phase3(P3 a) {
   const int e = ci(a.ws.slot_expert)[j], start = ci(a.ws.slot_start)[j];
   const int cnt = ci(a.ws.slot_count)[j];
   const int g = ((cu8_t)a.labels)[e];
-  switch (cnt) {
-    case 1: expert_down<1>(a, e, start, r, wave, lane, nw, smem); break;
-    case 2: if constexpr (T >= 2) expert_down<2>(a, e, start, r, wave, lane, nw, smem); break;
-    case 3: if constexpr (T >= 3) expert_down<3>(a, e, start, r, wave, lane, nw, smem); break;
-    case 4: if constexpr (T >= 4) expert_down<4>(a, e, start, r, wave, lane, nw, smem); break;
-    case 5: if constexpr (T >= 5) expert_down<5>(a, e, start, r, wave, lane, nw, smem); break;
-    case 6: if constexpr (T >= 6) expert_down<6>(a, e, start, r, wave, lane, nw, smem); break;
-    case 7: if constexpr (T >= 7) expert_down<7>(a, e, start, r, wave, lane, nw, smem); break;
-    default: if constexpr (T >= 8) expert_down<8>(a, e, start, r, wave, lane, nw, smem); break;
+  const uint8_t* base = a.experts + (size_t)e * a.stride;
+  const float* src[T];
+#pragma unroll
+  for (int i = 0; i < T; ++i) src[i] = a.ws.hbuf + (size_t)(start + (i < cnt ? i : 0)) * d.F + wave * kSSCols;
+  f4 acc[4];
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg) acc[rg] = (f4){0.f, 0.f, 0.f, 0.f};
+  char* xs = smem + wave * stage_bytes<T>();
+  f4* red = (f4*)(smem + nw * stage_bytes<T>());
+  if (wave < a.gdn.nss)
+    wave_ss<kFP4, T>(ss_ptr(base + a.gu_bytes, a.gdn, r, wave), ss_codes(kFP4, a.gdn, wave),
+                     ss_cols(a.gdn, wave), src, cnt, xs, lane, acc);
+  if (block_reduce_mf<T>(acc, red, wave, lane, nw)) {
+    cf_t ts = cf((const float*)(base + a.ts_off));
+    ci_t perm = ci(a.ws.perm);
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int i = 4 * (lane >> 4) + v;
+        if (i < cnt) {
+          const float w = a.ws.topk_w[perm[start + i]];
+          st_co(a.ws.obuf + (size_t)(start + i) * d.L + r * 64 + rg * 16 + (lane & 15),
+                acc[rg][v] * ts[2] * w);
+        }
+      }
   }
   ci_t gso = ci(a.ws.gslot_off);
   const unsigned expect = (unsigned)(gso[g + 1] - gso[g]);
   if (!arrive_last(a.ws.ctr_s + (size_t)g * tiles + r, expect, &flag)) return;
-  // s[t][g][row] = sum over k ascending of o for token t's experts in group g
+  // s[t][g][row] = sum over k ascending of o for token t's experts in group g;
+  // every load is issued before the sums (positions past a list's end are
+  // replaced by a valid one and their values dropped)
   if (wave == 0) {
     const int row = r * 64 + lane;
+    ci_t cnt_tab = ci(a.ws.tg_cnt);
+    ci_t pos_tab = ci(a.ws.tg_pos);
+    constexpr int M = 8;
+    float v[T][M];
+    int c[T];
+#pragma unroll
     for (int t = 0; t < T; ++t) {
-      float s = 0.f;
-      for (int k = 0; k < d.K; ++k) {
-        const int ee = a.ws.topk_idx[t * d.K + k];
-        if (a.labels[ee] == g) s += a.ws.obuf[(size_t)a.ws.inv[t * d.K + k] * d.L + row];
+      const int q = t * d.G + g;
+      c[t] = cnt_tab[q];
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        const int pos = (i < c[t]) ? pos_tab[q * d.K + min(i, d.K - 1)] : 0;
+        v[t][i] = ld_co(a.ws.obuf + (size_t)pos * d.L + row);
       }
-      a.ws.s[((size_t)t * d.G + g) * d.L + row] = s;
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int q = t * d.G + g;
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < M; ++i) s += i < c[t] ? v[t][i] : 0.f;
+      for (int i = M; i < c[t]; ++i) s += ld_co(a.ws.obuf + (size_t)pos_tab[q * d.K + i] * d.L + row);
+      a.ws.s[((size_t)q) * d.L + row] = s;
     }
   }
 }
@@ -674,9 +806,9 @@ __global__ __launch_bounds__(1024) void k_phase3(P3 a) {
 // ---------------------------------------------------------------------------
 // Phase 4: U_g per used group and the shared down; ordered sum per row tile.
 
-template <int T>
+template <int T, int DU>
 __global__ __launch_bounds__(1024) void k_phase4(P4 a) {
-  extern __shared__ char smem[];
+  extern __shared__ __align__(16) char smem[];
   __shared__ int flag;
   const Dims& d = a.d;
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6), nw = blockDim.x >> 6;
@@ -684,42 +816,69 @@ __global__ __launch_bounds__(1024) void k_phase4(P4 a) {
   const int b = blockIdx.x;
   const int part = b / tiles, r = b % tiles;   // part < G: U_part; part == G: shared down
   ci_t gso = ci(a.ws.gslot_off);
-  float acc[T];
+  f4 acc[4];
 #pragma unroll
-  for (int t = 0; t < T; ++t) acc[t] = 0.f;
+  for (int rg = 0; rg < 4; ++rg) acc[rg] = (f4){0.f, 0.f, 0.f, 0.f};
+  char* xs = smem + wave * stage_bytes<T>();
+  f4* red = (f4*)(smem + nw * stage_bytes<T>());
+  const float* src[T];
   bool active;
   if (part < d.G) {
     active = gso[part + 1] > gso[part];
-    if (active && wave < a.gu.nss) {
-      cf_t xv[T];
 #pragma unroll
-      for (int t = 0; t < T; ++t) xv[t] = cf(a.ws.s + ((size_t)t * d.G + part) * d.L + wave * kSSCols);
-      ss_du<T>(d.du_fmt, tile_ptr(a.umat + (size_t)part * a.gu.bytes(), a.gu, r, wave, lane),
-                     ss_codes(d.du_fmt, a.gu, wave), xv, acc);
-    }
+    for (int t = 0; t < T; ++t) src[t] = a.ws.s + ((size_t)t * d.G + part) * d.L + wave * kSSCols;
+    if (active && wave < a.gu.nss)
+      wave_ss<DU, T>(ss_ptr(a.umat + (size_t)part * a.gu.bytes(), a.gu, r, wave),
+                     ss_codes(DU, a.gu, wave), ss_cols(a.gu, wave), src, T, xs, lane, acc);
   } else {
     active = true;
-    if (wave < a.gsd.nss) {
-      cf_t xv[T];
 #pragma unroll
-      for (int t = 0; t < T; ++t) xv[t] = cf(a.ws.hs + (size_t)t * d.Fs + wave * kSSCols);
-      ss_bf16<T>(tile_ptr(a.sdn, a.gsd, r, wave, lane), ss_codes(kBF16, a.gsd, wave), xv, acc);
-    }
+    for (int t = 0; t < T; ++t) src[t] = a.ws.hs + (size_t)t * d.Fs + wave * kSSCols;
+    if (wave < a.gsd.nss)
+      wave_ss<kBF16, T>(ss_ptr(a.sdn, a.gsd, r, wave), ss_codes(kBF16, a.gsd, wave),
+                        ss_cols(a.gsd, wave), src, T, xs, lane, acc);
   }
-  if (active && block_reduce<T>(acc, (float*)smem, wave, lane, nw)) {
+  if (active && block_reduce_mf<T>(acc, red, wave, lane, nw)) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) a.ws.ypart[((size_t)part * T + t) * d.H + r * 64 + lane] = acc[t];
+    for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = 4 * (lane >> 4) + v;
+        if (t < T)
+          st_co(a.ws.ypart + ((size_t)part * T + t) * d.H + r * 64 + rg * 16 + (lane & 15), acc[rg][v]);
+      }
   }
   if (!arrive_last(a.ws.ctr_y + r, (unsigned)(d.G + 1), &flag)) return;
-  if (wave == 0) {
+  // Ordered sum of the G + 1 partials: wave w fetches parts w, w + nw, ...
+  // (all loads in flight together), wave 0 adds them in part order.
+  {
     const int row = r * 64 + lane;
-    for (int t = 0; t < T; ++t) {
-      float y = 0.f;
-      for (int g = 0; g < d.G; ++g)
-        if (gso[g + 1] > gso[g]) y += a.ws.ypart[((size_t)g * T + t) * d.H + row];
-      y += a.ws.ypart[((size_t)d.G * T + t) * d.H + row];
-      float* dst = a.y + (size_t)t * d.H + row;
-      *dst = a.accumulate ? *dst + y : y;
+    float* stage = (float*)smem;                     // [G + 1][T][64]
+    for (int p0 = wave; p0 <= d.G; p0 += 2 * nw) {
+      const int p1 = min(p0 + nw, d.G);
+      float v0[T], v1[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        v0[t] = ld_co(a.ws.ypart + ((size_t)p0 * T + t) * d.H + row);
+        v1[t] = ld_co(a.ws.ypart + ((size_t)p1 * T + t) * d.H + row);
+      }
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        stage[(p0 * T + t) * 64 + lane] = v0[t];
+        if (p0 + nw <= d.G) stage[(p1 * T + t) * 64 + lane] = v1[t];
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        float y = 0.f;
+        for (int g = 0; g < d.G; ++g)
+          if (gso[g + 1] > gso[g]) y += stage[(g * T + t) * 64 + lane];
+        y += stage[(d.G * T + t) * 64 + lane];
+        float* dst = a.y + (size_t)t * d.H + row;
+        *dst = a.accumulate ? *dst + y : y;
+      }
     }
   }
 }
@@ -742,11 +901,12 @@ __global__ void k_rms(const float* __restrict__ x, int H, float eps, float* __re
   }
 }
 
-template <int T>
+
+template <int T, int DU>
 int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st) {
   const lmoe_dims& dd = h->d;
   Dims d{T, dd.hidden, dd.latent, dd.n_experts, dd.top_k, dd.n_groups, dd.expert_ffn,
-         dd.shared_ffn, dd.du_bits == 8 ? kQ8 : kQ4};
+         dd.shared_ffn};
   Workspace ws = h->ws;
   const bool ev = h->phase_events.size() == (size_t)kDecodePhases + 1;
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[0], st));
@@ -763,49 +923,60 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st) {
   p1.sgu = h->sgu; p1.gs = h->g_sgu;
   const int nw1 = h->g_d.nss;               // waves per phase-1 block = H / 256
   p1.cw = nw1 * 64;
-  p1.nch = ws.nch;
+  p1.nch = kRouterChunks;
   p1.nrb = h->g_router.tiles * p1.nch;
   p1.ndb = d.G * h->g_d.tiles;
   p1.ws = ws;
   const int nb1 = p1.nrb + p1.ndb + h->g_sgu.tiles;
   const int n = T * d.K;
-  size_t sm1 = (size_t)nw1 * T * 64 * sizeof(double);
-  sm1 = sm1 > (size_t)3 * n * sizeof(int) ? sm1 : (size_t)3 * n * sizeof(int);
-  hipLaunchKernelGGL(k_phase1<T>, dim3(nb1), dim3(nw1 * 64), sm1, st, p1);
+  size_t sm1 = (size_t)nw1 * (stage_bytes<T>() + red_bytes_per_wave<T>());
+  const size_t sm_router = (size_t)nw1 * T * 64 * sizeof(double);
+  const size_t sm_routing = (size_t)T * d.E * sizeof(double) + (size_t)5 * n * sizeof(int);
+  sm1 = sm1 > sm_router ? sm1 : sm_router;
+  sm1 = sm1 > sm_routing ? sm1 : sm_routing;
+  hipLaunchKernelGGL((k_phase1<T, DU>), dim3(nb1), dim3(nw1 * 64), sm1, st, p1);
   LMOE_HIP(hipGetLastError());
+  if (ev) LMOE_HIP(hipEventRecord(h->phase_events[1], st));
 
   const int maxslots = n < d.E ? n : d.E;
-  if (ev) LMOE_HIP(hipEventRecord(h->phase_events[1], st));
   // phase 2
   P2 p2{};
   p2.d = d; p2.experts = h->experts; p2.ggu = h->g_gu; p2.stride = h->expert_stride;
   p2.ts_off = h->ts_off; p2.labels = h->labels; p2.ws = ws;
   const int nw2 = h->g_gu.nss;
   hipLaunchKernelGGL(k_phase2<T>, dim3(maxslots * h->g_gu.tiles), dim3(nw2 * 64),
-                     (size_t)nw2 * T * 64 * sizeof(float), st, p2);
+                     (size_t)nw2 * (stage_bytes<T>() + red_bytes_per_wave<T>()), st, p2);
   LMOE_HIP(hipGetLastError());
-
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[2], st));
+
   // phase 3
   P3 p3{};
   p3.d = d; p3.experts = h->experts; p3.gdn = h->g_dn; p3.stride = h->expert_stride;
   p3.gu_bytes = h->g_gu.bytes(); p3.ts_off = h->ts_off; p3.labels = h->labels; p3.ws = ws;
   const int nw3 = h->g_dn.nss;
   hipLaunchKernelGGL(k_phase3<T>, dim3(maxslots * h->g_dn.tiles), dim3(nw3 * 64),
-                     (size_t)nw3 * T * 64 * sizeof(float), st, p3);
+                     (size_t)nw3 * (stage_bytes<T>() + red_bytes_per_wave<T>()), st, p3);
   LMOE_HIP(hipGetLastError());
-
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[3], st));
+
   // phase 4
   P4 p4{};
   p4.d = d; p4.umat = h->umat; p4.gu = h->g_u; p4.sdn = h->sdn; p4.gsd = h->g_sdn;
   p4.y = y; p4.accumulate = norm ? 1 : 0; p4.ws = ws;
   const int nw4 = h->g_u.nss > h->g_sdn.nss ? h->g_u.nss : h->g_sdn.nss;
-  hipLaunchKernelGGL(k_phase4<T>, dim3((d.G + 1) * h->g_u.tiles), dim3(nw4 * 64),
-                     (size_t)nw4 * T * 64 * sizeof(float), st, p4);
+  size_t sm4 = (size_t)nw4 * (stage_bytes<T>() + red_bytes_per_wave<T>());
+  const size_t sm4r = (size_t)(d.G + 1) * T * 64 * sizeof(float);
+  sm4 = sm4 > sm4r ? sm4 : sm4r;
+  hipLaunchKernelGGL((k_phase4<T, DU>), dim3((d.G + 1) * h->g_u.tiles), dim3(nw4 * 64), sm4, st, p4);
   LMOE_HIP(hipGetLastError());
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[4], st));
   return 0;
+}
+
+template <int T>
+int launch_t(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st) {
+  return h->d.du_bits == 8 ? launch_all<T, kQ8>(h, x, y, norm, st)
+                           : launch_all<T, kQ4>(h, x, y, norm, st);
 }
 
 }  // namespace
@@ -818,14 +989,14 @@ int rms_rows(lmoe_t* h, const float* x, int T, float eps, hipStream_t st) {
 
 int forward_decode(lmoe_t* h, const float* x, int T, float* y, bool norm, hipStream_t st) {
   switch (T) {
-    case 1: return launch_all<1>(h, x, y, norm, st);
-    case 2: return launch_all<2>(h, x, y, norm, st);
-    case 3: return launch_all<3>(h, x, y, norm, st);
-    case 4: return launch_all<4>(h, x, y, norm, st);
-    case 5: return launch_all<5>(h, x, y, norm, st);
-    case 6: return launch_all<6>(h, x, y, norm, st);
-    case 7: return launch_all<7>(h, x, y, norm, st);
-    case 8: return launch_all<8>(h, x, y, norm, st);
+    case 1: return launch_t<1>(h, x, y, norm, st);
+    case 2: return launch_t<2>(h, x, y, norm, st);
+    case 3: return launch_t<3>(h, x, y, norm, st);
+    case 4: return launch_t<4>(h, x, y, norm, st);
+    case 5: return launch_t<5>(h, x, y, norm, st);
+    case 6: return launch_t<6>(h, x, y, norm, st);
+    case 7: return launch_t<7>(h, x, y, norm, st);
+    case 8: return launch_t<8>(h, x, y, norm, st);
     default: return LMOE_EUNSUPPORTED;
   }
 }

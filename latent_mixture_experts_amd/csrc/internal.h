@@ -16,32 +16,45 @@ namespace lm {
 // ---------------------------------------------------------------------------
 // Device weight layout: the "tiled stream".
 //
-// A weight matrix [rows][k] is cut into tiles of 64 rows. One lane of a
-// 64-wide wavefront owns one row of a tile, so a dot product never needs a
-// cross-lane reduction. Along k, a tile is a sequence of 1 KiB slots; slot j
-// holds 16 bytes of every lane's row, lane-major, so one global_load_dwordx4
-// per lane reads one slot as a single coalesced 1 KiB request. Columns are
-// grouped in super-steps of 256: the code slots of a super-step come first,
-// then (for scaled formats) one slot holding that super-step's scales.
+// A weight matrix [rows][k] is cut into tiles of 64 rows (four row groups of
+// 16). Along k, a tile is a sequence of 1 KiB slots, each read by one
+// global_load_dwordx4 per lane as a single coalesced request. Columns are
+// grouped in super-steps of 256 (the unit of work of one wavefront): a
+// super-step holds its code slots, then, for scaled formats, one scale slot.
 //
-//   format  columns per code slot  scale slot (16 B per lane)
-//   Q8      16 (int8)              8 fp16 scales, one per 32 columns
-//   Q4      32 (4-bit two's compl) 8 fp16 scales, one per 32 columns
-//   FP4     32 (E2M1)              16 E4M3 scales, one per 16 columns
-//   BF16     8                     none
+// Code slot j of a super-step holds chunk j/4 of row group j%4. Lane l owns
+// row l%16 of the group and, in every 32-column block of the chunk, the 8
+// columns 8*(l/16)..8*(l/16)+7: exactly the B operand of an MFMA
+// 16x16x32 instruction for that row.
 //
-// A super-step is the unit of work of one wavefront in the GEMV kernels.
-enum Fmt : int { kQ8 = 0, kQ4 = 1, kFP4 = 2, kBF16 = 3 };
+//   format  chunk   lane's 16 bytes                       scale slot (lane-chunk 16*rg + r)
+//   Q8      64      2 blocks x 8 int8, held as q + 128     8 fp16 scales of row r (per 32 cols)
+//   Q4      128     4 blocks x 8 nibbles, held as q + 8    8 fp16 scales of row r (per 32 cols)
+//                   (element i in the low nibble of byte i, element i+4 in its high nibble)
+//   FP4     128     4 blocks x 8 E2M1 codes (pairs per byte, low nibble first)
+//                                                         16 E4M3 scales of row r (per 16 cols)
+//   BF16    32      8 bf16                                none
+//
+// The router keeps a plainer layout (BF16R) for its fp64 dot products: lane
+// l of a slot holds 8 consecutive bf16 columns of row l of the tile.
+enum Fmt : int { kQ8 = 0, kQ4 = 1, kFP4 = 2, kBF16 = 3, kBF16R = 4 };
 constexpr int kSSCols = 256;
 constexpr int kSlot = 1024;
 constexpr int kMaxDecodeT = 8;     // tokens the GEMV (decode) path takes per forward
 constexpr int kMaxWaves = 16;
 constexpr int kDecodePhases = 4;
+constexpr int kRouterChunks = 4;  // router column chunks: H / (64 * H/256)
 
-__host__ __device__ constexpr int cols_per_slot(int f) {
-  return f == kQ8 ? 16 : (f == kBF16 ? 8 : 32);
+__host__ __device__ constexpr int chunk_cols(int f) {      // columns of one chunk
+  return f == kQ8 ? 64 : (f == kBF16 ? 32 : (f == kBF16R ? 8 : 128));
 }
-__host__ __device__ constexpr int scale_slots(int f) { return f == kBF16 ? 0 : 1; }
+__host__ __device__ constexpr int scale_slots(int f) { return (f == kBF16 || f == kBF16R) ? 0 : 1; }
+// Code slots of a super-step of `cols` columns: four row groups per chunk
+// (one slot per chunk for the router layout); a partial last chunk is
+// padded with zero codes.
+__host__ __device__ constexpr int ss_code_slots(int f, int cols) {
+  return f == kBF16R ? cols / 8 : 4 * ((cols + chunk_cols(f) - 1) / chunk_cols(f));
+}
 
 struct Geom {
   int rows = 0;        // real rows
@@ -59,9 +72,9 @@ inline Geom make_geom(int fmt, int rows, int k) {
   g.tiles = (rows + 63) / 64;
   g.k = k;
   g.nss = (k + kSSCols - 1) / kSSCols;
-  g.full = kSSCols / cols_per_slot(fmt) + scale_slots(fmt);
+  g.full = ss_code_slots(fmt, kSSCols) + scale_slots(fmt);
   int last = k - (g.nss - 1) * kSSCols;
-  g.tile_slots = (g.nss - 1) * g.full + last / cols_per_slot(fmt) + scale_slots(fmt);
+  g.tile_slots = (g.nss - 1) * g.full + ss_code_slots(fmt, last) + scale_slots(fmt);
   return g;
 }
 
@@ -70,11 +83,11 @@ inline Geom make_geom(int fmt, int rows, int k) {
 // min(max_tokens, kMaxDecodeT) tokens.
 struct Workspace {
   double* part64 = nullptr;      // [nch][T][Epad] router partial logits
-  double* logits = nullptr;      // [T][E]
   int* topk_idx = nullptr;       // [T][K]
   float* topk_w = nullptr;       // [T][K]
   int* perm = nullptr;           // [T*K]
-  int* inv = nullptr;            // [T*K] sorted position of assignment a
+  int* tg_cnt = nullptr;         // [T][G] assignments of token t in group g
+  int* tg_pos = nullptr;         // [T][G][K] their sorted positions, ascending k
   int* slot_expert = nullptr;    // [T*K] distinct experts in (label, expert) order
   int* slot_start = nullptr;     // [T*K]
   int* slot_count = nullptr;     // [T*K]

@@ -28,55 +28,88 @@ struct Src {
 
 __device__ inline size_t code_offset(int fmt, int row, int k, int col) {
   size_t e = (size_t)row * k + col;
-  return fmt == kQ8 ? e : (fmt == kBF16 ? 2 * e : e / 2);
+  return fmt == kQ8 ? e : ((fmt == kBF16 || fmt == kBF16R) ? 2 * e : e / 2);
 }
 
-// One thread writes one 16-byte lane chunk of one slot. `pair` tiles take
-// rows from two matrices: lanes 0..31 from a (rows 32*tile + lane), lanes
-// 32..63 from b (rows 32*tile + lane - 32), so gate and up rows of the same
-// index sit in lanes i and i + 32 of one tile.
+// One thread writes one 16-byte lane chunk of one slot (layouts in
+// internal.h). `pair` tiles take rows from two matrices: row groups 0,1 from
+// a (rows 32*tile + 16*rg + r), row groups 2,3 from b (same rows), so the
+// gate and up rows of the same index meet in one lane.
 __global__ void k_tile(int fmt, Src a, Src b, int pair, int k, Geom g, uint8_t* __restrict__ dst) {
   size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   size_t total = (size_t)g.tiles * g.tile_slots * 64;
   if (idx >= total) return;
-  int lane = (int)(idx % 64);
-  int slot = (int)((idx / 64) % g.tile_slots);
-  int tile = (int)(idx / 64 / g.tile_slots);
-  int ss = slot / g.full;
-  int j = slot % g.full;
-  int cols = min(kSSCols, k - ss * kSSCols);
-  int ncs = cols / cols_per_slot(fmt);
+  const int lane = (int)(idx % 64);
+  const int slot = (int)((idx / 64) % g.tile_slots);
+  const int tile = (int)(idx / 64 / g.tile_slots);
+  const int ss = slot / g.full;
+  const int j = slot % g.full;
+  const int cols = min(kSSCols, k - ss * kSSCols);
+  const int ncs = ss_code_slots(fmt, cols);
 
-  const Src* s = &a;
-  int row;
-  if (pair) {
-    row = 32 * tile + (lane & 31);
-    if (lane >= 32) s = &b;
-  } else {
-    row = 64 * tile + lane;
-  }
   uint8_t out[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) out[i] = 0;
-  if (row < s->rows) {
-    if (j < ncs) {
-      int col = ss * kSSCols + j * cols_per_slot(fmt);
-      const uint8_t* p = s->codes + code_offset(fmt, row, k, col);
-#pragma unroll
+  if (fmt == kBF16R) {
+    const int row = 64 * tile + lane;
+    if (row < a.rows) {
+      const uint8_t* p = a.codes + code_offset(fmt, row, k, ss * kSSCols + j * 8);
       for (int i = 0; i < 16; ++i) out[i] = p[i];
-      // Q4 packed codes hold q+8; the device keeps q as 4-bit two's
-      // complement, which is the nibble xor 8.
-      if (fmt == kQ4) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) out[i] ^= 0x88;
-      }
-    } else {
-      if (fmt == kFP4) {
-        const uint8_t* p = s->scales + (size_t)row * (k / 16) + ss * 16;
-        for (int i = 0; i < cols / 16; ++i) out[i] = p[i];
+    }
+  } else {
+    // code slot: row group j%4, chunk j/4; scale slot: lane-chunk 16*rg + r
+    const bool is_code = j < ncs;
+    const int rg = is_code ? (j % 4) : (lane / 16);
+    const int r16 = lane % 16;
+    const Src* s = (pair && rg >= 2) ? &b : &a;
+    const int row = pair ? 32 * tile + 16 * (rg & 1) + r16 : 64 * tile + 16 * rg + r16;
+    if (row < s->rows) {
+      if (is_code) {
+        const int c = j / 4, qg = lane / 16;
+        // 8-column pieces past k stay zero codes (k is a multiple of 32)
+        if (fmt == kQ8) {
+          for (int bb = 0; bb < 2; ++bb) {
+            const int col = ss * kSSCols + 64 * c + 32 * bb + 8 * qg;
+            if (col >= k) continue;
+            const uint8_t* p = s->codes + code_offset(fmt, row, k, col);
+            for (int i = 0; i < 8; ++i) out[8 * bb + i] = p[i] ^ 0x80;   // int8 -> q + 128
+          }
+        } else if (fmt == kBF16) {
+          const int col = ss * kSSCols + 32 * c + 8 * qg;
+          if (col < k) {
+            const uint8_t* p = s->codes + code_offset(fmt, row, k, col);
+            for (int i = 0; i < 16; ++i) out[i] = p[i];
+          }
+        } else {
+          for (int bb = 0; bb < 4; ++bb) {
+            const int col = ss * kSSCols + 128 * c + 32 * bb + 8 * qg;
+            if (col >= k) {
+              if (fmt == kQ4)
+                for (int i = 0; i < 4; ++i) out[4 * bb + i] = 0x88;         // q = 0
+              continue;
+            }
+            const uint8_t* p = s->codes + code_offset(fmt, row, k, col);
+            if (fmt == kFP4) {
+              for (int i = 0; i < 4; ++i) out[4 * bb + i] = p[i];
+            } else {
+              // packed Q4: byte i = e(2i) | e(2i+1) << 4; device: e(i) | e(i+4) << 4
+              uint8_t e[8];
+              for (int i = 0; i < 4; ++i) {
+                e[2 * i] = p[i] & 0xF;
+                e[2 * i + 1] = p[i] >> 4;
+              }
+              for (int i = 0; i < 4; ++i) out[4 * bb + i] = (uint8_t)(e[i] | (e[i + 4] << 4));
+            }
+          }
+        }
       } else {
-        const uint8_t* p = s->scales + ((size_t)row * (k / 32) + ss * 8) * 2;
-        for (int i = 0; i < 2 * (cols / 32); ++i) out[i] = p[i];
+        if (fmt == kFP4) {
+          const uint8_t* p = s->scales + (size_t)row * (k / 16) + ss * 16;
+          for (int i = 0; i < cols / 16; ++i) out[i] = p[i];
+        } else {
+          const uint8_t* p = s->scales + ((size_t)row * (k / 32) + ss * 8) * 2;
+          for (int i = 0; i < 2 * (cols / 32); ++i) out[i] = p[i];
+        }
       }
     }
   }
@@ -387,7 +420,7 @@ int load_weights_impl(lmoe_t* h, const lmoe_weights* w, hipStream_t st) {
     DevTemp t;
     if (int rc = copy_in(t, w->router_bf16, (size_t)E * H * 2, st)) return rc;
     Src a{(const uint8_t*)t.p, nullptr, E};
-    if (int rc = launch_tile(kBF16, a, a, 0, H, h->g_router, h->router, st)) return rc;
+    if (int rc = launch_tile(kBF16R, a, a, 0, H, h->g_router, h->router, st)) return rc;
     if (d.has_router_bias)
       LMOE_HIP(hipMemcpyAsync(h->bias, w->router_bias, sizeof(float) * E, hipMemcpyDefault, st));
     else

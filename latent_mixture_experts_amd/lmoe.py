@@ -11,6 +11,12 @@ import os
 
 import numpy as np
 
+# PyTorch ships its own copy of the HIP runtime under the same soname as
+# /opt/rocm's. Importing it first makes liblmoe.so bind to that copy, so the
+# library and PyTorch share one runtime (one device context, one set of
+# streams and allocations).
+import torch  # noqa: F401
+
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblmoe.so")
 
