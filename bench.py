@@ -163,53 +163,74 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    stack = w.n_layers > 1
+    n_handles = w.n_layers if stack else args.copies
     t_build = time.time()
     layers, labels = [], []
-    for r in range(args.copies):
+    for r in range(n_handles):
         L_, lab = build_layer(lm, wl, w, args.seed, r, torch)
         layers.append(L_)
         labels.append(lab)
-    log("built %d layer copies in %.1f s" % (args.copies, time.time() - t_build))
+    log("built %d layers in %.1f s" % (n_handles, time.time() - t_build))
 
     T = w.tokens
-    x = torch.from_numpy(wl.x(w, args.seed, 0)).cuda()
+    x0 = torch.from_numpy(wl.x(w, args.seed, 0)).cuda()
+    x = x0.clone()
     y = torch.empty(T, w.hidden, device="cuda")
 
-    # routing of each copy, for the algorithmic byte counts
-    bytes_per_copy, distinct, groups = [], [], []
+    def step(i):
+        if stack:
+            for L_ in layers:
+                L_.forward_block(x)
+        else:
+            layers[i % n_handles].forward(x, y)
+
+    # routing of each layer, for the algorithmic byte counts
+    bytes_per_layer, distinct, groups = [], [], []
+    xr = x0.clone()
     for r, L_ in enumerate(layers):
         idx = torch.empty(T, w.top_k, dtype=torch.int32, device="cuda")
-        L_.forward(x, y, debug=dict(topk_idx=idx))
+        if stack:
+            # the routing a block sees is that of its normalized input
+            xn = xr / torch.sqrt((xr.double() ** 2).mean(dim=1, keepdim=True) + 1e-6).float()
+            L_.forward(xn, y, debug=dict(topk_idx=idx))
+            xr = xr + y
+        else:
+            L_.forward(x, y, debug=dict(topk_idx=idx))
         torch.cuda.synchronize()
         pb, dn, ug = phase_bytes(w, idx.cpu().numpy(), labels[r])
-        bytes_per_copy.append(pb)
+        bytes_per_layer.append(pb)
         distinct.append(dn)
         groups.append(ug)
-    pbytes = np.mean(np.array(bytes_per_copy), axis=0)
+    pbytes = np.mean(np.array(bytes_per_layer), axis=0)
+    layer_bytes = float(np.sum(pbytes))
 
     for i in range(args.warmup):
-        layers[i % args.copies].forward(x, y)
+        step(i)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(args.steps):
-        layers[i % args.copies].forward(x, y)
+        step(i)
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
 
     # per-kernel durations with HIP events recorded on the forward's stream
     nph = lm.lib().lmoe_phase_count()
-    nprof = max(args.copies * 4, 32)
+    nprof = max(n_handles * 2, 32)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)] for _ in range(nprof)]
     for row in evs:
         for e in row:
             e.record()
     torch.cuda.synchronize()
     for i in range(nprof):
-        L_ = layers[i % args.copies]
+        L_ = layers[i % n_handles]
         L_.set_phase_events([e.cuda_event for e in evs[i]])
-        L_.forward(x, y)
+        if stack:
+            L_.forward_block(x)
+        else:
+            L_.forward(x, y)
     for L_ in layers:
         L_.set_phase_events(None)
     torch.cuda.synchronize()
@@ -217,15 +238,16 @@ def main():
     phase_avg = phase_ms.mean(axis=0)
     dom = int(np.argmax(phase_avg))
     achieved = pbytes[dom] / (phase_avg[dom] * 1e-3) / 1e9
-    total_bytes = float(np.sum(pbytes))
-    log("step %.2f us; phases (us): %s; phase GB/s: %s; whole-forward %.0f GB/s over %.1f MB" % (
+    step_bytes = layer_bytes * (w.n_layers if stack else 1)
+    log("step %.2f us; phases (us): %s; phase GB/s: %s; whole-step %.0f GB/s over %.1f MB" % (
         ms * 1e3, " ".join("%.2f" % (p * 1e3) for p in phase_avg),
         " ".join("%.0f" % (b / (p * 1e-3) / 1e9) for b, p in zip(pbytes, phase_avg)),
-        total_bytes / (ms * 1e-3) / 1e9, total_bytes / 1e6))
-    log("distinct experts per step %.1f, groups used %.1f" % (np.mean(distinct), np.mean(groups)))
+        step_bytes / (ms * 1e-3) / 1e9, step_bytes / 1e6))
+    log("distinct experts per layer %.1f, groups used %.1f" % (np.mean(distinct), np.mean(groups)))
 
     out = {
-        "metric": "latent-MoE layer tokens/s (decode; HBM roofline)",
+        "metric": ("latent-MoE %d-layer stack tokens/s (decode; HBM roofline)" % w.n_layers) if stack
+                  else "latent-MoE layer tokens/s (decode; HBM roofline)",
         "value": T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -241,9 +263,10 @@ def main():
                    "experts": w.n_experts, "top_k": w.top_k, "groups": w.n_groups,
                    "expert_ffn": w.expert_ffn, "shared_ffn": w.shared_ffn,
                    "du_format": "Q%d" % w.du_bits, "expert_format": "NVFP4",
-                   "weight_copies": args.copies,
-                   "forward_algorithmic_bytes": total_bytes,
-                   "forward_GBps": total_bytes / (ms * 1e-3) / 1e9},
+                   "layers": w.n_layers,
+                   "weight_copies": None if stack else args.copies,
+                   "step_algorithmic_bytes": step_bytes,
+                   "step_GBps": step_bytes / (ms * 1e-3) / 1e9},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic("k_phase%d" % (dom + 1), w.name),
@@ -251,7 +274,7 @@ def main():
                      "kernel_us": phase_avg[dom] * 1e3,
                      "kernel_algorithmic_bytes": pbytes[dom]},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not stack:
         out["cpu_baseline"] = cpu_baseline(w, args.seed, T)
     print(json.dumps(out), flush=True)
     for L_ in layers:

@@ -106,10 +106,18 @@ def decode_layer(dims, blobs, expert_ids=None):
 # Routing.
 
 
+def _exact_input(x):
+    """The layer input at its own precision: fp32 arrays are widened exactly;
+    fp64 arrays (a normalized input inside the stack) are used as they are."""
+    x = np.asarray(x)
+    return x.astype(np.float64) if x.dtype == np.float64 else \
+        x.astype(np.float32).astype(np.float64)
+
+
 def router_logits(x, wr_bf16_bits, bias=None):
     """l[t, e] = sum_i x[t, i] * Wr[e, i] (+ b[e]), fp64."""
     wr = fm.bf16_bits_to_f64(wr_bf16_bits)
-    lg = np.asarray(x, dtype=np.float32).astype(np.float64) @ wr.T
+    lg = _exact_input(x) @ wr.T
     if bias is not None:
         lg = lg + np.asarray(bias, dtype=np.float32).astype(np.float64)[None, :]
     return lg
@@ -160,17 +168,17 @@ def swiglu(gate, up, down, z):
 
 
 def layer_forward(dims, blobs, x, dec=None, intermediates=False):
-    """Forward of one layer for x fp32 [T, H]. Returns y fp64 [T, H], or a
-    dict with every intermediate when ``intermediates`` is set."""
+    """Forward of one layer for x [T, H] (fp32, or fp64 for a normalized
+    input inside the stack). Returns y fp64 [T, H], or a dict with every
+    intermediate when ``intermediates`` is set."""
     d = dims
-    x = np.asarray(x, dtype=np.float32)
-    t_n = x.shape[0]
-    xd = x.astype(np.float64)
+    xd = _exact_input(x)
+    t_n = xd.shape[0]
     if dec is None:
         dec = decode_layer(d, blobs)
     labels = np.asarray(blobs["labels"], dtype=np.int64)
 
-    logits = router_logits(x, blobs["router_bf16"], blobs.get("router_bias"))
+    logits = router_logits(xd, blobs["router_bf16"], blobs.get("router_bias"))
     idx, w = select_topk(logits, d.top_k)
     perm, count, group_off = permute(idx, labels, d.n_experts, d.n_groups)
 
@@ -229,10 +237,9 @@ def rmsnorm(x, eps=1e-6):
 
 def stack_forward(dims, layers, x, eps=1e-6):
     """x_{l+1} = x_l + layer_l(RMSNorm(x_l)); ``layers`` yields blob dicts.
-    The normalized input is handed to the layer in fp64 rounded to fp32, the
-    precision the layer input takes."""
+    Reading: the normalized input reaches the layer at full precision (not
+    rounded), so the router sees 1/rms(x) times the logits of x."""
     xd = np.asarray(x, dtype=np.float64)
     for blobs in layers:
-        xn = rmsnorm(xd, eps).astype(np.float32)
-        xd = xd + layer_forward(dims, blobs, xn)
+        xd = xd + layer_forward(dims, blobs, rmsnorm(xd, eps))
     return xd

@@ -279,8 +279,18 @@ def test_stack_is_residual_of_layers():
     xd = x.astype(np.float64)
     for blobs in layers:
         xn = xd / np.sqrt((xd ** 2).mean(axis=1, keepdims=True) + 1e-6)
-        xd = xd + layer_forward(d, blobs, xn.astype(np.float32))
+        xd = xd + layer_forward(d, blobs, xn)
     assert np.array_equal(out, xd)
+
+
+def test_normalized_input_scales_logits():
+    """A layer fed c * x routes like x: its logits are c times x's (no bias)."""
+    blobs = pack_layer(SMALL, _masters(SMALL))
+    x = _x(SMALL, 3)
+    a = layer_forward(SMALL, blobs, x, intermediates=True)
+    b = layer_forward(SMALL, blobs, x.astype(np.float64) * 0.25, intermediates=True)
+    assert np.array_equal(a["idx"], b["idx"])
+    assert np.array_equal(b["logits"], 0.25 * a["logits"])     # power of two: exact
 
 
 def test_empty_token_batch():
