@@ -11,6 +11,11 @@ same seeded generator as the tests). Steps rotate over --copies independently
 seeded layers so that the 256 MB Infinity Cache cannot hold the weights a
 step reads; inputs are resident in HBM before the timed region.
 
+The default line also carries a "prefill" object: the Edge0-145B-shaped
+prefill layer (T = 4096, router bias N(0, 1) skewing expert loads) on the
+prefill path, with its per-kernel MFMA roofline. --workload 145b_prefill makes
+that the primary line.
+
 Prints one JSON line (rank 0). --gpus above 1 is refused: this build runs on
 one GPU.
 """
@@ -27,6 +32,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 / bf16 matrix peak, published
+PREFILL_PHASES = ["route", "permute", "d", "shared_gate_up", "expert_gate_up", "expert_down",
+                  "combine", "u_shared_down"]
+PREFILL_KERNELS = ["k_prep + k_dense<BF16,Logits> + k_select", "k_perm_*", "k_dense<Q,F16>",
+                   "k_dense<BF16,SwigluB2>", "k_grouped<GateUp>", "k_grouped<Down>", "k_combine",
+                   "k_dense<Q,Y>"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_145b_t4_traffic.json")
 
 
@@ -110,6 +121,118 @@ def measured_traffic(kernel, workload):
     return None if k is None else k["traffic_bytes"]
 
 
+def prefill_flops(w, idx, labels):
+    """Algorithmic flops of each prefill phase for routing idx [T][K]: D and
+    U count the (token, group) pairs the tokens route into (the kernels run
+    all G groups; that figure is reported beside it), the router one pass of
+    bf16 products (the kernel runs two)."""
+    T, H, L, E, K, G, F, Fs = (idx.shape[0], w.hidden, w.latent, w.n_experts, w.top_k,
+                               w.n_groups, w.expert_ffn, w.shared_ffn)
+    lab = labels[idx]
+    pairs = int(sum(len(set(r.tolist())) for r in lab))
+    fl = [2.0 * T * E * H, 0.0, 2.0 * pairs * L * H, 2.0 * T * 2 * Fs * H,
+          2.0 * T * K * 2 * F * L, 2.0 * T * K * L * F, 0.0,
+          2.0 * pairs * H * L + 2.0 * T * H * Fs]
+    executed = [4.0 * T * E * H, 0.0, 2.0 * T * G * L * H, 4.0 * T * 2 * Fs * H, None, None, 0.0,
+                2.0 * T * G * H * L + 4.0 * T * H * Fs]
+    return fl, executed, pairs
+
+
+def bench_prefill(lm, wl, w, args, torch):
+    """Times lmoe_forward on the prefill path; returns the result dict."""
+    layers = []
+    t_build = time.time()
+    for r in range(args.prefill_copies):
+        L_, lab = build_layer(lm, wl, w, args.seed, r, torch)
+        layers.append((L_, lab))
+    log("prefill: built %d layers in %.1f s" % (len(layers), time.time() - t_build))
+    T = w.tokens
+    x = torch.from_numpy(wl.x(w, args.seed, 0)).cuda()
+    y = torch.empty(T, w.hidden, device="cuda")
+    fl, ex, pairs, counts = [], [], [], []
+    for L_, lab in layers:
+        idx = torch.empty(T, w.top_k, dtype=torch.int32, device="cuda")
+        cnt = torch.empty(w.n_experts, dtype=torch.int32, device="cuda")
+        L_.forward(x, y, debug=dict(topk_idx=idx, expert_count=cnt))
+        torch.cuda.synchronize()
+        f_, e_, p_ = prefill_flops(w, idx.cpu().numpy(), lab)
+        fl.append(f_); ex.append(e_); pairs.append(p_); counts.append(cnt.cpu().numpy())
+    flops = np.mean(np.array(fl), axis=0)
+    n = len(layers)
+    for i in range(args.prefill_warmup):
+        layers[i % n][0].forward(x, y)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.prefill_steps):
+        layers[i % n][0].forward(x, y)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.prefill_steps
+
+    nph = lm.lib().lmoe_phase_count(T)
+    assert nph == len(PREFILL_PHASES)
+    nprof = max(2 * n, 8)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)] for _ in range(nprof)]
+    for row in evs:          # torch creates the HIP event at its first record
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    for i in range(nprof):
+        L_ = layers[i % n][0]
+        L_.set_phase_events([e.cuda_event for e in evs[i]])
+        L_.forward(x, y)
+    for L_, _ in layers:
+        L_.set_phase_events(None)
+    torch.cuda.synchronize()
+    phase_ms = np.array([[row[k].elapsed_time(row[k + 1]) for k in range(nph)] for row in evs])
+    phase_avg = phase_ms.mean(axis=0)
+    tflops = [f / (p * 1e-3) / 1e12 if f else 0.0 for f, p in zip(flops, phase_avg)]
+    dom = int(np.argmax(phase_avg))
+    log("prefill step %.3f ms (%.0f tokens/s); phases (us): %s" % (
+        ms, T / (ms * 1e-3), " ".join("%s %.1f" % (nm, p * 1e3)
+                                       for nm, p in zip(PREFILL_PHASES, phase_avg))))
+    log("prefill phase TFLOP/s (algorithmic): %s" % " ".join(
+        "%s %.0f" % (nm, t) for nm, t in zip(PREFILL_PHASES, tflops) if t))
+    c = np.concatenate(counts)
+    gemm = [2, 3, 4, 5, 7]
+    gemm_fl = float(sum(flops[i] for i in gemm))
+    gemm_ms = float(sum(phase_avg[i] for i in gemm))
+    grouped_fl = float(flops[4] + flops[5])
+    grouped_ms = float(phase_avg[4] + phase_avg[5])
+    out = {
+        "workload": w.name,
+        "tokens": T,
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "ms_per_step": ms,
+        "steps": args.prefill_steps,
+        "warmup": args.prefill_warmup,
+        "weight_copies": n,
+        "step_algorithmic_tflop": float(np.sum(flops)) / 1e12,
+        "step_tflops": float(np.sum(flops)) / (ms * 1e-3) / 1e12,
+        "token_group_pairs": float(np.mean(pairs)),
+        "expert_tokens": {"max": int(c.max()), "median": float(np.median(c)),
+                          "zero": int((c == 0).sum()) // n},
+        "phases_us": {nm: float(p * 1e3) for nm, p in zip(PREFILL_PHASES, phase_avg)},
+        "phase_tflops": {nm: t for nm, t in zip(PREFILL_PHASES, tflops) if t},
+        "grouped_gemm": {"achieved": grouped_fl / (grouped_ms * 1e-3) / 1e12,
+                         "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": grouped_fl / (grouped_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS},
+        "all_gemms": {"achieved": gemm_fl / (gemm_ms * 1e-3) / 1e12,
+                      "frac": gemm_fl / (gemm_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS},
+        "roofline": {"bound": "mfma", "achieved": tflops[dom], "peak": MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops[dom] / MFMA_PEAK_TFLOPS,
+                     "traffic": None, "kernel": PREFILL_KERNELS[dom],
+                     "phase": PREFILL_PHASES[dom], "kernel_us": float(phase_avg[dom] * 1e3),
+                     "kernel_algorithmic_flop": float(flops[dom]),
+                     "kernel_executed_flop": ex[0][dom]},
+    }
+    for L_, _ in layers:
+        L_.close()
+    return out
+
+
 def cpu_baseline(w, seed, tokens):
     """The fp64 oracle timed on the host on a bounded sample: one forward of
     `tokens` tokens of layer 0 (including its on-the-fly dequantization of
@@ -147,6 +270,11 @@ def main():
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-workload", default="145b_prefill")
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--prefill-warmup", type=int, default=3)
+    ap.add_argument("--prefill-copies", type=int, default=2)
+    ap.add_argument("--no-prefill", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -158,11 +286,28 @@ def main():
     from latent_mixture_experts_amd import workloads as wl
 
     w = wl.WORKLOADS[args.workload]
-    if w.tokens > 8:
-        print("workload %s needs the prefill path, which bench.py does not time yet" % w.name,
-              file=sys.stderr)
-        sys.exit(2)
     torch.cuda.set_device(0)
+    if w.tokens > 8:
+        pre = bench_prefill(lm, wl, w, args, torch)
+        out = {
+            "metric": "latent-MoE layer tokens/s (prefill; MFMA roofline)",
+            "value": pre["value"], "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.prefill_steps, "warmup": args.prefill_warmup,
+            "ms_per_step": pre["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+            "config": {"workload": w.name, "tokens": w.tokens, "hidden": w.hidden,
+                       "latent": w.latent, "experts": w.n_experts, "top_k": w.top_k,
+                       "groups": w.n_groups, "expert_ffn": w.expert_ffn,
+                       "shared_ffn": w.shared_ffn, "du_format": "Q%d" % w.du_bits,
+                       "expert_format": "NVFP4", "router_bias": w.router_bias,
+                       "weight_copies": args.prefill_copies},
+            "roofline": pre["roofline"],
+            "prefill": pre,
+        }
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline(w, args.seed, 16)
+        print(json.dumps(out), flush=True)
+        return
     stack = w.n_layers > 1
     n_handles = w.n_layers if stack else args.copies
     t_build = time.time()
@@ -217,7 +362,7 @@ def main():
     ms = start.elapsed_time(end) / args.steps
 
     # per-kernel durations with HIP events recorded on the forward's stream
-    nph = lm.lib().lmoe_phase_count()
+    nph = lm.lib().lmoe_phase_count(T)
     nprof = max(n_handles * 2, 32)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)] for _ in range(nprof)]
     for row in evs:
@@ -274,11 +419,14 @@ def main():
                      "kernel_us": phase_avg[dom] * 1e3,
                      "kernel_algorithmic_bytes": pbytes[dom]},
     }
+    for L_ in layers:
+        L_.close()
+    del layers
+    if not args.no_prefill and not stack:
+        out["prefill"] = bench_prefill(lm, wl, wl.WORKLOADS[args.prefill_workload], args, torch)
     if not args.no_cpu_baseline and not stack:
         out["cpu_baseline"] = cpu_baseline(w, args.seed, T)
     print(json.dumps(out), flush=True)
-    for L_ in layers:
-        L_.close()
 
 
 if __name__ == "__main__":

@@ -76,7 +76,7 @@ extern "C" {
  * Constraints: hidden % 256 == 0, latent % 64 == 0, expert_ffn % 32 == 0,
  * shared_ffn % 32 == 0, hidden <= 4096, latent <= 4096, expert_ffn <= 4096,
  * shared_ffn <= 4096, 1 <= top_k <= min(n_experts, 64), n_experts <= 1024,
- * 1 <= n_groups <= 64, du_bits in {8, 4}, max_tokens >= 1. */
+ * 1 <= n_groups <= 64, du_bits in {8, 4}, 1 <= max_tokens <= 1048576. */
 typedef struct lmoe_dims {
   int32_t hidden;          /* H */
   int32_t latent;          /* ell */
@@ -113,13 +113,22 @@ typedef struct lmoe_debug {
   int32_t* expert_count;   /* [E] assignments per expert */
   int32_t* group_off;      /* [G+1] start of each group's segment in perm */
   float*   latent;         /* [T][G][ell] D_g x; entries of (t, g) pairs that
-                              token t does not use are unspecified */
+                              token t does not use are unspecified. For
+                              T > 8 these are the fp16 values the experts
+                              read, widened to fp32 */
 } lmoe_debug;
 
 typedef struct lmoe lmoe_t;
 
 /* Create a handle on HIP device `hip_device`: validates dims, allocates the
- * workspace for max_tokens. *out is set only on success. */
+ * workspace for max_tokens. *out is set only on success.
+ * Two paths serve a forward: T <= 8 tokens run the decode path (weights
+ * streamed once per call through a GEMV on matrix cores); T > 8 the prefill
+ * path (MFMA GEMMs over the sorted assignments). The prefill workspace
+ * exists only when max_tokens > 8; it takes about
+ *   T * (6H + 4 Epad + 8 G ell + K (2F + 4 ell + 48) + 4 Fs) bytes
+ * for T = max_tokens (Epad = E rounded up to 64), e.g. 0.68 GB at T 4096
+ * for the 145B shapes, plus a bf16 copy of the router in two layouts. */
 int lmoe_create(const lmoe_dims* dims, int hip_device, lmoe_t** out);
 
 /* Copy and re-lay the packed weights into device memory owned by the handle
@@ -130,7 +139,10 @@ int lmoe_load_weights(lmoe_t* h, const lmoe_weights* w, void* hip_stream);
 
 /* y[T][H] = layer(x[T][H]); x and y are device fp32, row-major, not
  * aliased. 1 <= T <= max_tokens. Asynchronous on `hip_stream`. `dbg` may be
- * NULL. */
+ * NULL. Top-K indices and the permutation are those of exact arithmetic
+ * (fp64 rescoring wherever fp32 cannot decide); y carries the rounding of the
+ * path's arithmetic (fp32 on the decode path; fp16 activations on the
+ * prefill path). */
 int lmoe_forward(lmoe_t* h, const float* x_dev, int32_t T, float* y_dev,
                  const lmoe_debug* dbg, void* hip_stream);
 
@@ -141,12 +153,16 @@ int lmoe_forward_block(lmoe_t* h, float* x_inout_dev, int32_t T, float rms_eps,
                        void* hip_stream);
 
 /* Profiling hook: when `events` is non-NULL, each following lmoe_forward /
- * lmoe_forward_block records events[0] on its stream before its first kernel
- * and events[i] after the i-th of its `n` kernels (hipEvent_t handles owned by
- * the caller; the decode path has lmoe_phase_count() kernels, so n must equal
- * lmoe_phase_count() + 1). NULL switches it off. EINVAL on a wrong n. */
+ * lmoe_forward_block of T tokens with lmoe_phase_count(T) == n - 1 records
+ * events[0] on its stream before its first kernel and events[i] after its
+ * i-th phase (hipEvent_t handles owned by the caller). Decode (T <= 8) has 4
+ * phases: router + D + shared gate/up, expert gate/up, expert down +
+ * combine, U + shared down. Prefill has 8: staging + router + top-K;
+ * permutation; D; shared gate/up; expert gate/up; expert down; combine;
+ * U + shared down. Forwards of the other path record nothing. NULL switches
+ * it off. EINVAL unless n is 5 or 9. */
 int lmoe_set_phase_events(lmoe_t* h, void* const* events, int32_t n);
-int32_t lmoe_phase_count(void);
+int32_t lmoe_phase_count(int32_t T);
 
 void lmoe_destroy(lmoe_t* h);
 

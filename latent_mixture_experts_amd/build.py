@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "liblmoe.so")
 BUILD = os.path.join(PKG, "_build")
-SOURCES = ["api.hip", "layout.hip", "decode.hip"]
+SOURCES = ["api.hip", "layout.hip", "decode.hip", "prefill.hip"]
 ARCH = "gfx950"
 
 

@@ -43,6 +43,7 @@ int check_dims(const lmoe_dims& d) {
     return unsup("widths above 4096");
   if (d.n_experts > 1024 || d.top_k > 64 || d.n_groups > 64)
     return unsup("n_experts <= 1024, top_k <= 64, n_groups <= 64");
+  if (d.max_tokens > kMaxTokens) return unsup("max_tokens above 1048576");
   return 0;
 }
 
@@ -119,6 +120,42 @@ int create_impl(lmoe_t* h) {
   A(w.ctr_router, sizeof(unsigned));
   A(w.ctr_s, sizeof(unsigned) * G * (L / 64));
   A(w.ctr_y, sizeof(unsigned) * (H / 64));
+
+  // prefill path (T > kMaxDecodeT): router copies and GEMM workspace
+  if (d.max_tokens > kMaxDecodeT) {
+    PrefillWs& p = h->pw;
+    const size_t Tp = (size_t)d.max_tokens, nk = Tp * K;
+    const size_t nchunk = (size_t)prefill_chunks(d.max_tokens);
+    h->g_router_m = make_geom(kBF16, E, H);
+    const size_t Epm = (size_t)h->g_router_m.tiles * 64;
+    p.tmax = d.max_tokens;
+    A(h->router_m, h->g_router_m.bytes());
+    A(h->router_rm, sizeof(uint16_t) * E * H);
+    A(p.wmax, sizeof(double));
+    A(p.xh, 2 * Tp * H);
+    A(p.xb, 4 * Tp * H);
+    A(p.xnorm, sizeof(double) * Tp);
+    A(p.r, sizeof(float) * Tp);
+    A(p.logits, sizeof(float) * Tp * Epm);
+    A(p.idx, sizeof(int) * nk);
+    A(p.w, sizeof(float) * nk);
+    A(p.cmask, sizeof(unsigned long long) * nchunk * E);
+    A(p.ccnt, sizeof(int) * nchunk * E);
+    A(p.cbase, sizeof(int) * nchunk * E);
+    A(p.eorder, sizeof(int) * E);
+    A(p.seg_start, sizeof(int) * E);
+    A(p.expert_count, sizeof(int) * E);
+    A(p.group_off, sizeof(int) * (G + 1));
+    A(p.pieces, prefill_piece_bytes() * prefill_max_pieces(d.max_tokens, K, E));
+    A(p.npieces, sizeof(int));
+    A(p.perm, sizeof(int) * nk);
+    A(p.inv, sizeof(int) * nk);
+    A(p.xl, 2 * Tp * G * L);
+    A(p.hsb, 4 * Tp * Fs);
+    A(p.h, 2 * nk * F);
+    A(p.o, sizeof(float) * nk * L);
+    A(p.s, 2 * Tp * G * L);
+  }
 #undef A
   LMOE_HIP(hipMemset(w.ctr_router, 0, sizeof(unsigned)));
   LMOE_HIP(hipMemset(w.ctr_s, 0, sizeof(unsigned) * G * (L / 64)));
@@ -141,19 +178,23 @@ struct DeviceGuard {
 int copy_debug(lmoe_t* h, const lmoe_debug* dbg, int T, hipStream_t st) {
   const lmoe_dims& d = h->d;
   const Workspace& w = h->ws;
+  const PrefillWs& p = h->pw;
+  const bool pre = T > kMaxDecodeT;
   const size_t n = (size_t)T * d.top_k;
-  if (dbg->topk_idx) LMOE_HIP(hipMemcpyAsync(dbg->topk_idx, w.topk_idx, 4 * n, hipMemcpyDeviceToDevice, st));
-  if (dbg->topk_w) LMOE_HIP(hipMemcpyAsync(dbg->topk_w, w.topk_w, 4 * n, hipMemcpyDeviceToDevice, st));
-  if (dbg->perm) LMOE_HIP(hipMemcpyAsync(dbg->perm, w.perm, 4 * n, hipMemcpyDeviceToDevice, st));
+  const auto D2D = hipMemcpyDeviceToDevice;
+  if (dbg->topk_idx) LMOE_HIP(hipMemcpyAsync(dbg->topk_idx, pre ? p.idx : w.topk_idx, 4 * n, D2D, st));
+  if (dbg->topk_w) LMOE_HIP(hipMemcpyAsync(dbg->topk_w, pre ? p.w : w.topk_w, 4 * n, D2D, st));
+  if (dbg->perm) LMOE_HIP(hipMemcpyAsync(dbg->perm, pre ? p.perm : w.perm, 4 * n, D2D, st));
   if (dbg->expert_count)
-    LMOE_HIP(hipMemcpyAsync(dbg->expert_count, w.expert_count, 4 * (size_t)d.n_experts,
-                            hipMemcpyDeviceToDevice, st));
+    LMOE_HIP(hipMemcpyAsync(dbg->expert_count, pre ? p.expert_count : w.expert_count,
+                            4 * (size_t)d.n_experts, D2D, st));
   if (dbg->group_off)
-    LMOE_HIP(hipMemcpyAsync(dbg->group_off, w.group_off, 4 * (size_t)(d.n_groups + 1),
-                            hipMemcpyDeviceToDevice, st));
-  if (dbg->latent)
-    LMOE_HIP(hipMemcpyAsync(dbg->latent, w.xl, 4 * (size_t)T * d.n_groups * d.latent,
-                            hipMemcpyDeviceToDevice, st));
+    LMOE_HIP(hipMemcpyAsync(dbg->group_off, pre ? p.group_off : w.group_off,
+                            4 * (size_t)(d.n_groups + 1), D2D, st));
+  if (dbg->latent) {
+    if (pre) return prefill_debug_latent(h, T, dbg->latent, st);
+    LMOE_HIP(hipMemcpyAsync(dbg->latent, w.xl, 4 * (size_t)T * d.n_groups * d.latent, D2D, st));
+  }
   return 0;
 }
 
@@ -173,10 +214,6 @@ int check_forward(lmoe_t* h, const void* x, int T, const void* y) {
   if (T <= 0 || T > h->d.max_tokens) {
     set_error("T must be in [1, max_tokens]");
     return LMOE_EINVAL;
-  }
-  if (T > kMaxDecodeT) {
-    set_error("T above the decode path's limit of 8 tokens");
-    return LMOE_EUNSUPPORTED;
   }
   return 0;
 }
@@ -232,7 +269,9 @@ int lmoe_forward(lmoe_t* h, const float* x, int32_t T, float* y, const lmoe_debu
   }
   DeviceGuard g(h->device);
   hipStream_t st = (hipStream_t)stream;
-  if (int rc = forward_decode(h, x, T, y, false, st)) return rc;
+  const int rc = T > kMaxDecodeT ? forward_prefill(h, x, T, y, false, 0.0f, st)
+                                 : forward_decode(h, x, T, y, false, st);
+  if (rc) return rc;
   if (dbg) return copy_debug(h, dbg, T, st);
   return 0;
 }
@@ -245,6 +284,7 @@ int lmoe_forward_block(lmoe_t* h, float* x, int32_t T, float eps, void* stream) 
   }
   DeviceGuard g(h->device);
   hipStream_t st = (hipStream_t)stream;
+  if (T > kMaxDecodeT) return forward_prefill(h, x, T, x, true, eps, st);
   if (int rc = rms_rows(h, x, T, eps, st)) return rc;
   return forward_decode(h, x, T, x, true, st);
 }
@@ -258,15 +298,15 @@ int lmoe_set_phase_events(lmoe_t* h, void* const* events, int32_t n) {
     h->phase_events.clear();
     return 0;
   }
-  if (n != kDecodePhases + 1) {
-    set_error("lmoe_set_phase_events: n must be lmoe_phase_count() + 1");
+  if (n != kDecodePhases + 1 && n != kPrefillPhases + 1) {
+    set_error("lmoe_set_phase_events: n must be lmoe_phase_count(T) + 1");
     return LMOE_EINVAL;
   }
   h->phase_events.assign((hipEvent_t*)events, (hipEvent_t*)events + n);
   return 0;
 }
 
-int32_t lmoe_phase_count(void) { return kDecodePhases; }
+int32_t lmoe_phase_count(int32_t T) { return T > kMaxDecodeT ? kPrefillPhases : kDecodePhases; }
 
 void lmoe_destroy(lmoe_t* h) {
   if (!h) return;

@@ -43,6 +43,8 @@ constexpr int kSlot = 1024;
 constexpr int kMaxDecodeT = 8;     // tokens the GEMV (decode) path takes per forward
 constexpr int kMaxWaves = 16;
 constexpr int kDecodePhases = 4;
+constexpr int kPrefillPhases = 8;
+constexpr int kMaxTokens = 1 << 20;   // largest max_tokens a handle accepts
 constexpr int kRouterChunks = 4;  // router column chunks: H / (64 * H/256)
 
 __host__ __device__ constexpr int chunk_cols(int f) {      // columns of one chunk
@@ -109,6 +111,35 @@ struct Workspace {
   int tmax = 0;                  // tokens the decode buffers hold
 };
 
+// Workspace of the prefill path (T > kMaxDecodeT), sized for max_tokens.
+struct PrefillWs {
+  uint16_t* xh = nullptr;          // [T][H] fp16 staged rows (D input)
+  uint16_t* xb = nullptr;          // [T][2][H] bf16 parts (router, shared gate/up)
+  double* xnorm = nullptr;         // [T] 2-norm of the staged rows
+  float* r = nullptr;              // [T] row scale (1/rms in the block forward, else 1)
+  float* logits = nullptr;         // [T][Epad] fp32 router logits
+  int* idx = nullptr;              // [T][K]
+  float* w = nullptr;              // [T][K]
+  unsigned long long* cmask = nullptr;  // [nchunk][E] tokens of a 64-token chunk per expert
+  int* ccnt = nullptr;             // [nchunk][E]
+  int* cbase = nullptr;            // [nchunk][E]
+  int* eorder = nullptr;           // [E] experts in (label, expert) order
+  int* seg_start = nullptr;        // [E]
+  int* expert_count = nullptr;     // [E]
+  int* group_off = nullptr;        // [G+1]
+  void* pieces = nullptr;          // [max pieces] grouped-GEMM work list
+  int* npieces = nullptr;          // [1]
+  int* perm = nullptr;             // [T*K]
+  int* inv = nullptr;              // [T*K] assignment -> sorted position
+  uint16_t* xl = nullptr;          // [T][G][ell] fp16
+  uint16_t* hsb = nullptr;         // [T][2][Fs] shared hidden, bf16 parts
+  uint16_t* h = nullptr;           // [T*K][F] fp16 expert hidden, sorted order
+  float* o = nullptr;              // [T*K][ell] weighted expert outputs
+  uint16_t* s = nullptr;           // [T][G][ell] fp16 per-group sums
+  double* wmax = nullptr;          // [1] max_e |Wr_e|_2
+  int tmax = 0;                    // tokens the buffers hold (0: no prefill path)
+};
+
 }  // namespace lm
 
 struct lmoe {
@@ -116,9 +147,12 @@ struct lmoe {
   int device = 0;
   bool loaded = false;
   lm::Geom g_router, g_d, g_u, g_gu, g_dn, g_sgu, g_sdn;
+  lm::Geom g_router_m;        // router in the MFMA layout (prefill)
   size_t expert_stride = 0;   // bytes per expert in device memory
   size_t ts_off = 0;          // offset of the three fp32 tensor scales
   uint8_t* router = nullptr;  // tiled bf16 [Epad][H]
+  uint8_t* router_m = nullptr;  // prefill: router tiled for MFMA
+  uint16_t* router_rm = nullptr;  // prefill: router bf16 [E][H] row-major
   float* bias = nullptr;      // [E] (zeros without a bias)
   uint8_t* dmat = nullptr;    // G tiled D_g
   uint8_t* umat = nullptr;    // G tiled U_g
@@ -128,6 +162,7 @@ struct lmoe {
   uint8_t* labels = nullptr;  // [E] device copy
   std::vector<uint8_t> labels_host;
   lm::Workspace ws;
+  lm::PrefillWs pw;
   std::vector<void*> allocations;
   std::vector<hipEvent_t> phase_events;   // empty: no phase timing
 };
@@ -145,6 +180,15 @@ int pack_experts_impl(const float* gate, const float* up, const float* down, int
 // decode.hip
 int forward_decode(lmoe_t* h, const float* x, int T, float* y, bool norm, hipStream_t stream);
 int rms_rows(lmoe_t* h, const float* x, int T, float eps, hipStream_t stream);
+
+// prefill.hip
+int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float eps,
+                    hipStream_t stream);
+size_t prefill_max_pieces(int T, int K, int E);
+int prefill_chunks(int T);
+size_t prefill_piece_bytes();
+int prefill_router_wmax(lmoe_t* h, hipStream_t stream);
+int prefill_debug_latent(lmoe_t* h, int T, float* dst, hipStream_t stream);
 
 // api.hip
 void set_error(const std::string& msg);

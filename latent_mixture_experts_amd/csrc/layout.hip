@@ -421,6 +421,19 @@ int load_weights_impl(lmoe_t* h, const lmoe_weights* w, hipStream_t st) {
     if (int rc = copy_in(t, w->router_bf16, (size_t)E * H * 2, st)) return rc;
     Src a{(const uint8_t*)t.p, nullptr, E};
     if (int rc = launch_tile(kBF16R, a, a, 0, H, h->g_router, h->router, st)) return rc;
+    if (h->pw.tmax) {
+      // prefill: the MFMA layout for the logits GEMM, the plain rows for the
+      // fp64 rescoring, and max_e |Wr_e|_2 for its rounding bound
+      if (int rc = launch_tile(kBF16, a, a, 0, H, h->g_router_m, h->router_m, st)) return rc;
+      LMOE_HIP(hipMemcpyAsync(h->router_rm, t.p, (size_t)E * H * 2, hipMemcpyDeviceToDevice, st));
+      if (int rc = prefill_router_wmax(h, st)) return rc;
+      // experts in (label, expert) order
+      std::vector<int> order(E);
+      for (int e = 0; e < E; ++e) order[e] = e;
+      std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return lab[x] < lab[y]; });
+      LMOE_HIP(hipMemcpyAsync(h->pw.eorder, order.data(), sizeof(int) * E, hipMemcpyHostToDevice, st));
+      LMOE_HIP(hipStreamSynchronize(st));
+    }
     if (d.has_router_bias)
       LMOE_HIP(hipMemcpyAsync(h->bias, w->router_bias, sizeof(float) * E, hipMemcpyDefault, st));
     else

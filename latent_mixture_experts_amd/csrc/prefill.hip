@@ -1,0 +1,1049 @@
+// Prefill forward (T > 8 tokens): the layer as MFMA GEMMs.
+//
+// The layer is the one of "Edge0-145B: a Qwen MoE with its experts squeezed,
+// and a 51B table left on the SSD", section "A latent in front of the
+// experts" (layer equation; D over all groups, U once per group a token
+// routed into), with the shapes and formats of the "Edge0 145B and Edge0
+// 120B" model page ("Model profile" and architecture tables).
+//
+//   prep     x (or x / rms(x)) staged once: fp16 for D, two bf16 parts for
+//            the router and the shared expert, and |x|_2 per token
+//   router   logits on MFMA (bf16 x bf16 products are exact, fp32 sums);
+//            per token every expert whose fp32 logit lies within twice the
+//            rounding bound of the K-th largest is rescored in fp64, and
+//            top-K and softmax are taken on the fp64 logits. The bound holds
+//            for any summation order, so the kept set is the one exact
+//            arithmetic gives.
+//   permute  stable order of the assignments by (group label, expert): per
+//            64-token chunk a bitmask per expert gives each assignment its
+//            rank among earlier tokens of the chunk; chunk counts are
+//            prefix-summed per expert. No sort, no atomics on positions.
+//   D        dense GEMM over the stacked D_g: xl[t][g] = D_g x[t] (fp16)
+//   experts  grouped GEMMs over the (label, expert) segments, in pieces of
+//            up to 128 assignments: gate/up with SwiGLU in the epilogue
+//            (fp16 h), down scaled by the routing weight (fp32 o)
+//   combine  s[t][g] = sum of token t's outputs in group g, ascending k
+//            (fp16; zero for groups t did not route into)
+//   U        dense GEMM with the G matrices concatenated along K, followed in
+//            the same accumulators by the shared expert's down projection
+//   shared   gate/up GEMM with SwiGLU in the epilogue
+//
+// GEMM tile: 128 tokens x 128 weight rows (two 64-row tiles of the tiled
+// stream) per 256-thread workgroup. Wave w takes tokens 64*(w&1).. and weight
+// tile w>>1: 4 x 4 accumulators of v_mfma_f32_16x16x32. The weight operand
+// is loaded from HBM straight into registers (the tiled stream is already
+// the MFMA B-operand layout) one stage ahead and decoded in registers just
+// before use: NVFP4 to fp16 exactly (e2m1 * e4m3 <= 6 significant bits),
+// Q8/Q4 to fp16(q * d), bf16 as stored. The activation stage (128 columns,
+// or 64 columns in two bf16 parts) goes through a double-buffered LDS tile
+// shared by the two waves of the same tokens.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include <algorithm>
+
+#include "internal.h"
+
+namespace lm {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+
+constexpr int NTH = 256;       // threads per GEMM workgroup (4 waves)
+constexpr int BM = 128;        // tokens per GEMM tile
+constexpr int MB = BM / 32;    // 16-token MFMA blocks per wave
+constexpr int WM = BM / 2;     // tokens per wave
+constexpr int CHUNK_T = 64;    // tokens per permutation chunk
+
+__device__ __forceinline__ uint4 ldnt(const uint8_t* p) {
+  const u4v v = __builtin_nontemporal_load((const u4v*)p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
+
+// ---------------------------------------------------------------------------
+// Weight decoding: the 8 columns one lane holds of one 32-column block.
+
+__device__ __forceinline__ half8 q8_row8(uint32_t w0, uint32_t w1, _Float16 d) {
+  // offset-binary q + 128 as the low byte of fp16 1024 + u, minus 1152 = q
+  const half2v off = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const half2v dd = {d, d};
+  const uint32_t p[4] = {__builtin_amdgcn_perm(0x64646464u, w0, 0x05010400u),
+                         __builtin_amdgcn_perm(0x64646464u, w0, 0x05030402u),
+                         __builtin_amdgcn_perm(0x64646464u, w1, 0x05010400u),
+                         __builtin_amdgcn_perm(0x64646464u, w1, 0x05030402u)};
+  half8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const half2v h = (__builtin_bit_cast(half2v, p[i]) - off) * dd;
+    r[2 * i] = h[0];
+    r[2 * i + 1] = h[1];
+  }
+  return r;
+}
+
+__device__ __forceinline__ half8 q4_row8(uint32_t w, _Float16 d) {
+  // nibble i (low) and i + 4 (high) of byte i hold q + 8 of elements i, i + 4
+  const half2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const half2v dd = {d, d};
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  const uint32_t p[4] = {__builtin_amdgcn_perm(0x64646464u, lo, 0x05010400u),
+                         __builtin_amdgcn_perm(0x64646464u, lo, 0x05030402u),
+                         __builtin_amdgcn_perm(0x64646464u, hi, 0x05010400u),
+                         __builtin_amdgcn_perm(0x64646464u, hi, 0x05030402u)};
+  half8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const half2v h = (__builtin_bit_cast(half2v, p[i]) - off) * dd;
+    r[2 * i] = h[0];
+    r[2 * i + 1] = h[1];
+  }
+  return r;
+}
+
+__device__ __forceinline__ half8 fp4_row8(uint32_t w, _Float16 s) {
+  const half2v ss = {s, s};
+  const half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
+  const half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
+  const half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
+  const half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
+  half8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// The GEMM core.
+
+template <int WF>
+struct Fm {
+  static constexpr int CC = chunk_cols(WF);               // columns per chunk (memory)
+  static constexpr int SCOLS = WF == kBF16 ? 64 : 128;    // columns per stage
+  static constexpr int SC = SCOLS / CC;                   // chunks per stage
+  static constexpr int KB = SCOLS / 32;                   // MFMA k-steps per stage
+  static constexpr int BPC = CC / 32;                     // k-steps per chunk
+  static constexpr int NP = WF == kBF16 ? 2 : 1;          // activation parts
+  static constexpr int AST = SCOLS + 8;                   // LDS row stride (elements)
+  static constexpr int PPR = SCOLS / 8;                   // 16-byte pieces per row
+  static constexpr int PPT = NP * BM * PPR / NTH;         // pieces per thread
+  static constexpr int LDSA = NP * BM * AST;              // elements per LDS buffer
+};
+constexpr int kLdsA = Fm<kBF16>::LDSA > Fm<kFP4>::LDSA ? Fm<kBF16>::LDSA : Fm<kFP4>::LDSA;
+static_assert(Fm<kQ8>::LDSA <= kLdsA && Fm<kQ4>::LDSA <= kLdsA, "LDS sizing");
+
+// A weight operand: `nmat` matrices of one geometry concatenated along K
+// (U_0 .. U_{G-1}); tile j of a matrix at base + j * tile_slots slots.
+struct WMat {
+  const uint8_t* base;
+  Geom g;
+  size_t mat_bytes;
+  int nmat;
+};
+
+// An activation operand: element (row, part, col) of matrix m at
+// p + row * rs + part * ps + m * kmat + col; 16-bit elements.
+struct AMat {
+  const uint16_t* p;
+  size_t rs;
+  int ps;
+  int kmat;
+};
+
+template <int WF>
+struct BStage {
+  uint4 raw[Fm<WF>::SC][4];
+  uint2 sc[4];
+};
+
+template <int WF>
+__device__ __forceinline__ void fetch_b(const WMat& W, int tile, int s, BStage<WF>& B) {
+  using F = Fm<WF>;
+  const int lane = threadIdx.x & 63;
+  const int kmat = W.g.k;
+  const int spm = (kmat + F::SCOLS - 1) / F::SCOLS;
+  const int cpm = (kmat + F::CC - 1) / F::CC;
+  const int mat = s / spm, sm = s % spm;
+  const int col0 = sm * F::SCOLS;
+  const int ss = col0 / kSSCols, cin0 = (col0 % kSSCols) / F::CC;
+  const int ncs = ss_code_slots(WF, min(kSSCols, kmat - ss * kSSCols));
+  const uint8_t* sb = W.base + (size_t)mat * W.mat_bytes +
+                      ((size_t)tile * W.g.tile_slots + (size_t)ss * W.g.full) * kSlot;
+#pragma unroll
+  for (int j = 0; j < F::SC; ++j)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+      B.raw[j][rg] = (sm * F::SC + j < cpm)
+                         ? ldnt(sb + (size_t)((cin0 + j) * 4 + rg) * kSlot + lane * 16)
+                         : make_uint4(0, 0, 0, 0);
+  if constexpr (WF != kBF16) {
+    const int off = WF == kQ8 ? 4 * cin0 : 8 * cin0;
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+      B.sc[rg] = *(const uint2*)(sb + (size_t)ncs * kSlot + (16 * rg + (lane & 15)) * 16 + off);
+  }
+}
+
+// decoded B operand of k-step kb for row group rg
+template <int WF>
+__device__ __forceinline__ uint4 decode_b(const BStage<WF>& B, int kb, int rg) {
+  using F = Fm<WF>;
+  const int j = kb / F::BPC, b = kb % F::BPC;
+  const uint4 w = B.raw[j][rg];
+  if constexpr (WF == kBF16) {
+    return w;
+  } else if constexpr (WF == kFP4) {
+    const int qg = (threadIdx.x & 63) >> 4;
+    const int byte = 2 * b + (qg >> 1);
+    const uint32_t sw = byte < 4 ? B.sc[rg].x : B.sc[rg].y;
+    const uint32_t code = (sw >> (8 * (byte & 3))) & 0xFFu;
+    const _Float16 s = (_Float16)__builtin_amdgcn_cvt_f32_fp8(code, 0);
+    return __builtin_bit_cast(uint4, fp4_row8(word(w, b), s));
+  } else {
+    const int blk = F::BPC * j + b;          // block within the stage: 0..3
+    const uint32_t sw = blk < 2 ? B.sc[rg].x : B.sc[rg].y;
+    const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(sw >> (16 * (blk & 1))));
+    if constexpr (WF == kQ8) return __builtin_bit_cast(uint4, q8_row8(word(w, 2 * b), word(w, 2 * b + 1), d));
+    else return __builtin_bit_cast(uint4, q4_row8(word(w, b), d));
+  }
+}
+
+template <int WF>
+__device__ __forceinline__ void fetch_a(const AMat& A, const int* arow, int s, uint4 (&ar)[Fm<WF>::PPT]) {
+  using F = Fm<WF>;
+  const int spm = (A.kmat + F::SCOLS - 1) / F::SCOLS;
+  const int mat = s / spm, col0 = (s % spm) * F::SCOLS;
+#pragma unroll
+  for (int i = 0; i < F::PPT; ++i) {
+    const int p = threadIdx.x + i * NTH;
+    const int part = p / (BM * F::PPR), rem = p % (BM * F::PPR);
+    const int m = rem / F::PPR, kk = col0 + (rem % F::PPR) * 8;
+    const int row = arow[m];
+    ar[i] = make_uint4(0, 0, 0, 0);
+    if (row >= 0 && kk < A.kmat)
+      ar[i] = *(const uint4*)(A.p + (size_t)row * A.rs + (size_t)part * A.ps + (size_t)mat * A.kmat + kk);
+  }
+}
+
+template <int WF>
+__device__ __forceinline__ void store_a(uint16_t* As, const uint4 (&ar)[Fm<WF>::PPT]) {
+  using F = Fm<WF>;
+#pragma unroll
+  for (int i = 0; i < F::PPT; ++i) {
+    const int p = threadIdx.x + i * NTH;
+    const int part = p / (BM * F::PPR), rem = p % (BM * F::PPR);
+    const int m = rem / F::PPR, c = (rem % F::PPR) * 8;
+    *(uint4*)(As + (size_t)(part * BM + m) * F::AST + c) = ar[i];
+  }
+}
+
+template <int WF>
+__device__ __forceinline__ void mfma_stage(const uint16_t* As, const BStage<WF>& B, int wm,
+                                           f4 (&acc)[MB][4]) {
+  using F = Fm<WF>;
+  const int lane = threadIdx.x & 63, tok = lane & 15, qg = lane >> 4;
+#pragma unroll
+  for (int kb = 0; kb < F::KB; ++kb) {
+    uint4 bw[4];
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) bw[rg] = decode_b<WF>(B, kb, rg);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = WM * wm + 16 * mb + tok;
+      if constexpr (WF == kBF16) {
+        bf16x8 a[F::NP];
+#pragma unroll
+        for (int p = 0; p < F::NP; ++p)
+          a[p] = *(const bf16x8*)(As + (size_t)(p * BM + m) * F::AST + 32 * kb + 8 * qg);
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+          for (int p = 0; p < F::NP; ++p)
+            acc[mb][rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                a[p], __builtin_bit_cast(bf16x8, bw[rg]), acc[mb][rg], 0, 0, 0);
+      } else {
+        const half8 a = *(const half8*)(As + (size_t)m * F::AST + 32 * kb + 8 * qg);
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg)
+          acc[mb][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              a, __builtin_bit_cast(half8, bw[rg]), acc[mb][rg], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Accumulates the tile's product over all stages of W (all nmat matrices).
+// `tile` is this wave's weight tile, `b_on` whether it exists, `on` whether
+// the wave has any work (tile exists and some of its tokens are valid).
+// Every thread of the block takes part in the staging and the barriers.
+template <int WF>
+__device__ __forceinline__ void gemm_loop(const WMat& W, int tile, bool b_on, bool on, const AMat& A,
+                                          const int* arow, uint16_t* As, f4 (&acc)[MB][4]) {
+  using F = Fm<WF>;
+  const int wm = (threadIdx.x >> 6) & 1;
+  const int nst = ((W.g.k + F::SCOLS - 1) / F::SCOLS) * W.nmat;
+  uint4 ar[F::PPT];
+  BStage<WF> b0, b1;
+  fetch_a<WF>(A, arow, 0, ar);
+  if (b_on) fetch_b<WF>(W, tile, 0, b0);
+  for (int s = 0; s < nst; s += 2) {
+    // even stage: LDS buffer 0, weights b0; prefetch s + 1 into b1
+    store_a<WF>(As, ar);
+    __syncthreads();
+    if (s + 1 < nst) {
+      fetch_a<WF>(A, arow, s + 1, ar);
+      if (b_on) fetch_b<WF>(W, tile, s + 1, b1);
+    }
+    if (on) mfma_stage<WF>(As, b0, wm, acc);
+    if (s + 1 >= nst) break;
+    // odd stage: LDS buffer 1, weights b1; prefetch s + 2 into b0
+    store_a<WF>(As + kLdsA, ar);
+    __syncthreads();
+    if (s + 2 < nst) {
+      fetch_a<WF>(A, arow, s + 2, ar);
+      if (b_on) fetch_b<WF>(W, tile, s + 2, b0);
+    }
+    if (on) mfma_stage<WF>(As + kLdsA, b1, wm, acc);
+  }
+  // the caller may restage the LDS right after
+  __syncthreads();
+}
+
+__device__ __forceinline__ void zero_acc(f4 (&acc)[MB][4]) {
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) acc[mb][rg] = (f4){0.f, 0.f, 0.f, 0.f};
+}
+
+// Lane l of wave (wm, wn) holds in acc[mb][rg][v] the tile-relative token
+// WM*wm + 16*mb + 4*(l/16) + v and the row 16*rg + l%16 of its weight tile.
+__device__ __forceinline__ int acc_tok(int wm, int lane, int mb, int v) {
+  return WM * wm + 16 * mb + 4 * (lane >> 4) + v;
+}
+
+// ---------------------------------------------------------------------------
+// Dense GEMMs: router, D, shared gate/up, U (+ shared down).
+
+enum Epi : int {
+  kEpiLogits = 0,   // fp32 out[t][n], n < nvalid
+  kEpiF16 = 1,      // fp16 out[t][n]
+  kEpiSwigluB2 = 2, // paired gate/up tile: h = silu(g) * u as two bf16 parts
+  kEpiY = 3,        // fp32 y[t][n] (+ residual)
+};
+
+struct Dense {
+  WMat W;
+  AMat A;
+  WMat W2;       // kEpiY: the shared down projection, same accumulators
+  AMat A2;
+  int T, mtiles, ntiles, npairs;
+  void* out;
+  size_t ostride;
+  int nvalid;
+  const float* res;   // kEpiY: residual rows [T][ostride] or null
+};
+
+template <int WF, int EPI>
+__global__ __launch_bounds__(NTH, 2) void k_dense(Dense a) {
+  __shared__ __align__(16) uint16_t As[2 * kLdsA];
+  __shared__ int arow[BM];
+  // XCD-aware order: each of the 8 XCDs takes a contiguous range of logical
+  // tiles; within it, groups of 8 token tiles sweep the weight tiles with the
+  // token tile fastest, so neighbours in time share A and B in L2.
+  const int nblk = a.mtiles * a.npairs;
+  const int bid = blockIdx.x, xcd = bid & 7, q = bid >> 3;
+  const int per = nblk >> 3, rem = nblk & 7;
+  const int L = xcd * per + min(xcd, rem) + q;
+  constexpr int GM = 8;
+  const int span = GM * a.npairs;
+  const int first = (L / span) * GM, gsz = min(a.mtiles - first, GM);
+  const int mt = first + (L % span) % gsz, pair = (L % span) / gsz;
+
+  if (threadIdx.x < BM) {
+    const int t = mt * BM + threadIdx.x;
+    arow[threadIdx.x] = t < a.T ? t : -1;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
+  const int tile = 2 * pair + wn;
+  const bool b_on = tile < a.ntiles;
+  const bool on = b_on && mt * BM + WM * wm < a.T;
+  f4 acc[MB][4];
+  zero_acc(acc);
+  gemm_loop<WF>(a.W, tile, b_on, on, a.A, arow, As, acc);
+  if constexpr (EPI == kEpiY) gemm_loop<kBF16>(a.W2, tile, b_on, on, a.A2, arow, As, acc);
+  if (!on) return;
+
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int t = mt * BM + acc_tok(wm, lane, mb, v);
+      if (t >= a.T) continue;
+      if constexpr (EPI == kEpiSwigluB2) {
+        // rows 0..31 of the tile are gate rows 32*tile + 0..31, rows 32..63
+        // the up rows of the same indices
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg) {
+          const int f = 32 * tile + 16 * rg + (lane & 15);
+          const float hv = silu(acc[mb][rg][v]) * acc[mb][rg + 2][v];
+          const __bf16 h0 = (__bf16)hv;
+          const __bf16 h1 = (__bf16)(hv - (float)h0);
+          __bf16* o = (__bf16*)a.out + (size_t)t * a.ostride;
+          o[f] = h0;
+          o[a.nvalid + f] = h1;
+        }
+      } else {
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int n = 64 * tile + 16 * rg + (lane & 15);
+          const float val = acc[mb][rg][v];
+          if constexpr (EPI == kEpiLogits) {
+            if (n < a.nvalid) ((float*)a.out)[(size_t)t * a.ostride + n] = val;
+          } else if constexpr (EPI == kEpiF16) {
+            ((_Float16*)a.out)[(size_t)t * a.ostride + n] = (_Float16)val;
+          } else {
+            const size_t i = (size_t)t * a.ostride + n;
+            ((float*)a.out)[i] = a.res ? a.res[i] + val : val;
+          }
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Grouped GEMMs over the expert segments.
+
+struct Piece {
+  int expert, start, count, pad;
+};
+
+enum GEpi : int { kGateUp = 0, kDown = 1 };
+
+struct Grouped {
+  const uint8_t* experts;
+  size_t estride;       // bytes per expert
+  size_t woff;          // offset of this matrix in an expert
+  size_t ts_off;        // offset of the three fp32 tensor scales
+  Geom g;
+  AMat A;
+  const Piece* pieces;
+  const int* npieces;
+  int ntiles, npairs, G, F;
+  const int* perm;      // [T*K] sorted position -> assignment t*K + k
+  const float* topk_w;  // [T*K]
+  const uint8_t* labels;
+  int K;
+  void* out;
+  size_t ostride;
+};
+
+template <int EPI>
+__global__ __launch_bounds__(NTH, 2) void k_grouped(Grouped a) {
+  __shared__ __align__(16) uint16_t As[2 * kLdsA];
+  __shared__ int arow[BM];
+  // piece p runs on XCD p % 8, all its weight-tile pairs back to back
+  const int bid = blockIdx.x, xcd = bid & 7, q = bid >> 3;
+  const int p = xcd + 8 * (q / a.npairs), pair = q % a.npairs;
+  if (p >= *a.npieces) return;
+  const Piece pc = a.pieces[p];
+  const int e = pc.expert;
+  if (threadIdx.x < BM) {
+    const int i = threadIdx.x;
+    int row = -1;
+    if (i < pc.count) {
+      const int pos = pc.start + i;
+      row = EPI == kGateUp ? (a.perm[pos] / a.K) * a.G + a.labels[e] : pos;
+    }
+    arow[i] = row;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
+  const int tile = 2 * pair + wn;
+  const bool b_on = tile < a.ntiles;
+  const bool on = b_on && WM * wm < pc.count;
+  const uint8_t* base = a.experts + (size_t)e * a.estride;
+  const WMat W{base + a.woff, a.g, 0, 1};
+  f4 acc[MB][4];
+  zero_acc(acc);
+  gemm_loop<kFP4>(W, tile, b_on, on, a.A, arow, As, acc);
+  if (!on) return;
+  const float* ts = (const float*)(base + a.ts_off);
+
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = acc_tok(wm, lane, mb, v);
+      if (i >= pc.count) continue;
+      const size_t pos = (size_t)pc.start + i;
+      if constexpr (EPI == kGateUp) {
+        const float tg = ts[0], tu = ts[1];
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg) {
+          const int f = 32 * tile + 16 * rg + (lane & 15);
+          const float hv = silu(acc[mb][rg][v] * tg) * (acc[mb][rg + 2][v] * tu);
+          ((_Float16*)a.out)[pos * a.ostride + f] = (_Float16)hv;
+        }
+      } else {
+        const float sc = a.topk_w[a.perm[pos]] * ts[2];
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int n = 64 * tile + 16 * rg + (lane & 15);
+          ((float*)a.out)[pos * a.ostride + n] = acc[mb][rg][v] * sc;
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Staging of the input rows.
+
+struct Prep {
+  const float* x;
+  int T, H;
+  int norm;
+  float eps;
+  _Float16* xh;     // [T][H]
+  __bf16* xb;       // [T][2][H]
+  double* xnorm;    // [T] |staged row|_2
+  float* r;         // [T] the row scale (1/rms, or 1)
+};
+
+__device__ __forceinline__ double block_sum(double v, double* red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  double s = 0.0;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += red[i];
+  __syncthreads();
+  return s;
+}
+
+__global__ __launch_bounds__(256) void k_prep(Prep a) {
+  __shared__ double red[4];
+  const int t = blockIdx.x;
+  const float* xr = a.x + (size_t)t * a.H;
+  float r = 1.0f;
+  if (a.norm) {
+    double s = 0.0;
+    for (int i = threadIdx.x; i < a.H; i += blockDim.x) {
+      const double v = xr[i];
+      s += v * v;
+    }
+    s = block_sum(s, red);
+    r = (float)(1.0 / sqrt(s / a.H + (double)a.eps));
+  }
+  double s2 = 0.0;
+  for (int i = threadIdx.x; i < a.H; i += blockDim.x) {
+    const float v = a.norm ? xr[i] * r : xr[i];
+    a.xh[(size_t)t * a.H + i] = (_Float16)v;
+    const __bf16 b0 = (__bf16)v;
+    a.xb[(size_t)t * 2 * a.H + i] = b0;
+    a.xb[(size_t)t * 2 * a.H + a.H + i] = (__bf16)(v - (float)b0);
+    s2 += (double)v * v;
+  }
+  s2 = block_sum(s2, red);
+  if (threadIdx.x == 0) {
+    a.xnorm[t] = sqrt(s2);
+    a.r[t] = r;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Routing: certified candidates, fp64 rescoring, top-K, softmax.
+
+struct Select {
+  const float* logits;       // [T][Epad] fp32 router GEMM output
+  int Epad, T, E, H, K;
+  const float* bias;         // [E]
+  const float* x;            // [T][H] raw input rows
+  const float* r;            // [T] row scale
+  const double* xnorm;       // [T]
+  const double* wmax;        // max_e |Wr_e|_2
+  const uint16_t* wr;        // router bf16 [E][H] row-major
+  double cbeta;              // rounding bound per unit |x| |w|
+  int* idx;                  // [T][K]
+  float* w;                  // [T][K]
+};
+
+__device__ __forceinline__ double bf16_to_f64(uint32_t bits) {
+  return (double)__uint_as_float(bits << 16);
+}
+
+// fp64 dot product of x row (fp32) and router row e (bf16), whole wave
+__device__ double dot64(const float* xr, const uint16_t* wrow, int H) {
+  const int lane = threadIdx.x & 63;
+  double s = 0.0;
+  for (int c = 8 * lane; c < H; c += 512) {
+    const float4 x0 = *(const float4*)(xr + c);
+    const float4 x1 = *(const float4*)(xr + c + 4);
+    const uint4 w = *(const uint4*)(wrow + c);
+    s = fma((double)x0.x, bf16_to_f64(w.x & 0xFFFFu), s);
+    s = fma((double)x0.y, bf16_to_f64(w.x >> 16), s);
+    s = fma((double)x0.z, bf16_to_f64(w.y & 0xFFFFu), s);
+    s = fma((double)x0.w, bf16_to_f64(w.y >> 16), s);
+    s = fma((double)x1.x, bf16_to_f64(w.z & 0xFFFFu), s);
+    s = fma((double)x1.y, bf16_to_f64(w.z >> 16), s);
+    s = fma((double)x1.z, bf16_to_f64(w.w & 0xFFFFu), s);
+    s = fma((double)x1.w, bf16_to_f64(w.w >> 16), s);
+  }
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  return s;
+}
+
+// wave arg-max over (value desc, index asc)
+__device__ __forceinline__ void wave_argmax(double& v, int& i) {
+  for (int o = 32; o > 0; o >>= 1) {
+    const double ov = __shfl_xor(v, o);
+    const int oi = __shfl_xor(i, o);
+    if (ov > v || (ov == v && oi < i)) {
+      v = ov;
+      i = oi;
+    }
+  }
+}
+
+constexpr int kMaxE = 1024;
+constexpr int kEPL = kMaxE / 64;   // experts per lane
+
+__global__ __launch_bounds__(256) void k_select(Select a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= a.T) return;
+  // fp32 logits + bias, exactly in fp64
+  double v[kEPL];
+#pragma unroll
+  for (int i = 0; i < kEPL; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < a.E ? (double)a.logits[(size_t)t * a.Epad + e] + (double)a.bias[e] : -INFINITY;
+  }
+  // the K-th largest approximate logit: K rounds removing one maximum each
+  double vk = -INFINITY;
+  {
+    double u[kEPL];
+#pragma unroll
+    for (int i = 0; i < kEPL; ++i) u[i] = v[i];
+    for (int k = 0; k < a.K; ++k) {
+      double bv = -INFINITY;
+      int bi = 0x7FFFFFFF;
+#pragma unroll
+      for (int i = 0; i < kEPL; ++i) {
+        const int e = lane + 64 * i;
+        if (u[i] > bv) {
+          bv = u[i];
+          bi = e;
+        }
+      }
+      wave_argmax(bv, bi);
+      vk = bv;
+#pragma unroll
+      for (int i = 0; i < kEPL; ++i)
+        if (lane + 64 * i == bi) u[i] = -INFINITY;
+    }
+  }
+  // every expert whose exact logit can reach the top K: its fp32 logit is
+  // within 2 beta of the K-th largest (|fp32 - exact| <= beta for all e)
+  const double beta = a.cbeta * a.xnorm[t] * *a.wmax + 1e-30;
+  const double thr = vk - 2.0 * beta;
+  const double rt = (double)a.r[t];
+  const float* xr = a.x + (size_t)t * a.H;
+  double ex[kEPL];
+#pragma unroll
+  for (int i = 0; i < kEPL; ++i) ex[i] = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kEPL; ++i) {
+    unsigned long long m = __ballot(v[i] >= thr);
+    while (m) {
+      const int src = __builtin_ctzll(m);
+      m &= m - 1;
+      const int e = src + 64 * i;
+      const double l = dot64(xr, a.wr + (size_t)e * a.H, a.H) * rt + (double)a.bias[e];
+      if (lane == src) ex[i] = l;
+    }
+  }
+  // top K of the exact logits; lane k keeps the k-th. Taken experts and
+  // e >= E are NaN (never chosen); experts outside the candidate set stay at
+  // -inf, so K distinct valid experts come out even for rows with NaN logits.
+#pragma unroll
+  for (int i = 0; i < kEPL; ++i)
+    if (lane + 64 * i >= a.E) ex[i] = NAN;
+  double kv = 0.0, top = 0.0;
+  int ki = 0;
+  for (int k = 0; k < a.K; ++k) {
+    double bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < kEPL; ++i) {
+      const int e = lane + 64 * i;
+      if (ex[i] > bv || (ex[i] == bv && e < bi)) {
+        bv = ex[i];
+        bi = e;
+      }
+    }
+    wave_argmax(bv, bi);
+    if (k == 0) top = bv;
+    if (lane == k) {
+      kv = bv;
+      ki = bi;
+    }
+#pragma unroll
+    for (int i = 0; i < kEPL; ++i)
+      if (lane + 64 * i == bi) ex[i] = NAN;
+  }
+  const double z = lane < a.K ? exp(kv - top) : 0.0;
+  double zs = z;
+  for (int o = 32; o > 0; o >>= 1) zs += __shfl_xor(zs, o);
+  if (lane < a.K) {
+    a.idx[(size_t)t * a.K + lane] = ki;
+    a.w[(size_t)t * a.K + lane] = (float)(z / zs);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Permutation.
+
+struct Perm {
+  const int* idx;        // [T][K]
+  int T, K, E, G, nchunk;
+  unsigned long long* cmask;   // [nchunk][E]
+  int* ccnt;             // [nchunk][E] tokens of the chunk per expert
+  int* cbase;            // [nchunk][E] tokens of earlier chunks per expert
+  const int* eorder;     // [E] experts in (label, expert) order
+  const uint8_t* labels;
+  int* seg_start;        // [E]
+  int* expert_count;     // [E]
+  int* group_off;        // [G+1]
+  Piece* pieces;
+  int* npieces;
+  int* perm;             // [T*K]
+  int* inv;              // [T*K]
+};
+
+__global__ __launch_bounds__(256) void k_perm_mask(Perm a) {
+  __shared__ unsigned long long m[kMaxE];
+  const int c = blockIdx.x;
+  for (int e = threadIdx.x; e < a.E; e += blockDim.x) m[e] = 0ull;
+  __syncthreads();
+  const int n = CHUNK_T * a.K;
+  for (int j = threadIdx.x; j < n; j += blockDim.x) {
+    const int t = c * CHUNK_T + j / a.K;
+    if (t < a.T) atomicOr(&m[a.idx[(size_t)t * a.K + j % a.K]], 1ull << (t % CHUNK_T));
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < a.E; e += blockDim.x) {
+    a.cmask[(size_t)c * a.E + e] = m[e];
+    a.ccnt[(size_t)c * a.E + e] = __popcll(m[e]);
+  }
+}
+
+// one block of kMaxE threads: chunk prefixes, segment starts, group offsets
+// and the piece list of the grouped GEMMs
+__global__ __launch_bounds__(kMaxE) void k_perm_scan(Perm a) {
+  __shared__ int sc[kMaxE];
+  __shared__ int sp[kMaxE];
+  const int j = threadIdx.x;
+  if (j < a.E) {
+    int cnt = 0;
+    for (int c = 0; c < a.nchunk; ++c) {
+      const size_t i = (size_t)c * a.E + j;
+      const int v = a.ccnt[i];
+      a.cbase[i] = cnt;
+      cnt += v;
+    }
+    a.expert_count[j] = cnt;
+  }
+  __syncthreads();
+  // counts in (label, expert) order
+  const int e = j < a.E ? a.eorder[j] : 0;
+  const int c_e = j < a.E ? a.expert_count[e] : 0;
+  const int np = (c_e + BM - 1) / BM;
+  sc[j] = c_e;
+  sp[j] = np;
+  __syncthreads();
+  for (int o = 1; o < kMaxE; o <<= 1) {
+    const int x0 = j >= o ? sc[j - o] : 0, x1 = j >= o ? sp[j - o] : 0;
+    __syncthreads();
+    sc[j] += x0;
+    sp[j] += x1;
+    __syncthreads();
+  }
+  const int start = sc[j] - c_e, pstart = sp[j] - np;
+  if (j < a.E) {
+    a.seg_start[e] = start;
+    for (int i = 0; i < np; ++i) {
+      Piece p;
+      p.expert = e;
+      p.start = start + i * BM;
+      p.count = min(BM, c_e - i * BM);
+      p.pad = 0;
+      a.pieces[pstart + i] = p;
+    }
+    // the first expert of each label opens its group's segment
+    const int lab = a.labels[e];
+    const int prev = j > 0 ? a.labels[a.eorder[j - 1]] : -1;
+    for (int g = prev + 1; g <= lab; ++g) a.group_off[g] = start;
+    if (j == a.E - 1) {
+      for (int g = lab + 1; g <= a.G; ++g) a.group_off[g] = sc[j];
+      *a.npieces = sp[j];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_perm_scatter(Perm a) {
+  const int n = a.T * a.K;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int t = i / a.K, e = a.idx[i];
+  const size_t ci = (size_t)(t / CHUNK_T) * a.E + e;
+  const unsigned long long below = (1ull << (t % CHUNK_T)) - 1ull;
+  const int pos = a.seg_start[e] + a.cbase[ci] + __popcll(a.cmask[ci] & below);
+  a.perm[pos] = i;
+  a.inv[i] = pos;
+}
+
+// ---------------------------------------------------------------------------
+// Combine: s[t][g] = sum over k ascending of o[pos(t, k)] for label g.
+
+struct Combine {
+  const int* idx;
+  const int* inv;
+  const uint8_t* labels;
+  const float* o;     // [T*K][L]
+  _Float16* s;        // [T][G][L]
+  int K, G, L;
+};
+
+__global__ __launch_bounds__(256) void k_combine(Combine a) {
+  __shared__ int pos[64];
+  __shared__ int lab[64];
+  const int t = blockIdx.x;
+  if (threadIdx.x < a.K) {
+    const size_t i = (size_t)t * a.K + threadIdx.x;
+    pos[threadIdx.x] = a.inv[i];
+    lab[threadIdx.x] = a.labels[a.idx[i]];
+  }
+  __syncthreads();
+  const int nq = a.L / 4;
+  for (int g = 0; g < a.G; ++g) {
+    for (int q = threadIdx.x; q < nq; q += blockDim.x) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k = 0; k < a.K; ++k) {
+        if (lab[k] != g) continue;
+        const float4 v = *(const float4*)(a.o + (size_t)pos[k] * a.L + 4 * q);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+      }
+      _Float16* d = a.s + ((size_t)t * a.G + g) * a.L + 4 * q;
+      half2v h0 = {(_Float16)acc.x, (_Float16)acc.y};
+      half2v h1 = {(_Float16)acc.z, (_Float16)acc.w};
+      *(half2v*)d = h0;
+      *(half2v*)(d + 2) = h1;
+    }
+  }
+}
+
+// fp16 latent rows to fp32 (debug copy)
+__global__ void k_f16_to_f32(const _Float16* src, size_t n, float* dst) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = (float)src[i];
+}
+
+// max_e |Wr_e|_2 of the row-major bf16 router, fp64, one block
+__global__ __launch_bounds__(1024) void k_router_wmax(const uint16_t* wr, int E, int H, double* out) {
+  __shared__ double red[16];
+  double mx = 0.0;
+  for (int e = threadIdx.x >> 6; e < E; e += 16) {
+    double s = 0.0;
+    for (int c = threadIdx.x & 63; c < H; c += 64) {
+      const double w = bf16_to_f64(wr[(size_t)e * H + c]);
+      s += w * w;
+    }
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    mx = fmax(mx, sqrt(s));
+  }
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double m = 0.0;
+    for (int i = 0; i < 16; ++i) m = fmax(m, red[i]);
+    // |w| is computed with relative error far below 1e-12; round it up
+    *out = m * (1.0 + 1e-12);
+  }
+}
+
+template <int WF, int EPI>
+int launch_dense(const Dense& a, hipStream_t st) {
+  const unsigned nblk = (unsigned)(a.mtiles * a.npairs);
+  if (nblk == 0) return 0;
+  hipLaunchKernelGGL((k_dense<WF, EPI>), dim3(nblk), dim3(NTH), 0, st, a);
+  LMOE_HIP(hipGetLastError());
+  return 0;
+}
+
+}  // namespace
+
+size_t prefill_max_pieces(int T, int K, int E) {
+  const size_t n = (size_t)T * K;
+  return n / BM + 1 + std::min<size_t>(n, (size_t)E);
+}
+int prefill_chunks(int T) { return (T + CHUNK_T - 1) / CHUNK_T; }
+size_t prefill_piece_bytes() { return sizeof(Piece); }
+
+int prefill_router_wmax(lmoe_t* h, hipStream_t st) {
+  hipLaunchKernelGGL(k_router_wmax, dim3(1), dim3(1024), 0, st, (const uint16_t*)h->router_rm,
+                     h->d.n_experts, h->d.hidden, h->pw.wmax);
+  LMOE_HIP(hipGetLastError());
+  return 0;
+}
+
+int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float eps,
+                    hipStream_t st) {
+  const lmoe_dims& d = h->d;
+  const PrefillWs& p = h->pw;
+  const int H = d.hidden, L = d.latent, E = d.n_experts, K = d.top_k, G = d.n_groups,
+            F = d.expert_ffn, Fs = d.shared_ffn;
+  const int Epad = h->g_router_m.tiles * 64;
+  const int mtiles = (T + BM - 1) / BM;
+  const bool ev = h->phase_events.size() == (size_t)kPrefillPhases + 1;
+  if (ev) LMOE_HIP(hipEventRecord(h->phase_events[0], st));
+
+  // staging
+  {
+    Prep a{x, T, H, norm ? 1 : 0, eps, (_Float16*)p.xh, (__bf16*)p.xb, p.xnorm, p.r};
+    hipLaunchKernelGGL(k_prep, dim3(T), dim3(256), 0, st, a);
+    LMOE_HIP(hipGetLastError());
+  }
+  // router logits
+  {
+    Dense a{};
+    a.W = WMat{h->router_m, h->g_router_m, 0, 1};
+    a.A = AMat{p.xb, (size_t)2 * H, H, H};
+    a.T = T; a.mtiles = mtiles; a.ntiles = h->g_router_m.tiles; a.npairs = (a.ntiles + 1) / 2;
+    a.out = p.logits; a.ostride = Epad; a.nvalid = E;
+    if (int rc = launch_dense<kBF16, kEpiLogits>(a, st)) return rc;
+  }
+  // selection
+  {
+    Select a{};
+    a.logits = p.logits; a.Epad = Epad; a.T = T; a.E = E; a.H = H; a.K = K;
+    a.bias = h->bias; a.x = x; a.r = p.r; a.xnorm = p.xnorm; a.wmax = p.wmax;
+    a.wr = (const uint16_t*)h->router_rm;
+    // |fp32 logit - exact| <= beta: 2H bf16 x bf16 products, each exact,
+    // summed in fp32 in any order (each addition within 2 ulp, allowing
+    // truncation): 2 * (2H + 1) * 2^-24 * sum |x_i w_i|; the two-part split
+    // of the staged row leaves 2^-16 |x_i|, and the staged row is x * r
+    // rounded (2^-24); sum |x_i w_i| <= |x|_2 |w|_2. Margin 2%.
+    a.cbeta = 1.02 * (2.0 * (2.0 * H + 1.0) * ldexp(1.0, -24) + ldexp(1.0, -15));
+    a.idx = p.idx; a.w = p.w;
+    hipLaunchKernelGGL(k_select, dim3((T + 3) / 4), dim3(256), 0, st, a);
+    LMOE_HIP(hipGetLastError());
+  }
+  if (ev) LMOE_HIP(hipEventRecord(h->phase_events[1], st));
+  // permutation
+  {
+    Perm a{};
+    a.idx = p.idx; a.T = T; a.K = K; a.E = E; a.G = G; a.nchunk = prefill_chunks(T);
+    a.cmask = p.cmask; a.ccnt = p.ccnt; a.cbase = p.cbase; a.eorder = p.eorder;
+    a.labels = h->labels; a.seg_start = p.seg_start; a.expert_count = p.expert_count;
+    a.group_off = p.group_off; a.pieces = (Piece*)p.pieces; a.npieces = p.npieces;
+    a.perm = p.perm; a.inv = p.inv;
+    hipLaunchKernelGGL(k_perm_mask, dim3(a.nchunk), dim3(256), 0, st, a);
+    LMOE_HIP(hipGetLastError());
+    hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(kMaxE), 0, st, a);
+    LMOE_HIP(hipGetLastError());
+    hipLaunchKernelGGL(k_perm_scatter, dim3((T * K + 255) / 256), dim3(256), 0, st, a);
+    LMOE_HIP(hipGetLastError());
+  }
+  if (ev) LMOE_HIP(hipEventRecord(h->phase_events[2], st));
+  // D over all groups, and the shared expert's gate/up
+  {
+    Dense a{};
+    a.W = WMat{h->dmat, h->g_d, 0, 1};
+    a.A = AMat{p.xh, (size_t)H, 0, H};
+    a.T = T; a.mtiles = mtiles; a.ntiles = G * h->g_d.tiles; a.npairs = (a.ntiles + 1) / 2;
+    a.out = p.xl; a.ostride = (size_t)G * L; a.nvalid = G * L;
+    const int rc = d.du_bits == 8 ? launch_dense<kQ8, kEpiF16>(a, st) : launch_dense<kQ4, kEpiF16>(a, st);
+    if (rc) return rc;
+  }
+  if (ev) LMOE_HIP(hipEventRecord(h->phase_events[3], st));
+  {
+    Dense a{};
+    a.W = WMat{h->sgu, h->g_sgu, 0, 1};
+    a.A = AMat{p.xb, (size_t)2 * H, H, H};
+    a.T = T; a.mtiles = mtiles; a.ntiles = h->g_sgu.tiles; a.npairs = (a.ntiles + 1) / 2;
+    a.out = p.hsb; a.ostride = (size_t)2 * Fs; a.nvalid = Fs;
+    if (int rc = launch_dense<kBF16, kEpiSwigluB2>(a, st)) return rc;
+  }
+  if (ev) LMOE_HIP(hipEventRecord(h->phase_events[4], st));
+  // experts
+  const unsigned maxp = (unsigned)prefill_max_pieces(T, K, E);
+  {
+    Grouped a{};
+    a.experts = h->experts; a.estride = h->expert_stride; a.woff = 0; a.ts_off = h->ts_off;
+    a.g = h->g_gu; a.A = AMat{p.xl, (size_t)L, 0, L};
+    a.pieces = (const Piece*)p.pieces; a.npieces = p.npieces;
+    a.ntiles = h->g_gu.tiles; a.npairs = (a.ntiles + 1) / 2; a.G = G; a.F = F;
+    a.perm = p.perm; a.topk_w = p.w; a.labels = h->labels; a.K = K;
+    a.out = p.h; a.ostride = F;
+    const unsigned grid = 8u * a.npairs * ((maxp + 7) / 8);
+    hipLaunchKernelGGL(k_grouped<kGateUp>, dim3(grid), dim3(NTH), 0, st, a);
+    LMOE_HIP(hipGetLastError());
+  }
+  if (ev) LMOE_HIP(hipEventRecord(h->phase_events[5], st));
+  {
+    Grouped a{};
+    a.experts = h->experts; a.estride = h->expert_stride; a.woff = h->g_gu.bytes();
+    a.ts_off = h->ts_off; a.g = h->g_dn; a.A = AMat{p.h, (size_t)F, 0, F};
+    a.pieces = (const Piece*)p.pieces; a.npieces = p.npieces;
+    a.ntiles = h->g_dn.tiles; a.npairs = (a.ntiles + 1) / 2; a.G = G; a.F = F;
+    a.perm = p.perm; a.topk_w = p.w; a.labels = h->labels; a.K = K;
+    a.out = p.o; a.ostride = L;
+    const unsigned grid = 8u * a.npairs * ((maxp + 7) / 8);
+    hipLaunchKernelGGL(k_grouped<kDown>, dim3(grid), dim3(NTH), 0, st, a);
+    LMOE_HIP(hipGetLastError());
+  }
+  if (ev) LMOE_HIP(hipEventRecord(h->phase_events[6], st));
+  // combine
+  {
+    Combine a{p.idx, p.inv, h->labels, p.o, (_Float16*)p.s, K, G, L};
+    hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, st, a);
+    LMOE_HIP(hipGetLastError());
+  }
+  if (ev) LMOE_HIP(hipEventRecord(h->phase_events[7], st));
+  // U over the concatenated groups, then the shared down projection
+  {
+    Dense a{};
+    a.W = WMat{h->umat, h->g_u, h->g_u.bytes(), G};
+    a.A = AMat{p.s, (size_t)G * L, 0, L};
+    a.W2 = WMat{h->sdn, h->g_sdn, 0, 1};
+    a.A2 = AMat{p.hsb, (size_t)2 * Fs, Fs, Fs};
+    a.T = T; a.mtiles = mtiles; a.ntiles = h->g_u.tiles; a.npairs = (a.ntiles + 1) / 2;
+    a.out = y; a.ostride = H; a.nvalid = H; a.res = norm ? x : nullptr;
+    const int rc = d.du_bits == 8 ? launch_dense<kQ8, kEpiY>(a, st) : launch_dense<kQ4, kEpiY>(a, st);
+    if (rc) return rc;
+  }
+  if (ev) LMOE_HIP(hipEventRecord(h->phase_events[8], st));
+  return 0;
+}
+
+int prefill_debug_latent(lmoe_t* h, int T, float* dst, hipStream_t st) {
+  const size_t n = (size_t)T * h->d.n_groups * h->d.latent;
+  hipLaunchKernelGGL(k_f16_to_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     (const _Float16*)h->pw.xl, n, dst);
+  LMOE_HIP(hipGetLastError());
+  return 0;
+}
+
+}  // namespace lm

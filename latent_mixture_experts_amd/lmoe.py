@@ -66,7 +66,7 @@ def _load():
         "lmoe_forward_block": (ctypes.c_int, [vp, vp, i32, ctypes.c_float, vp]),
         "lmoe_destroy": (None, [vp]),
         "lmoe_set_phase_events": (ctypes.c_int, [vp, ctypes.POINTER(vp), i32]),
-        "lmoe_phase_count": (i32, []),
+        "lmoe_phase_count": (i32, [i32]),
         "lmoe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "lmoe_last_error": (ctypes.c_char_p, []),
         "lmoe_expert_record_bytes": (sz, [i32, i32]),

@@ -22,7 +22,7 @@ class Case:
     experts some token routes to are quantized; other records stay zero (they
     are never read by a correct forward)."""
 
-    def __init__(self, w, seed=0, tokens=None, layer=0, x=None, masters=None):
+    def __init__(self, w, seed=0, tokens=None, layer=0, x=None, masters=None, pack_tokens=None):
         self.w = w
         self.d = dims_of(w)
         t = w.tokens if tokens is None else tokens
@@ -31,7 +31,11 @@ class Case:
         bits = oracle.f32_to_bf16_bits(m["router"])
         lg = oracle.router_logits(self.x, bits, m["router_bias"])
         idx, _ = oracle.select_topk(lg, w.top_k)
-        m["expert_ids"] = sorted(set(idx.ravel().tolist()))
+        # pack_tokens: quantize only the experts these tokens route to (the
+        # other tokens' outputs are then not meaningful; their routing is)
+        sel = idx if pack_tokens is None else idx[np.asarray(pack_tokens)]
+        m["expert_ids"] = sorted(set(sel.ravel().tolist()))
+        self.logits, self.idx = lg, idx
         self.blobs = oracle.pack_layer(self.d, m)
         self.dec = oracle.decode_layer(self.d, self.blobs)
 
