@@ -63,6 +63,11 @@ int dalloc(lmoe_t* h, P** p, size_t bytes) {
 void free_all(lmoe_t* h) {
   for (void* p : h->allocations) (void)hipFree(p);
   h->allocations.clear();
+  if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+  if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+  if (h->aux) (void)hipStreamDestroy(h->aux);
+  h->ev_fork = h->ev_join = nullptr;
+  h->aux = nullptr;
 }
 
 int create_impl(lmoe_t* h) {
@@ -130,6 +135,10 @@ int create_impl(lmoe_t* h) {
     const size_t Epm = (size_t)h->g_router_m.tiles * 64;
     p.tmax = d.max_tokens;
     A(h->router_m, h->g_router_m.bytes());
+    h->g_d16 = make_geom(kF16, L, H);
+    h->g_u16 = make_geom(kF16, H, L);
+    A(h->dmat16, h->g_d16.bytes() * G);
+    A(h->umat16, h->g_u16.bytes() * G);
     A(h->router_rm, sizeof(uint16_t) * E * H);
     A(p.wmax, sizeof(double));
     A(p.xh, 2 * Tp * H);
@@ -155,6 +164,9 @@ int create_impl(lmoe_t* h) {
     A(p.h, 2 * nk * F);
     A(p.o, sizeof(float) * nk * L);
     A(p.s, 2 * Tp * G * L);
+    LMOE_HIP(hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking));
+    LMOE_HIP(hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming));
+    LMOE_HIP(hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming));
   }
 #undef A
   LMOE_HIP(hipMemset(w.ctr_router, 0, sizeof(unsigned)));

@@ -36,8 +36,10 @@ namespace lm {
 //   BF16    32      8 bf16                                none
 //
 // The router keeps a plainer layout (BF16R) for its fp64 dot products: lane
-// l of a slot holds 8 consecutive bf16 columns of row l of the tile.
-enum Fmt : int { kQ8 = 0, kQ4 = 1, kFP4 = 2, kBF16 = 3, kBF16R = 4 };
+// l of a slot holds 8 consecutive bf16 columns of row l of the tile. F16 is
+// the BF16 layout holding fp16 values: the prefill path keeps D and U
+// dequantized to fp16(q * d) in it.
+enum Fmt : int { kQ8 = 0, kQ4 = 1, kFP4 = 2, kBF16 = 3, kBF16R = 4, kF16 = 5 };
 constexpr int kSSCols = 256;
 constexpr int kSlot = 1024;
 constexpr int kMaxDecodeT = 8;     // tokens the GEMV (decode) path takes per forward
@@ -48,9 +50,11 @@ constexpr int kMaxTokens = 1 << 20;   // largest max_tokens a handle accepts
 constexpr int kRouterChunks = 4;  // router column chunks: H / (64 * H/256)
 
 __host__ __device__ constexpr int chunk_cols(int f) {      // columns of one chunk
-  return f == kQ8 ? 64 : (f == kBF16 ? 32 : (f == kBF16R ? 8 : 128));
+  return f == kQ8 ? 64 : ((f == kBF16 || f == kF16) ? 32 : (f == kBF16R ? 8 : 128));
 }
-__host__ __device__ constexpr int scale_slots(int f) { return (f == kBF16 || f == kBF16R) ? 0 : 1; }
+__host__ __device__ constexpr int scale_slots(int f) {
+  return (f == kBF16 || f == kBF16R || f == kF16) ? 0 : 1;
+}
 // Code slots of a super-step of `cols` columns: four row groups per chunk
 // (one slot per chunk for the router layout); a partial last chunk is
 // padded with zero codes.
@@ -148,10 +152,13 @@ struct lmoe {
   bool loaded = false;
   lm::Geom g_router, g_d, g_u, g_gu, g_dn, g_sgu, g_sdn;
   lm::Geom g_router_m;        // router in the MFMA layout (prefill)
+  lm::Geom g_d16, g_u16;      // D_g, U_g dequantized to fp16 (prefill)
   size_t expert_stride = 0;   // bytes per expert in device memory
   size_t ts_off = 0;          // offset of the three fp32 tensor scales
   uint8_t* router = nullptr;  // tiled bf16 [Epad][H]
   uint8_t* router_m = nullptr;  // prefill: router tiled for MFMA
+  uint8_t* dmat16 = nullptr;    // prefill: G tiled fp16 D_g
+  uint8_t* umat16 = nullptr;    // prefill: G tiled fp16 U_g
   uint16_t* router_rm = nullptr;  // prefill: router bf16 [E][H] row-major
   float* bias = nullptr;      // [E] (zeros without a bias)
   uint8_t* dmat = nullptr;    // G tiled D_g
@@ -163,6 +170,10 @@ struct lmoe {
   std::vector<uint8_t> labels_host;
   lm::Workspace ws;
   lm::PrefillWs pw;
+  // prefill: a second stream (default priority) on which D and the shared
+  // gate/up run while the router, top-K and permutation run on the caller's
+  hipStream_t aux = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   std::vector<void*> allocations;
   std::vector<hipEvent_t> phase_events;   // empty: no phase timing
 };
@@ -188,6 +199,7 @@ size_t prefill_max_pieces(int T, int K, int E);
 int prefill_chunks(int T);
 size_t prefill_piece_bytes();
 int prefill_router_wmax(lmoe_t* h, hipStream_t stream);
+int prefill_dequant_du(lmoe_t* h, hipStream_t stream);
 int prefill_debug_latent(lmoe_t* h, int T, float* dst, hipStream_t stream);
 
 // api.hip

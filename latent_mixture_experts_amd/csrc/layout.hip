@@ -457,6 +457,10 @@ int load_weights_impl(lmoe_t* h, const lmoe_weights* w, hipStream_t st) {
     }
     LMOE_HIP(hipStreamSynchronize(st));
   }
+  if (h->pw.tmax) {
+    if (int rc = prefill_dequant_du(h, st)) return rc;
+    LMOE_HIP(hipStreamSynchronize(st));
+  }
   // shared expert
   {
     DevTemp tg, tu, td;

@@ -28,15 +28,18 @@
 //            the same accumulators by the shared expert's down projection
 //   shared   gate/up GEMM with SwiGLU in the epilogue
 //
-// GEMM tile: 128 tokens x 128 weight rows (two 64-row tiles of the tiled
-// stream) per 256-thread workgroup. Wave w takes tokens 64*(w&1).. and weight
-// tile w>>1: 4 x 4 accumulators of v_mfma_f32_16x16x32. The weight operand
-// is loaded from HBM straight into registers (the tiled stream is already
-// the MFMA B-operand layout) one stage ahead and decoded in registers just
-// before use: NVFP4 to fp16 exactly (e2m1 * e4m3 <= 6 significant bits),
-// Q8/Q4 to fp16(q * d), bf16 as stored. The activation stage (128 columns,
-// or 64 columns in two bf16 parts) goes through a double-buffered LDS tile
-// shared by the two waves of the same tokens.
+// GEMM tile: 128 tokens x 256 weight rows (four 64-row tiles of the tiled
+// stream) per 512-thread workgroup, two waves per SIMD. Wave w takes weight
+// tile w/2 for tokens 64*(w%2) .. +63 with v_mfma_f32_32x32x16 (2 x 2
+// accumulators of 32 x 32); the two waves of a SIMD overlap each other's
+// MFMAs with their loads, LDS traffic and weight decoding. Per stage (128
+// columns, 64 for 16-bit weights) the activation rows and the raw weight
+// slots go through a double-buffered LDS ring, loads running two stages
+// ahead. Weights are decoded in registers right before use: NVFP4 to fp16
+// exactly (e2m1 * e4m3 <= 6 significant bits), bf16 / fp16 as stored. D and
+// U run on fp16 copies made at load time with the same rounding the Q8/Q4
+// decode has (fp16(q * d)). 32-token blocks past the last valid token are
+// skipped (ragged tails, small expert segments).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -51,12 +54,14 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));
 typedef unsigned u4v __attribute__((ext_vector_type(4)));
 
-constexpr int NTH = 256;       // threads per GEMM workgroup (4 waves)
+constexpr int NTH = 512;       // threads per GEMM workgroup (8 waves)
 constexpr int BM = 128;        // tokens per GEMM tile
-constexpr int MB = BM / 32;    // 16-token MFMA blocks per wave
-constexpr int WM = BM / 2;     // tokens per wave
+constexpr int WTOK = 64;       // tokens per wave
+constexpr int MB = WTOK / 32;  // 32-token MFMA blocks per wave
+constexpr int NTW = 4;         // 64-row weight tiles per workgroup (two waves each)
 constexpr int CHUNK_T = 64;    // tokens per permutation chunk
 
 __device__ __forceinline__ uint4 ldnt(const uint8_t* p) {
@@ -125,19 +130,34 @@ __device__ __forceinline__ half8 fp4_row8(uint32_t w, _Float16 s) {
 
 template <int WF>
 struct Fm {
+  static constexpr bool W16 = WF == kBF16 || WF == kF16;  // 16-bit weights, no decode
   static constexpr int CC = chunk_cols(WF);               // columns per chunk (memory)
-  static constexpr int SCOLS = WF == kBF16 ? 64 : 128;    // columns per stage
+  static constexpr int SCOLS = W16 ? 64 : 128;            // columns per stage
   static constexpr int SC = SCOLS / CC;                   // chunks per stage
-  static constexpr int KB = SCOLS / 32;                   // MFMA k-steps per stage
-  static constexpr int BPC = CC / 32;                     // k-steps per chunk
+  static constexpr int KS = SCOLS / 16;                   // MFMA k-steps (16 columns) per stage
+  static constexpr int BPC = CC / 32;                     // 32-column blocks per chunk
   static constexpr int NP = WF == kBF16 ? 2 : 1;          // activation parts
   static constexpr int AST = SCOLS + 8;                   // LDS row stride (elements)
   static constexpr int PPR = SCOLS / 8;                   // 16-byte pieces per row
-  static constexpr int PPT = NP * BM * PPR / NTH;         // pieces per thread
-  static constexpr int LDSA = NP * BM * AST;              // elements per LDS buffer
+  static constexpr int PPT = NP * BM * PPR / NTH;         // A pieces per thread
+  static constexpr int NS = SC * 4;                       // weight slots per tile and stage
+  static constexpr int BPW = NS / 2;                      // of which each wave of the pair loads
+  static constexpr int LDSA = NP * BM * AST * 2;          // A bytes per stage
 };
-constexpr int kLdsA = Fm<kBF16>::LDSA > Fm<kFP4>::LDSA ? Fm<kBF16>::LDSA : Fm<kFP4>::LDSA;
-static_assert(Fm<kQ8>::LDSA <= kLdsA && Fm<kQ4>::LDSA <= kLdsA, "LDS sizing");
+
+// One LDS stage: the activation tile, the raw weight slots of the four
+// tiles, and the scale words of their rows.
+constexpr int kAOff = 0;
+constexpr int kABytes = Fm<kBF16>::LDSA > Fm<kFP4>::LDSA ? Fm<kBF16>::LDSA : Fm<kFP4>::LDSA;
+constexpr int kBOff = kABytes;
+constexpr int kBBytes = NTW * 8 * 1024;                  // NS <= 8 slots of 1 KB per tile
+constexpr int kSOff = kBOff + kBBytes;
+constexpr int kStage = kSOff + NTW * 64 * 8;
+static_assert(Fm<kQ8>::LDSA <= kABytes && Fm<kQ4>::LDSA <= kABytes && Fm<kF16>::LDSA <= kABytes,
+              "LDS sizing");
+static_assert(Fm<kQ8>::NS <= 8 && Fm<kBF16>::NS <= 8 && Fm<kFP4>::NS <= 8 && Fm<kF16>::NS <= 8,
+              "LDS sizing");
+static_assert(2 * kStage <= 160 * 1024, "two stages fit the LDS");
 
 // A weight operand: `nmat` matrices of one geometry concatenated along K
 // (U_0 .. U_{G-1}); tile j of a matrix at base + j * tile_slots slots.
@@ -157,176 +177,225 @@ struct AMat {
   int kmat;
 };
 
+// The global loads of one stage, held in registers until stored to LDS.
 template <int WF>
-struct BStage {
-  uint4 raw[Fm<WF>::SC][4];
-  uint2 sc[4];
+struct Reg {
+  uint4 a[Fm<WF>::PPT];
+  uint4 b[Fm<WF>::BPW];
+  uint2 sc;
 };
 
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Issues the loads of stage s: the activation pieces (all threads); for the
+// wave pair of a weight tile, alternate code slots each plus, from both, the
+// scale word of lane-chunk `lane` (row group lane/16, row lane%16). Every
+// load is issued: addresses of padding rows, of columns past k and of a
+// missing last chunk are clamped to valid ones (the values are masked when
+// stored, or meet zero activations).
 template <int WF>
-__device__ __forceinline__ void fetch_b(const WMat& W, int tile, int s, BStage<WF>& B) {
+__device__ __forceinline__ void fetch(const WMat& W, int tile, const AMat& A, const int* arow, int s,
+                                      Reg<WF>& R) {
   using F = Fm<WF>;
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, wm = wave_id() & 1;
   const int kmat = W.g.k;
   const int spm = (kmat + F::SCOLS - 1) / F::SCOLS;
-  const int cpm = (kmat + F::CC - 1) / F::CC;
   const int mat = s / spm, sm = s % spm;
   const int col0 = sm * F::SCOLS;
+#pragma unroll
+  for (int i = 0; i < F::PPT; ++i) {
+    const int p = threadIdx.x + i * NTH;
+    const int part = p / (BM * F::PPR), rem = p % (BM * F::PPR);
+    const int m = rem / F::PPR, kk = min(col0 + (rem % F::PPR) * 8, A.kmat - 8);
+    const int row = max(arow[m], 0);
+    R.a[i] = *(const uint4*)(A.p + (size_t)row * A.rs + (size_t)part * A.ps + (size_t)mat * A.kmat + kk);
+  }
+  const int cpm = (kmat + F::CC - 1) / F::CC;
   const int ss = col0 / kSSCols, cin0 = (col0 % kSSCols) / F::CC;
   const int ncs = ss_code_slots(WF, min(kSSCols, kmat - ss * kSSCols));
+  const int jmax = cpm - 1 - sm * F::SC;
   const uint8_t* sb = W.base + (size_t)mat * W.mat_bytes +
                       ((size_t)tile * W.g.tile_slots + (size_t)ss * W.g.full) * kSlot;
 #pragma unroll
-  for (int j = 0; j < F::SC; ++j)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg)
-      B.raw[j][rg] = (sm * F::SC + j < cpm)
-                         ? ldnt(sb + (size_t)((cin0 + j) * 4 + rg) * kSlot + lane * 16)
-                         : make_uint4(0, 0, 0, 0);
-  if constexpr (WF != kBF16) {
+  for (int i2 = 0; i2 < F::BPW; ++i2) {
+    const int i = 2 * i2 + wm;
+    const int j = min(i / 4, jmax), rg = i % 4;
+    R.b[i2] = ldnt(sb + (size_t)((cin0 + j) * 4 + rg) * kSlot + lane * 16);
+  }
+  if constexpr (!F::W16) {
     const int off = WF == kQ8 ? 4 * cin0 : 8 * cin0;
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg)
-      B.sc[rg] = *(const uint2*)(sb + (size_t)ncs * kSlot + (16 * rg + (lane & 15)) * 16 + off);
+    R.sc = *(const uint2*)(sb + (size_t)ncs * kSlot + lane * 16 + off);
   }
 }
 
-// decoded B operand of k-step kb for row group rg
 template <int WF>
-__device__ __forceinline__ uint4 decode_b(const BStage<WF>& B, int kb, int rg) {
+__device__ __forceinline__ void store(uint8_t* st, Reg<WF>& R, const AMat& A, const int* arow, int s) {
   using F = Fm<WF>;
-  const int j = kb / F::BPC, b = kb % F::BPC;
-  const uint4 w = B.raw[j][rg];
-  if constexpr (WF == kBF16) {
+  const int spm = (A.kmat + F::SCOLS - 1) / F::SCOLS;
+  const int col0 = (s % spm) * F::SCOLS;
+  uint16_t* As = (uint16_t*)(st + kAOff);
+#pragma unroll
+  for (int i = 0; i < F::PPT; ++i) {
+    const int p = threadIdx.x + i * NTH;
+    const int part = p / (BM * F::PPR), rem = p % (BM * F::PPR);
+    const int m = rem / F::PPR, c = (rem % F::PPR) * 8;
+    const bool ok = arow[m] >= 0 && col0 + c < A.kmat;
+    const uint4 v = ok ? R.a[i] : make_uint4(0, 0, 0, 0);
+    *(uint4*)(As + (size_t)(part * BM + m) * F::AST + c) = v;
+  }
+  const int lane = threadIdx.x & 63, w = wave_id(), tl = w >> 1, wm = w & 1;
+  uint4* Bs = (uint4*)(st + kBOff);
+#pragma unroll
+  for (int i2 = 0; i2 < F::BPW; ++i2) Bs[(tl * 8 + 2 * i2 + wm) * 64 + lane] = R.b[i2];
+  // both waves of the pair hold the same scale word and store it
+  if constexpr (!F::W16) ((uint2*)(st + kSOff))[tl * 64 + lane] = R.sc;
+}
+
+// The B operand of v_mfma_f32_32x32x16 for weight rows 32*nb + l%32 and
+// k-step ks: lane l needs columns 16*ks + 8*(l/32) .. +7. In the tiled stream
+// those sit in row group 2*nb + (l%32)/16, in the lane-chunk of k-group
+// 2*(ks%2) + l/32 and row l%16, of block (ks/2) % BPC of chunk (ks/2) / BPC.
+__device__ __forceinline__ int b_lane(int nb, int kk, int lane) {
+  return (((2 * nb + ((lane & 31) >> 4)) * 64) + 16 * (2 * kk + (lane >> 5)) + (lane & 15));
+}
+
+// decodes the 8 columns of block b held in raw word(s), with the scale word
+// pair `sc` of the lane's row (k-group qg of the 32-column block)
+template <int WF>
+__device__ __forceinline__ uint4 decode_b(uint4 w, uint2 sc, int blk, int b, int qg) {
+  if constexpr (Fm<WF>::W16) {
     return w;
   } else if constexpr (WF == kFP4) {
-    const int qg = (threadIdx.x & 63) >> 4;
     const int byte = 2 * b + (qg >> 1);
-    const uint32_t sw = byte < 4 ? B.sc[rg].x : B.sc[rg].y;
+    const uint32_t sw = byte < 4 ? sc.x : sc.y;
     const uint32_t code = (sw >> (8 * (byte & 3))) & 0xFFu;
     const _Float16 s = (_Float16)__builtin_amdgcn_cvt_f32_fp8(code, 0);
     return __builtin_bit_cast(uint4, fp4_row8(word(w, b), s));
   } else {
-    const int blk = F::BPC * j + b;          // block within the stage: 0..3
-    const uint32_t sw = blk < 2 ? B.sc[rg].x : B.sc[rg].y;
+    const uint32_t sw = blk < 2 ? sc.x : sc.y;
     const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(sw >> (16 * (blk & 1))));
     if constexpr (WF == kQ8) return __builtin_bit_cast(uint4, q8_row8(word(w, 2 * b), word(w, 2 * b + 1), d));
     else return __builtin_bit_cast(uint4, q4_row8(word(w, b), d));
   }
 }
 
-template <int WF>
-__device__ __forceinline__ void fetch_a(const AMat& A, const int* arow, int s, uint4 (&ar)[Fm<WF>::PPT]) {
+// One stage of MFMAs for this wave over its first NMB 32-token blocks: per
+// k-step the activation fragments are read, the two weight fragments (rows
+// 0..31 and 32..63 of the wave's tile) decoded, then 2 * NMB MFMAs issued.
+template <int WF, int NMB>
+__device__ __forceinline__ void mfma_stage(const uint8_t* st, f16v (&acc)[MB][2]) {
   using F = Fm<WF>;
-  const int spm = (A.kmat + F::SCOLS - 1) / F::SCOLS;
-  const int mat = s / spm, col0 = (s % spm) * F::SCOLS;
+  const int lane = threadIdx.x & 63, w = wave_id(), tl = w >> 1, wm = w & 1;
+  const int row = lane & 31, kh = lane >> 5;
+  const uint16_t* As = (const uint16_t*)(st + kAOff);
+  const uint4* Bs = (const uint4*)(st + kBOff) + tl * 8 * 64;
+  // raw weight words: chunk j, row block nb, k-half kk (ks % 2)
+  uint4 raw[F::SC][2][2];
 #pragma unroll
-  for (int i = 0; i < F::PPT; ++i) {
-    const int p = threadIdx.x + i * NTH;
-    const int part = p / (BM * F::PPR), rem = p % (BM * F::PPR);
-    const int m = rem / F::PPR, kk = col0 + (rem % F::PPR) * 8;
-    const int row = arow[m];
-    ar[i] = make_uint4(0, 0, 0, 0);
-    if (row >= 0 && kk < A.kmat)
-      ar[i] = *(const uint4*)(A.p + (size_t)row * A.rs + (size_t)part * A.ps + (size_t)mat * A.kmat + kk);
+  for (int j = 0; j < F::SC; ++j)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) raw[j][nb][kk] = Bs[j * 4 * 64 + b_lane(nb, kk, lane)];
+  uint2 sc[2] = {make_uint2(0, 0), make_uint2(0, 0)};
+  if constexpr (!F::W16) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      sc[nb] = ((const uint2*)(st + kSOff))[tl * 64 + 16 * (2 * nb + (row >> 4)) + (lane & 15)];
   }
-}
-
-template <int WF>
-__device__ __forceinline__ void store_a(uint16_t* As, const uint4 (&ar)[Fm<WF>::PPT]) {
-  using F = Fm<WF>;
 #pragma unroll
-  for (int i = 0; i < F::PPT; ++i) {
-    const int p = threadIdx.x + i * NTH;
-    const int part = p / (BM * F::PPR), rem = p % (BM * F::PPR);
-    const int m = rem / F::PPR, c = (rem % F::PPR) * 8;
-    *(uint4*)(As + (size_t)(part * BM + m) * F::AST + c) = ar[i];
-  }
-}
-
-template <int WF>
-__device__ __forceinline__ void mfma_stage(const uint16_t* As, const BStage<WF>& B, int wm,
-                                           f4 (&acc)[MB][4]) {
-  using F = Fm<WF>;
-  const int lane = threadIdx.x & 63, tok = lane & 15, qg = lane >> 4;
+  for (int ks = 0; ks < F::KS; ++ks) {
+    const int kk = ks & 1, c32 = ks >> 1;           // 32-column block of the stage
+    const int j = c32 / F::BPC, b = c32 % F::BPC;   // chunk, block within the chunk
+    uint4 a[F::NP][NMB];
 #pragma unroll
-  for (int kb = 0; kb < F::KB; ++kb) {
-    uint4 bw[4];
+    for (int p = 0; p < F::NP; ++p)
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) bw[rg] = decode_b<WF>(B, kb, rg);
+      for (int mb = 0; mb < NMB; ++mb)
+        a[p][mb] = *(const uint4*)(As + (size_t)(p * BM + WTOK * wm + 32 * mb + row) * F::AST +
+                                   16 * ks + 8 * kh);
+    uint4 bw[2];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int m = WM * wm + 16 * mb + tok;
-      if constexpr (WF == kBF16) {
-        bf16x8 a[F::NP];
+    for (int nb = 0; nb < 2; ++nb) bw[nb] = decode_b<WF>(raw[j][nb][kk], sc[nb], F::BPC * j + b, b, 2 * kk + kh);
 #pragma unroll
-        for (int p = 0; p < F::NP; ++p)
-          a[p] = *(const bf16x8*)(As + (size_t)(p * BM + m) * F::AST + 32 * kb + 8 * qg);
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg)
+      for (int nb = 0; nb < 2; ++nb) {
+        if constexpr (WF == kBF16) {
 #pragma unroll
           for (int p = 0; p < F::NP; ++p)
-            acc[mb][rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                a[p], __builtin_bit_cast(bf16x8, bw[rg]), acc[mb][rg], 0, 0, 0);
-      } else {
-        const half8 a = *(const half8*)(As + (size_t)m * F::AST + 32 * kb + 8 * qg);
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg)
-          acc[mb][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              a, __builtin_bit_cast(half8, bw[rg]), acc[mb][rg], 0, 0, 0);
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, a[p][mb]), __builtin_bit_cast(bf16x8, bw[nb]), acc[mb][nb], 0, 0, 0);
+        } else {
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              __builtin_bit_cast(half8, a[0][mb]), __builtin_bit_cast(half8, bw[nb]), acc[mb][nb], 0, 0, 0);
+        }
       }
-    }
   }
 }
 
-// Accumulates the tile's product over all stages of W (all nmat matrices).
-// `tile` is this wave's weight tile, `b_on` whether it exists, `on` whether
-// the wave has any work (tile exists and some of its tokens are valid).
-// Every thread of the block takes part in the staging and the barriers.
-template <int WF>
-__device__ __forceinline__ void gemm_loop(const WMat& W, int tile, bool b_on, bool on, const AMat& A,
-                                          const int* arow, uint16_t* As, f4 (&acc)[MB][4]) {
+// Accumulates the tile's product over all stages of W (all nmat matrices)
+// for the wave's first NMB token blocks (NMB 0: the wave only stages);
+// `tile` is the wave's weight tile (a wave whose tile is past the last one
+// computes on tile 0 and discards the result). One barrier per stage:
+// between two barriers a wave issues the global loads of stage s + 2, the
+// MFMAs of stage s (LDS buffer s % 2) and the LDS stores of stage s + 1 (the
+// other buffer, whose last readers finished before the barrier). Every
+// thread of the block takes part in the staging and the barriers.
+template <int WF, int NMB>
+__device__ __forceinline__ void gemm_loop(const WMat& W, int tile, bool b_on, const AMat& A,
+                                          const int* arow, uint8_t* smem, f16v (&acc)[MB][2]) {
   using F = Fm<WF>;
-  const int wm = (threadIdx.x >> 6) & 1;
+  const int ld_tile = b_on ? tile : 0;     // a valid tile for the unused loads
   const int nst = ((W.g.k + F::SCOLS - 1) / F::SCOLS) * W.nmat;
-  uint4 ar[F::PPT];
-  BStage<WF> b0, b1;
-  fetch_a<WF>(A, arow, 0, ar);
-  if (b_on) fetch_b<WF>(W, tile, 0, b0);
-  for (int s = 0; s < nst; s += 2) {
-    // even stage: LDS buffer 0, weights b0; prefetch s + 1 into b1
-    store_a<WF>(As, ar);
-    __syncthreads();
-    if (s + 1 < nst) {
-      fetch_a<WF>(A, arow, s + 1, ar);
-      if (b_on) fetch_b<WF>(W, tile, s + 1, b1);
-    }
-    if (on) mfma_stage<WF>(As, b0, wm, acc);
-    if (s + 1 >= nst) break;
-    // odd stage: LDS buffer 1, weights b1; prefetch s + 2 into b0
-    store_a<WF>(As + kLdsA, ar);
-    __syncthreads();
-    if (s + 2 < nst) {
-      fetch_a<WF>(A, arow, s + 2, ar);
-      if (b_on) fetch_b<WF>(W, tile, s + 2, b0);
-    }
-    if (on) mfma_stage<WF>(As + kLdsA, b1, wm, acc);
-  }
-  // the caller may restage the LDS right after
+  Reg<WF> r0, r1;
+  fetch<WF>(W, ld_tile, A, arow, 0, r0);
+  fetch<WF>(W, ld_tile, A, arow, min(1, nst - 1), r1);
+  store<WF>(smem, r0, A, arow, 0);
   __syncthreads();
+  int s = 0;
+  for (; s + 1 < nst; s += 2) {
+    // stage s from buffer 0; stage s + 1 into buffer 1
+    fetch<WF>(W, ld_tile, A, arow, min(s + 2, nst - 1), r0);
+    if constexpr (NMB > 0) mfma_stage<WF, NMB>(smem, acc);
+    store<WF>(smem + kStage, r1, A, arow, s + 1);
+    __syncthreads();
+    // stage s + 1 from buffer 1; stage s + 2 into buffer 0
+    fetch<WF>(W, ld_tile, A, arow, min(s + 3, nst - 1), r1);
+    if constexpr (NMB > 0) mfma_stage<WF, NMB>(smem + kStage, acc);
+    store<WF>(smem, r0, A, arow, min(s + 2, nst - 1));
+    __syncthreads();
+  }
+  // odd stage count: the last stage is in buffer 0
+  if (s < nst) {
+    if constexpr (NMB > 0) mfma_stage<WF, NMB>(smem, acc);
+    __syncthreads();
+  }
 }
 
-__device__ __forceinline__ void zero_acc(f4 (&acc)[MB][4]) {
+// runs gemm_loop with the wave's token-block count: 0, 1 or 2
+template <int WF>
+__device__ __forceinline__ void gemm_wave(const WMat& W, int tile, bool b_on, int nmb, const AMat& A,
+                                          const int* arow, uint8_t* smem, f16v (&acc)[MB][2]) {
+  if (nmb >= 2) gemm_loop<WF, 2>(W, tile, b_on, A, arow, smem, acc);
+  else if (nmb == 1) gemm_loop<WF, 1>(W, tile, b_on, A, arow, smem, acc);
+  else gemm_loop<WF, 0>(W, tile, b_on, A, arow, smem, acc);
+}
+
+__device__ __forceinline__ void zero_acc(f16v (&acc)[MB][2]) {
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) acc[mb][rg] = (f4){0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
 }
 
-// Lane l of wave (wm, wn) holds in acc[mb][rg][v] the tile-relative token
-// WM*wm + 16*mb + 4*(l/16) + v and the row 16*rg + l%16 of its weight tile.
-__device__ __forceinline__ int acc_tok(int wm, int lane, int mb, int v) {
-  return WM * wm + 16 * mb + 4 * (lane >> 4) + v;
+// Lane l holds in acc[mb][nb][i] the tile-relative token
+// 32*mb + 8*(i/4) + 4*(l/32) + i%4 and the row 32*nb + l%32 of its wave's
+// weight tile (the v_mfma_f32_32x32x16 accumulator layout).
+__device__ __forceinline__ int acc_tok(int lane, int mb, int i) {
+  return 32 * mb + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
 }
 
 // ---------------------------------------------------------------------------
@@ -344,7 +413,7 @@ struct Dense {
   AMat A;
   WMat W2;       // kEpiY: the shared down projection, same accumulators
   AMat A2;
-  int T, mtiles, ntiles, npairs;
+  int T, mtiles, ntiles, nquads;
   void* out;
   size_t ostride;
   int nvalid;
@@ -352,59 +421,56 @@ struct Dense {
 };
 
 template <int WF, int EPI>
-__global__ __launch_bounds__(NTH, 2) void k_dense(Dense a) {
-  __shared__ __align__(16) uint16_t As[2 * kLdsA];
+__global__ __launch_bounds__(NTH) void k_dense(Dense a) {
+  __shared__ __align__(16) uint8_t smem[2 * kStage];
   __shared__ int arow[BM];
   // XCD-aware order: each of the 8 XCDs takes a contiguous range of logical
   // tiles; within it, groups of 8 token tiles sweep the weight tiles with the
   // token tile fastest, so neighbours in time share A and B in L2.
-  const int nblk = a.mtiles * a.npairs;
+  const int nblk = a.mtiles * a.nquads;
   const int bid = blockIdx.x, xcd = bid & 7, q = bid >> 3;
   const int per = nblk >> 3, rem = nblk & 7;
   const int L = xcd * per + min(xcd, rem) + q;
   constexpr int GM = 8;
-  const int span = GM * a.npairs;
+  const int span = GM * a.nquads;
   const int first = (L / span) * GM, gsz = min(a.mtiles - first, GM);
-  const int mt = first + (L % span) % gsz, pair = (L % span) / gsz;
+  const int mt = first + (L % span) % gsz, quad = (L % span) / gsz;
 
   if (threadIdx.x < BM) {
     const int t = mt * BM + threadIdx.x;
     arow[threadIdx.x] = t < a.T ? t : -1;
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
-  const int tile = 2 * pair + wn;
+  const int lane = threadIdx.x & 63, wave = wave_id(), wm = wave & 1;
+  const int tile = NTW * quad + (wave >> 1);
   const bool b_on = tile < a.ntiles;
-  const bool on = b_on && mt * BM + WM * wm < a.T;
-  f4 acc[MB][4];
+  const int nmb = min(MB, max(0, a.T - mt * BM - WTOK * wm + 31) / 32);
+  f16v acc[MB][2];
   zero_acc(acc);
-  gemm_loop<WF>(a.W, tile, b_on, on, a.A, arow, As, acc);
-  if constexpr (EPI == kEpiY) gemm_loop<kBF16>(a.W2, tile, b_on, on, a.A2, arow, As, acc);
-  if (!on) return;
+  gemm_wave<WF>(a.W, tile, b_on, nmb, a.A, arow, smem, acc);
+  if constexpr (EPI == kEpiY) gemm_wave<kBF16>(a.W2, tile, b_on, nmb, a.A2, arow, smem, acc);
+  if (!b_on) return;
 
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int t = mt * BM + acc_tok(wm, lane, mb, v);
+    for (int v = 0; v < 16; ++v) {
+      const int t = mt * BM + WTOK * wm + acc_tok(lane, mb, v);
       if (t >= a.T) continue;
       if constexpr (EPI == kEpiSwigluB2) {
         // rows 0..31 of the tile are gate rows 32*tile + 0..31, rows 32..63
         // the up rows of the same indices
-#pragma unroll
-        for (int rg = 0; rg < 2; ++rg) {
-          const int f = 32 * tile + 16 * rg + (lane & 15);
-          const float hv = silu(acc[mb][rg][v]) * acc[mb][rg + 2][v];
-          const __bf16 h0 = (__bf16)hv;
-          const __bf16 h1 = (__bf16)(hv - (float)h0);
-          __bf16* o = (__bf16*)a.out + (size_t)t * a.ostride;
-          o[f] = h0;
-          o[a.nvalid + f] = h1;
-        }
+        const int f = 32 * tile + (lane & 31);
+        const float hv = silu(acc[mb][0][v]) * acc[mb][1][v];
+        const __bf16 h0 = (__bf16)hv;
+        const __bf16 h1 = (__bf16)(hv - (float)h0);
+        __bf16* o = (__bf16*)a.out + (size_t)t * a.ostride;
+        o[f] = h0;
+        o[a.nvalid + f] = h1;
       } else {
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int n = 64 * tile + 16 * rg + (lane & 15);
+        for (int rg = 0; rg < 2; ++rg) {
+          const int n = 64 * tile + 32 * rg + (lane & 31);
           const float val = acc[mb][rg][v];
           if constexpr (EPI == kEpiLogits) {
             if (n < a.nvalid) ((float*)a.out)[(size_t)t * a.ostride + n] = val;
@@ -437,7 +503,7 @@ struct Grouped {
   AMat A;
   const Piece* pieces;
   const int* npieces;
-  int ntiles, npairs, G, F;
+  int ntiles, nquads, G, F;
   const int* perm;      // [T*K] sorted position -> assignment t*K + k
   const float* topk_w;  // [T*K]
   const uint8_t* labels;
@@ -447,12 +513,12 @@ struct Grouped {
 };
 
 template <int EPI>
-__global__ __launch_bounds__(NTH, 2) void k_grouped(Grouped a) {
-  __shared__ __align__(16) uint16_t As[2 * kLdsA];
+__global__ __launch_bounds__(NTH) void k_grouped(Grouped a) {
+  __shared__ __align__(16) uint8_t smem[2 * kStage];
   __shared__ int arow[BM];
-  // piece p runs on XCD p % 8, all its weight-tile pairs back to back
+  // piece p runs on XCD p % 8, all its weight-tile quads back to back
   const int bid = blockIdx.x, xcd = bid & 7, q = bid >> 3;
-  const int p = xcd + 8 * (q / a.npairs), pair = q % a.npairs;
+  const int p = xcd + 8 * (q / a.nquads), quad = q % a.nquads;
   if (p >= *a.npieces) return;
   const Piece pc = a.pieces[p];
   const int e = pc.expert;
@@ -466,38 +532,35 @@ __global__ __launch_bounds__(NTH, 2) void k_grouped(Grouped a) {
     arow[i] = row;
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
-  const int tile = 2 * pair + wn;
+  const int lane = threadIdx.x & 63, wave = wave_id(), wm = wave & 1;
+  const int tile = NTW * quad + (wave >> 1);
   const bool b_on = tile < a.ntiles;
-  const bool on = b_on && WM * wm < pc.count;
+  const int nmb = min(MB, max(0, pc.count - WTOK * wm + 31) / 32);
   const uint8_t* base = a.experts + (size_t)e * a.estride;
   const WMat W{base + a.woff, a.g, 0, 1};
-  f4 acc[MB][4];
+  f16v acc[MB][2];
   zero_acc(acc);
-  gemm_loop<kFP4>(W, tile, b_on, on, a.A, arow, As, acc);
-  if (!on) return;
+  gemm_wave<kFP4>(W, tile, b_on, nmb, a.A, arow, smem, acc);
+  if (!b_on) return;
   const float* ts = (const float*)(base + a.ts_off);
 
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int i = acc_tok(wm, lane, mb, v);
+    for (int v = 0; v < 16; ++v) {
+      const int i = WTOK * wm + acc_tok(lane, mb, v);
       if (i >= pc.count) continue;
       const size_t pos = (size_t)pc.start + i;
       if constexpr (EPI == kGateUp) {
         const float tg = ts[0], tu = ts[1];
-#pragma unroll
-        for (int rg = 0; rg < 2; ++rg) {
-          const int f = 32 * tile + 16 * rg + (lane & 15);
-          const float hv = silu(acc[mb][rg][v] * tg) * (acc[mb][rg + 2][v] * tu);
-          ((_Float16*)a.out)[pos * a.ostride + f] = (_Float16)hv;
-        }
+        const int f = 32 * tile + (lane & 31);
+        const float hv = silu(acc[mb][0][v] * tg) * (acc[mb][1][v] * tu);
+        ((_Float16*)a.out)[pos * a.ostride + f] = (_Float16)hv;
       } else {
         const float sc = a.topk_w[a.perm[pos]] * ts[2];
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int n = 64 * tile + 16 * rg + (lane & 15);
+        for (int rg = 0; rg < 2; ++rg) {
+          const int n = 64 * tile + 32 * rg + (lane & 31);
           ((float*)a.out)[pos * a.ostride + n] = acc[mb][rg][v] * sc;
         }
       }
@@ -854,6 +917,36 @@ __global__ __launch_bounds__(256) void k_combine(Combine a) {
   }
 }
 
+// Load time: the Q8 / Q4 tiled stream of `nmat` matrices into the fp16
+// tiled stream, with the decode the GEMM would do in registers (fp16(q * d),
+// the same instructions), one thread per 16-byte lane-chunk of the output.
+__global__ void k_dequant_du(const uint8_t* src, Geom gs, int fmt, uint8_t* dst, Geom gd, int nmat) {
+  const size_t per_mat = (size_t)gd.tiles * gd.tile_slots * 64;
+  size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= per_mat * nmat) return;
+  const int mat = (int)(idx / per_mat);
+  idx %= per_mat;
+  const int lane = (int)(idx % 64);
+  const int slot = (int)((idx / 64) % gd.tile_slots);
+  const int tile = (int)(idx / 64 / gd.tile_slots);
+  const int ss = slot / gd.full, j = slot % gd.full;
+  const int c = j / 4, rg = j % 4;               // 32-column chunk of the super-step, row group
+  const int cols = min(kSSCols, gd.k - ss * kSSCols);
+  const uint8_t* sb = src + (size_t)mat * gs.bytes() + ((size_t)tile * gs.tile_slots + (size_t)ss * gs.full) * kSlot;
+  const uint4 scw = *(const uint4*)(sb + (size_t)ss_code_slots(fmt, cols) * kSlot + (16 * rg + lane % 16) * 16);
+  const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(word(scw, c >> 1) >> (16 * (c & 1))));
+  uint4 out;
+  if (fmt == kQ8) {
+    const uint4 w = *(const uint4*)(sb + (size_t)((c / 2) * 4 + rg) * kSlot + lane * 16);
+    const int b = c % 2;
+    out = __builtin_bit_cast(uint4, q8_row8(word(w, 2 * b), word(w, 2 * b + 1), d));
+  } else {
+    const uint4 w = *(const uint4*)(sb + (size_t)((c / 4) * 4 + rg) * kSlot + lane * 16);
+    out = __builtin_bit_cast(uint4, q4_row8(word(w, c % 4), d));
+  }
+  *(uint4*)(dst + (size_t)mat * gd.bytes() + ((size_t)tile * gd.tile_slots + slot) * kSlot + lane * 16) = out;
+}
+
 // fp16 latent rows to fp32 (debug copy)
 __global__ void k_f16_to_f32(const _Float16* src, size_t n, float* dst) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -885,7 +978,7 @@ __global__ __launch_bounds__(1024) void k_router_wmax(const uint16_t* wr, int E,
 
 template <int WF, int EPI>
 int launch_dense(const Dense& a, hipStream_t st) {
-  const unsigned nblk = (unsigned)(a.mtiles * a.npairs);
+  const unsigned nblk = (unsigned)(a.mtiles * a.nquads);
   if (nblk == 0) return 0;
   hipLaunchKernelGGL((k_dense<WF, EPI>), dim3(nblk), dim3(NTH), 0, st, a);
   LMOE_HIP(hipGetLastError());
@@ -908,6 +1001,20 @@ int prefill_router_wmax(lmoe_t* h, hipStream_t st) {
   return 0;
 }
 
+int prefill_dequant_du(lmoe_t* h, hipStream_t st) {
+  const int fmt = h->d.du_bits == 8 ? kQ8 : kQ4, G = h->d.n_groups;
+  for (int which = 0; which < 2; ++which) {
+    const Geom& gs = which == 0 ? h->g_d : h->g_u;
+    const Geom& gd = which == 0 ? h->g_d16 : h->g_u16;
+    const size_t n = (size_t)gd.tiles * gd.tile_slots * 64 * G;
+    hipLaunchKernelGGL(k_dequant_du, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       (const uint8_t*)(which == 0 ? h->dmat : h->umat), gs, fmt,
+                       which == 0 ? h->dmat16 : h->umat16, gd, G);
+    LMOE_HIP(hipGetLastError());
+  }
+  return 0;
+}
+
 int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float eps,
                     hipStream_t st) {
   const lmoe_dims& d = h->d;
@@ -925,12 +1032,43 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     hipLaunchKernelGGL(k_prep, dim3(T), dim3(256), 0, st, a);
     LMOE_HIP(hipGetLastError());
   }
+  // D and the shared gate/up need only the staged rows: they run on the aux
+  // stream while the routing chain runs on the caller's. When phases are
+  // timed everything runs on the caller's stream in phase order, so that
+  // each phase is measured alone.
+  auto dense_front = [&](hipStream_t sd) -> int {
+    {
+      Dense a{};
+      a.W = WMat{h->dmat16, h->g_d16, 0, 1};
+      a.A = AMat{p.xh, (size_t)H, 0, H};
+      a.T = T; a.mtiles = mtiles; a.ntiles = G * h->g_d16.tiles; a.nquads = (a.ntiles + NTW - 1) / NTW;
+      a.out = p.xl; a.ostride = (size_t)G * L; a.nvalid = G * L;
+      if (int rc = launch_dense<kF16, kEpiF16>(a, sd)) return rc;
+      if (ev) LMOE_HIP(hipEventRecord(h->phase_events[3], sd));
+    }
+    {
+      Dense a{};
+      a.W = WMat{h->sgu, h->g_sgu, 0, 1};
+      a.A = AMat{p.xb, (size_t)2 * H, H, H};
+      a.T = T; a.mtiles = mtiles; a.ntiles = h->g_sgu.tiles; a.nquads = (a.ntiles + NTW - 1) / NTW;
+      a.out = p.hsb; a.ostride = (size_t)2 * Fs; a.nvalid = Fs;
+      if (int rc = launch_dense<kBF16, kEpiSwigluB2>(a, sd)) return rc;
+      if (ev) LMOE_HIP(hipEventRecord(h->phase_events[4], sd));
+    }
+    return 0;
+  };
+  if (!ev) {
+    LMOE_HIP(hipEventRecord(h->ev_fork, st));
+    LMOE_HIP(hipStreamWaitEvent(h->aux, h->ev_fork, 0));
+    if (int rc = dense_front(h->aux)) return rc;
+    LMOE_HIP(hipEventRecord(h->ev_join, h->aux));
+  }
   // router logits
   {
     Dense a{};
     a.W = WMat{h->router_m, h->g_router_m, 0, 1};
     a.A = AMat{p.xb, (size_t)2 * H, H, H};
-    a.T = T; a.mtiles = mtiles; a.ntiles = h->g_router_m.tiles; a.npairs = (a.ntiles + 1) / 2;
+    a.T = T; a.mtiles = mtiles; a.ntiles = h->g_router_m.tiles; a.nquads = (a.ntiles + NTW - 1) / NTW;
     a.out = p.logits; a.ostride = Epad; a.nvalid = E;
     if (int rc = launch_dense<kBF16, kEpiLogits>(a, st)) return rc;
   }
@@ -966,27 +1104,12 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     hipLaunchKernelGGL(k_perm_scatter, dim3((T * K + 255) / 256), dim3(256), 0, st, a);
     LMOE_HIP(hipGetLastError());
   }
-  if (ev) LMOE_HIP(hipEventRecord(h->phase_events[2], st));
-  // D over all groups, and the shared expert's gate/up
-  {
-    Dense a{};
-    a.W = WMat{h->dmat, h->g_d, 0, 1};
-    a.A = AMat{p.xh, (size_t)H, 0, H};
-    a.T = T; a.mtiles = mtiles; a.ntiles = G * h->g_d.tiles; a.npairs = (a.ntiles + 1) / 2;
-    a.out = p.xl; a.ostride = (size_t)G * L; a.nvalid = G * L;
-    const int rc = d.du_bits == 8 ? launch_dense<kQ8, kEpiF16>(a, st) : launch_dense<kQ4, kEpiF16>(a, st);
-    if (rc) return rc;
+  if (ev) {
+    LMOE_HIP(hipEventRecord(h->phase_events[2], st));
+    if (int rc = dense_front(st)) return rc;
+  } else {
+    LMOE_HIP(hipStreamWaitEvent(st, h->ev_join, 0));
   }
-  if (ev) LMOE_HIP(hipEventRecord(h->phase_events[3], st));
-  {
-    Dense a{};
-    a.W = WMat{h->sgu, h->g_sgu, 0, 1};
-    a.A = AMat{p.xb, (size_t)2 * H, H, H};
-    a.T = T; a.mtiles = mtiles; a.ntiles = h->g_sgu.tiles; a.npairs = (a.ntiles + 1) / 2;
-    a.out = p.hsb; a.ostride = (size_t)2 * Fs; a.nvalid = Fs;
-    if (int rc = launch_dense<kBF16, kEpiSwigluB2>(a, st)) return rc;
-  }
-  if (ev) LMOE_HIP(hipEventRecord(h->phase_events[4], st));
   // experts
   const unsigned maxp = (unsigned)prefill_max_pieces(T, K, E);
   {
@@ -994,10 +1117,10 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     a.experts = h->experts; a.estride = h->expert_stride; a.woff = 0; a.ts_off = h->ts_off;
     a.g = h->g_gu; a.A = AMat{p.xl, (size_t)L, 0, L};
     a.pieces = (const Piece*)p.pieces; a.npieces = p.npieces;
-    a.ntiles = h->g_gu.tiles; a.npairs = (a.ntiles + 1) / 2; a.G = G; a.F = F;
+    a.ntiles = h->g_gu.tiles; a.nquads = (a.ntiles + NTW - 1) / NTW; a.G = G; a.F = F;
     a.perm = p.perm; a.topk_w = p.w; a.labels = h->labels; a.K = K;
     a.out = p.h; a.ostride = F;
-    const unsigned grid = 8u * a.npairs * ((maxp + 7) / 8);
+    const unsigned grid = 8u * a.nquads * ((maxp + 7) / 8);
     hipLaunchKernelGGL(k_grouped<kGateUp>, dim3(grid), dim3(NTH), 0, st, a);
     LMOE_HIP(hipGetLastError());
   }
@@ -1007,10 +1130,10 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     a.experts = h->experts; a.estride = h->expert_stride; a.woff = h->g_gu.bytes();
     a.ts_off = h->ts_off; a.g = h->g_dn; a.A = AMat{p.h, (size_t)F, 0, F};
     a.pieces = (const Piece*)p.pieces; a.npieces = p.npieces;
-    a.ntiles = h->g_dn.tiles; a.npairs = (a.ntiles + 1) / 2; a.G = G; a.F = F;
+    a.ntiles = h->g_dn.tiles; a.nquads = (a.ntiles + NTW - 1) / NTW; a.G = G; a.F = F;
     a.perm = p.perm; a.topk_w = p.w; a.labels = h->labels; a.K = K;
     a.out = p.o; a.ostride = L;
-    const unsigned grid = 8u * a.npairs * ((maxp + 7) / 8);
+    const unsigned grid = 8u * a.nquads * ((maxp + 7) / 8);
     hipLaunchKernelGGL(k_grouped<kDown>, dim3(grid), dim3(NTH), 0, st, a);
     LMOE_HIP(hipGetLastError());
   }
@@ -1025,14 +1148,13 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
   // U over the concatenated groups, then the shared down projection
   {
     Dense a{};
-    a.W = WMat{h->umat, h->g_u, h->g_u.bytes(), G};
+    a.W = WMat{h->umat16, h->g_u16, h->g_u16.bytes(), G};
     a.A = AMat{p.s, (size_t)G * L, 0, L};
     a.W2 = WMat{h->sdn, h->g_sdn, 0, 1};
     a.A2 = AMat{p.hsb, (size_t)2 * Fs, Fs, Fs};
-    a.T = T; a.mtiles = mtiles; a.ntiles = h->g_u.tiles; a.npairs = (a.ntiles + 1) / 2;
+    a.T = T; a.mtiles = mtiles; a.ntiles = h->g_u16.tiles; a.nquads = (a.ntiles + NTW - 1) / NTW;
     a.out = y; a.ostride = H; a.nvalid = H; a.res = norm ? x : nullptr;
-    const int rc = d.du_bits == 8 ? launch_dense<kQ8, kEpiY>(a, st) : launch_dense<kQ4, kEpiY>(a, st);
-    if (rc) return rc;
+    if (int rc = launch_dense<kF16, kEpiY>(a, st)) return rc;
   }
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[8], st));
   return 0;
