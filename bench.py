@@ -35,10 +35,14 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 / bf16 matrix peak, published
 PREFILL_PHASES = ["route", "permute", "d", "shared_gate_up", "expert_gate_up", "expert_down",
                   "combine", "u_shared_down"]
-PREFILL_KERNELS = ["k_prep + k_dense<BF16,Logits> + k_select", "k_perm_*", "k_dense<Q,F16>",
-                   "k_dense<BF16,SwigluB2>", "k_grouped<GateUp>", "k_grouped<Down>", "k_combine",
-                   "k_dense<Q,Y>"]
+PREFILL_KERNELS = ["k_prep + k_dense<BF16,Logits> + k_select", "k_perm_*", "k_dense<F16,F16> (D)",
+                   "k_dense<BF16,SwigluB2> (shared gate/up)", "k_grouped<GateUp>",
+                   "k_grouped<Down>", "k_combine", "k_dense<F16,Y> (U + shared down)"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_145b_t4_traffic.json")
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_145b_t4096_traffic.json")
+# kernel of each prefill phase as rocprofv3 names it (D and U on fp16 weights)
+PREFILL_KERNEL_IDS = ["k_select", "k_perm_scan", "k_dense<5, 1>", "k_dense<3, 2>", "k_grouped<0>",
+                      "k_grouped<1>", "k_combine", "k_dense<5, 3>"]
 
 
 def log(*a):
@@ -104,13 +108,13 @@ def phase_bytes(w, idx, labels):
     return [p1, p2, p3, p4], distinct, used_groups
 
 
-def measured_traffic(kernel, workload):
+def measured_traffic(kernel, workload, path=TRAFFIC_FILE):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary, or None when there is none or the kernel source has changed
     since the counters were taken."""
     import hashlib
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
         src = open(os.path.join(ROOT, t["source"]), "rb").read()
     except (OSError, ValueError, KeyError):
@@ -223,7 +227,8 @@ def bench_prefill(lm, wl, w, args, torch):
                       "frac": gemm_fl / (gemm_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS},
         "roofline": {"bound": "mfma", "achieved": tflops[dom], "peak": MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops[dom] / MFMA_PEAK_TFLOPS,
-                     "traffic": None, "kernel": PREFILL_KERNELS[dom],
+                     "traffic": measured_traffic(PREFILL_KERNEL_IDS[dom], w.name, PREFILL_TRAFFIC_FILE),
+                     "kernel": PREFILL_KERNELS[dom],
                      "phase": PREFILL_PHASES[dom], "kernel_us": float(phase_avg[dom] * 1e3),
                      "kernel_algorithmic_flop": float(flops[dom]),
                      "kernel_executed_flop": ex[0][dom]},
