@@ -435,6 +435,13 @@ struct P4 {
 // ---------------------------------------------------------------------------
 // Routing, done by the last router block.
 
+// LDS of the routing block: logits [T][E] (fp64), then per assignment
+// key, sorted order, inverse, label and segment flags, per expert a counter,
+// per wave 64-entry scratch for the top-K candidates.
+__host__ __device__ constexpr size_t routing_lds_bytes(int T, int E, int n, int nw) {
+  return (size_t)T * E * 8 + (size_t)(6 * n + E + 8) * 4 + 8 + (size_t)nw * 64 * (8 + 8 + 4);
+}
+
 template <int T>
 __device__ void routing(const P1& a, char* smem) {
   const Dims& d = a.d;
@@ -445,10 +452,16 @@ __device__ void routing(const P1& a, char* smem) {
   const int n = T * d.K;
   double* lg = (double*)smem;      // [T][E] logits
   int* key = (int*)(lg + T * d.E); // [n] label * E + expert, assignment order
-  int* sperm = key + n;            // [n]
-  int* start = sperm + n;          // [n]
-  int* inv = start + n;            // [n]
+  int* sperm = key + n;            // [n] sorted position -> assignment
+  int* inv = sperm + n;            // [n] assignment -> sorted position
   int* slab = inv + n;             // [n] label at each sorted position
+  int* sid = slab + n;             // [n] slot of each sorted position
+  int* aexp = sid + n;             // [n] expert of each assignment
+  int* ecnt = aexp + n;            // [E] assignments per expert
+  int* nslot = ecnt + d.E;         // [1]
+  double* wv = (double*)(((uintptr_t)(nslot + 8) + 7) & ~(uintptr_t)7);   // [nw][64]
+  double* cv = wv + nw * 64;       // [nw][64]
+  int* ce = (int*)(cv + nw * 64);  // [nw][64]
 
   // logits = the chunk partials summed in chunk order (scaled by 1/rms in the
   // block forward) + bias; every thread issues all its loads before summing
@@ -479,48 +492,99 @@ __device__ void routing(const P1& a, char* smem) {
       }
     }
   }
+  for (int e = tid; e < d.E; e += nth) ecnt[e] = 0;
   __syncthreads();
 
-  // Top K per token, one wavefront per token: K rounds of a wave arg-max over
-  // (logit desc, expert asc); lane k keeps the k-th winner; then the softmax
-  // of the kept logits.
+  // Top K per token, one wavefront per token, exact. theta = the K-th largest
+  // of the 64 per-lane maxima is <= the K-th largest logit, so every logit
+  // >= theta is a candidate; each candidate's rank by (logit desc, expert
+  // asc) among the candidates equals its rank among all experts when it is
+  // in the top K, and is >= K otherwise. More than 64 candidates (heavy
+  // ties): rank among all experts instead.
+  const unsigned long long lower = (1ull << lane) - 1ull;
   for (int t = wave; t < T; t += nw) {
-    double v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int e = lane + 64 * i;
-      v[i] = e < d.E ? lg[t * d.E + e] : -INFINITY;
+    const double* l = lg + t * d.E;
+    double m = -INFINITY;
+    for (int e = lane; e < d.E; e += 64) m = fmax(m, l[e]);
+    wv[wave * 64 + lane] = m;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    int r = 0;
+    for (int j = 0; j < 64; ++j) {
+      const double vj = wv[wave * 64 + j];
+      r += (vj > m) || (vj == m && j < lane);
     }
-    double kv = -INFINITY, l0 = 0.0;
+    // rank K - 1 exists (K <= 64) and is unique: its value is theta
+    const unsigned long long at = __ballot(r == d.K - 1);
+    const double theta = __shfl(m, __builtin_ctzll(at));
+    int c = 0;
+    for (int e0 = 0; e0 < d.E; e0 += 64) {
+      const int e = e0 + lane;
+      c += __popcll(__ballot(e < d.E && l[e] >= theta));
+    }
+    int rank = 64;
+    double kv = -INFINITY;
     int ki = 0;
-    for (int k = 0; k < d.K; ++k) {
-      double bv = -INFINITY;
-      int bi = 0x7FFFFFFF;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int e = lane + 64 * i;
-        if (v[i] > bv || (v[i] == bv && e < bi)) { bv = v[i]; bi = e; }
+    if (c <= 64) {
+      int base = 0;
+      for (int e0 = 0; e0 < d.E; e0 += 64) {
+        const int e = e0 + lane;
+        const bool in = e < d.E && l[e] >= theta;
+        const unsigned long long mk = __ballot(in);
+        if (in) {
+          const int slot = base + __popcll(mk & lower);
+          cv[wave * 64 + slot] = l[e];
+          ce[wave * 64 + slot] = e;
+        }
+        base += __popcll(mk);
       }
-      for (int o = 32; o > 0; o >>= 1) {
-        const double ov = __shfl_xor(bv, o);
-        const int oi = __shfl_xor(bi, o);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      if (lane < c) {
+        kv = cv[wave * 64 + lane];
+        ki = ce[wave * 64 + lane];
+        rank = 0;
+        for (int j = 0; j < c; ++j) {
+          const double vj = cv[wave * 64 + j];
+          rank += (vj > kv) || (vj == kv && ce[wave * 64 + j] < ki);
+        }
       }
-      if ((bi & 63) == lane) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (i == (bi >> 6)) v[i] = -INFINITY;
+      __builtin_amdgcn_wave_barrier();
+      if (rank < d.K) {
+        cv[wave * 64 + rank] = kv;
+        ce[wave * 64 + rank] = ki;
       }
-      if (k == 0) l0 = bv;
-      if (lane == k) { kv = bv; ki = bi; }
+    } else {
+      for (int e0 = 0; e0 < d.E; e0 += 64) {
+        const int e = e0 + lane;
+        if (e < d.E) {
+          const double v = l[e];
+          int rk = 0;
+          for (int j = 0; j < d.E; ++j) rk += (l[j] > v) || (l[j] == v && j < e);
+          if (rk < d.K) {
+            cv[wave * 64 + rk] = v;
+            ce[wave * 64 + rk] = e;
+          }
+        }
+      }
     }
-    const double ex = lane < d.K ? exp(kv - l0) : 0.0;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    if (lane < d.K) {
+      kv = cv[wave * 64 + lane];
+      ki = ce[wave * 64 + lane];
+    }
+    const double top = cv[wave * 64];
+    const double ex = lane < d.K ? exp(kv - top) : 0.0;
     double z = ex;
     for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
     if (lane < d.K) {
-      ws.topk_idx[t * d.K + lane] = ki;
-      ws.topk_w[t * d.K + lane] = (float)(ex / z);
-      key[t * d.K + lane] = (int)a.labels[ki] * d.E + ki;
+      const int i = t * d.K + lane;
+      ws.topk_idx[i] = ki;
+      ws.topk_w[i] = (float)(ex / z);
+      key[i] = (int)a.labels[ki] * d.E + ki;
+      aexp[i] = ki;
+      atomicAdd(&ecnt[ki], 1);
     }
   }
   __syncthreads();
@@ -537,43 +601,46 @@ __device__ void routing(const P1& a, char* smem) {
     inv[i] = r;
     ws.perm[r] = i;
   }
+  for (int e = tid; e < d.E; e += nth) ws.expert_count[e] = ecnt[e];
   __syncthreads();
-  for (int j = tid; j < n; j += nth) {
-    start[j] = (j == 0 || key[sperm[j]] != key[sperm[j - 1]]) ? 1 : 0;
-    slab[j] = key[sperm[j]] / d.E;
-  }
-  __syncthreads();
-  // one slot per distinct expert, in (label, expert) order
-  for (int j = tid; j < n; j += nth) {
-    if (!start[j]) continue;
-    int sid = 0;
-    for (int q = 0; q < j; ++q) sid += start[q];
-    int end = j + 1;
-    while (end < n && !start[end]) ++end;
-    ws.slot_expert[sid] = key[sperm[j]] % d.E;
-    ws.slot_start[sid] = j;
-    ws.slot_count[sid] = end - j;
-  }
-  if (tid == 0) {
-    int ns = 0;
-    for (int j = 0; j < n; ++j) ns += start[j];
-    *ws.n_slots = ns;
-  }
-  for (int g = tid; g <= d.G; g += nth) {
-    int gs = 0, ga = 0;
-    for (int j = 0; j < n; ++j) {
-      if (slab[j] < g) {
-        ga += 1;
-        gs += start[j];
-      }
+  for (int j = tid; j < n; j += nth) slab[j] = (int)a.labels[aexp[sperm[j]]];
+  // slot of each sorted position: prefix count of segment starts, by wave 0
+  if (wave == 0) {
+    int run = 0;
+    for (int j0 = 0; j0 < n; j0 += 64) {
+      const int j = j0 + lane;
+      const bool st = j < n && (j == 0 || key[sperm[j]] != key[sperm[j - 1]]);
+      const unsigned long long mk = __ballot(st);
+      if (j < n) sid[j] = run + __popcll(mk & lower) + (st ? 0 : -1);
+      run += __popcll(mk);
     }
-    ws.gslot_off[g] = gs;
-    ws.group_off[g] = ga;
+    if (lane == 0) {
+      *nslot = run;
+      *ws.n_slots = run;
+    }
   }
-  for (int e = tid; e < d.E; e += nth) {
-    int c = 0;
-    for (int j = 0; j < n; ++j) c += (key[j] % d.E) == e;
-    ws.expert_count[e] = c;
+  __syncthreads();
+  // slots: expert, first sorted position, count; group offsets (positions
+  // and slots) from the boundaries of the sorted labels
+  for (int j = tid; j < n; j += nth) {
+    const int s0 = sid[j];
+    if (j == 0 || sid[j - 1] != s0) {
+      int end = j + 1;
+      while (end < n && sid[end] == s0) ++end;
+      ws.slot_expert[s0] = aexp[sperm[j]];
+      ws.slot_start[s0] = j;
+      ws.slot_count[s0] = end - j;
+    }
+    const int lo = j == 0 ? 0 : slab[j - 1] + 1;
+    for (int g = lo; g <= slab[j]; ++g) {
+      ws.group_off[g] = j;
+      ws.gslot_off[g] = s0;
+    }
+    if (j == n - 1)
+      for (int g = slab[j] + 1; g <= d.G; ++g) {
+        ws.group_off[g] = n;
+        ws.gslot_off[g] = *nslot;
+      }
   }
   // for each (token, group): the sorted positions of its assignments, in
   // ascending k (the order the per-group sum takes)
@@ -581,17 +648,17 @@ __device__ void routing(const P1& a, char* smem) {
     const int t = q / d.G, g = q % d.G;
     int c = 0;
     for (int k = 0; k < d.K; ++k)
-      if (key[t * d.K + k] / d.E == g) ws.tg_pos[q * d.K + c++] = inv[t * d.K + k];
+      if ((int)a.labels[aexp[t * d.K + k]] == g) ws.tg_pos[q * d.K + c++] = inv[t * d.K + k];
     ws.tg_cnt[q] = c;
   }
 }
 
-
 // ---------------------------------------------------------------------------
 // Phase 1: router | D_g | shared gate/up, by block index range.
 
-template <int T, int DU>
-__global__ __launch_bounds__(1024) void k_phase1(P1 a) {
+// W: most waves a block of this launch has (the register budget follows it)
+template <int T, int DU, int W>
+__global__ __launch_bounds__(64 * W) void k_phase1(P1 a) {
   extern __shared__ __align__(16) char smem[];
   const Dims& d = a.d;
   const int lane = threadIdx.x & 63;
@@ -806,8 +873,8 @@ __global__ __launch_bounds__(1024) void k_phase3(P3 a) {
 // ---------------------------------------------------------------------------
 // Phase 4: U_g per used group and the shared down; ordered sum per row tile.
 
-template <int T, int DU>
-__global__ __launch_bounds__(1024) void k_phase4(P4 a) {
+template <int T, int DU, int W>
+__global__ __launch_bounds__(64 * W) void k_phase4(P4 a) {
   extern __shared__ __align__(16) char smem[];
   __shared__ int flag;
   const Dims& d = a.d;
@@ -931,10 +998,13 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st) {
   const int n = T * d.K;
   size_t sm1 = (size_t)nw1 * (stage_bytes<T>() + red_bytes_per_wave<T>());
   const size_t sm_router = (size_t)nw1 * T * 64 * sizeof(double);
-  const size_t sm_routing = (size_t)T * d.E * sizeof(double) + (size_t)5 * n * sizeof(int);
+  const size_t sm_routing = routing_lds_bytes(T, d.E, n, nw1);
   sm1 = sm1 > sm_router ? sm1 : sm_router;
   sm1 = sm1 > sm_routing ? sm1 : sm_routing;
-  hipLaunchKernelGGL((k_phase1<T, DU>), dim3(nb1), dim3(nw1 * 64), sm1, st, p1);
+  if (nw1 <= 10)
+    hipLaunchKernelGGL((k_phase1<T, DU, 10>), dim3(nb1), dim3(nw1 * 64), sm1, st, p1);
+  else
+    hipLaunchKernelGGL((k_phase1<T, DU, 16>), dim3(nb1), dim3(nw1 * 64), sm1, st, p1);
   LMOE_HIP(hipGetLastError());
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[1], st));
 
@@ -967,7 +1037,10 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st) {
   size_t sm4 = (size_t)nw4 * (stage_bytes<T>() + red_bytes_per_wave<T>());
   const size_t sm4r = (size_t)(d.G + 1) * T * 64 * sizeof(float);
   sm4 = sm4 > sm4r ? sm4 : sm4r;
-  hipLaunchKernelGGL((k_phase4<T, DU>), dim3((d.G + 1) * h->g_u.tiles), dim3(nw4 * 64), sm4, st, p4);
+  if (nw4 <= 10)
+    hipLaunchKernelGGL((k_phase4<T, DU, 10>), dim3((d.G + 1) * h->g_u.tiles), dim3(nw4 * 64), sm4, st, p4);
+  else
+    hipLaunchKernelGGL((k_phase4<T, DU, 16>), dim3((d.G + 1) * h->g_u.tiles), dim3(nw4 * 64), sm4, st, p4);
   LMOE_HIP(hipGetLastError());
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[4], st));
   return 0;

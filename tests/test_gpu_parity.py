@@ -138,6 +138,21 @@ def test_exact_ties_break_to_lower_index():
     check(c, layer, 6, "tiny exact ties")
 
 
+def test_145b_zero_rows_all_logits_tie():
+    """Zero token rows at the 145B shape: all 512 logits are exactly 0, more
+    candidates than one wavefront ranks at once; experts 0..K-1 must win."""
+    w = wl.WORKLOADS["145b_decode"]
+    x = wl.x(w, 0, tokens=4)
+    x[1] = 0.0
+    x[3] = 0.0
+    c = Case(w, x=x)
+    layer = make_layer(c, max_tokens=4)
+    _, dbg = run(layer, c, 4)
+    assert (dbg["topk_idx"][1] == np.arange(w.top_k)).all()
+    assert (dbg["topk_idx"][3] == np.arange(w.top_k)).all()
+    check(c, layer, 4, "145b zero rows")
+
+
 def test_argument_errors_on_device():
     lm = _lmoe()
     c = Case(wl.WORKLOADS["tiny"], tokens=4)
