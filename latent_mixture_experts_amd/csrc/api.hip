@@ -89,7 +89,7 @@ int create_impl(lmoe_t* h) {
 #define A(p, n) if ((rc = dalloc(h, &(p), (n)))) return rc
   A(h->router, h->g_router.bytes());
   A(h->bias, sizeof(float) * E);
-  A(h->labels, (size_t)E);
+  A(h->labels, (size_t)(E + 3) / 4 * 4);   // whole 32-bit words: kernels read labels by word
   A(h->dmat, h->g_d.bytes() * G);
   A(h->umat, h->g_u.bytes() * G);
   A(h->experts, h->expert_stride * E);

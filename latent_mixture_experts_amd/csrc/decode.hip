@@ -55,6 +55,26 @@ __device__ __forceinline__ uint4 ldnt(const uint8_t* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Group label of expert e, read as a 32-bit scalar load (the label array is
+// allocated in whole words).
+__device__ __forceinline__ int label_of(const uint8_t* labels, int e) {
+  typedef const __attribute__((address_space(4))) uint32_t* cu32_t;
+  return (int)((((cu32_t)labels)[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+}
+
+// Raw buffer resource over [p, p + bytes): wave-uniform base in SGPRs, so a
+// lane addresses it with one 32-bit offset register; loads past the end
+// return zero.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int kAuxNT = 2;   // cache policy: non-temporal
+template <int AUX = 0>
+__device__ __forceinline__ uint4 ldb(rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX));
+}
+
 __device__ __forceinline__ float h2f(uint32_t bits) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFFFu));
 }
@@ -195,30 +215,68 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
 // xs: this wave's staging area; src[i]: vector i at the super-step's first
 // column; n: valid vectors; ncs: code slots present.
 template <int FMT, int NT>
-__device__ __forceinline__ void wave_ss(const uint8_t* p, int ncs, int cols,
-                                        const float* const (&src)[NT], int n, void* xs,
-                                        int lane, f4 (&acc)[4]) {
-  constexpr int CC = FMT == kQ8 ? 64 : (FMT == kBF16 ? 32 : 128);   // columns per chunk
-  constexpr int MAXCH = kSSCols / CC;
-  constexpr int NSL = 4 * MAXCH;
-  const int tok = lane & 15, qg = lane >> 4;
-
-  // activations first, then scales, then the weight stream: loads are
-  // counted in order, so the staging waits only for its own data
+struct WRegs {
+  static constexpr int CC = FMT == kQ8 ? 64 : (FMT == kBF16 ? 32 : 128);   // columns per chunk
+  static constexpr int NSL = 4 * (kSSCols / CC);
   XRegs<NT> xr;
-  x_load<NT>(xr, src, n, cols, lane);
   uint4 sc[4];
+  uint4 q[NSL];
+};
+
+// Issues the loads of one super-step: activations first, then scales, then
+// the weight stream (loads are counted in order, so the staging waits only
+// for its own data).
+template <int FMT, int NT>
+__device__ __forceinline__ void wave_load(WRegs<FMT, NT>& R, const uint8_t* p, int ncs, int cols,
+                                          const float* const (&src)[NT], int n, int lane) {
+  const int tok = lane & 15;
+  x_load<NT>(R.xr, src, n, cols, lane);
   if (FMT != kBF16) {
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) sc[rg] = ldw(p + ncs * kSlot + (rg * 16 + tok) * 16);
+    for (int rg = 0; rg < 4; ++rg) R.sc[rg] = ldw(p + ncs * kSlot + (rg * 16 + tok) * 16);
   }
-  uint4 q[NSL];
 #pragma unroll
-  for (int j = 0; j < NSL; ++j)
-    if (j < ncs) q[j] = ldnt(p + j * kSlot + lane * 16);
+  for (int j = 0; j < WRegs<FMT, NT>::NSL; ++j)
+    if (j < ncs) R.q[j] = ldnt(p + j * kSlot + lane * 16);
+}
 
-  if (FMT == kBF16) x_stage_bf16<NT>(xr, (__bf16*)xs, lane);
-  else x_stage_f16<NT>(xr, (_Float16*)xs, lane);
+// wave_load for loops over items: weights through resource w (the
+// super-step's first slot at offset 0, ncs code slots then the scale slot),
+// vector i of the activations at byte offset xoff[i] of resource x. All
+// per-lane addresses are the one lane offset, which stays in a register
+// across items instead of one 64-bit address per load.
+template <int FMT, int NT>
+__device__ __forceinline__ void wave_load_b(WRegs<FMT, NT>& R, rsrc_t w, int ncs, rsrc_t x,
+                                            const int (&xoff)[NT], int n, int cols, int lane) {
+  const int tok = lane & 15;
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    R.xr.v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < n && 4 * lane < cols) {
+      const uint4 v = ldb(x, 16 * lane, xoff[i]);
+      R.xr.v[i] = __builtin_bit_cast(float4, v);
+    }
+  }
+  if (FMT != kBF16) {
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) R.sc[rg] = ldb(w, 16 * tok, ncs * kSlot + rg * 256);
+  }
+#pragma unroll
+  for (int j = 0; j < WRegs<FMT, NT>::NSL; ++j)
+    if (j < ncs) R.q[j] = ldb<kAuxNT>(w, 16 * lane, j * kSlot);
+}
+
+// The MFMAs of a loaded super-step (xs: this wave's staging area).
+template <int FMT, int NT>
+__device__ __forceinline__ void wave_compute(const WRegs<FMT, NT>& R, int ncs, int n, void* xs,
+                                             int lane, f4 (&acc)[4]) {
+  constexpr int CC = WRegs<FMT, NT>::CC;
+  constexpr int MAXCH = kSSCols / CC;
+  const int tok = lane & 15, qg = lane >> 4;
+  const uint4 (&sc)[4] = R.sc;
+  const uint4 (&q)[WRegs<FMT, NT>::NSL] = R.q;
+  if (FMT == kBF16) x_stage_bf16<NT>(R.xr, (__bf16*)xs, lane);
+  else x_stage_f16<NT>(R.xr, (_Float16*)xs, lane);
   __builtin_amdgcn_wave_barrier();
 
   const int nch = ncs / 4;
@@ -241,32 +299,30 @@ __device__ __forceinline__ void wave_ss(const uint8_t* p, int ncs, int cols,
     } else {
       constexpr int NB = CC / 32;                      // 32-column blocks per chunk
       const _Float16* x = (const _Float16*)xs;
-      half8 ah[NB], al[NB];
+      // one 32-column block's A operands at a time; every acc[rg] still sums
+      // in (chunk, block, hi before lo) order
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int col = CC * c + 32 * b + 8 * qg;
-        ah[b] = a_read<NT, _Float16, half8>(x, 0, tok, n, col);
-        al[b] = a_read<NT, _Float16, half8>(x, 1, tok, n, col);
-      }
+        const half8 ahb = a_read<NT, _Float16, half8>(x, 0, tok, n, col);
+        const half8 alb = a_read<NT, _Float16, half8>(x, 1, tok, n, col);
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const uint4 w = q[4 * c + rg];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
+        for (int rg = 0; rg < 4; ++rg) {
+          const uint4 w = q[4 * c + rg];
           if constexpr (FMT == kFP4) {
             // block of 16 columns holding this lane's 8: 8c + 2b + qg/2
             const int k = 4 * c + b;                     // scale half-word index
             const uint32_t sb = (word(sc[rg], k >> 1) >> (16 * (k & 1) + 8 * (qg >> 1))) & 0xFFu;
             const _Float16 s = (_Float16)__builtin_amdgcn_cvt_f32_fp8(sb, 0);
             const half8 bw = dec_fp4(word(w, b), s);
-            acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[b], bw, acc[rg], 0, 0, 0);
-            acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[b], bw, acc[rg], 0, 0, 0);
+            acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahb, bw, acc[rg], 0, 0, 0);
+            acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alb, bw, acc[rg], 0, 0, 0);
           } else {
             const half8 bw = FMT == kQ8 ? dec_q8(word(w, 2 * b), word(w, 2 * b + 1))
                                         : dec_q4(word(w, b));
             f4 d = {0.f, 0.f, 0.f, 0.f};
-            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[b], bw, d, 0, 0, 0);
-            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[b], bw, d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahb, bw, d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(alb, bw, d, 0, 0, 0);
             const int blk = NB * c + b;                  // fp16 scale of this 32-column block
             const float s = h2f(word(sc[rg], blk >> 1) >> (16 * (blk & 1)));
             acc[rg] += s * d;
@@ -275,6 +331,15 @@ __device__ __forceinline__ void wave_ss(const uint8_t* p, int ncs, int cols,
       }
     }
   }
+}
+
+template <int FMT, int NT>
+__device__ __forceinline__ void wave_ss(const uint8_t* p, int ncs, int cols,
+                                        const float* const (&src)[NT], int n, void* xs,
+                                        int lane, f4 (&acc)[4]) {
+  WRegs<FMT, NT> R;
+  wave_load<FMT, NT>(R, p, ncs, cols, src, n, lane);
+  wave_compute<FMT, NT>(R, ncs, n, xs, lane, acc);
 }
 
 // Sum the per-wave MFMA accumulators of the block in wave order into wave 0.
@@ -425,6 +490,7 @@ struct P3 {
 
 struct P4 {
   Dims d;
+  int nub;                 // blocks striding over the U items; the rest take the shared down
   const uint8_t* umat; Geom gu;
   const uint8_t* sdn; Geom gsd;
   float* y;
@@ -748,47 +814,74 @@ __global__ __launch_bounds__(64 * W) void k_phase1(P1 a) {
 }
 
 // ---------------------------------------------------------------------------
-// Phase 2: routed-expert gate/up + SwiGLU, one block per (slot, tile).
+// Phases 2 to 4 run as many blocks as are resident at once; a block strides
+// over the items (one item = one 64-row tile of one matrix, every wave one
+// super-step of it) and issues the weight loads of its next item as soon as
+// the MFMAs of the current one have consumed its registers, so that the
+// reduction and the stores of an item overlap the loads of the next.
+// The cross-wave reduction buffer alternates between two halves by item
+// parity: wave 0 may still read one while the others fill the other.
+
+// Phase 2: routed-expert gate/up + SwiGLU, item = (slot, tile).
 
 template <int T>
 __global__ __launch_bounds__(1024) void k_phase2(P2 a) {
   extern __shared__ __align__(16) char smem[];
   const Dims& d = a.d;
   const int tiles = a.ggu.tiles;
-  const int j = blockIdx.x / tiles, r = blockIdx.x % tiles;
   ci_t ns = ci(a.ws.n_slots);
-  if (j >= ns[0]) return;
+  const int nvalid = ns[0] * tiles;            // items of real slots come first
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6), nw = blockDim.x >> 6;
-  const int e = ci(a.ws.slot_expert)[j], start = ci(a.ws.slot_start)[j];
-  const int cnt = ci(a.ws.slot_count)[j];
-  const int g = ((cu8_t)a.labels)[e];
-  const uint8_t* base = a.experts + (size_t)e * a.stride;
   ci_t perm = ci(a.ws.perm);
-  const float* src[T];
-#pragma unroll
-  for (int i = 0; i < T; ++i) {
-    const int t = i < cnt ? perm[start + i] / d.K : 0;
-    src[i] = a.ws.xl + ((size_t)t * d.G + g) * d.L + wave * kSSCols;
-  }
-  f4 acc[4];
-#pragma unroll
-  for (int rg = 0; rg < 4; ++rg) acc[rg] = (f4){0.f, 0.f, 0.f, 0.f};
   char* xs = smem + wave * stage_bytes<T>();
-  f4* red = (f4*)(smem + nw * stage_bytes<T>());
-  if (wave < a.ggu.nss)
-    wave_ss<kFP4, T>(ss_ptr(base, a.ggu, r, wave), ss_codes(kFP4, a.ggu, wave),
-                     ss_cols(a.ggu, wave), src, cnt, xs, lane, acc);
-  if (block_reduce_mf<T>(acc, red, wave, lane, nw)) {
-    cf_t ts = cf((const float*)(base + a.ts_off));
+  f4* red0 = (f4*)(smem + nw * stage_bytes<T>());
+  const int red_len = nw * red_bytes_per_wave<T>() / (int)sizeof(f4);
+  const bool active = wave < a.ggu.nss;
+
+  // activations: xl [T][G][L] fp32; item (slot j, tile r)
+  const rsrc_t xr = rsrc(a.ws.xl, (uint32_t)((size_t)T * d.G * d.L * sizeof(float)));
+  const int wbytes = (ss_codes(kFP4, a.ggu, wave) + scale_slots(kFP4)) * kSlot;
+  auto issue = [&](int item, WRegs<kFP4, T>& R) {
+    const int j = item / tiles;
+    const int e = ci(a.ws.slot_expert)[j], start = ci(a.ws.slot_start)[j];
+    const int cnt = ci(a.ws.slot_count)[j];
+    const int g = label_of(a.labels, e);
+    int xoff[T];
 #pragma unroll
-    for (int rg = 0; rg < 2; ++rg)
+    for (int i = 0; i < T; ++i) {
+      const int t = i < cnt ? perm[start + i] / d.K : 0;
+      xoff[i] = (int)(((t * d.G + g) * d.L + wave * kSSCols) * sizeof(float));
+    }
+    const uint8_t* base = a.experts + (size_t)e * a.stride;
+    wave_load_b<kFP4, T>(R, rsrc(ss_ptr(base, a.ggu, item % tiles, wave), wbytes),
+                         ss_codes(kFP4, a.ggu, wave), xr, xoff, cnt, ss_cols(a.ggu, wave), lane);
+  };
+  WRegs<kFP4, T> R;
+  int it = blockIdx.x;
+  if (it < nvalid && active) issue(it, R);
+  for (int par = 0; it < nvalid; it += gridDim.x, par ^= 1) {
+    const int j = it / tiles, r = it % tiles;
+    const int start = ci(a.ws.slot_start)[j], cnt = ci(a.ws.slot_count)[j];
+    const uint8_t* base = a.experts + (size_t)ci(a.ws.slot_expert)[j] * a.stride;
+    f4 acc[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int i = 4 * (lane >> 4) + v;
-        const int f = r * 32 + rg * 16 + (lane & 15);
-        if (i < cnt && f < d.F)
-          a.ws.hbuf[(size_t)(start + i) * d.F + f] = silu(acc[rg][v] * ts[0]) * (acc[rg + 2][v] * ts[1]);
-      }
+    for (int rg = 0; rg < 4; ++rg) acc[rg] = (f4){0.f, 0.f, 0.f, 0.f};
+    if (active) wave_compute<kFP4, T>(R, ss_codes(kFP4, a.ggu, wave), cnt, xs, lane, acc);
+    __builtin_amdgcn_sched_barrier(0);   // the next loads reuse this item's registers
+    const int nx = it + gridDim.x;
+    if (nx < nvalid && active) issue(nx, R);
+    if (block_reduce_mf<T>(acc, red0 + par * red_len, wave, lane, nw)) {
+      cf_t ts = cf((const float*)(base + a.ts_off));
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int i = 4 * (lane >> 4) + v;
+          const int f = r * 32 + rg * 16 + (lane & 15);
+          if (i < cnt && f < d.F)
+            a.ws.hbuf[(size_t)(start + i) * d.F + f] = silu(acc[rg][v] * ts[0]) * (acc[rg + 2][v] * ts[1]);
+        }
+    }
   }
 }
 
@@ -872,39 +965,55 @@ __global__ __launch_bounds__(1024) void k_phase3(P3 a) {
 
 // ---------------------------------------------------------------------------
 // Phase 4: U_g per used group and the shared down; ordered sum per row tile.
+// Item it = part * tiles + r (part < G: U_part, part == G: shared down). The
+// last of the G + 1 items of row tile r to finish adds the partials in part
+// order. Blocks [0, nub) stride over the U items, prefetching the next
+// item's weights; each of the others takes one shared-down tile (a bf16
+// super-step fills 128 VGPRs, which a loop could not carry without spills).
 
-template <int T, int DU, int W>
-__global__ __launch_bounds__(64 * W) void k_phase4(P4 a) {
-  extern __shared__ __align__(16) char smem[];
-  __shared__ int flag;
+template <int T, int FMT>
+__device__ __forceinline__ void phase4_issue(const P4& a, WRegs<FMT, T>& R, int part, int r,
+                                             int wave, int lane) {
+  constexpr bool kU = FMT != kBF16;
+  const Dims& d = a.d;
+  const Geom& geo = kU ? a.gu : a.gsd;
+  const float* src[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+    src[t] = kU ? a.ws.s + ((size_t)t * d.G + part) * d.L + wave * kSSCols
+                : a.ws.hs + (size_t)t * d.Fs + wave * kSSCols;
+  const uint8_t* base = kU ? a.umat + (size_t)part * a.gu.bytes() : a.sdn;
+  wave_load<FMT, T>(R, ss_ptr(base, geo, r, wave), ss_codes(FMT, geo, wave), ss_cols(geo, wave),
+                    src, T, lane);
+}
+
+// The U loop's loads: s [T][G][L] fp32 through one resource.
+template <int T, int DU>
+__device__ __forceinline__ void phase4_issue_u(const P4& a, WRegs<DU, T>& R, rsrc_t sr, int part,
+                                               int r, int wave, int lane) {
+  const Dims& d = a.d;
+  int xoff[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) xoff[t] = (int)(((t * d.G + part) * d.L + wave * kSSCols) * sizeof(float));
+  const int ncs = ss_codes(DU, a.gu, wave);
+  const uint8_t* p = ss_ptr(a.umat + (size_t)part * a.gu.bytes(), a.gu, r, wave);
+  wave_load_b<DU, T>(R, rsrc(p, (ncs + scale_slots(DU)) * kSlot), ncs, sr, xoff, T,
+                     ss_cols(a.gu, wave), lane);
+}
+
+// Writes the block's partial of (part, r) (if `active`), arrives at row
+// tile r's counter and, in the last block to arrive, writes y's tile.
+// `after_wait` runs on wave 0 once its stores have completed.
+template <int T, typename F>
+__device__ __forceinline__ void phase4_finish(const P4& a, int part, int r, bool active,
+                                              f4 (&acc)[4], char* smem, int* flag, F&& after_wait) {
   const Dims& d = a.d;
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6), nw = blockDim.x >> 6;
-  const int tiles = a.gu.tiles;      // H / 64
-  const int b = blockIdx.x;
-  const int part = b / tiles, r = b % tiles;   // part < G: U_part; part == G: shared down
   ci_t gso = ci(a.ws.gslot_off);
-  f4 acc[4];
-#pragma unroll
-  for (int rg = 0; rg < 4; ++rg) acc[rg] = (f4){0.f, 0.f, 0.f, 0.f};
-  char* xs = smem + wave * stage_bytes<T>();
   f4* red = (f4*)(smem + nw * stage_bytes<T>());
-  const float* src[T];
-  bool active;
-  if (part < d.G) {
-    active = gso[part + 1] > gso[part];
-#pragma unroll
-    for (int t = 0; t < T; ++t) src[t] = a.ws.s + ((size_t)t * d.G + part) * d.L + wave * kSSCols;
-    if (active && wave < a.gu.nss)
-      wave_ss<DU, T>(ss_ptr(a.umat + (size_t)part * a.gu.bytes(), a.gu, r, wave),
-                     ss_codes(DU, a.gu, wave), ss_cols(a.gu, wave), src, T, xs, lane, acc);
-  } else {
-    active = true;
-#pragma unroll
-    for (int t = 0; t < T; ++t) src[t] = a.ws.hs + (size_t)t * d.Fs + wave * kSSCols;
-    if (wave < a.gsd.nss)
-      wave_ss<kBF16, T>(ss_ptr(a.sdn, a.gsd, r, wave), ss_codes(kBF16, a.gsd, wave),
-                        ss_cols(a.gsd, wave), src, T, xs, lane, acc);
-  }
+  // Both branches pass one barrier, which also orders this item's write of
+  // *flag after every wave's read of the previous item's.
+  if (!active) __syncthreads();
   if (active && block_reduce_mf<T>(acc, red, wave, lane, nw)) {
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg)
@@ -915,38 +1024,99 @@ __global__ __launch_bounds__(64 * W) void k_phase4(P4 a) {
           st_co(a.ws.ypart + ((size_t)part * T + t) * d.H + r * 64 + rg * 16 + (lane & 15), acc[rg][v]);
       }
   }
-  if (!arrive_last(a.ws.ctr_y + r, (unsigned)(d.G + 1), &flag)) return;
+  if (wave == 0) {
+    // only wave 0 stored: it alone waits for its stores before the arrival
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    if (lane == 0) {
+      unsigned* ctr = a.ws.ctr_y + r;
+      const unsigned old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = old + 1 == (unsigned)(d.G + 1);
+      *flag = last;
+      if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    after_wait();
+  }
+  __syncthreads();
+  if (*flag == 0) return;
   // Ordered sum of the G + 1 partials: wave w fetches parts w, w + nw, ...
   // (all loads in flight together), wave 0 adds them in part order.
-  {
-    const int row = r * 64 + lane;
-    float* stage = (float*)smem;                     // [G + 1][T][64]
-    for (int p0 = wave; p0 <= d.G; p0 += 2 * nw) {
-      const int p1 = min(p0 + nw, d.G);
-      float v0[T], v1[T];
+  const int row = r * 64 + lane;
+  float* stage = (float*)smem;                       // [G + 1][T][64]
+  for (int p0 = wave; p0 <= d.G; p0 += 2 * nw) {
+    const int p1 = min(p0 + nw, d.G);
+    float v0[T], v1[T];
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        v0[t] = ld_co(a.ws.ypart + ((size_t)p0 * T + t) * d.H + row);
-        v1[t] = ld_co(a.ws.ypart + ((size_t)p1 * T + t) * d.H + row);
-      }
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        stage[(p0 * T + t) * 64 + lane] = v0[t];
-        if (p0 + nw <= d.G) stage[(p1 * T + t) * 64 + lane] = v1[t];
-      }
+    for (int t = 0; t < T; ++t) {
+      v0[t] = ld_co(a.ws.ypart + ((size_t)p0 * T + t) * d.H + row);
+      v1[t] = ld_co(a.ws.ypart + ((size_t)p1 * T + t) * d.H + row);
     }
-    __syncthreads();
-    if (wave == 0) {
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        float y = 0.f;
-        for (int g = 0; g < d.G; ++g)
-          if (gso[g + 1] > gso[g]) y += stage[(g * T + t) * 64 + lane];
-        y += stage[(d.G * T + t) * 64 + lane];
-        float* dst = a.y + (size_t)t * d.H + row;
-        *dst = a.accumulate ? *dst + y : y;
-      }
+    for (int t = 0; t < T; ++t) {
+      stage[(p0 * T + t) * 64 + lane] = v0[t];
+      if (p0 + nw <= d.G) stage[(p1 * T + t) * 64 + lane] = v1[t];
     }
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float y = 0.f;
+      for (int g = 0; g < d.G; ++g)
+        if (gso[g + 1] > gso[g]) y += stage[(g * T + t) * 64 + lane];
+      y += stage[(d.G * T + t) * 64 + lane];
+      float* dst = a.y + (size_t)t * d.H + row;
+      *dst = a.accumulate ? *dst + y : y;
+    }
+  }
+  __syncthreads();                                   // stage overlaps the wave staging areas
+}
+
+template <int T, int DU, int W>
+__global__ __launch_bounds__(64 * W) void k_phase4(P4 a) {
+  extern __shared__ __align__(16) char smem[];
+  __shared__ int flag;
+  const Dims& d = a.d;
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+  const int tiles = a.gu.tiles;                      // H / 64
+  char* xs = smem + wave * stage_bytes<T>();
+  if ((int)blockIdx.x >= a.nub) {
+    const int r = blockIdx.x - a.nub;                // shared down, row tile r
+    f4 acc[4];
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) acc[rg] = (f4){0.f, 0.f, 0.f, 0.f};
+    if (wave < a.gsd.nss) {
+      WRegs<kBF16, T> R;
+      phase4_issue<T, kBF16>(a, R, d.G, r, wave, lane);
+      wave_compute<kBF16, T>(R, ss_codes(kBF16, a.gsd, wave), T, xs, lane, acc);
+    }
+    phase4_finish<T>(a, d.G, r, true, acc, smem, &flag, [] {});
+    return;
+  }
+  ci_t gso = ci(a.ws.gslot_off);
+  const int nu = d.G * tiles;
+  const bool has_ss = wave < a.gu.nss;
+  const rsrc_t sr = rsrc(a.ws.s, (uint32_t)((size_t)T * d.G * d.L * sizeof(float)));
+  WRegs<DU, T> R;
+  int it = blockIdx.x;
+  if (it < nu && has_ss && gso[it / tiles + 1] > gso[it / tiles])
+    phase4_issue_u<T, DU>(a, R, sr, it / tiles, it % tiles, wave, lane);
+  for (; it < nu; it += a.nub) {
+    const int part = it / tiles, r = it % tiles;
+    const bool active = gso[part + 1] > gso[part];
+    f4 acc[4];
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) acc[rg] = (f4){0.f, 0.f, 0.f, 0.f};
+    if (active && has_ss) wave_compute<DU, T>(R, ss_codes(DU, a.gu, wave), T, xs, lane, acc);
+    __builtin_amdgcn_sched_barrier(0);               // the next loads reuse this item's registers
+    const int nx = it + a.nub;
+    const bool nx_load = nx < nu && has_ss && gso[nx / tiles + 1] > gso[nx / tiles];
+    // wave 0 issues its next loads after waiting for its stores; the other
+    // waves issue them now
+    if (wave != 0 && nx_load) phase4_issue_u<T, DU>(a, R, sr, nx / tiles, nx % tiles, wave, lane);
+    phase4_finish<T>(a, part, r, active, acc, smem, &flag, [&] {
+      if (nx_load) phase4_issue_u<T, DU>(a, R, sr, nx / tiles, nx % tiles, wave, lane);
+    });
   }
 }
 
@@ -968,6 +1138,20 @@ __global__ void k_rms(const float* __restrict__ x, int H, float eps, float* __re
   }
 }
 
+
+// Blocks of `kernel` the device holds at once with `threads` threads and
+// `lds` dynamic LDS bytes (the persistent phases launch that many).
+int resident_blocks(lmoe_t* h, const void* kernel, int threads, size_t lds) {
+  for (const auto& r : h->resident)
+    if (r.kernel == kernel && r.threads == threads && r.lds == lds) return r.blocks;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess)
+    return -1;
+  const int n = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+  h->resident.push_back({kernel, threads, lds, n});
+  return n;
+}
 
 template <int T, int DU>
 int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st) {
@@ -1014,8 +1198,11 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st) {
   p2.d = d; p2.experts = h->experts; p2.ggu = h->g_gu; p2.stride = h->expert_stride;
   p2.ts_off = h->ts_off; p2.labels = h->labels; p2.ws = ws;
   const int nw2 = h->g_gu.nss;
-  hipLaunchKernelGGL(k_phase2<T>, dim3(maxslots * h->g_gu.tiles), dim3(nw2 * 64),
-                     (size_t)nw2 * (stage_bytes<T>() + red_bytes_per_wave<T>()), st, p2);
+  const size_t sm2 = (size_t)nw2 * (stage_bytes<T>() + 2 * red_bytes_per_wave<T>());
+  const int items2 = maxslots * h->g_gu.tiles;
+  const int res2 = resident_blocks(h, (const void*)k_phase2<T>, nw2 * 64, sm2);
+  if (res2 <= 0) { set_error("phase 2: occupancy query failed"); return LMOE_EHIP; }
+  hipLaunchKernelGGL(k_phase2<T>, dim3(items2 < res2 ? items2 : res2), dim3(nw2 * 64), sm2, st, p2);
   LMOE_HIP(hipGetLastError());
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[2], st));
 
@@ -1037,10 +1224,20 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st) {
   size_t sm4 = (size_t)nw4 * (stage_bytes<T>() + red_bytes_per_wave<T>());
   const size_t sm4r = (size_t)(d.G + 1) * T * 64 * sizeof(float);
   sm4 = sm4 > sm4r ? sm4 : sm4r;
+  const void* k4 = nw4 <= 10 ? (const void*)k_phase4<T, DU, 10> : (const void*)k_phase4<T, DU, 16>;
+  const int res4 = resident_blocks(h, k4, nw4 * 64, sm4);
+  if (res4 <= 0) { set_error("phase 4: occupancy query failed"); return LMOE_EHIP; }
+  // one block per shared-down tile; the U blocks fill the rest of the
+  // device and stride over the U items
+  const int nu = d.G * h->g_u.tiles, ns = h->g_sdn.tiles;
+  int nub = res4 - ns;
+  nub = nub < 1 ? 1 : (nub > nu ? nu : nub);
+  const int grid4 = nub + ns;
+  p4.nub = nub;
   if (nw4 <= 10)
-    hipLaunchKernelGGL((k_phase4<T, DU, 10>), dim3((d.G + 1) * h->g_u.tiles), dim3(nw4 * 64), sm4, st, p4);
+    hipLaunchKernelGGL((k_phase4<T, DU, 10>), dim3(grid4), dim3(nw4 * 64), sm4, st, p4);
   else
-    hipLaunchKernelGGL((k_phase4<T, DU, 16>), dim3((d.G + 1) * h->g_u.tiles), dim3(nw4 * 64), sm4, st, p4);
+    hipLaunchKernelGGL((k_phase4<T, DU, 16>), dim3(grid4), dim3(nw4 * 64), sm4, st, p4);
   LMOE_HIP(hipGetLastError());
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[4], st));
   return 0;

@@ -176,6 +176,9 @@ struct lmoe {
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   std::vector<void*> allocations;
   std::vector<hipEvent_t> phase_events;   // empty: no phase timing
+  // blocks of a kernel resident at once, by (kernel, threads, LDS bytes)
+  struct Resident { const void* kernel; int threads; size_t lds; int blocks; };
+  std::vector<Resident> resident;
 };
 
 namespace lm {
