@@ -118,12 +118,11 @@ int create_impl(lmoe_t* h) {
   A(w.rms, sizeof(float) * T);
   A(w.xl, sizeof(float) * T * G * L);
   A(w.hs, sizeof(float) * T * Fs);
+  A(w.hsp, sizeof(float) * h->g_sgu.nss * T * 2 * Fs);
   A(w.hbuf, sizeof(float) * n * F);
-  A(w.obuf, sizeof(float) * n * L);
   A(w.s, sizeof(float) * T * G * L);
   A(w.ypart, sizeof(float) * (G + 1) * T * H);
   A(w.ctr_router, sizeof(unsigned));
-  A(w.ctr_s, sizeof(unsigned) * G * (L / 64));
   A(w.ctr_y, sizeof(unsigned) * (H / 64));
 
   // prefill path (T > kMaxDecodeT): router copies and GEMM workspace
@@ -170,7 +169,6 @@ int create_impl(lmoe_t* h) {
   }
 #undef A
   LMOE_HIP(hipMemset(w.ctr_router, 0, sizeof(unsigned)));
-  LMOE_HIP(hipMemset(w.ctr_s, 0, sizeof(unsigned) * G * (L / 64)));
   LMOE_HIP(hipMemset(w.ctr_y, 0, sizeof(unsigned) * (H / 64)));
   LMOE_HIP(hipDeviceSynchronize());
   return 0;

@@ -470,12 +470,15 @@ struct P1 {
   const uint8_t* dmat; Geom gd;
   const uint8_t* sgu; Geom gs;
   int nrb, nch, cw;        // router blocks, column chunks per tile, columns per chunk
-  int ndb;                 // D blocks
+  int ndb;                 // D tiles
+  int nsh;                 // shared gate/up (tile, super-step) tasks
   Workspace ws;
 };
 
 struct P2 {
   Dims d;
+  int nps;                 // shared gate/up partials (super-steps of H)
+  const float* rms;        // [T] or null
   const uint8_t* experts; Geom ggu; size_t stride, ts_off;
   const uint8_t* labels;
   Workspace ws;
@@ -483,6 +486,7 @@ struct P2 {
 
 struct P3 {
   Dims d;
+  int spr, wps;            // slots per round of a block, waves per slot
   const uint8_t* experts; Geom gdn; size_t stride, gu_bytes, ts_off;
   const uint8_t* labels;
   Workspace ws;
@@ -501,11 +505,13 @@ struct P4 {
 // ---------------------------------------------------------------------------
 // Routing, done by the last router block.
 
-// LDS of the routing block: logits [T][E] (fp64), then per assignment
-// key, sorted order, inverse, label and segment flags, per expert a counter,
-// per wave 64-entry scratch for the top-K candidates.
-__host__ __device__ constexpr size_t routing_lds_bytes(int T, int E, int n, int nw) {
-  return (size_t)T * E * 8 + (size_t)(6 * n + E + 8) * 4 + 8 + (size_t)nw * 64 * (8 + 8 + 4);
+// LDS of the routing block: logits [T][Epad] (fp64, -inf past E), per-wave
+// top-K scratch,
+// then per assignment (at least 64 entries) key, sorted order, inverse,
+// label and slot of each sorted position, expert and label; per expert a
+// counter and its group label; the slot count.
+__host__ __device__ constexpr size_t routing_lds_bytes(int T, int E, int Epad, int n, int nw) {
+  return (size_t)T * Epad * 8 + (size_t)nw * 3 * 64 * 8 + (size_t)(7 * (n > 64 ? n : 64) + 2 * E + 8) * 4;
 }
 
 template <int T>
@@ -516,26 +522,29 @@ __device__ void routing(const P1& a, char* smem) {
   const int nw = nth >> 6;
   const int Epad = a.gr.tiles * 64;
   const int n = T * d.K;
-  double* lg = (double*)smem;      // [T][E] logits
-  int* key = (int*)(lg + T * d.E); // [n] label * E + expert, assignment order
-  int* sperm = key + n;            // [n] sorted position -> assignment
-  int* inv = sperm + n;            // [n] assignment -> sorted position
-  int* slab = inv + n;             // [n] label at each sorted position
-  int* sid = slab + n;             // [n] slot of each sorted position
-  int* aexp = sid + n;             // [n] expert of each assignment
-  int* ecnt = aexp + n;            // [E] assignments per expert
-  int* nslot = ecnt + d.E;         // [1]
-  double* wv = (double*)(((uintptr_t)(nslot + 8) + 7) & ~(uintptr_t)7);   // [nw][64]
-  double* cv = wv + nw * 64;       // [nw][64]
-  int* ce = (int*)(cv + nw * 64);  // [nw][64]
+  const int na = n > 64 ? n : 64;  // assignment arrays, at least 64 entries
+  double* lg = (double*)smem;      // [T][Epad] logits, -inf past E
+  double* scr = lg + T * Epad;     // [nw][3][64] per-wave top-K scratch
+  int* key = (int*)(scr + nw * 3 * 64);  // [n] (label * E + expert) * 64 + assignment % 64
+  int* sperm = key + na;           // [n] sorted position -> assignment
+  int* inv = sperm + na;           // [n] assignment -> sorted position
+  int* slab = inv + na;            // [n] label at each sorted position
+  int* sid = slab + na;            // [n] slot of each sorted position
+  int* aexp = sid + na;            // [n] expert of each assignment
+  int* alab = aexp + na;           // [n] group label of each assignment
+  int* ecnt = alab + na;           // [E] assignments per expert
+  int* elab = ecnt + d.E;          // [E] group label of each expert
+  int* nslot = elab + d.E;         // [1]
 
   // logits = the chunk partials summed in chunk order (scaled by 1/rms in the
-  // block forward) + bias; every thread issues all its loads before summing
+  // block forward) + bias; the labels come in with the token-0 entries.
+  // Every thread issues all its loads before summing.
   {
     constexpr int U = 4;
     const int total = T * d.E;
     for (int base = 0; base < total; base += U * nth) {
       double part[U][kRouterChunks];
+      int lab[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = min(base + tid + u * nth, total - 1);
@@ -543,6 +552,7 @@ __device__ void routing(const P1& a, char* smem) {
 #pragma unroll
         for (int c = 0; c < kRouterChunks; ++c)
           part[u][c] = ld_co(ws.part64 + ((size_t)c * T + t) * Epad + e);
+        lab[u] = t == 0 ? (int)a.labels[e] : 0;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -553,83 +563,98 @@ __device__ void routing(const P1& a, char* smem) {
 #pragma unroll
           for (int c = 0; c < kRouterChunks; ++c) l += part[u][c];
           if (a.rms) l *= (double)a.rms[t];
-          lg[i] = l + (double)a.bias[e];
+          lg[t * Epad + e] = l + (double)a.bias[e];
+          if (t == 0) elab[e] = lab[u];
         }
       }
     }
+    for (int i = tid; i < T * (Epad - d.E); i += nth)
+      lg[(i / (Epad - d.E)) * Epad + d.E + i % (Epad - d.E)] = -INFINITY;
   }
   for (int e = tid; e < d.E; e += nth) ecnt[e] = 0;
   __syncthreads();
 
-  // Top K per token, one wavefront per token, exact. theta = the K-th largest
-  // of the 64 per-lane maxima is <= the K-th largest logit, so every logit
-  // >= theta is a candidate; each candidate's rank by (logit desc, expert
-  // asc) among the candidates equals its rank among all experts when it is
-  // in the top K, and is >= K otherwise. More than 64 candidates (heavy
-  // ties): rank among all experts instead.
+  // Top K per token, one wavefront per token, exact. Candidates: the logits
+  // whose fp32 rounding is >= theta32, the K-th largest fp32-rounded lane
+  // maximum. Rounding is monotone, so theta32 = fl(K-th largest lane max)
+  // <= fl(K-th largest logit) and every top-K logit is a candidate. The
+  // candidates are ranked exactly in fp64 by (logit desc, expert asc): a
+  // candidate's rank among them equals its rank among all experts when it is
+  // in the top K. More than 64 candidates (heavy ties): rank among all
+  // experts instead. A single wavefront runs this, so it is written for few
+  // instructions: unique 64-bit keys, loops over the candidates only.
   const unsigned long long lower = (1ull << lane) - 1ull;
   for (int t = wave; t < T; t += nw) {
-    const double* l = lg + t * d.E;
+    const double* l = lg + t * Epad;
+    const int per = Epad >> 6;
+    unsigned long long* wk = (unsigned long long*)(scr + wave * 3 * 64);  // lane-max keys
+    double* cv = scr + wave * 3 * 64 + 64;    // candidate values, then the picks
+    int* we = (int*)(cv + 64);                // candidate experts, then the picks
     double m = -INFINITY;
-    for (int e = lane; e < d.E; e += 64) m = fmax(m, l[e]);
-    wv[wave * 64 + lane] = m;
+#pragma unroll 8
+    for (int j = 0; j < per; ++j) {
+      const double x = l[j * 64 + lane];
+      m = x > m ? x : m;
+    }
+    const float m32 = (float)m;
+    const unsigned mb = __float_as_uint(m32);
+    const unsigned mo = (mb & 0x80000000u) ? ~mb : (mb | 0x80000000u);   // order-preserving
+    const unsigned long long mk = ((unsigned long long)mo << 6) | (unsigned)(63 - lane);
+    wk[lane] = mk;
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     int r = 0;
-    for (int j = 0; j < 64; ++j) {
-      const double vj = wv[wave * 64 + j];
-      r += (vj > m) || (vj == m && j < lane);
+#pragma unroll 8
+    for (int j = 0; j < 64; j += 2) {
+      const ulonglong2 p = *(const ulonglong2*)(wk + j);
+      r += (int)(p.x > mk) + (int)(p.y > mk);
     }
-    // rank K - 1 exists (K <= 64) and is unique: its value is theta
-    const unsigned long long at = __ballot(r == d.K - 1);
-    const double theta = __shfl(m, __builtin_ctzll(at));
-    int c = 0;
-    for (int e0 = 0; e0 < d.E; e0 += 64) {
-      const int e = e0 + lane;
-      c += __popcll(__ballot(e < d.E && l[e] >= theta));
+    // rank K - 1 exists (K <= 64) and is unique: its fp32 value is theta32
+    const float theta = __shfl(m32, __builtin_ctzll(__ballot(r == d.K - 1)));
+    int base = 0;
+#pragma unroll 4
+    for (int j = 0; j < per; ++j) {
+      const double x = l[j * 64 + lane];
+      const bool in = (float)x >= theta;
+      const unsigned long long bm = __ballot(in);
+      const int q = base + __popcll(bm & lower);
+      if (in && q < 64) {
+        cv[q] = x;
+        we[q] = j * 64 + lane;
+      }
+      base += __popcll(bm);
     }
-    int rank = 64;
-    double kv = -INFINITY;
+    const int c = base;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    double kv = 0.0;
     int ki = 0;
     if (c <= 64) {
-      int base = 0;
-      for (int e0 = 0; e0 < d.E; e0 += 64) {
-        const int e = e0 + lane;
-        const bool in = e < d.E && l[e] >= theta;
-        const unsigned long long mk = __ballot(in);
-        if (in) {
-          const int slot = base + __popcll(mk & lower);
-          cv[wave * 64 + slot] = l[e];
-          ce[wave * 64 + slot] = e;
-        }
-        base += __popcll(mk);
+      const double mv = lane < c ? cv[lane] : 0.0;
+      const int me = lane < c ? we[lane] : 0;
+      int rank = 0;
+#pragma unroll 4
+      for (int q = 0; q < c; ++q) {
+        const double x = cv[q];
+        rank += (int)((x > mv) | ((x == mv) & (we[q] < me)));
       }
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      if (lane < c) {
-        kv = cv[wave * 64 + lane];
-        ki = ce[wave * 64 + lane];
-        rank = 0;
-        for (int j = 0; j < c; ++j) {
-          const double vj = cv[wave * 64 + j];
-          rank += (vj > kv) || (vj == kv && ce[wave * 64 + j] < ki);
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-      if (rank < d.K) {
-        cv[wave * 64 + rank] = kv;
-        ce[wave * 64 + rank] = ki;
+      if (lane < c && rank < d.K) {
+        cv[rank] = mv;
+        we[rank] = me;
       }
     } else {
+      __builtin_amdgcn_wave_barrier();
       for (int e0 = 0; e0 < d.E; e0 += 64) {
         const int e = e0 + lane;
         if (e < d.E) {
-          const double v = l[e];
+          const double x = l[e];
           int rk = 0;
-          for (int j = 0; j < d.E; ++j) rk += (l[j] > v) || (l[j] == v && j < e);
+          for (int j = 0; j < d.E; ++j) rk += (int)((l[j] > x) | ((l[j] == x) & (j < e)));
           if (rk < d.K) {
-            cv[wave * 64 + rk] = v;
-            ce[wave * 64 + rk] = e;
+            cv[rk] = x;
+            we[rk] = e;
           }
         }
       }
@@ -637,45 +662,66 @@ __device__ void routing(const P1& a, char* smem) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     if (lane < d.K) {
-      kv = cv[wave * 64 + lane];
-      ki = ce[wave * 64 + lane];
+      kv = cv[lane];
+      ki = min(max(we[lane], 0), d.E - 1);   // in range even for NaN logits
     }
-    const double top = cv[wave * 64];
-    const double ex = lane < d.K ? exp(kv - top) : 0.0;
-    double z = ex;
-    for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
+    // softmax over the K picks: exp relative to the largest, the denominator
+    // summed in rank order
+    const double ex = lane < d.K ? exp(kv - cv[0]) : 0.0;
+    double* exs = (double*)wk;                // the lane-max keys are no longer needed
+    if (lane < d.K) exs[lane] = ex;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    double z = 0.0;
+    for (int k = 0; k < d.K; ++k) z += exs[k];
     if (lane < d.K) {
       const int i = t * d.K + lane;
+      const int g = elab[ki];
       ws.topk_idx[i] = ki;
       ws.topk_w[i] = (float)(ex / z);
-      key[i] = (int)a.labels[ki] * d.E + ki;
+      key[i] = (g * d.E + ki) * 64 + (i & 63);   // unique when n <= 64
+      alab[i] = g;
       aexp[i] = ki;
       atomicAdd(&ecnt[ki], 1);
     }
   }
   __syncthreads();
 
-  // stable rank of each assignment by key (label, expert)
-  for (int i = tid; i < n; i += nth) {
-    const int ki = key[i];
-    int r = 0;
-    for (int j = 0; j < n; ++j) {
-      const int kj = key[j];
-      r += (kj < ki) || (kj == ki && j < i);
+  // stable order of the assignments by (label, expert): for n <= 64 the keys
+  // are unique and an assignment's rank is the count of smaller keys; beyond,
+  // ties in (label, expert) are broken by assignment index
+  if (n <= 64) {
+    if (wave == 0 && lane < n) {
+      const int ki = key[lane];
+      int r = 0;
+#pragma unroll 8
+      for (int j = 0; j < n; ++j) r += (int)(key[j] < ki);
+      sperm[r] = lane;
+      inv[lane] = r;
+      ws.perm[r] = lane;
     }
-    sperm[r] = i;
-    inv[i] = r;
-    ws.perm[r] = i;
+  } else {
+    for (int i = tid; i < n; i += nth) {
+      const int ki = key[i] >> 6;
+      int r = 0;
+      for (int j = 0; j < n; ++j) {
+        const int kj = key[j] >> 6;
+        r += (int)((kj < ki) | ((kj == ki) & (j < i)));
+      }
+      sperm[r] = i;
+      inv[i] = r;
+      ws.perm[r] = i;
+    }
   }
   for (int e = tid; e < d.E; e += nth) ws.expert_count[e] = ecnt[e];
   __syncthreads();
-  for (int j = tid; j < n; j += nth) slab[j] = (int)a.labels[aexp[sperm[j]]];
+  for (int j = tid; j < n; j += nth) slab[j] = alab[sperm[j]];
   // slot of each sorted position: prefix count of segment starts, by wave 0
   if (wave == 0) {
     int run = 0;
     for (int j0 = 0; j0 < n; j0 += 64) {
       const int j = j0 + lane;
-      const bool st = j < n && (j == 0 || key[sperm[j]] != key[sperm[j - 1]]);
+      const bool st = j < n && (j == 0 || (key[sperm[j]] >> 6) != (key[sperm[j - 1]] >> 6));
       const unsigned long long mk = __ballot(st);
       if (j < n) sid[j] = run + __popcll(mk & lower) + (st ? 0 : -1);
       run += __popcll(mk);
@@ -714,13 +760,40 @@ __device__ void routing(const P1& a, char* smem) {
     const int t = q / d.G, g = q % d.G;
     int c = 0;
     for (int k = 0; k < d.K; ++k)
-      if ((int)a.labels[aexp[t * d.K + k]] == g) ws.tg_pos[q * d.K + c++] = inv[t * d.K + k];
+      if (alab[t * d.K + k] == g) ws.tg_pos[q * d.K + c++] = inv[t * d.K + k];
     ws.tg_cnt[q] = c;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Phase 1: router | D_g | shared gate/up, by block index range.
+// Shared expert gate/up, super-step ss of row tile r, by this wavefront
+// alone: the partial pre-activations go to hsp[ss]; the start of phase 2
+// adds them in super-step order and applies SwiGLU.
+
+template <int T>
+__device__ __forceinline__ void shared_gu_part(const P1& a, int r, int ss, char* xs, int lane) {
+  const Dims& d = a.d;
+  f4 acc[4];
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg) acc[rg] = (f4){0.f, 0.f, 0.f, 0.f};
+  const float* src[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) src[t] = a.x + (size_t)t * d.H + ss * kSSCols;
+  wave_ss<kBF16, T>(ss_ptr(a.sgu, a.gs, r, ss), ss_codes(kBF16, a.gs, ss), ss_cols(a.gs, ss), src, T,
+                    xs, lane, acc);
+  float* out = a.ws.hsp + (size_t)ss * T * 2 * d.Fs;
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int t = 4 * (lane >> 4) + v;
+      if (t < T) out[(size_t)t * 2 * d.Fs + r * 64 + rg * 16 + (lane & 15)] = acc[rg][v];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Phase 1: router | D_g (and on the first D blocks one shared gate/up
+// super-step each), by block index range.
 
 // W: most waves a block of this launch has (the register budget follows it)
 template <int T, int DU, int W>
@@ -767,9 +840,9 @@ __global__ __launch_bounds__(64 * W) void k_phase1(P1 a) {
 #pragma unroll
   for (int t = 0; t < T; ++t) src[t] = a.x + (size_t)t * d.H + wave * kSSCols;
 
-  if (b < a.nrb + a.ndb) {
-    // D_g, tile r; wave = super-step
-    const int i = b - a.nrb;
+  // D_g, tile r; wave = super-step
+  const int i = b - a.nrb;
+  if (i < a.ndb) {
     const int g = i / a.gd.tiles, r = i % a.gd.tiles;
     if (wave < a.gd.nss)
       wave_ss<DU, T>(ss_ptr(a.dmat + (size_t)g * a.gd.bytes(), a.gd, r, wave),
@@ -787,30 +860,12 @@ __global__ __launch_bounds__(64 * W) void k_phase1(P1 a) {
           }
         }
     }
-    return;
   }
-  // shared gate/up: row groups 0,1 hold gate rows, 2,3 the matching up rows
-  const int r = b - a.nrb - a.ndb;
-  if (wave < a.gs.nss)
-    wave_ss<kBF16, T>(ss_ptr(a.sgu, a.gs, r, wave), ss_codes(kBF16, a.gs, wave),
-                      ss_cols(a.gs, wave), src, T, xs, lane, acc);
-  if (block_reduce_mf<T>(acc, red, wave, lane, nw)) {
-#pragma unroll
-    for (int rg = 0; rg < 2; ++rg)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int t = 4 * (lane >> 4) + v;
-        const int f = r * 32 + rg * 16 + (lane & 15);
-        if (t < T && f < d.Fs) {
-          float gv = acc[rg][v], uv = acc[rg + 2][v];
-          if (a.rms) {
-            gv *= a.rms[t];
-            uv *= a.rms[t];
-          }
-          a.ws.hs[(size_t)t * d.Fs + f] = silu(gv) * uv;
-        }
-      }
-  }
+  // Then one wavefront of each of the first nsh of these blocks computes one
+  // super-step of one shared gate/up tile: the D blocks end well before the
+  // routing block, and spreading the shared weights over them keeps every
+  // CU's share of the stream even.
+  if (i < a.nsh && wave == i % nw) shared_gu_part<T>(a, i / a.gs.nss, i % a.gs.nss, xs, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -883,83 +938,139 @@ __global__ __launch_bounds__(1024) void k_phase2(P2 a) {
         }
     }
   }
+  // shared expert: hs[t][f] = silu(g) * u from the phase-1 partials, summed
+  // in super-step order (gate row f % 32 of tile f / 32 at tile row f % 32,
+  // the up row 32 rows below). Done by the blocks that had one item fewer
+  // (all blocks when the items divide evenly), after their items.
+  {
+    const int rem = nvalid % (int)gridDim.x;
+    const int nc = rem > 0 ? (int)gridDim.x - rem : (int)gridDim.x;
+    const int cb = (int)blockIdx.x - (rem > 0 ? rem : 0);
+    const int nps = a.nps, Fs2 = 2 * d.Fs;
+    if (cb >= 0) {
+      for (int v = cb + nc * (int)threadIdx.x; v < T * d.Fs; v += nc * (int)blockDim.x) {
+        const int t = v / d.Fs, f = v % d.Fs;
+        const int row = (f >> 5) * 64 + (f & 31);
+        const float* p = a.ws.hsp + (size_t)t * Fs2 + row;
+        float gv = 0.f, uv = 0.f;
+        for (int k0 = 0; k0 < nps; k0 += 8) {
+          float gp[8], up[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            gp[k] = k0 + k < nps ? p[(size_t)(k0 + k) * T * Fs2] : 0.f;
+            up[k] = k0 + k < nps ? p[(size_t)(k0 + k) * T * Fs2 + 32] : 0.f;
+          }
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            gv += gp[k];
+            uv += up[k];
+          }
+        }
+        if (a.rms) {
+          gv *= a.rms[t];
+          uv *= a.rms[t];
+        }
+        a.ws.hs[v] = silu(gv) * uv;
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Phase 3: routed-expert down, scaled by the routing weight; per-group sums.
+// Phase 3: routed-expert down, scaled by the routing weight, and the
+// per-group sums s[t][g] = sum over token t's experts in group g, ascending k.
+//
+// One block per (group g, row tile r of ell). The group's slots are
+// contiguous in slot order and their assignments occupy one contiguous run
+// of sorted positions [P0, P1), so the block keeps every weighted expert
+// output of the group for its 64 rows in LDS and adds them per token there:
+// no partials leave the block. A round runs spr slots with wps waves per
+// slot; wave w of a slot takes super-steps w, w + wps, ... of the ffn width
+// into one accumulator, and the slot's wave partials are added in w order
+// (wps = nss, one super-step per wave, unless the LDS is short).
+
+constexpr size_t kLdsBytes = 160 * 1024;   // LDS of one CU
+
+// LDS of the fp16-staged kernels: hi and lo parts only.
+template <int NT>
+constexpr int stage_bytes_f16() { return 2 * NT * kXStr * 2; }
 
 template <int T>
 __global__ __launch_bounds__(1024) void k_phase3(P3 a) {
   extern __shared__ __align__(16) char smem[];
-  __shared__ int flag;
   const Dims& d = a.d;
-  const int tiles = a.gdn.tiles;
-  const int j = blockIdx.x / tiles, r = blockIdx.x % tiles;
-  ci_t ns = ci(a.ws.n_slots);
-  if (j >= ns[0]) return;
+  const int tiles = a.gdn.tiles;                     // ell / 64
+  const int g = blockIdx.x / tiles, r = blockIdx.x % tiles;
+  ci_t gso = ci(a.ws.gslot_off);
+  const int j0 = gso[g], ng = gso[g + 1] - j0;
+  if (ng == 0) return;                               // group unused: phase 4 skips it
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6), nw = blockDim.x >> 6;
-  const int e = ci(a.ws.slot_expert)[j], start = ci(a.ws.slot_start)[j];
-  const int cnt = ci(a.ws.slot_count)[j];
-  const int g = ((cu8_t)a.labels)[e];
-  const uint8_t* base = a.experts + (size_t)e * a.stride;
-  const float* src[T];
+  const int nss = a.gdn.nss, spr = a.spr, wps = a.wps;
+  ci_t sstart = ci(a.ws.slot_start);
+  ci_t scount = ci(a.ws.slot_count);
+  ci_t sexp = ci(a.ws.slot_expert);
+  ci_t perm = ci(a.ws.perm);
+  const int P0 = sstart[j0];
+  char* xs = smem + wave * stage_bytes_f16<T>();     // staging, then this wave's partial
+  float* ol = (float*)(smem + nw * stage_bytes_f16<T>());   // [P1 - P0][64]
+  constexpr int LN = 16 * ((T + 3) / 4);             // lanes holding tokens < T
+  const rsrc_t hr = rsrc(a.ws.hbuf, (uint32_t)((size_t)T * d.K * d.F * sizeof(float)));
+  const int u_in = wave / wps, sw = wave % wps;
+  for (int u0 = 0; u0 < ng; u0 += spr) {
+    const int u = u0 + u_in;
+    const bool valid = u_in < spr && u < ng;
+    const int j = j0 + (valid ? u : 0);
+    const int start = sstart[j], cnt = scount[j];
+    f4 acc[4];
 #pragma unroll
-  for (int i = 0; i < T; ++i) src[i] = a.ws.hbuf + (size_t)(start + (i < cnt ? i : 0)) * d.F + wave * kSSCols;
-  f4 acc[4];
+    for (int rg = 0; rg < 4; ++rg) acc[rg] = (f4){0.f, 0.f, 0.f, 0.f};
+    if (valid) {
+      const uint8_t* base = a.experts + (size_t)sexp[j] * a.stride + a.gu_bytes;
+      for (int ss = sw; ss < nss; ss += wps) {
+        int xoff[T];
 #pragma unroll
-  for (int rg = 0; rg < 4; ++rg) acc[rg] = (f4){0.f, 0.f, 0.f, 0.f};
-  char* xs = smem + wave * stage_bytes<T>();
-  f4* red = (f4*)(smem + nw * stage_bytes<T>());
-  if (wave < a.gdn.nss)
-    wave_ss<kFP4, T>(ss_ptr(base + a.gu_bytes, a.gdn, r, wave), ss_codes(kFP4, a.gdn, wave),
-                     ss_cols(a.gdn, wave), src, cnt, xs, lane, acc);
-  if (block_reduce_mf<T>(acc, red, wave, lane, nw)) {
-    cf_t ts = cf((const float*)(base + a.ts_off));
-    ci_t perm = ci(a.ws.perm);
+        for (int i = 0; i < T; ++i)
+          xoff[i] = (int)(((size_t)(start + (i < cnt ? i : 0)) * d.F + ss * kSSCols) * sizeof(float));
+        const int ncs = ss_codes(kFP4, a.gdn, ss);
+        WRegs<kFP4, T> R;
+        wave_load_b<kFP4, T>(R, rsrc(ss_ptr(base, a.gdn, r, ss), (ncs + scale_slots(kFP4)) * kSlot),
+                             ncs, hr, xoff, cnt, ss_cols(a.gdn, ss), lane);
+        wave_compute<kFP4, T>(R, ncs, cnt, xs, lane, acc);
+      }
+    }
+    f4* red = (f4*)xs;                               // this wave's staging is free again
+    if (valid && lane < LN) {
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg)
+      for (int rg = 0; rg < 4; ++rg) red[rg * LN + lane] = acc[rg];
+    }
+    __syncthreads();
+    if (valid && sw == 0 && lane < LN) {
+      cf_t ts = cf((const float*)(a.experts + (size_t)sexp[j] * a.stride + a.ts_off));
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int i = 4 * (lane >> 4) + v;
-        if (i < cnt) {
-          const float w = a.ws.topk_w[perm[start + i]];
-          st_co(a.ws.obuf + (size_t)(start + i) * d.L + r * 64 + rg * 16 + (lane & 15),
-                acc[rg][v] * ts[2] * w);
+      for (int rg = 0; rg < 4; ++rg) {
+        f4 v = acc[rg];
+        for (int k = 1; k < wps; ++k) v += ((const f4*)(smem + (wave + k) * stage_bytes_f16<T>()))[rg * LN + lane];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = 4 * (lane >> 4) + q;
+          if (i < cnt) {
+            const float w = a.ws.topk_w[perm[start + i]];
+            ol[(start + i - P0) * 64 + rg * 16 + (lane & 15)] = v[q] * ts[2] * w;
+          }
         }
       }
+    }
+    __syncthreads();
   }
-  ci_t gso = ci(a.ws.gslot_off);
-  const unsigned expect = (unsigned)(gso[g + 1] - gso[g]);
-  if (!arrive_last(a.ws.ctr_s + (size_t)g * tiles + r, expect, &flag)) return;
-  // s[t][g][row] = sum over k ascending of o for token t's experts in group g;
-  // every load is issued before the sums (positions past a list's end are
-  // replaced by a valid one and their values dropped)
-  if (wave == 0) {
-    const int row = r * 64 + lane;
-    ci_t cnt_tab = ci(a.ws.tg_cnt);
-    ci_t pos_tab = ci(a.ws.tg_pos);
-    constexpr int M = 8;
-    float v[T][M];
-    int c[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const int q = t * d.G + g;
-      c[t] = cnt_tab[q];
-#pragma unroll
-      for (int i = 0; i < M; ++i) {
-        const int pos = (i < c[t]) ? pos_tab[q * d.K + min(i, d.K - 1)] : 0;
-        v[t][i] = ld_co(a.ws.obuf + (size_t)pos * d.L + row);
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const int q = t * d.G + g;
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < M; ++i) s += i < c[t] ? v[t][i] : 0.f;
-      for (int i = M; i < c[t]; ++i) s += ld_co(a.ws.obuf + (size_t)pos_tab[q * d.K + i] * d.L + row);
-      a.ws.s[((size_t)q) * d.L + row] = s;
-    }
+  // s[t][g][row] for every token (0 where token t has no expert in g)
+  ci_t cnt_tab = ci(a.ws.tg_cnt);
+  ci_t pos_tab = ci(a.ws.tg_pos);
+  for (int t = wave; t < T; t += nw) {
+    const int q = t * d.G + g;
+    const int c = cnt_tab[q];
+    float v = 0.f;
+    for (int i = 0; i < c; ++i) v += ol[(pos_tab[q * d.K + i] - P0) * 64 + lane];
+    a.ws.s[(size_t)q * d.L + r * 64 + lane] = v;
   }
 }
 
@@ -1178,11 +1289,12 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st) {
   p1.nrb = h->g_router.tiles * p1.nch;
   p1.ndb = d.G * h->g_d.tiles;
   p1.ws = ws;
-  const int nb1 = p1.nrb + p1.ndb + h->g_sgu.tiles;
+  p1.nsh = h->g_sgu.tiles * h->g_sgu.nss;
+  const int nb1 = p1.nrb + (p1.ndb > p1.nsh ? p1.ndb : p1.nsh);
   const int n = T * d.K;
   size_t sm1 = (size_t)nw1 * (stage_bytes<T>() + red_bytes_per_wave<T>());
   const size_t sm_router = (size_t)nw1 * T * 64 * sizeof(double);
-  const size_t sm_routing = routing_lds_bytes(T, d.E, n, nw1);
+  const size_t sm_routing = routing_lds_bytes(T, d.E, h->g_router.tiles * 64, n, nw1);
   sm1 = sm1 > sm_router ? sm1 : sm_router;
   sm1 = sm1 > sm_routing ? sm1 : sm_routing;
   if (nw1 <= 10)
@@ -1197,6 +1309,7 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st) {
   P2 p2{};
   p2.d = d; p2.experts = h->experts; p2.ggu = h->g_gu; p2.stride = h->expert_stride;
   p2.ts_off = h->ts_off; p2.labels = h->labels; p2.ws = ws;
+  p2.nps = h->g_sgu.nss; p2.rms = norm ? ws.rms : nullptr;
   const int nw2 = h->g_gu.nss;
   const size_t sm2 = (size_t)nw2 * (stage_bytes<T>() + 2 * red_bytes_per_wave<T>());
   const int items2 = maxslots * h->g_gu.tiles;
@@ -1210,9 +1323,23 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st) {
   P3 p3{};
   p3.d = d; p3.experts = h->experts; p3.gdn = h->g_dn; p3.stride = h->expert_stride;
   p3.gu_bytes = h->g_gu.bytes(); p3.ts_off = h->ts_off; p3.labels = h->labels; p3.ws = ws;
-  const int nw3 = h->g_dn.nss;
-  hipLaunchKernelGGL(k_phase3<T>, dim3(maxslots * h->g_dn.tiles), dim3(nw3 * 64),
-                     (size_t)nw3 * (stage_bytes<T>() + red_bytes_per_wave<T>()), st, p3);
+  // as many slots per round as 16 waves and the LDS hold; a wave per
+  // super-step unless even one slot's waves do not fit
+  const int nss3 = h->g_dn.nss;
+  const size_t ol_bytes = (size_t)n * 64 * sizeof(float);
+  auto lds3 = [&](int spr_, int wps_) { return (size_t)spr_ * wps_ * stage_bytes_f16<T>() + ol_bytes; };
+  int spr = 16 / nss3, wps = nss3;
+  while (spr > 1 && lds3(spr, wps) > kLdsBytes) --spr;
+  while (wps > 1 && lds3(spr, wps) > kLdsBytes) --wps;
+  if (lds3(spr, wps) > kLdsBytes) {
+    set_error("decode phase 3: T * top_k too large for the LDS");
+    return LMOE_EUNSUPPORTED;
+  }
+  p3.spr = spr;
+  p3.wps = wps;
+  const int nw3 = spr * wps;
+  hipLaunchKernelGGL(k_phase3<T>, dim3(d.G * h->g_dn.tiles), dim3(nw3 * 64),
+                     (size_t)nw3 * stage_bytes_f16<T>() + ol_bytes, st, p3);
   LMOE_HIP(hipGetLastError());
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[3], st));
 

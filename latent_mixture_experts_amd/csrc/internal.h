@@ -104,12 +104,11 @@ struct Workspace {
   float* rms = nullptr;          // [T] 1/rms of the input rows (block forward)
   float* xl = nullptr;           // [T][G][ell]
   float* hs = nullptr;           // [T][Fs] shared-expert hidden
+  float* hsp = nullptr;          // [H/256][T][2 Fs] shared gate/up partials per super-step
   float* hbuf = nullptr;         // [T*K][F] expert hidden, sorted position order
-  float* obuf = nullptr;         // [T*K][ell] weighted expert outputs
   float* s = nullptr;            // [T][G][ell] per-group sums
   float* ypart = nullptr;        // [G+1][T][H]
   unsigned* ctr_router = nullptr;  // [1]
-  unsigned* ctr_s = nullptr;       // [G][ell/64]
   unsigned* ctr_y = nullptr;       // [H/64]
   int nch = 0;                   // router column chunks
   int tmax = 0;                  // tokens the decode buffers hold
