@@ -121,7 +121,7 @@ int create_impl(lmoe_t* h) {
   A(w.hsp, sizeof(float) * h->g_sgu.nss * T * 2 * Fs);
   A(w.hbuf, sizeof(float) * n * F);
   A(w.s, sizeof(float) * T * G * L);
-  A(w.ypart, sizeof(float) * (G + 1) * T * H);
+  A(w.ypart, sizeof(float) * (2 * G + (Fs + 127) / 128) * T * H);   // 2G + shared-down blocks (at most one per half-step)
   A(w.ctr_router, sizeof(unsigned));
   A(w.ctr_y, sizeof(unsigned) * (H / 64));
 

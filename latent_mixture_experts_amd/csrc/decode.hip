@@ -214,10 +214,14 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
 //
 // xs: this wave's staging area; src[i]: vector i at the super-step's first
 // column; n: valid vectors; ncs: code slots present.
-template <int FMT, int NT>
+__host__ __device__ constexpr int cc_of(int fmt) { return fmt == kQ8 ? 64 : (fmt == kBF16 ? 32 : 128); }
+
+// SL: code slots the registers hold (a full super-step by default; fewer
+// for waves that take only the first columns of one).
+template <int FMT, int NT, int SL = 4 * (kSSCols / cc_of(FMT))>
 struct WRegs {
-  static constexpr int CC = FMT == kQ8 ? 64 : (FMT == kBF16 ? 32 : 128);   // columns per chunk
-  static constexpr int NSL = 4 * (kSSCols / CC);
+  static constexpr int CC = cc_of(FMT);   // columns per chunk
+  static constexpr int NSL = SL;
   XRegs<NT> xr;
   uint4 sc[4];
   uint4 q[NSL];
@@ -226,8 +230,8 @@ struct WRegs {
 // Issues the loads of one super-step: activations first, then scales, then
 // the weight stream (loads are counted in order, so the staging waits only
 // for its own data).
-template <int FMT, int NT>
-__device__ __forceinline__ void wave_load(WRegs<FMT, NT>& R, const uint8_t* p, int ncs, int cols,
+template <int FMT, int NT, int SL>
+__device__ __forceinline__ void wave_load(WRegs<FMT, NT, SL>& R, const uint8_t* p, int ncs, int cols,
                                           const float* const (&src)[NT], int n, int lane) {
   const int tok = lane & 15;
   x_load<NT>(R.xr, src, n, cols, lane);
@@ -236,7 +240,7 @@ __device__ __forceinline__ void wave_load(WRegs<FMT, NT>& R, const uint8_t* p, i
     for (int rg = 0; rg < 4; ++rg) R.sc[rg] = ldw(p + ncs * kSlot + (rg * 16 + tok) * 16);
   }
 #pragma unroll
-  for (int j = 0; j < WRegs<FMT, NT>::NSL; ++j)
+  for (int j = 0; j < SL; ++j)
     if (j < ncs) R.q[j] = ldnt(p + j * kSlot + lane * 16);
 }
 
@@ -245,8 +249,8 @@ __device__ __forceinline__ void wave_load(WRegs<FMT, NT>& R, const uint8_t* p, i
 // vector i of the activations at byte offset xoff[i] of resource x. All
 // per-lane addresses are the one lane offset, which stays in a register
 // across items instead of one 64-bit address per load.
-template <int FMT, int NT>
-__device__ __forceinline__ void wave_load_b(WRegs<FMT, NT>& R, rsrc_t w, int ncs, rsrc_t x,
+template <int FMT, int NT, int SL>
+__device__ __forceinline__ void wave_load_b(WRegs<FMT, NT, SL>& R, rsrc_t w, int ncs, rsrc_t x,
                                             const int (&xoff)[NT], int n, int cols, int lane) {
   const int tok = lane & 15;
 #pragma unroll
@@ -262,19 +266,19 @@ __device__ __forceinline__ void wave_load_b(WRegs<FMT, NT>& R, rsrc_t w, int ncs
     for (int rg = 0; rg < 4; ++rg) R.sc[rg] = ldb(w, 16 * tok, ncs * kSlot + rg * 256);
   }
 #pragma unroll
-  for (int j = 0; j < WRegs<FMT, NT>::NSL; ++j)
+  for (int j = 0; j < SL; ++j)
     if (j < ncs) R.q[j] = ldb<kAuxNT>(w, 16 * lane, j * kSlot);
 }
 
 // The MFMAs of a loaded super-step (xs: this wave's staging area).
-template <int FMT, int NT>
-__device__ __forceinline__ void wave_compute(const WRegs<FMT, NT>& R, int ncs, int n, void* xs,
+template <int FMT, int NT, int SL>
+__device__ __forceinline__ void wave_compute(const WRegs<FMT, NT, SL>& R, int ncs, int n, void* xs,
                                              int lane, f4 (&acc)[4]) {
-  constexpr int CC = WRegs<FMT, NT>::CC;
-  constexpr int MAXCH = kSSCols / CC;
+  constexpr int CC = WRegs<FMT, NT, SL>::CC;
+  constexpr int MAXCH = SL / 4;
   const int tok = lane & 15, qg = lane >> 4;
   const uint4 (&sc)[4] = R.sc;
-  const uint4 (&q)[WRegs<FMT, NT>::NSL] = R.q;
+  const uint4 (&q)[SL] = R.q;
   if (FMT == kBF16) x_stage_bf16<NT>(R.xr, (__bf16*)xs, lane);
   else x_stage_f16<NT>(R.xr, (_Float16*)xs, lane);
   __builtin_amdgcn_wave_barrier();
@@ -494,7 +498,8 @@ struct P3 {
 
 struct P4 {
   Dims d;
-  int nub;                 // blocks striding over the U items; the rest take the shared down
+  int hu;                  // super-steps of U's first half = waves of every block
+  int nsb;                 // shared-down blocks per row tile
   const uint8_t* umat; Geom gu;
   const uint8_t* sdn; Geom gsd;
   float* y;
@@ -1016,6 +1021,24 @@ __global__ __launch_bounds__(1024) void k_phase3(P3 a) {
   constexpr int LN = 16 * ((T + 3) / 4);             // lanes holding tokens < T
   const rsrc_t hr = rsrc(a.ws.hbuf, (uint32_t)((size_t)T * d.K * d.F * sizeof(float)));
   const int u_in = wave / wps, sw = wave % wps;
+  // This wave's tasks, in order: slot u0 + u_in of each round, its
+  // super-steps sw, sw + wps, ... The loads of the next task are issued as
+  // soon as the MFMAs of the current one have consumed its registers, so a
+  // second round does not wait a full load latency.
+  WRegs<kFP4, T> R;
+  auto issue = [&](int u, int ss) {
+    const int j = j0 + u;
+    const int start = sstart[j], cnt = scount[j];
+    int xoff[T];
+#pragma unroll
+    for (int i = 0; i < T; ++i)
+      xoff[i] = (int)(((size_t)(start + (i < cnt ? i : 0)) * d.F + ss * kSSCols) * sizeof(float));
+    const int ncs = ss_codes(kFP4, a.gdn, ss);
+    const uint8_t* base = a.experts + (size_t)sexp[j] * a.stride + a.gu_bytes;
+    wave_load_b<kFP4, T>(R, rsrc(ss_ptr(base, a.gdn, r, ss), (ncs + scale_slots(kFP4)) * kSlot),
+                         ncs, hr, xoff, cnt, ss_cols(a.gdn, ss), lane);
+  };
+  if (u_in < spr && u_in < ng) issue(u_in, sw);
   for (int u0 = 0; u0 < ng; u0 += spr) {
     const int u = u0 + u_in;
     const bool valid = u_in < spr && u < ng;
@@ -1025,17 +1048,11 @@ __global__ __launch_bounds__(1024) void k_phase3(P3 a) {
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) acc[rg] = (f4){0.f, 0.f, 0.f, 0.f};
     if (valid) {
-      const uint8_t* base = a.experts + (size_t)sexp[j] * a.stride + a.gu_bytes;
       for (int ss = sw; ss < nss; ss += wps) {
-        int xoff[T];
-#pragma unroll
-        for (int i = 0; i < T; ++i)
-          xoff[i] = (int)(((size_t)(start + (i < cnt ? i : 0)) * d.F + ss * kSSCols) * sizeof(float));
-        const int ncs = ss_codes(kFP4, a.gdn, ss);
-        WRegs<kFP4, T> R;
-        wave_load_b<kFP4, T>(R, rsrc(ss_ptr(base, a.gdn, r, ss), (ncs + scale_slots(kFP4)) * kSlot),
-                             ncs, hr, xoff, cnt, ss_cols(a.gdn, ss), lane);
-        wave_compute<kFP4, T>(R, ncs, cnt, xs, lane, acc);
+        wave_compute<kFP4, T>(R, ss_codes(kFP4, a.gdn, ss), cnt, xs, lane, acc);
+        __builtin_amdgcn_sched_barrier(0);   // the next loads reuse these registers
+        if (ss + wps < nss) issue(u, ss + wps);
+        else if (u + spr < ng) issue(u + spr, sw);
       }
     }
     f4* red = (f4*)xs;                               // this wave's staging is free again
@@ -1076,55 +1093,71 @@ __global__ __launch_bounds__(1024) void k_phase3(P3 a) {
 
 // ---------------------------------------------------------------------------
 // Phase 4: U_g per used group and the shared down; ordered sum per row tile.
-// Item it = part * tiles + r (part < G: U_part, part == G: shared down). The
-// last of the G + 1 items of row tile r to finish adds the partials in part
-// order. Blocks [0, nub) stride over the U items, prefetching the next
-// item's weights; each of the others takes one shared-down tile (a bf16
-// super-step fills 128 VGPRs, which a loop could not carry without spills).
+//
+// U_g's ell columns are split into two halves of super-steps, so an item is
+// (group g, half h, row tile r) or (shared down block k, row tile r): small
+// blocks, several per CU, so that every item's loads are in flight in one
+// round. Item (g, h) writes partial 2g + h of row tile r, shared down block
+// k partial 2G + k; the last of a row tile's items to finish adds the
+// partials in that order.
 
-template <int T, int FMT>
-__device__ __forceinline__ void phase4_issue(const P4& a, WRegs<FMT, T>& R, int part, int r,
-                                             int wave, int lane) {
-  constexpr bool kU = FMT != kBF16;
-  const Dims& d = a.d;
-  const Geom& geo = kU ? a.gu : a.gsd;
-  const float* src[T];
-#pragma unroll
-  for (int t = 0; t < T; ++t)
-    src[t] = kU ? a.ws.s + ((size_t)t * d.G + part) * d.L + wave * kSSCols
-                : a.ws.hs + (size_t)t * d.Fs + wave * kSSCols;
-  const uint8_t* base = kU ? a.umat + (size_t)part * a.gu.bytes() : a.sdn;
-  wave_load<FMT, T>(R, ss_ptr(base, geo, r, wave), ss_codes(FMT, geo, wave), ss_cols(geo, wave),
-                    src, T, lane);
-}
-
-// The U loop's loads: s [T][G][L] fp32 through one resource.
-template <int T, int DU>
-__device__ __forceinline__ void phase4_issue_u(const P4& a, WRegs<DU, T>& R, rsrc_t sr, int part,
-                                               int r, int wave, int lane) {
-  const Dims& d = a.d;
-  int xoff[T];
-#pragma unroll
-  for (int t = 0; t < T; ++t) xoff[t] = (int)(((t * d.G + part) * d.L + wave * kSSCols) * sizeof(float));
-  const int ncs = ss_codes(DU, a.gu, wave);
-  const uint8_t* p = ss_ptr(a.umat + (size_t)part * a.gu.bytes(), a.gu, r, wave);
-  wave_load_b<DU, T>(R, rsrc(p, (ncs + scale_slots(DU)) * kSlot), ncs, sr, xoff, T,
-                     ss_cols(a.gu, wave), lane);
-}
-
-// Writes the block's partial of (part, r) (if `active`), arrives at row
-// tile r's counter and, in the last block to arrive, writes y's tile.
-// `after_wait` runs on wave 0 once its stores have completed.
-template <int T, typename F>
-__device__ __forceinline__ void phase4_finish(const P4& a, int part, int r, bool active,
-                                              f4 (&acc)[4], char* smem, int* flag, F&& after_wait) {
+template <int T, int DU, int W>
+__global__ __launch_bounds__(64 * W) void k_phase4(P4 a) {
+  extern __shared__ __align__(16) char smem[];
+  __shared__ int flag;
   const Dims& d = a.d;
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6), nw = blockDim.x >> 6;
+  const int tiles = a.gu.tiles;                      // H / 64
+  const int nu = 2 * d.G * tiles;
+  const int b = blockIdx.x;
   ci_t gso = ci(a.ws.gslot_off);
+  char* xs = smem + wave * stage_bytes<T>();
   f4* red = (f4*)(smem + nw * stage_bytes<T>());
-  // Both branches pass one barrier, which also orders this item's write of
-  // *flag after every wave's read of the previous item's.
-  if (!active) __syncthreads();
+  f4 acc[4];
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg) acc[rg] = (f4){0.f, 0.f, 0.f, 0.f};
+  int part, r;
+  bool active;
+  if (b < nu) {
+    const int gh = b / tiles, g = gh >> 1, h = gh & 1;
+    r = b % tiles;
+    part = gh;
+    active = gso[g + 1] > gso[g];
+    const int ss = h * a.hu + wave;
+    if (active && wave < a.hu && ss < a.gu.nss) {
+      int xoff[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) xoff[t] = (int)(((t * d.G + g) * d.L + ss * kSSCols) * sizeof(float));
+      const int ncs = ss_codes(DU, a.gu, ss);
+      const uint8_t* p = ss_ptr(a.umat + (size_t)g * a.gu.bytes(), a.gu, r, ss);
+      WRegs<DU, T> R;
+      wave_load_b<DU, T>(R, rsrc(p, (ncs + scale_slots(DU)) * kSlot), ncs,
+                         rsrc(a.ws.s, (uint32_t)((size_t)T * d.G * d.L * sizeof(float))), xoff, T,
+                         ss_cols(a.gu, ss), lane);
+      wave_compute<DU, T>(R, ncs, T, xs, lane, acc);
+    }
+  } else {
+    // shared down, block k of row tile r: wave w takes half-step
+    // k * nw + w, i.e. half hs % 2 (128 columns, 16 code slots) of
+    // super-step hs / 2, which keeps a bf16 wave's weights at 64 VGPRs
+    const int k = (b - nu) / tiles;
+    r = (b - nu) % tiles;
+    part = 2 * d.G + k;
+    active = true;
+    const int hs = k * nw + wave;
+    const int ss = hs >> 1, hf = hs & 1;
+    const int cols = ss < a.gsd.nss ? min(128, ss_cols(a.gsd, ss) - 128 * hf) : 0;
+    if (cols > 0) {
+      const float* src[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) src[t] = a.ws.hs + (size_t)t * d.Fs + ss * kSSCols + 128 * hf;
+      const int ncs = ss_code_slots(kBF16, cols);
+      WRegs<kBF16, T, 16> R;
+      wave_load<kBF16, T>(R, ss_ptr(a.sdn, a.gsd, r, ss) + (size_t)16 * hf * kSlot, ncs, cols, src, T,
+                          lane);
+      wave_compute<kBF16, T>(R, ncs, T, xs, lane, acc);
+    }
+  }
   if (active && block_reduce_mf<T>(acc, red, wave, lane, nw)) {
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg)
@@ -1135,27 +1168,14 @@ __device__ __forceinline__ void phase4_finish(const P4& a, int part, int r, bool
           st_co(a.ws.ypart + ((size_t)part * T + t) * d.H + r * 64 + rg * 16 + (lane & 15), acc[rg][v]);
       }
   }
-  if (wave == 0) {
-    // only wave 0 stored: it alone waits for its stores before the arrival
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    if (lane == 0) {
-      unsigned* ctr = a.ws.ctr_y + r;
-      const unsigned old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const bool last = old + 1 == (unsigned)(d.G + 1);
-      *flag = last;
-      if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    after_wait();
-  }
-  __syncthreads();
-  if (*flag == 0) return;
-  // Ordered sum of the G + 1 partials: wave w fetches parts w, w + nw, ...
-  // (all loads in flight together), wave 0 adds them in part order.
+  const int np = 2 * d.G + a.nsb;
+  if (!arrive_last(a.ws.ctr_y + r, (unsigned)np, &flag)) return;
+  // Ordered sum of the partials: wave w fetches parts w, w + nw, ... (all
+  // loads in flight together), wave 0 adds them in part order.
   const int row = r * 64 + lane;
-  float* stage = (float*)smem;                       // [G + 1][T][64]
-  for (int p0 = wave; p0 <= d.G; p0 += 2 * nw) {
-    const int p1 = min(p0 + nw, d.G);
+  float* stage = (float*)smem;                       // [np][T][64]
+  for (int p0 = wave; p0 < np; p0 += 2 * nw) {
+    const int p1 = min(p0 + nw, np - 1);
     float v0[T], v1[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -1165,7 +1185,7 @@ __device__ __forceinline__ void phase4_finish(const P4& a, int part, int r, bool
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       stage[(p0 * T + t) * 64 + lane] = v0[t];
-      if (p0 + nw <= d.G) stage[(p1 * T + t) * 64 + lane] = v1[t];
+      if (p0 + nw < np) stage[(p1 * T + t) * 64 + lane] = v1[t];
     }
   }
   __syncthreads();
@@ -1174,60 +1194,14 @@ __device__ __forceinline__ void phase4_finish(const P4& a, int part, int r, bool
     for (int t = 0; t < T; ++t) {
       float y = 0.f;
       for (int g = 0; g < d.G; ++g)
-        if (gso[g + 1] > gso[g]) y += stage[(g * T + t) * 64 + lane];
-      y += stage[(d.G * T + t) * 64 + lane];
+        if (gso[g + 1] > gso[g]) {
+          y += stage[((2 * g) * T + t) * 64 + lane];
+          y += stage[((2 * g + 1) * T + t) * 64 + lane];
+        }
+      for (int p = 2 * d.G; p < np; ++p) y += stage[(p * T + t) * 64 + lane];
       float* dst = a.y + (size_t)t * d.H + row;
       *dst = a.accumulate ? *dst + y : y;
     }
-  }
-  __syncthreads();                                   // stage overlaps the wave staging areas
-}
-
-template <int T, int DU, int W>
-__global__ __launch_bounds__(64 * W) void k_phase4(P4 a) {
-  extern __shared__ __align__(16) char smem[];
-  __shared__ int flag;
-  const Dims& d = a.d;
-  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
-  const int tiles = a.gu.tiles;                      // H / 64
-  char* xs = smem + wave * stage_bytes<T>();
-  if ((int)blockIdx.x >= a.nub) {
-    const int r = blockIdx.x - a.nub;                // shared down, row tile r
-    f4 acc[4];
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) acc[rg] = (f4){0.f, 0.f, 0.f, 0.f};
-    if (wave < a.gsd.nss) {
-      WRegs<kBF16, T> R;
-      phase4_issue<T, kBF16>(a, R, d.G, r, wave, lane);
-      wave_compute<kBF16, T>(R, ss_codes(kBF16, a.gsd, wave), T, xs, lane, acc);
-    }
-    phase4_finish<T>(a, d.G, r, true, acc, smem, &flag, [] {});
-    return;
-  }
-  ci_t gso = ci(a.ws.gslot_off);
-  const int nu = d.G * tiles;
-  const bool has_ss = wave < a.gu.nss;
-  const rsrc_t sr = rsrc(a.ws.s, (uint32_t)((size_t)T * d.G * d.L * sizeof(float)));
-  WRegs<DU, T> R;
-  int it = blockIdx.x;
-  if (it < nu && has_ss && gso[it / tiles + 1] > gso[it / tiles])
-    phase4_issue_u<T, DU>(a, R, sr, it / tiles, it % tiles, wave, lane);
-  for (; it < nu; it += a.nub) {
-    const int part = it / tiles, r = it % tiles;
-    const bool active = gso[part + 1] > gso[part];
-    f4 acc[4];
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) acc[rg] = (f4){0.f, 0.f, 0.f, 0.f};
-    if (active && has_ss) wave_compute<DU, T>(R, ss_codes(DU, a.gu, wave), T, xs, lane, acc);
-    __builtin_amdgcn_sched_barrier(0);               // the next loads reuse this item's registers
-    const int nx = it + a.nub;
-    const bool nx_load = nx < nu && has_ss && gso[nx / tiles + 1] > gso[nx / tiles];
-    // wave 0 issues its next loads after waiting for its stores; the other
-    // waves issue them now
-    if (wave != 0 && nx_load) phase4_issue_u<T, DU>(a, R, sr, nx / tiles, nx % tiles, wave, lane);
-    phase4_finish<T>(a, part, r, active, acc, smem, &flag, [&] {
-      if (nx_load) phase4_issue_u<T, DU>(a, R, sr, nx / tiles, nx % tiles, wave, lane);
-    });
   }
 }
 
@@ -1347,22 +1321,21 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st) {
   P4 p4{};
   p4.d = d; p4.umat = h->umat; p4.gu = h->g_u; p4.sdn = h->sdn; p4.gsd = h->g_sdn;
   p4.y = y; p4.accumulate = norm ? 1 : 0; p4.ws = ws;
-  const int nw4 = h->g_u.nss > h->g_sdn.nss ? h->g_u.nss : h->g_sdn.nss;
+  // every block has hu waves (one per SIMD for hu = 4, so several blocks
+  // share a CU evenly); the shared down takes ceil(half-steps / hu) blocks
+  const int hu = (h->g_u.nss + 1) / 2;
+  const int nhs = (dd.shared_ffn + 127) / 128;        // shared-down half super-steps
+  p4.hu = hu;
+  p4.nsb = (nhs + hu - 1) / hu;
+  const int nw4 = hu;
   size_t sm4 = (size_t)nw4 * (stage_bytes<T>() + red_bytes_per_wave<T>());
-  const size_t sm4r = (size_t)(d.G + 1) * T * 64 * sizeof(float);
+  const size_t sm4r = (size_t)(2 * d.G + p4.nsb) * T * 64 * sizeof(float);
   sm4 = sm4 > sm4r ? sm4 : sm4r;
-  const void* k4 = nw4 <= 10 ? (const void*)k_phase4<T, DU, 10> : (const void*)k_phase4<T, DU, 16>;
-  const int res4 = resident_blocks(h, k4, nw4 * 64, sm4);
-  if (res4 <= 0) { set_error("phase 4: occupancy query failed"); return LMOE_EHIP; }
-  // one block per shared-down tile; the U blocks fill the rest of the
-  // device and stride over the U items
-  const int nu = d.G * h->g_u.tiles, ns = h->g_sdn.tiles;
-  int nub = res4 - ns;
-  nub = nub < 1 ? 1 : (nub > nu ? nu : nub);
-  const int grid4 = nub + ns;
-  p4.nub = nub;
-  if (nw4 <= 10)
-    hipLaunchKernelGGL((k_phase4<T, DU, 10>), dim3(grid4), dim3(nw4 * 64), sm4, st, p4);
+  const int grid4 = (2 * d.G + p4.nsb) * h->g_u.tiles;
+  if (nw4 <= 4)
+    hipLaunchKernelGGL((k_phase4<T, DU, 4>), dim3(grid4), dim3(nw4 * 64), sm4, st, p4);
+  else if (nw4 <= 8)
+    hipLaunchKernelGGL((k_phase4<T, DU, 8>), dim3(grid4), dim3(nw4 * 64), sm4, st, p4);
   else
     hipLaunchKernelGGL((k_phase4<T, DU, 16>), dim3(grid4), dim3(nw4 * 64), sm4, st, p4);
   LMOE_HIP(hipGetLastError());

@@ -107,7 +107,7 @@ struct Workspace {
   float* hsp = nullptr;          // [H/256][T][2 Fs] shared gate/up partials per super-step
   float* hbuf = nullptr;         // [T*K][F] expert hidden, sorted position order
   float* s = nullptr;            // [T][G][ell] per-group sums
-  float* ypart = nullptr;        // [G+1][T][H]
+  float* ypart = nullptr;        // [2G + shared-down blocks][T][H] phase-4 partials
   unsigned* ctr_router = nullptr;  // [1]
   unsigned* ctr_y = nullptr;       // [H/64]
   int nch = 0;                   // router column chunks
