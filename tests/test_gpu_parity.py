@@ -153,6 +153,18 @@ def test_145b_zero_rows_all_logits_tie():
     check(c, layer, 4, "145b zero rows")
 
 
+def test_wide_ffn_many_picks():
+    """expert_ffn 4096 and top-16 at T = 8: 128 assignments (ranked, not the
+    one-wavefront sort), sixteen down super-steps per slot, and a group's
+    weighted outputs that leave the down phase too little LDS for one
+    wavefront per super-step, so some wavefronts take two in turn."""
+    w = wl.Workload("wide_ffn", 256, 128, 32, 16, 2, 4096, 64, 8, 8)
+    c = Case(w, seed=7)
+    layer = make_layer(c)
+    for T in (8, 3):
+        check(c, layer, T, "wide ffn T=%d" % T)
+
+
 def test_argument_errors_on_device():
     lm = _lmoe()
     c = Case(wl.WORKLOADS["tiny"], tokens=4)
