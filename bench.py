@@ -366,26 +366,44 @@ def main():
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
 
-    # per-kernel durations with HIP events recorded on the forward's stream
+    # per-kernel durations, with HIP events on the stream the kernels run on.
+    # Single layer: each phase is launched alone, back to back over the weight
+    # copies (cold, as in the forward), one event pair around the run, so a
+    # figure is one kernel's launch-to-launch time. Stack (block forwards):
+    # events between the phases of each forward, which add their own gaps.
     nph = lm.lib().lmoe_phase_count(T)
-    nprof = max(n_handles * 2, 32)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)] for _ in range(nprof)]
-    for row in evs:
-        for e in row:
-            e.record()
-    torch.cuda.synchronize()
-    for i in range(nprof):
-        L_ = layers[i % n_handles]
-        L_.set_phase_events([e.cuda_event for e in evs[i]])
-        if stack:
+    if not stack:
+        for L_ in layers:
+            L_.forward(x, y)               # the workspace state each phase reads
+        nrep = max(n_handles * 8, 64)
+        phase_avg = []
+        for k in range(1, nph + 1):
+            for i in range(n_handles):
+                layers[i].run_phase(x, y, k)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(nrep):
+                layers[i % n_handles].run_phase(x, y, k)
+            e1.record()
+            torch.cuda.synchronize()
+            phase_avg.append(e0.elapsed_time(e1) / nrep)
+        phase_avg = np.array(phase_avg)
+    else:
+        nprof = max(n_handles * 2, 32)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)] for _ in range(nprof)]
+        for row in evs:
+            for e in row:
+                e.record()
+        torch.cuda.synchronize()
+        for i in range(nprof):
+            L_ = layers[i % n_handles]
+            L_.set_phase_events([e.cuda_event for e in evs[i]])
             L_.forward_block(x)
-        else:
-            L_.forward(x, y)
-    for L_ in layers:
-        L_.set_phase_events(None)
-    torch.cuda.synchronize()
-    phase_ms = np.array([[row[k].elapsed_time(row[k + 1]) for k in range(nph)] for row in evs])
-    phase_avg = phase_ms.mean(axis=0)
+        for L_ in layers:
+            L_.set_phase_events(None)
+        torch.cuda.synchronize()
+        phase_ms = np.array([[row[k].elapsed_time(row[k + 1]) for k in range(nph)] for row in evs])
+        phase_avg = phase_ms.mean(axis=0)
     dom = int(np.argmax(phase_avg))
     achieved = pbytes[dom] / (phase_avg[dom] * 1e-3) / 1e9
     step_bytes = layer_bytes * (w.n_layers if stack else 1)

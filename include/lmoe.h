@@ -164,6 +164,16 @@ int lmoe_forward_block(lmoe_t* h, float* x_inout_dev, int32_t T, float rms_eps,
 int lmoe_set_phase_events(lmoe_t* h, void* const* events, int32_t n);
 int32_t lmoe_phase_count(int32_t T);
 
+/* Profiling hook: runs phase `phase` (1 .. 4) of a decode forward of
+ * T <= 8 tokens by itself on the stream. It reads what the handle's last
+ * decode forward left in its workspace, which must have been an
+ * lmoe_forward of the same T (else LMOE_ESTATE), and writes what that phase
+ * writes there (phase 4: y, as lmoe_forward does). Calls back to back time
+ * one kernel as a forward runs it. x: [T][H] as given to that forward;
+ * y: [T][H] (written by phase 4 only). EINVAL: NULL or aliased x/y, phase
+ * outside 1..4, T outside 1..8 or above max_tokens. */
+int lmoe_run_phase(lmoe_t* h, const float* x, int32_t T, int32_t phase, float* y, void* stream);
+
 void lmoe_destroy(lmoe_t* h);
 
 const char* lmoe_strerror(int code);

@@ -282,6 +282,7 @@ int lmoe_forward(lmoe_t* h, const float* x, int32_t T, float* y, const lmoe_debu
   const int rc = T > kMaxDecodeT ? forward_prefill(h, x, T, y, false, 0.0f, st)
                                  : forward_decode(h, x, T, y, false, st);
   if (rc) return rc;
+  h->last_decode_T = T > kMaxDecodeT ? h->last_decode_T : T;
   if (dbg) return copy_debug(h, dbg, T, st);
   return 0;
 }
@@ -296,6 +297,7 @@ int lmoe_forward_block(lmoe_t* h, float* x, int32_t T, float eps, void* stream) 
   hipStream_t st = (hipStream_t)stream;
   if (T > kMaxDecodeT) return forward_prefill(h, x, T, x, true, eps, st);
   if (int rc = rms_rows(h, x, T, eps, st)) return rc;
+  h->last_decode_T = 0;                            // the decode workspace now holds a block forward
   return forward_decode(h, x, T, x, true, st);
 }
 
@@ -317,6 +319,20 @@ int lmoe_set_phase_events(lmoe_t* h, void* const* events, int32_t n) {
 }
 
 int32_t lmoe_phase_count(int32_t T) { return T > kMaxDecodeT ? kPrefillPhases : kDecodePhases; }
+
+int lmoe_run_phase(lmoe_t* h, const float* x, int32_t T, int32_t phase, float* y, void* stream) {
+  if (int rc = check_forward(h, x, T, y)) return rc;
+  if (x == y || T > kMaxDecodeT || phase < 1 || phase > kDecodePhases) {
+    set_error("lmoe_run_phase: x and y alias, T above 8 or phase outside 1..4");
+    return LMOE_EINVAL;
+  }
+  if (h->last_decode_T != T) {
+    set_error("lmoe_run_phase: the last decode forward on this handle was not of T tokens");
+    return LMOE_ESTATE;
+  }
+  DeviceGuard g(h->device);
+  return forward_decode(h, x, T, y, false, (hipStream_t)stream, phase);
+}
 
 void lmoe_destroy(lmoe_t* h) {
   if (!h) return;

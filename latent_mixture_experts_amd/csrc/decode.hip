@@ -1238,13 +1238,15 @@ int resident_blocks(lmoe_t* h, const void* kernel, int threads, size_t lds) {
   return n;
 }
 
+// only: 0 launches every phase, k in 1..4 phase k alone (its inputs are in
+// the workspace from an earlier forward of T tokens)
 template <int T, int DU>
-int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st) {
+int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st, int only) {
   const lmoe_dims& dd = h->d;
   Dims d{T, dd.hidden, dd.latent, dd.n_experts, dd.top_k, dd.n_groups, dd.expert_ffn,
          dd.shared_ffn};
   Workspace ws = h->ws;
-  const bool ev = h->phase_events.size() == (size_t)kDecodePhases + 1;
+  const bool ev = only == 0 && h->phase_events.size() == (size_t)kDecodePhases + 1;
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[0], st));
 
   // phase 1
@@ -1271,10 +1273,12 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st) {
   const size_t sm_routing = routing_lds_bytes(T, d.E, h->g_router.tiles * 64, n, nw1);
   sm1 = sm1 > sm_router ? sm1 : sm_router;
   sm1 = sm1 > sm_routing ? sm1 : sm_routing;
-  if (nw1 <= 10)
-    hipLaunchKernelGGL((k_phase1<T, DU, 10>), dim3(nb1), dim3(nw1 * 64), sm1, st, p1);
-  else
-    hipLaunchKernelGGL((k_phase1<T, DU, 16>), dim3(nb1), dim3(nw1 * 64), sm1, st, p1);
+  if (only == 0 || only == 1) {
+    if (nw1 <= 10)
+      hipLaunchKernelGGL((k_phase1<T, DU, 10>), dim3(nb1), dim3(nw1 * 64), sm1, st, p1);
+    else
+      hipLaunchKernelGGL((k_phase1<T, DU, 16>), dim3(nb1), dim3(nw1 * 64), sm1, st, p1);
+  }
   LMOE_HIP(hipGetLastError());
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[1], st));
 
@@ -1289,7 +1293,8 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st) {
   const int items2 = maxslots * h->g_gu.tiles;
   const int res2 = resident_blocks(h, (const void*)k_phase2<T>, nw2 * 64, sm2);
   if (res2 <= 0) { set_error("phase 2: occupancy query failed"); return LMOE_EHIP; }
-  hipLaunchKernelGGL(k_phase2<T>, dim3(items2 < res2 ? items2 : res2), dim3(nw2 * 64), sm2, st, p2);
+  if (only == 0 || only == 2)
+    hipLaunchKernelGGL(k_phase2<T>, dim3(items2 < res2 ? items2 : res2), dim3(nw2 * 64), sm2, st, p2);
   LMOE_HIP(hipGetLastError());
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[2], st));
 
@@ -1312,7 +1317,8 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st) {
   p3.spr = spr;
   p3.wps = wps;
   const int nw3 = spr * wps;
-  hipLaunchKernelGGL(k_phase3<T>, dim3(d.G * h->g_dn.tiles), dim3(nw3 * 64),
+  if (only == 0 || only == 3)
+    hipLaunchKernelGGL(k_phase3<T>, dim3(d.G * h->g_dn.tiles), dim3(nw3 * 64),
                      (size_t)nw3 * stage_bytes_f16<T>() + ol_bytes, st, p3);
   LMOE_HIP(hipGetLastError());
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[3], st));
@@ -1332,21 +1338,23 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st) {
   const size_t sm4r = (size_t)(2 * d.G + p4.nsb) * T * 64 * sizeof(float);
   sm4 = sm4 > sm4r ? sm4 : sm4r;
   const int grid4 = (2 * d.G + p4.nsb) * h->g_u.tiles;
-  if (nw4 <= 4)
-    hipLaunchKernelGGL((k_phase4<T, DU, 4>), dim3(grid4), dim3(nw4 * 64), sm4, st, p4);
-  else if (nw4 <= 8)
-    hipLaunchKernelGGL((k_phase4<T, DU, 8>), dim3(grid4), dim3(nw4 * 64), sm4, st, p4);
-  else
-    hipLaunchKernelGGL((k_phase4<T, DU, 16>), dim3(grid4), dim3(nw4 * 64), sm4, st, p4);
+  if (only == 0 || only == 4) {
+    if (nw4 <= 4)
+      hipLaunchKernelGGL((k_phase4<T, DU, 4>), dim3(grid4), dim3(nw4 * 64), sm4, st, p4);
+    else if (nw4 <= 8)
+      hipLaunchKernelGGL((k_phase4<T, DU, 8>), dim3(grid4), dim3(nw4 * 64), sm4, st, p4);
+    else
+      hipLaunchKernelGGL((k_phase4<T, DU, 16>), dim3(grid4), dim3(nw4 * 64), sm4, st, p4);
+  }
   LMOE_HIP(hipGetLastError());
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[4], st));
   return 0;
 }
 
 template <int T>
-int launch_t(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st) {
-  return h->d.du_bits == 8 ? launch_all<T, kQ8>(h, x, y, norm, st)
-                           : launch_all<T, kQ4>(h, x, y, norm, st);
+int launch_t(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st, int only) {
+  return h->d.du_bits == 8 ? launch_all<T, kQ8>(h, x, y, norm, st, only)
+                           : launch_all<T, kQ4>(h, x, y, norm, st, only);
 }
 
 }  // namespace
@@ -1357,16 +1365,16 @@ int rms_rows(lmoe_t* h, const float* x, int T, float eps, hipStream_t st) {
   return 0;
 }
 
-int forward_decode(lmoe_t* h, const float* x, int T, float* y, bool norm, hipStream_t st) {
+int forward_decode(lmoe_t* h, const float* x, int T, float* y, bool norm, hipStream_t st, int only) {
   switch (T) {
-    case 1: return launch_t<1>(h, x, y, norm, st);
-    case 2: return launch_t<2>(h, x, y, norm, st);
-    case 3: return launch_t<3>(h, x, y, norm, st);
-    case 4: return launch_t<4>(h, x, y, norm, st);
-    case 5: return launch_t<5>(h, x, y, norm, st);
-    case 6: return launch_t<6>(h, x, y, norm, st);
-    case 7: return launch_t<7>(h, x, y, norm, st);
-    case 8: return launch_t<8>(h, x, y, norm, st);
+    case 1: return launch_t<1>(h, x, y, norm, st, only);
+    case 2: return launch_t<2>(h, x, y, norm, st, only);
+    case 3: return launch_t<3>(h, x, y, norm, st, only);
+    case 4: return launch_t<4>(h, x, y, norm, st, only);
+    case 5: return launch_t<5>(h, x, y, norm, st, only);
+    case 6: return launch_t<6>(h, x, y, norm, st, only);
+    case 7: return launch_t<7>(h, x, y, norm, st, only);
+    case 8: return launch_t<8>(h, x, y, norm, st, only);
     default: return LMOE_EUNSUPPORTED;
   }
 }

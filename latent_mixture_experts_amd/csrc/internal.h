@@ -175,6 +175,7 @@ struct lmoe {
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   std::vector<void*> allocations;
   std::vector<hipEvent_t> phase_events;   // empty: no phase timing
+  int last_decode_T = 0;                  // T of the last plain decode forward (0: none)
   // blocks of a kernel resident at once, by (kernel, threads, LDS bytes)
   struct Resident { const void* kernel; int threads; size_t lds; int blocks; };
   std::vector<Resident> resident;
@@ -191,7 +192,9 @@ int pack_experts_impl(const float* gate, const float* up, const float* down, int
                       int f, uint8_t* dst, hipStream_t stream);
 
 // decode.hip
-int forward_decode(lmoe_t* h, const float* x, int T, float* y, bool norm, hipStream_t stream);
+// only: 0 runs the whole forward, 1..4 that phase alone
+int forward_decode(lmoe_t* h, const float* x, int T, float* y, bool norm, hipStream_t stream,
+                   int only = 0);
 int rms_rows(lmoe_t* h, const float* x, int T, float eps, hipStream_t stream);
 
 // prefill.hip

@@ -67,6 +67,7 @@ def _load():
         "lmoe_destroy": (None, [vp]),
         "lmoe_set_phase_events": (ctypes.c_int, [vp, ctypes.POINTER(vp), i32]),
         "lmoe_phase_count": (i32, [i32]),
+        "lmoe_run_phase": (ctypes.c_int, [vp, vp, i32, i32, vp, vp]),
         "lmoe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "lmoe_last_error": (ctypes.c_char_p, []),
         "lmoe_expert_record_bytes": (sz, [i32, i32]),
@@ -170,6 +171,14 @@ class Layer:
         _check(_lib.lmoe_forward_block(self._h, _ptr(x), T, eps, _stream(stream)),
                "lmoe_forward_block")
         return x
+
+    def run_phase(self, x, y, phase, T=None, stream=None):
+        """Decode phase `phase` (1..4) alone, on what the last forward of the
+        same T left in the workspace (profiling)."""
+        T = x.shape[0] if T is None else T
+        _check(_lib.lmoe_run_phase(self._h, _ptr(x), T, phase, _ptr(y), _stream(stream)),
+               "lmoe_run_phase")
+        return y
 
     def set_phase_events(self, events):
         """events: sequence of hipEvent_t handles (ints), or None."""

@@ -189,3 +189,34 @@ def test_argument_errors_on_device():
     with pytest.raises(lm.LmoeError) as e:
         fresh.load(bad)
     assert e.value.code == lm.EINVAL
+
+
+def test_run_phase_repeats_the_forward():
+    """Each decode phase run alone after a forward (the profiling hook) reads
+    and writes the same workspace state: rerunning phases 1..4 in order gives
+    y bit for bit; a phase before any forward of that T is refused."""
+    lm = _lmoe()
+    w = wl.WORKLOADS["145b_decode"]
+    c = Case(w, tokens=4)
+    layer = make_layer(c, max_tokens=8)
+    x = torch.from_numpy(np.ascontiguousarray(c.x[:4])).cuda()
+    y = torch.empty(4, w.hidden, device="cuda")
+    with pytest.raises(lm.LmoeError) as e:
+        layer.run_phase(x, y, 1)
+    assert e.value.code == lm.ESTATE
+    layer.forward(x, y)
+    torch.cuda.synchronize()
+    want = y.cpu().numpy().copy()
+    for _ in range(2):
+        y.zero_()
+        for k in (1, 2, 3, 4):
+            layer.run_phase(x, y, k)
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy(), want)
+    for k in (0, 5):
+        with pytest.raises(lm.LmoeError) as e:
+            layer.run_phase(x, y, k)
+        assert e.value.code == lm.EINVAL
+    with pytest.raises(lm.LmoeError) as e:
+        layer.run_phase(x[:2], y[:2], 1)               # last forward was of 4 tokens
+    assert e.value.code == lm.ESTATE
