@@ -62,19 +62,6 @@ __device__ __forceinline__ int label_of(const uint8_t* labels, int e) {
   return (int)((((cu32_t)labels)[e >> 2] >> (8 * (e & 3))) & 0xFFu);
 }
 
-// Raw buffer resource over [p, p + bytes): wave-uniform base in SGPRs, so a
-// lane addresses it with one 32-bit offset register; loads past the end
-// return zero.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-__device__ __forceinline__ rsrc_t rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-constexpr int kAuxNT = 2;   // cache policy: non-temporal
-template <int AUX = 0>
-__device__ __forceinline__ uint4 ldb(rsrc_t r, int voff, int soff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX));
-}
-
 __device__ __forceinline__ float h2f(uint32_t bits) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFFFu));
 }

@@ -64,10 +64,6 @@ constexpr int MB = WTOK / 32;  // 32-token MFMA blocks per wave
 constexpr int NTW = 4;         // 64-row weight tiles per workgroup (two waves each)
 constexpr int CHUNK_T = 64;    // tokens per permutation chunk
 
-__device__ __forceinline__ uint4 ldnt(const uint8_t* p) {
-  const u4v v = __builtin_nontemporal_load((const u4v*)p);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
@@ -187,61 +183,97 @@ struct Reg {
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// The thread's activation pieces, fixed for a whole GEMM: piece i is 16
+// bytes of row m = (threadIdx.x + i * NTH) / PPR (modulo the tile, per part)
+// at column c = 8 * (threadIdx.x % PPR) of each stage; p[i] points at that
+// column of stage 0 of matrix 0 (padding rows at row 0), bit i of `valid`
+// says the row exists.
+template <int WF>
+struct ARows {
+  const uint16_t* p[Fm<WF>::PPT];
+  uint32_t valid;
+  int c;
+};
+
+template <int WF>
+__device__ __forceinline__ ARows<WF> a_rows(const AMat& A, const int* arow) {
+  using F = Fm<WF>;
+  ARows<WF> R;
+  R.valid = 0;
+  R.c = 8 * (threadIdx.x % F::PPR);
+#pragma unroll
+  for (int i = 0; i < F::PPT; ++i) {
+    const int p = threadIdx.x + i * NTH;
+    const int part = p / (BM * F::PPR), m = (p % (BM * F::PPR)) / F::PPR;
+    const int row = arow[m];
+    R.valid |= (row >= 0 ? 1u : 0u) << i;
+    R.p[i] = A.p + (size_t)max(row, 0) * A.rs + (size_t)part * A.ps + R.c;
+  }
+  return R;
+}
+
 // Issues the loads of stage s: the activation pieces (all threads); for the
 // wave pair of a weight tile, alternate code slots each plus, from both, the
 // scale word of lane-chunk `lane` (row group lane/16, row lane%16). Every
-// load is issued: addresses of padding rows, of columns past k and of a
-// missing last chunk are clamped to valid ones (the values are masked when
-// stored, or meet zero activations).
-template <int WF>
-__device__ __forceinline__ void fetch(const WMat& W, int tile, const AMat& A, const int* arow, int s,
-                                      Reg<WF>& R) {
+// load is issued: columns past k and a missing last chunk are clamped to
+// valid ones (the values are masked when stored, or meet zero activations).
+// The weight loads address the wave's tile through a buffer resource with a
+// wave-uniform base, so only the lane offset lives in a vector register;
+// BAUX is their cache policy. A stage past the last one (s >= nst) issues
+// the loads of stage nst - 1 with an empty weight resource: its weight loads
+// return zeros without a memory access and its activation loads hit the
+// lines the same thread just fetched; no branch, so the compiler's counts of
+// loads in flight stay exact.
+template <int WF, int BAUX>
+__device__ __forceinline__ void fetch(const WMat& W, int tile, const AMat& A, const ARows<WF>& ar,
+                                      int s, int nst, Reg<WF>& R) {
+  const bool live = s < nst;
+  s = min(s, nst - 1);
   using F = Fm<WF>;
   const int lane = threadIdx.x & 63, wm = wave_id() & 1;
   const int kmat = W.g.k;
   const int spm = (kmat + F::SCOLS - 1) / F::SCOLS;
   const int mat = s / spm, sm = s % spm;
   const int col0 = sm * F::SCOLS;
+  const size_t aoff = (size_t)mat * A.kmat + min(col0, A.kmat - 8 - ar.c);
 #pragma unroll
-  for (int i = 0; i < F::PPT; ++i) {
-    const int p = threadIdx.x + i * NTH;
-    const int part = p / (BM * F::PPR), rem = p % (BM * F::PPR);
-    const int m = rem / F::PPR, kk = min(col0 + (rem % F::PPR) * 8, A.kmat - 8);
-    const int row = max(arow[m], 0);
-    R.a[i] = *(const uint4*)(A.p + (size_t)row * A.rs + (size_t)part * A.ps + (size_t)mat * A.kmat + kk);
-  }
+  for (int i = 0; i < F::PPT; ++i) R.a[i] = *(const uint4*)(ar.p[i] + aoff);
   const int cpm = (kmat + F::CC - 1) / F::CC;
   const int ss = col0 / kSSCols, cin0 = (col0 % kSSCols) / F::CC;
   const int ncs = ss_code_slots(WF, min(kSSCols, kmat - ss * kSSCols));
   const int jmax = cpm - 1 - sm * F::SC;
-  const uint8_t* sb = W.base + (size_t)mat * W.mat_bytes +
-                      ((size_t)tile * W.g.tile_slots + (size_t)ss * W.g.full) * kSlot;
+  const rsrc_t wt = rsrc(W.base + (size_t)mat * W.mat_bytes + (size_t)tile * W.g.tile_slots * kSlot,
+                         live ? (uint32_t)(W.g.tile_slots * kSlot) : 0u);
+  const int sso = ss * W.g.full * kSlot;
 #pragma unroll
   for (int i2 = 0; i2 < F::BPW; ++i2) {
     const int i = 2 * i2 + wm;
     const int j = min(i / 4, jmax), rg = i % 4;
-    R.b[i2] = ldnt(sb + (size_t)((cin0 + j) * 4 + rg) * kSlot + lane * 16);
+    R.b[i2] = ldb<BAUX>(wt, lane * 16, sso + ((cin0 + j) * 4 + rg) * kSlot);
   }
   if constexpr (!F::W16) {
     const int off = WF == kQ8 ? 4 * cin0 : 8 * cin0;
-    R.sc = *(const uint2*)(sb + (size_t)ncs * kSlot + lane * 16 + off);
+    R.sc = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wt, lane * 16 + off,
+                                                                           sso + ncs * kSlot, BAUX));
   }
 }
 
 template <int WF>
-__device__ __forceinline__ void store(uint8_t* st, Reg<WF>& R, const AMat& A, const int* arow, int s) {
+__device__ __forceinline__ void store(uint8_t* st, Reg<WF>& R, const AMat& A, const ARows<WF>& ar, int s) {
   using F = Fm<WF>;
   const int spm = (A.kmat + F::SCOLS - 1) / F::SCOLS;
   const int col0 = (s % spm) * F::SCOLS;
+  const bool cok = col0 + ar.c < A.kmat;
   uint16_t* As = (uint16_t*)(st + kAOff);
 #pragma unroll
   for (int i = 0; i < F::PPT; ++i) {
     const int p = threadIdx.x + i * NTH;
-    const int part = p / (BM * F::PPR), rem = p % (BM * F::PPR);
-    const int m = rem / F::PPR, c = (rem % F::PPR) * 8;
-    const bool ok = arow[m] >= 0 && col0 + c < A.kmat;
-    const uint4 v = ok ? R.a[i] : make_uint4(0, 0, 0, 0);
-    *(uint4*)(As + (size_t)(part * BM + m) * F::AST + c) = v;
+    const int part = p / (BM * F::PPR), m = (p % (BM * F::PPR)) / F::PPR;
+    // masked with an AND rather than a select: the loaded value is always
+    // used, so the compiler cannot sink the load down to this store
+    const uint32_t mk = (cok && ((ar.valid >> i) & 1u)) ? ~0u : 0u;
+    const uint4 v = make_uint4(R.a[i].x & mk, R.a[i].y & mk, R.a[i].z & mk, R.a[i].w & mk);
+    *(uint4*)(As + (size_t)(part * BM + m) * F::AST + ar.c) = v;
   }
   const int lane = threadIdx.x & 63, w = wave_id(), tl = w >> 1, wm = w & 1;
   uint4* Bs = (uint4*)(st + kBOff);
@@ -303,17 +335,27 @@ __device__ __forceinline__ void mfma_stage(const uint8_t* st, f16v (&acc)[MB][2]
     for (int nb = 0; nb < 2; ++nb)
       sc[nb] = ((const uint2*)(st + kSOff))[tl * 64 + 16 * (2 * nb + (row >> 4)) + (lane & 15)];
   }
-#pragma unroll
-  for (int ks = 0; ks < F::KS; ++ks) {
-    const int kk = ks & 1, c32 = ks >> 1;           // 32-column block of the stage
-    const int j = c32 / F::BPC, b = c32 % F::BPC;   // chunk, block within the chunk
-    uint4 a[F::NP][NMB];
+  // activation fragments of k-step ks (rows of the wave's token blocks)
+  const auto load_a = [&](int ks, uint4 (&a)[F::NP][NMB]) {
 #pragma unroll
     for (int p = 0; p < F::NP; ++p)
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
         a[p][mb] = *(const uint4*)(As + (size_t)(p * BM + WTOK * wm + 32 * mb + row) * F::AST +
                                    16 * ks + 8 * kh);
+  };
+  // the fragments of k-step ks + 1 are read while ks computes; for the
+  // decoded formats a scheduling barrier closes each k-step, so the compiler
+  // does not hoist every read and decode of the stage ahead of the first MFMA
+  // (that needs more registers than two waves per SIMD have)
+  uint4 a[2][F::NP][NMB];
+  load_a(0, a[0]);
+#pragma unroll
+  for (int ks = 0; ks < F::KS; ++ks) {
+    const int kk = ks & 1, c32 = ks >> 1;           // 32-column block of the stage
+    const int j = c32 / F::BPC, b = c32 % F::BPC;   // chunk, block within the chunk
+    if (ks + 1 < F::KS) load_a(ks + 1, a[(ks + 1) & 1]);
+    const uint4 (&ac)[F::NP][NMB] = a[ks & 1];
     uint4 bw[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) bw[nb] = decode_b<WF>(raw[j][nb][kk], sc[nb], F::BPC * j + b, b, 2 * kk + kh);
@@ -325,61 +367,68 @@ __device__ __forceinline__ void mfma_stage(const uint8_t* st, f16v (&acc)[MB][2]
 #pragma unroll
           for (int p = 0; p < F::NP; ++p)
             acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, a[p][mb]), __builtin_bit_cast(bf16x8, bw[nb]), acc[mb][nb], 0, 0, 0);
+                __builtin_bit_cast(bf16x8, ac[p][mb]), __builtin_bit_cast(bf16x8, bw[nb]), acc[mb][nb], 0, 0, 0);
         } else {
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              __builtin_bit_cast(half8, a[0][mb]), __builtin_bit_cast(half8, bw[nb]), acc[mb][nb], 0, 0, 0);
+              __builtin_bit_cast(half8, ac[0][mb]), __builtin_bit_cast(half8, bw[nb]), acc[mb][nb], 0, 0, 0);
         }
       }
+    if constexpr (!F::W16) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // Accumulates the tile's product over all stages of W (all nmat matrices)
 // for the wave's first NMB token blocks (NMB 0: the wave only stages);
 // `tile` is the wave's weight tile (a wave whose tile is past the last one
-// computes on tile 0 and discards the result). One barrier per stage:
-// between two barriers a wave issues the global loads of stage s + 2, the
-// MFMAs of stage s (LDS buffer s % 2) and the LDS stores of stage s + 1 (the
-// other buffer, whose last readers finished before the barrier). Every
-// thread of the block takes part in the staging and the barriers.
-template <int WF, int NMB>
+// computes on tile 0 and discards the result). Global loads run NSET - 1
+// stages ahead in NSET register sets; one barrier per stage: between two
+// barriers a wave issues the global loads of stage s + NSET (into the set
+// stage s left), the MFMAs of stage s (LDS buffer s % 2) and the LDS stores
+// of stage s + 1 (the other buffer, whose last readers finished before the
+// barrier). The register set is the stage index modulo NSET (the body is
+// unrolled NSET times, with one loop exit); the buffer is picked at run
+// time. Every thread of the block takes part in the staging and the
+// barriers; the closing barrier also frees the buffers for a following call.
+template <int WF, int NMB, int BAUX, int NSET>
 __device__ __forceinline__ void gemm_loop(const WMat& W, int tile, bool b_on, const AMat& A,
                                           const int* arow, uint8_t* smem, f16v (&acc)[MB][2]) {
-  using F = Fm<WF>;
+  static_assert(NSET == 2 || NSET == 3, "two or three register sets");
   const int ld_tile = b_on ? tile : 0;     // a valid tile for the unused loads
-  const int nst = ((W.g.k + F::SCOLS - 1) / F::SCOLS) * W.nmat;
-  Reg<WF> r0, r1;
-  fetch<WF>(W, ld_tile, A, arow, 0, r0);
-  fetch<WF>(W, ld_tile, A, arow, min(1, nst - 1), r1);
-  store<WF>(smem, r0, A, arow, 0);
+  const int nst = ((W.g.k + Fm<WF>::SCOLS - 1) / Fm<WF>::SCOLS) * W.nmat;
+  const ARows<WF> ar = a_rows<WF>(A, arow);
+  Reg<WF> r[NSET];
+#pragma unroll
+  for (int i = 0; i < NSET; ++i) fetch<WF, BAUX>(W, ld_tile, A, ar, i, nst, r[i]);
+  store<WF>(smem, r[0], A, ar, 0);
   __syncthreads();
-  int s = 0;
-  for (; s + 1 < nst; s += 2) {
-    // stage s from buffer 0; stage s + 1 into buffer 1
-    fetch<WF>(W, ld_tile, A, arow, min(s + 2, nst - 1), r0);
-    if constexpr (NMB > 0) mfma_stage<WF, NMB>(smem, acc);
-    store<WF>(smem + kStage, r1, A, arow, s + 1);
+  // stage s: loads of s + NSET into the set stage s left, MFMAs of s, stores
+  // of s + 1 (past the last stage, a stale set into the buffer no wave reads
+  // again); the body has no branch
+  const auto step = [&](int s, Reg<WF>& mine, Reg<WF>& next) {
+    fetch<WF, BAUX>(W, ld_tile, A, ar, s + NSET, nst, mine);
+    if constexpr (NMB > 0) mfma_stage<WF, NMB>(smem + (s & 1) * kStage, acc);
+    store<WF>(smem + ((s + 1) & 1) * kStage, next, A, ar, min(s + 1, nst - 1));
     __syncthreads();
-    // stage s + 1 from buffer 1; stage s + 2 into buffer 0
-    fetch<WF>(W, ld_tile, A, arow, min(s + 3, nst - 1), r1);
-    if constexpr (NMB > 0) mfma_stage<WF, NMB>(smem + kStage, acc);
-    store<WF>(smem, r0, A, arow, min(s + 2, nst - 1));
-    __syncthreads();
+  };
+  int s0 = 0;
+  for (; s0 + NSET <= nst; s0 += NSET) {
+#pragma unroll
+    for (int i = 0; i < NSET; ++i) step(s0 + i, r[i], r[(i + 1) % NSET]);
   }
-  // odd stage count: the last stage is in buffer 0
-  if (s < nst) {
-    if constexpr (NMB > 0) mfma_stage<WF, NMB>(smem, acc);
-    __syncthreads();
-  }
+#pragma unroll
+  for (int i = 0; i + 1 < NSET; ++i)
+    if (s0 + i < nst) step(s0 + i, r[i], r[(i + 1) % NSET]);
 }
 
-// runs gemm_loop with the wave's token-block count: 0, 1 or 2
-template <int WF>
+// runs gemm_loop with the wave's token-block count: 0, 1 or 2; BAUX is the
+// cache policy of the weight loads, NSET the register sets of the prefetch
+// (three where they fit the registers: the 16-bit weight formats)
+template <int WF, int BAUX = 0, int NSET = 3>
 __device__ __forceinline__ void gemm_wave(const WMat& W, int tile, bool b_on, int nmb, const AMat& A,
                                           const int* arow, uint8_t* smem, f16v (&acc)[MB][2]) {
-  if (nmb >= 2) gemm_loop<WF, 2>(W, tile, b_on, A, arow, smem, acc);
-  else if (nmb == 1) gemm_loop<WF, 1>(W, tile, b_on, A, arow, smem, acc);
-  else gemm_loop<WF, 0>(W, tile, b_on, A, arow, smem, acc);
+  if (nmb >= 2) gemm_loop<WF, 2, BAUX, NSET>(W, tile, b_on, A, arow, smem, acc);
+  else if (nmb == 1) gemm_loop<WF, 1, BAUX, NSET>(W, tile, b_on, A, arow, smem, acc);
+  else gemm_loop<WF, 0, BAUX, NSET>(W, tile, b_on, A, arow, smem, acc);
 }
 
 __device__ __forceinline__ void zero_acc(f16v (&acc)[MB][2]) {
@@ -540,7 +589,8 @@ __global__ __launch_bounds__(NTH) void k_grouped(Grouped a) {
   const WMat W{base + a.woff, a.g, 0, 1};
   f16v acc[MB][2];
   zero_acc(acc);
-  gemm_wave<kFP4>(W, tile, b_on, nmb, a.A, arow, smem, acc);
+  // each expert's weights are streamed once per piece: non-temporal
+  gemm_wave<kFP4, kAuxNT>(W, tile, b_on, nmb, a.A, arow, smem, acc);
   if (!b_on) return;
   const float* ts = (const float*)(base + a.ts_off);
 
