@@ -252,6 +252,10 @@ int lmoe_create(const lmoe_dims* dims, int hip_device, lmoe_t** out) {
   if (!h) return LMOE_ENOMEM;
   h->d = *dims;
   h->device = hip_device;
+  int ncu = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, hip_device) == hipSuccess &&
+      ncu > 0)
+    h->ncu = ncu;
   if (int rc = create_impl(h)) {
     free_all(h);
     delete h;

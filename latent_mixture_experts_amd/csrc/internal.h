@@ -161,6 +161,7 @@ struct PrefillWs {
 struct lmoe {
   lmoe_dims d{};
   int device = 0;
+  int ncu = 1;                // compute units of the device
   bool loaded = false;
   lm::Geom g_router, g_d, g_u, g_gu, g_dn, g_sgu, g_sdn;
   lm::Geom g_router_m;        // router in the MFMA layout (prefill)

@@ -219,8 +219,8 @@ __device__ __forceinline__ ARows<WF> a_rows(const AMat& A, const int* arow) {
 // valid ones (the values are masked when stored, or meet zero activations).
 // The weight loads address the wave's tile through a buffer resource with a
 // wave-uniform base, so only the lane offset lives in a vector register;
-// BAUX is their cache policy. A stage past the last one (s >= nst) issues
-// the loads of stage nst - 1 with an empty weight resource: its weight loads
+// BAUX is their cache policy. A stage at or past the range end (s >= nst)
+// issues the loads of stage nst - 1 with an empty weight resource: its weight loads
 // return zeros without a memory access and its activation loads hit the
 // lines the same thread just fetched; no branch, so the compiler's counts of
 // loads in flight stay exact.
@@ -377,58 +377,69 @@ __device__ __forceinline__ void mfma_stage(const uint8_t* st, f16v (&acc)[MB][2]
   }
 }
 
-// Accumulates the tile's product over all stages of W (all nmat matrices)
-// for the wave's first NMB token blocks (NMB 0: the wave only stages);
-// `tile` is the wave's weight tile (a wave whose tile is past the last one
-// computes on tile 0 and discards the result). Global loads run NSET - 1
-// stages ahead in NSET register sets; one barrier per stage: between two
-// barriers a wave issues the global loads of stage s + NSET (into the set
-// stage s left), the MFMAs of stage s (LDS buffer s % 2) and the LDS stores
-// of stage s + 1 (the other buffer, whose last readers finished before the
-// barrier). The register set is the stage index modulo NSET (the body is
+// Accumulates the tile's product over stages [sb, se) of W (stage s covers
+// SCOLS columns of matrix s / stages-per-matrix) for the wave's first NMB
+// token blocks (NMB 0: the wave only stages); `tile` is the wave's weight
+// tile (a wave whose tile is past the last one computes on tile 0 and
+// discards the result). Global loads run NSET - 1 stages ahead in NSET
+// register sets; one barrier per stage: between two barriers a wave issues
+// the global loads of stage s + NSET (into the set stage s left), the MFMAs
+// of stage s (LDS buffer (s - sb) % 2) and the LDS stores of stage s + 1 (the
+// other buffer, whose last readers finished before the barrier). The
+// register set is the stage's index in the range modulo NSET (the body is
 // unrolled NSET times, with one loop exit); the buffer is picked at run
 // time. Every thread of the block takes part in the staging and the
-// barriers; the closing barrier also frees the buffers for a following call.
+// barriers (the range is the block's); the closing barrier also frees the
+// buffers for a following call. An empty range does nothing.
 template <int WF, int NMB, int BAUX, int NSET>
 __device__ __forceinline__ void gemm_loop(const WMat& W, int tile, bool b_on, const AMat& A,
-                                          const int* arow, uint8_t* smem, f16v (&acc)[MB][2]) {
+                                          const int* arow, uint8_t* smem, f16v (&acc)[MB][2],
+                                          int sb, int se) {
   static_assert(NSET == 2 || NSET == 3, "two or three register sets");
+  if (sb >= se) return;
   const int ld_tile = b_on ? tile : 0;     // a valid tile for the unused loads
-  const int nst = ((W.g.k + Fm<WF>::SCOLS - 1) / Fm<WF>::SCOLS) * W.nmat;
   const ARows<WF> ar = a_rows<WF>(A, arow);
   Reg<WF> r[NSET];
 #pragma unroll
-  for (int i = 0; i < NSET; ++i) fetch<WF, BAUX>(W, ld_tile, A, ar, i, nst, r[i]);
-  store<WF>(smem, r[0], A, ar, 0);
+  for (int i = 0; i < NSET; ++i) fetch<WF, BAUX>(W, ld_tile, A, ar, sb + i, se, r[i]);
+  store<WF>(smem, r[0], A, ar, sb);
   __syncthreads();
   // stage s: loads of s + NSET into the set stage s left, MFMAs of s, stores
   // of s + 1 (past the last stage, a stale set into the buffer no wave reads
   // again); the body has no branch
   const auto step = [&](int s, Reg<WF>& mine, Reg<WF>& next) {
-    fetch<WF, BAUX>(W, ld_tile, A, ar, s + NSET, nst, mine);
-    if constexpr (NMB > 0) mfma_stage<WF, NMB>(smem + (s & 1) * kStage, acc);
-    store<WF>(smem + ((s + 1) & 1) * kStage, next, A, ar, min(s + 1, nst - 1));
+    fetch<WF, BAUX>(W, ld_tile, A, ar, s + NSET, se, mine);
+    if constexpr (NMB > 0) mfma_stage<WF, NMB>(smem + ((s - sb) & 1) * kStage, acc);
+    store<WF>(smem + ((s - sb + 1) & 1) * kStage, next, A, ar, min(s + 1, se - 1));
     __syncthreads();
   };
-  int s0 = 0;
-  for (; s0 + NSET <= nst; s0 += NSET) {
+  int s0 = sb;
+  for (; s0 + NSET <= se; s0 += NSET) {
 #pragma unroll
     for (int i = 0; i < NSET; ++i) step(s0 + i, r[i], r[(i + 1) % NSET]);
   }
 #pragma unroll
   for (int i = 0; i + 1 < NSET; ++i)
-    if (s0 + i < nst) step(s0 + i, r[i], r[(i + 1) % NSET]);
+    if (s0 + i < se) step(s0 + i, r[i], r[(i + 1) % NSET]);
 }
 
-// runs gemm_loop with the wave's token-block count: 0, 1 or 2; BAUX is the
-// cache policy of the weight loads, NSET the register sets of the prefetch
-// (three where they fit the registers: the 16-bit weight formats)
+// stages of a weight operand: SCOLS-column steps of each of its matrices
+template <int WF>
+__host__ __device__ __forceinline__ int n_stages(const WMat& W) {
+  return ((W.g.k + Fm<WF>::SCOLS - 1) / Fm<WF>::SCOLS) * W.nmat;
+}
+
+// runs gemm_loop over stages [sb, se) (default: all) with the wave's
+// token-block count: 0, 1 or 2; BAUX is the cache policy of the weight
+// loads, NSET the register sets of the prefetch
 template <int WF, int BAUX = 0, int NSET = 3>
 __device__ __forceinline__ void gemm_wave(const WMat& W, int tile, bool b_on, int nmb, const AMat& A,
-                                          const int* arow, uint8_t* smem, f16v (&acc)[MB][2]) {
-  if (nmb >= 2) gemm_loop<WF, 2, BAUX, NSET>(W, tile, b_on, A, arow, smem, acc);
-  else if (nmb == 1) gemm_loop<WF, 1, BAUX, NSET>(W, tile, b_on, A, arow, smem, acc);
-  else gemm_loop<WF, 0, BAUX, NSET>(W, tile, b_on, A, arow, smem, acc);
+                                          const int* arow, uint8_t* smem, f16v (&acc)[MB][2],
+                                          int sb = 0, int se = -1) {
+  if (se < 0) se = n_stages<WF>(W);
+  if (nmb >= 2) gemm_loop<WF, 2, BAUX, NSET>(W, tile, b_on, A, arow, smem, acc, sb, se);
+  else if (nmb == 1) gemm_loop<WF, 1, BAUX, NSET>(W, tile, b_on, A, arow, smem, acc, sb, se);
+  else gemm_loop<WF, 0, BAUX, NSET>(W, tile, b_on, A, arow, smem, acc, sb, se);
 }
 
 __device__ __forceinline__ void zero_acc(f16v (&acc)[MB][2]) {
@@ -467,23 +478,52 @@ struct Dense {
   size_t ostride;
   int nvalid;
   const float* res;   // kEpiY: residual rows [T][ostride] or null
+  // kEpiY: the first nfull logical tiles (whole rounds of the chip) run
+  // whole; each of the remaining nrem runs as nsplit blocks along k. Split
+  // sp covers a balanced share of the stages of W then W2 (a W2 stage, bf16
+  // in two parts, counts twice) and, with nsplit > 1, writes its BM x 256
+  // sum to part + (sp * nrem + j) * BM * 256 for the j-th split tile, with
+  // no residual; k_ytiles adds them up.
+  int nfull, nrem, nsplit;
+  float* part;
 };
+
+// XCD-aware order: block b of n runs on XCD b % 8; each XCD takes a
+// contiguous range of the n logical indices
+__device__ __forceinline__ int xcd_order(int b, int n) {
+  const int xcd = b & 7, q = b >> 3, per = n >> 3, rem = n & 7;
+  return xcd * per + min(xcd, rem) + q;
+}
+
+// logical tile L -> (token tile, weight quad): groups of 8 token tiles sweep
+// the weight quads with the token tile fastest, so neighbours in time share
+// A and B in L2
+__device__ __forceinline__ void tile_of(int L, int mtiles, int nquads, int& mt, int& quad) {
+  constexpr int GM = 8;
+  const int span = GM * nquads;
+  const int first = (L / span) * GM, gsz = min(mtiles - first, GM);
+  mt = first + (L % span) % gsz;
+  quad = (L % span) / gsz;
+}
 
 template <int WF, int EPI>
 __global__ __launch_bounds__(NTH) void k_dense(Dense a) {
   __shared__ __align__(16) uint8_t smem[2 * kStage];
   __shared__ int arow[BM];
-  // XCD-aware order: each of the 8 XCDs takes a contiguous range of logical
-  // tiles; within it, groups of 8 token tiles sweep the weight tiles with the
-  // token tile fastest, so neighbours in time share A and B in L2.
-  const int nblk = a.mtiles * a.nquads;
-  const int bid = blockIdx.x, xcd = bid & 7, q = bid >> 3;
-  const int per = nblk >> 3, rem = nblk & 7;
-  const int L = xcd * per + min(xcd, rem) + q;
-  constexpr int GM = 8;
-  const int span = GM * a.nquads;
-  const int first = (L / span) * GM, gsz = min(a.mtiles - first, GM);
-  const int mt = first + (L % span) % gsz, quad = (L % span) / gsz;
+  const int nblk0 = a.mtiles * a.nquads;
+  int L = 0, sp = 0, nsp = 1;
+  if (EPI != kEpiY || (int)blockIdx.x < a.nfull) {
+    L = xcd_order(blockIdx.x, EPI == kEpiY ? a.nfull : nblk0);
+  } else {
+    // split blocks follow the whole tiles (nfull is a multiple of 8, so the
+    // XCD of a block is still its index modulo 8); the split is slowest
+    const int Ls = xcd_order(blockIdx.x - a.nfull, a.nrem * a.nsplit);
+    sp = Ls / a.nrem;
+    L = a.nfull + Ls % a.nrem;
+    nsp = a.nsplit;
+  }
+  int mt, quad;
+  tile_of(L, a.mtiles, a.nquads, mt, quad);
 
   if (threadIdx.x < BM) {
     const int t = mt * BM + threadIdx.x;
@@ -496,8 +536,17 @@ __global__ __launch_bounds__(NTH) void k_dense(Dense a) {
   const int nmb = min(MB, max(0, a.T - mt * BM - WTOK * wm + 31) / 32);
   f16v acc[MB][2];
   zero_acc(acc);
-  gemm_wave<WF>(a.W, tile, b_on, nmb, a.A, arow, smem, acc);
-  if constexpr (EPI == kEpiY) gemm_wave<kBF16>(a.W2, tile, b_on, nmb, a.A2, arow, smem, acc);
+  if constexpr (EPI == kEpiY) {
+    // unit boundaries of the split: W stages count one, W2 stages two
+    const int n1 = n_stages<WF>(a.W), n2 = n_stages<kBF16>(a.W2), units = n1 + 2 * n2;
+    const int c0 = (int)((long long)units * sp / nsp);
+    const int c1 = (int)((long long)units * (sp + 1) / nsp);
+    const auto w2_stage = [&](int c) { return min(n2, max(0, (c - n1 + 1) / 2)); };
+    gemm_wave<WF>(a.W, tile, b_on, nmb, a.A, arow, smem, acc, min(c0, n1), min(c1, n1));
+    gemm_wave<kBF16>(a.W2, tile, b_on, nmb, a.A2, arow, smem, acc, w2_stage(c0), w2_stage(c1));
+  } else {
+    gemm_wave<WF>(a.W, tile, b_on, nmb, a.A, arow, smem, acc);
+  }
   if (!b_on) return;
 
 #pragma unroll
@@ -525,6 +574,9 @@ __global__ __launch_bounds__(NTH) void k_dense(Dense a) {
             if (n < a.nvalid) ((float*)a.out)[(size_t)t * a.ostride + n] = val;
           } else if constexpr (EPI == kEpiF16) {
             ((_Float16*)a.out)[(size_t)t * a.ostride + n] = (_Float16)val;
+          } else if (nsp > 1) {
+            const size_t j = (size_t)sp * a.nrem + (L - a.nfull);
+            a.part[(j * BM + (t - mt * BM)) * 256 + (n - 256 * quad)] = val;
           } else {
             const size_t i = (size_t)t * a.ostride + n;
             ((float*)a.out)[i] = a.res ? a.res[i] + val : val;
@@ -1026,9 +1078,26 @@ __global__ __launch_bounds__(1024) void k_router_wmax(const uint16_t* wr, int E,
   }
 }
 
+// y = residual + the nsplit partial sums of each split tile of a kEpiY
+// launch, added in split order (deterministic): block b takes row b % BM of
+// split tile b / BM, one column per thread. Plain float accesses: y and the
+// residual are caller pointers with no alignment promise beyond float's.
+__global__ __launch_bounds__(256) void k_ytiles(Dense a, const float* res) {
+  const int j = blockIdx.x / BM, r = blockIdx.x % BM, L = a.nfull + j;
+  int mt, quad;
+  tile_of(L, a.mtiles, a.nquads, mt, quad);
+  const int t = mt * BM + r, n = 256 * quad + threadIdx.x;
+  if (t >= a.T || n >= a.nvalid) return;
+  const size_t tsz = (size_t)BM * 256, e = (size_t)r * 256 + threadIdx.x;
+  const size_t i = (size_t)t * a.ostride + n;
+  float v = res ? res[i] : 0.f;
+  for (int k = 0; k < a.nsplit; ++k) v += a.part[((size_t)k * a.nrem + j) * tsz + e];
+  ((float*)a.out)[i] = v;
+}
+
 template <int WF, int EPI>
 int launch_dense(const Dense& a, hipStream_t st) {
-  const unsigned nblk = (unsigned)(a.mtiles * a.nquads);
+  const unsigned nblk = (unsigned)(EPI == kEpiY ? a.nfull + a.nrem * a.nsplit : a.mtiles * a.nquads);
   if (nblk == 0) return 0;
   hipLaunchKernelGGL((k_dense<WF, EPI>), dim3(nblk), dim3(NTH), 0, st, a);
   LMOE_HIP(hipGetLastError());
@@ -1204,7 +1273,31 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     a.A2 = AMat{p.hsb, (size_t)2 * Fs, Fs, Fs};
     a.T = T; a.mtiles = mtiles; a.ntiles = h->g_u16.tiles; a.nquads = (a.ntiles + NTW - 1) / NTW;
     a.out = y; a.ostride = H; a.nvalid = H; a.res = norm ? x : nullptr;
+    // One block per CU at a time. Every tile is split along k into ns
+    // blocks, ns minimising rounds of the chip per split plus a small charge
+    // per split for writing and re-reading its partial sums (as many as the
+    // expert outputs' buffer, dead once combined, holds). Splitting every
+    // tile (rather than only those of a last, partial round) also evens out
+    // the blocks' run times, which memory contention spreads.
+    const int nblk0 = mtiles * a.nquads;
+    const size_t cap = (size_t)p.tmax * K * L / ((size_t)nblk0 * BM * 256);
+    const int smax = (int)std::max<size_t>(1, std::min<size_t>(8, cap));
+    int ns = 1;
+    double best = 1e30;
+    for (int c = 1; c <= smax; ++c) {
+      const double rounds = (double)((nblk0 * c + h->ncu - 1) / h->ncu);
+      const double cost = rounds / c + 0.02 * c;
+      if (cost < best - 1e-9) { best = cost; ns = c; }
+    }
+    a.nsplit = ns;
+    a.nfull = ns == 1 ? nblk0 : 0;
+    a.nrem = ns == 1 ? 0 : nblk0;
+    a.part = p.o;
     if (int rc = launch_dense<kF16, kEpiY>(a, st)) return rc;
+    if (a.nsplit > 1) {
+      hipLaunchKernelGGL(k_ytiles, dim3(a.nrem * BM), dim3(256), 0, st, a, norm ? x : nullptr);
+      LMOE_HIP(hipGetLastError());
+    }
   }
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[8], st));
   return 0;

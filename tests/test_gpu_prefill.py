@@ -170,6 +170,22 @@ def test_tiny_prefill_block():
     print("  update rel L2 %.3g max/rms %.3g" % (rel, mx), flush=True)
 
 
+def test_prefill_u_split_along_k():
+    """latent 256 and top-8: the U + shared-down GEMM has 2 token tiles
+    (fewer than a round of the chip) and room for 6 partial sums per tile, so
+    it splits k six ways; the boundaries fall inside U, across the U /
+    shared-down seam and inside the shared down, and the last split has no U
+    stage at all. Every token is checked."""
+    w = wl.Workload("u_split", 256, 256, 32, 8, 4, 128, 192, 8, 200)
+    c = Case(w, seed=11, tokens=200)
+    layer = make_layer(c, 200)
+    for T in (200, 137):
+        print("case u_split prefill T", T, flush=True)
+        got, dbg = run(layer, w, c.x[:T])
+        check_routing(c, dbg, T)
+        check_outputs(c, got, dbg, np.arange(T))
+
+
 # ---------------------------------------------------------------------------
 # 145B / 120B shapes, routing over all tokens, outputs on a sample
 
