@@ -37,12 +37,13 @@ PREFILL_PHASES = ["route", "permute", "d", "shared_gate_up", "expert_gate_up", "
                   "combine", "u_shared_down"]
 PREFILL_KERNELS = ["k_prep + k_dense<BF16,Logits> + k_select", "k_perm_*", "k_dense<F16,F16> (D)",
                    "k_dense<BF16,SwigluB2> (shared gate/up)", "k_grouped<GateUp>",
-                   "k_grouped<Down>", "k_combine", "k_dense<F16,Y> (U + shared down)"]
+                   "k_grouped<Down>", "k_combine",
+                   "k_dense<F16,Y> (U + shared down, split along k) + k_ytiles (split sums)"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_145b_t4_traffic.json")
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_145b_t4096_traffic.json")
 # kernel of each prefill phase as rocprofv3 names it (D and U on fp16 weights)
 PREFILL_KERNEL_IDS = ["k_select", "k_perm_scan", "k_dense<5, 1>", "k_dense<3, 2>", "k_grouped<0>",
-                      "k_grouped<1>", "k_combine", "k_dense<5, 3>"]
+                      "k_grouped<1>", "k_combine", ["k_dense<5, 3>", "k_ytiles"]]
 
 
 def log(*a):
@@ -109,9 +110,10 @@ def phase_bytes(w, idx, labels):
 
 
 def measured_traffic(kernel, workload, path=TRAFFIC_FILE):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None when there is none or the kernel source has changed
-    since the counters were taken."""
+    """HBM bytes per launch of `kernel` (a name, or a list of names whose
+    launches make up one phase: their bytes add) from the committed rocprofv3
+    counter summary, or None when there is none or the kernel source has
+    changed since the counters were taken."""
     import hashlib
     try:
         with open(path) as f:
@@ -121,8 +123,9 @@ def measured_traffic(kernel, workload, path=TRAFFIC_FILE):
         return None
     if t.get("workload") != workload or hashlib.sha256(src).hexdigest() != t["source_sha256"]:
         return None
-    k = t["kernels"].get(kernel)
-    return None if k is None else k["traffic_bytes"]
+    names = kernel if isinstance(kernel, list) else [kernel]
+    ks = [t["kernels"].get(n) for n in names]
+    return None if any(k is None for k in ks) else sum(k["traffic_bytes"] for k in ks)
 
 
 def prefill_flops(w, idx, labels):

@@ -478,12 +478,13 @@ struct Dense {
   size_t ostride;
   int nvalid;
   const float* res;   // kEpiY: residual rows [T][ostride] or null
-  // kEpiY: the first nfull logical tiles (whole rounds of the chip) run
-  // whole; each of the remaining nrem runs as nsplit blocks along k. Split
-  // sp covers a balanced share of the stages of W then W2 (a W2 stage, bf16
-  // in two parts, counts twice) and, with nsplit > 1, writes its BM x 256
+  // kEpiY and kEpiLogits: the first nfull logical tiles run whole; each of
+  // the remaining nrem runs as nsplit blocks along k. Split sp covers a
+  // balanced share of the stages of W (kEpiY: then W2, a W2 stage, bf16 in
+  // two parts, counting twice). With nsplit > 1, kEpiY writes its BM x 256
   // sum to part + (sp * nrem + j) * BM * 256 for the j-th split tile, with
-  // no residual; k_ytiles adds them up.
+  // no residual (k_ytiles adds them up); kEpiLogits writes its sum to
+  // out + sp * T * ostride (k_select adds them up).
   int nfull, nrem, nsplit;
   float* part;
 };
@@ -510,10 +511,11 @@ template <int WF, int EPI>
 __global__ __launch_bounds__(NTH) void k_dense(Dense a) {
   __shared__ __align__(16) uint8_t smem[2 * kStage];
   __shared__ int arow[BM];
+  constexpr bool SPLIT = EPI == kEpiY || EPI == kEpiLogits;
   const int nblk0 = a.mtiles * a.nquads;
   int L = 0, sp = 0, nsp = 1;
-  if (EPI != kEpiY || (int)blockIdx.x < a.nfull) {
-    L = xcd_order(blockIdx.x, EPI == kEpiY ? a.nfull : nblk0);
+  if (!SPLIT || (int)blockIdx.x < a.nfull) {
+    L = xcd_order(blockIdx.x, SPLIT ? a.nfull : nblk0);
   } else {
     // split blocks follow the whole tiles (nfull is a multiple of 8, so the
     // XCD of a block is still its index modulo 8); the split is slowest
@@ -544,6 +546,10 @@ __global__ __launch_bounds__(NTH) void k_dense(Dense a) {
     const auto w2_stage = [&](int c) { return min(n2, max(0, (c - n1 + 1) / 2)); };
     gemm_wave<WF>(a.W, tile, b_on, nmb, a.A, arow, smem, acc, min(c0, n1), min(c1, n1));
     gemm_wave<kBF16>(a.W2, tile, b_on, nmb, a.A2, arow, smem, acc, w2_stage(c0), w2_stage(c1));
+  } else if constexpr (EPI == kEpiLogits) {
+    const int n1 = n_stages<WF>(a.W);
+    gemm_wave<WF>(a.W, tile, b_on, nmb, a.A, arow, smem, acc,
+                  (int)((long long)n1 * sp / nsp), (int)((long long)n1 * (sp + 1) / nsp));
   } else {
     gemm_wave<WF>(a.W, tile, b_on, nmb, a.A, arow, smem, acc);
   }
@@ -571,7 +577,7 @@ __global__ __launch_bounds__(NTH) void k_dense(Dense a) {
           const int n = 64 * tile + 32 * rg + (lane & 31);
           const float val = acc[mb][rg][v];
           if constexpr (EPI == kEpiLogits) {
-            if (n < a.nvalid) ((float*)a.out)[(size_t)t * a.ostride + n] = val;
+            if (n < a.nvalid) ((float*)a.out)[((size_t)sp * a.T + t) * a.ostride + n] = val;
           } else if constexpr (EPI == kEpiF16) {
             ((_Float16*)a.out)[(size_t)t * a.ostride + n] = (_Float16)val;
           } else if (nsp > 1) {
@@ -728,7 +734,8 @@ __global__ __launch_bounds__(256) void k_prep(Prep a) {
 // Routing: certified candidates, fp64 rescoring, top-K, softmax.
 
 struct Select {
-  const float* logits;       // [T][Epad] fp32 router GEMM output
+  const float* logits;       // [nsplit][T][Epad] fp32 router GEMM partial sums
+  int nsplit;
   int Epad, T, E, H, K;
   const float* bias;         // [E]
   const float* x;            // [T][H] raw input rows
@@ -745,25 +752,29 @@ __device__ __forceinline__ double bf16_to_f64(uint32_t bits) {
   return (double)__uint_as_float(bits << 16);
 }
 
-// fp64 dot product of x row (fp32) and router row e (bf16), whole wave
-__device__ double dot64(const float* xr, const uint16_t* wrow, int H) {
+// The x row of a token in the registers of a wave (in fp64, exact): lane l
+// holds columns 8 l + 512 j .. + 7 for j < NJ (H <= 512 NJ), zeros past H.
+template <int NJ>
+struct XRow {
+  double v[NJ][8];   // the fp32 values, held converted for the fp64 products
+};
+
+template <int NJ>
+__device__ __forceinline__ XRow<NJ> load_xrow(const float* xr, int H) {
   const int lane = threadIdx.x & 63;
-  double s = 0.0;
-  for (int c = 8 * lane; c < H; c += 512) {
-    const float4 x0 = *(const float4*)(xr + c);
-    const float4 x1 = *(const float4*)(xr + c + 4);
-    const uint4 w = *(const uint4*)(wrow + c);
-    s = fma((double)x0.x, bf16_to_f64(w.x & 0xFFFFu), s);
-    s = fma((double)x0.y, bf16_to_f64(w.x >> 16), s);
-    s = fma((double)x0.z, bf16_to_f64(w.y & 0xFFFFu), s);
-    s = fma((double)x0.w, bf16_to_f64(w.y >> 16), s);
-    s = fma((double)x1.x, bf16_to_f64(w.z & 0xFFFFu), s);
-    s = fma((double)x1.y, bf16_to_f64(w.z >> 16), s);
-    s = fma((double)x1.z, bf16_to_f64(w.w & 0xFFFFu), s);
-    s = fma((double)x1.w, bf16_to_f64(w.w >> 16), s);
+  XRow<NJ> X;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int c = 8 * lane + 512 * j;
+    float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
+    if (c < H) {
+      x0 = *(const float4*)(xr + c);
+      x1 = *(const float4*)(xr + c + 4);
+    }
+    X.v[j][0] = x0.x; X.v[j][1] = x0.y; X.v[j][2] = x0.z; X.v[j][3] = x0.w;
+    X.v[j][4] = x1.x; X.v[j][5] = x1.y; X.v[j][6] = x1.z; X.v[j][7] = x1.w;
   }
-  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-  return s;
+  return X;
 }
 
 // wave arg-max over (value desc, index asc)
@@ -779,98 +790,225 @@ __device__ __forceinline__ void wave_argmax(double& v, int& i) {
 }
 
 constexpr int kMaxE = 1024;
-constexpr int kEPL = kMaxE / 64;   // experts per lane
 
+// Sum over the wave, every lane gets it: DPP exchanges within each row of
+// 16 lanes (xor 1, xor 2, half-row mirror, row mirror), then the four row
+// sums from lanes 0, 16, 32, 48, added in that order. Fixed order:
+// deterministic.
+__device__ __forceinline__ double dpp_f64(double v, int ctrl_id) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
+  switch (ctrl_id) {
+    case 0: lo = __builtin_amdgcn_update_dpp(0, lo, 0xB1, 0xF, 0xF, false);
+            hi = __builtin_amdgcn_update_dpp(0, hi, 0xB1, 0xF, 0xF, false); break;
+    case 1: lo = __builtin_amdgcn_update_dpp(0, lo, 0x4E, 0xF, 0xF, false);
+            hi = __builtin_amdgcn_update_dpp(0, hi, 0x4E, 0xF, 0xF, false); break;
+    case 2: lo = __builtin_amdgcn_update_dpp(0, lo, 0x141, 0xF, 0xF, false);
+            hi = __builtin_amdgcn_update_dpp(0, hi, 0x141, 0xF, 0xF, false); break;
+    default: lo = __builtin_amdgcn_update_dpp(0, lo, 0x140, 0xF, 0xF, false);
+             hi = __builtin_amdgcn_update_dpp(0, hi, 0x140, 0xF, 0xF, false); break;
+  }
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_f64(v, 0);
+  v += dpp_f64(v, 1);
+  v += dpp_f64(v, 2);
+  v += dpp_f64(v, 3);
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+// fp32 -> unsigned key with the same order (NaN lowest)
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if (f != f) return 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// NJ: 512-column chunks of a row (H <= 512 NJ); EPL: experts per lane
+// (E <= 64 EPL), so the registers fit the layer
+template <int NJ, int EPL>
 __global__ __launch_bounds__(256) void k_select(Select a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   if (t >= a.T) return;
-  // fp32 logits + bias, exactly in fp64
-  double v[kEPL];
+  // fp32 logits (the router GEMM's k-splits added in fp32, in split order:
+  // one more fp32 summation order of the same products) + bias, exactly in
+  // fp64; their fp32 roundings as ordered keys
+  double v[EPL];
+  uint32_t key[EPL];
 #pragma unroll
-  for (int i = 0; i < kEPL; ++i) {
+  for (int i = 0; i < EPL; ++i) {
     const int e = lane + 64 * i;
-    v[i] = e < a.E ? (double)a.logits[(size_t)t * a.Epad + e] + (double)a.bias[e] : -INFINITY;
-  }
-  // the K-th largest approximate logit: K rounds removing one maximum each
-  double vk = -INFINITY;
-  {
-    double u[kEPL];
-#pragma unroll
-    for (int i = 0; i < kEPL; ++i) u[i] = v[i];
-    for (int k = 0; k < a.K; ++k) {
-      double bv = -INFINITY;
-      int bi = 0x7FFFFFFF;
-#pragma unroll
-      for (int i = 0; i < kEPL; ++i) {
-        const int e = lane + 64 * i;
-        if (u[i] > bv) {
-          bv = u[i];
-          bi = e;
-        }
-      }
-      wave_argmax(bv, bi);
-      vk = bv;
-#pragma unroll
-      for (int i = 0; i < kEPL; ++i)
-        if (lane + 64 * i == bi) u[i] = -INFINITY;
+    if (e < a.E) {
+      float l = a.logits[(size_t)t * a.Epad + e];
+      for (int k = 1; k < a.nsplit; ++k) l += a.logits[((size_t)k * a.T + t) * a.Epad + e];
+      v[i] = (double)l + (double)a.bias[e];
+      key[i] = order_key((float)v[i]);
+    } else {
+      v[i] = -INFINITY;
+      key[i] = 0u;
     }
   }
+  // the K-th largest fp32-rounded value, bit by bit from the top: the
+  // largest key kt with at least K keys >= kt (ballots and popcounts, no
+  // lane exchanges). Rounding is monotone, so it is the rounding of the
+  // K-th largest v; one fp32 ulp (and a subnormal step) below it bounds
+  // that v from below.
+  uint32_t kt = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = kt | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) cnt += __popcll(__ballot(key[i] >= c));
+    if (cnt >= a.K) kt = c;
+  }
+  const float fk = key_float(kt);
+  const double vk = kt == 0u ? -INFINITY
+                  : isinf(fk) ? (double)fk
+                              : (double)fk - (fabs((double)fk) * 0x1p-23 + 0x1p-149);
   // every expert whose exact logit can reach the top K: its fp32 logit is
   // within 2 beta of the K-th largest (|fp32 - exact| <= beta for all e)
   const double beta = a.cbeta * a.xnorm[t] * *a.wmax + 1e-30;
   const double thr = vk - 2.0 * beta;
   const double rt = (double)a.r[t];
-  const float* xr = a.x + (size_t)t * a.H;
-  double ex[kEPL];
+  const XRow<NJ> X = load_xrow<NJ>(a.x + (size_t)t * a.H, a.H);   // read once for every candidate
+  unsigned long long cm[EPL];                              // candidates, per slot (uniform)
+  int nc = 0;
 #pragma unroll
-  for (int i = 0; i < kEPL; ++i) ex[i] = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kEPL; ++i) {
-    unsigned long long m = __ballot(v[i] >= thr);
-    while (m) {
-      const int src = __builtin_ctzll(m);
-      m &= m - 1;
-      const int e = src + 64 * i;
-      const double l = dot64(xr, a.wr + (size_t)e * a.H, a.H) * rt + (double)a.bias[e];
-      if (lane == src) ex[i] = l;
-    }
+  for (int i = 0; i < EPL; ++i) {
+    cm[i] = __ballot(lane + 64 * i < a.E && v[i] >= thr);
+    nc += __popcll(cm[i]);
   }
-  // top K of the exact logits; lane k keeps the k-th. Taken experts and
-  // e >= E are NaN (never chosen); experts outside the candidate set stay at
-  // -inf, so K distinct valid experts come out even for rows with NaN logits.
+  // the candidate after expert e (or -1): the next set bit in slot order
+  const auto next_cand = [&](int e) {
+    int i0 = (e + 1) >> 6;
+    unsigned long long m0 = i0 < EPL ? cm[i0] & (~0ull << ((e + 1) & 63)) : 0ull;
+    for (int i = i0; i < EPL; ++i) {
+      const unsigned long long m = i == i0 ? m0 : cm[i];
+      if (m) return 64 * i + __builtin_ctzll(m);
+    }
+    return -1;
+  };
+  // the lane's router words of expert e: columns 8 lane + 512 j .. + 7
+  const auto load_row = [&](int e, uint4 (&w)[NJ]) {
 #pragma unroll
-  for (int i = 0; i < kEPL; ++i)
-    if (lane + 64 * i >= a.E) ex[i] = NAN;
+    for (int j = 0; j < NJ; ++j) {
+      const int c = 8 * lane + 512 * j;
+      w[j] = c < a.H ? *(const uint4*)(a.wr + (size_t)e * a.H + c) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  // exact fp64 logits of the candidates, in expert order; the next
+  // candidate's router row is loaded while the current one's dot product
+  // runs. Lane c keeps candidate c (c < 64); ex[] keeps them by expert.
+  double ex[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) ex[i] = -INFINITY;
+  double cl = -INFINITY;
+  int ce = 0x7FFFFFFF;
+  bool nan_seen = false;
+  int e = next_cand(-1), c = 0;
+  uint4 wc[NJ];
+  if (e >= 0) load_row(e, wc);
+  while (e >= 0) {
+    const int en = next_cand(e);
+    uint4 wn[NJ];
+    if (en >= 0) load_row(en, wn);
+    double sd = 0.0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const uint4 w = wc[j];
+      sd = fma(X.v[j][0], bf16_to_f64(w.x & 0xFFFFu), sd);
+      sd = fma(X.v[j][1], bf16_to_f64(w.x >> 16), sd);
+      sd = fma(X.v[j][2], bf16_to_f64(w.y & 0xFFFFu), sd);
+      sd = fma(X.v[j][3], bf16_to_f64(w.y >> 16), sd);
+      sd = fma(X.v[j][4], bf16_to_f64(w.z & 0xFFFFu), sd);
+      sd = fma(X.v[j][5], bf16_to_f64(w.z >> 16), sd);
+      sd = fma(X.v[j][6], bf16_to_f64(w.w & 0xFFFFu), sd);
+      sd = fma(X.v[j][7], bf16_to_f64(w.w >> 16), sd);
+    }
+    const double l = wave_sum_f64(sd) * rt + (double)a.bias[e];
+    nan_seen |= l != l;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (e == lane + 64 * i) ex[i] = l;
+    if (lane == c) {
+      cl = l;
+      ce = e;
+    }
+    ++c;
+    if (en >= 0) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) wc[j] = wn[j];
+    }
+    e = en;
+  }
   double kv = 0.0, top = 0.0;
   int ki = 0;
-  for (int k = 0; k < a.K; ++k) {
-    double bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+  bool mine = false;   // this lane writes output slot `slot`
+  int slot = 0;
+  if (nc >= a.K && nc <= 64 && !nan_seen) {
+    // rank of lane c's candidate among all: larger logit first, then lower
+    // expert index; the K best go to slots 0 .. K-1
+    int rank = 0;
+    top = -INFINITY;
+    for (int j = 0; j < nc; ++j) {
+      const double lj = readlane_f64(cl, j);
+      const int ej = __builtin_amdgcn_readlane(ce, j);
+      top = fmax(top, lj);
+      rank += (lj > cl || (lj == cl && ej < ce)) ? 1 : 0;
+    }
+    mine = lane < nc && rank < a.K;
+    slot = rank;
+    kv = cl;
+    ki = ce;
+  } else {
+    // general case (more than 64 candidates, fewer than K, or a NaN): top K
+    // of the exact logits by K wave arg-max rounds; lane k keeps the k-th.
+    // Taken experts and e >= E are NaN (never chosen); experts outside the
+    // candidate set stay at -inf, so K distinct valid experts come out even
+    // for rows with NaN logits.
 #pragma unroll
-    for (int i = 0; i < kEPL; ++i) {
-      const int e = lane + 64 * i;
-      if (ex[i] > bv || (ex[i] == bv && e < bi)) {
-        bv = ex[i];
-        bi = e;
+    for (int i = 0; i < EPL; ++i)
+      if (lane + 64 * i >= a.E) ex[i] = NAN;
+    for (int k = 0; k < a.K; ++k) {
+      double bv = -INFINITY;
+      int bi = 0x7FFFFFFF;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int ee = lane + 64 * i;
+        if (ex[i] > bv || (ex[i] == bv && ee < bi)) {
+          bv = ex[i];
+          bi = ee;
+        }
       }
-    }
-    wave_argmax(bv, bi);
-    if (k == 0) top = bv;
-    if (lane == k) {
-      kv = bv;
-      ki = bi;
-    }
+      wave_argmax(bv, bi);
+      if (k == 0) top = bv;
+      if (lane == k) {
+        kv = bv;
+        ki = bi;
+      }
 #pragma unroll
-    for (int i = 0; i < kEPL; ++i)
-      if (lane + 64 * i == bi) ex[i] = NAN;
+      for (int i = 0; i < EPL; ++i)
+        if (lane + 64 * i == bi) ex[i] = NAN;
+    }
+    mine = lane < a.K;
+    slot = lane;
   }
-  const double z = lane < a.K ? exp(kv - top) : 0.0;
-  double zs = z;
-  for (int o = 32; o > 0; o >>= 1) zs += __shfl_xor(zs, o);
-  if (lane < a.K) {
-    a.idx[(size_t)t * a.K + lane] = ki;
-    a.w[(size_t)t * a.K + lane] = (float)(z / zs);
+  const double z = mine ? exp(kv - top) : 0.0;
+  const double zs = wave_sum_f64(z);
+  if (mine) {
+    a.idx[(size_t)t * a.K + slot] = ki;
+    a.w[(size_t)t * a.K + slot] = (float)(z / zs);
   }
 }
 
@@ -918,12 +1056,19 @@ __global__ __launch_bounds__(kMaxE) void k_perm_scan(Perm a) {
   __shared__ int sp[kMaxE];
   const int j = threadIdx.x;
   if (j < a.E) {
+    // running count over the chunks, 16 chunk loads in flight at a time
     int cnt = 0;
-    for (int c = 0; c < a.nchunk; ++c) {
-      const size_t i = (size_t)c * a.E + j;
-      const int v = a.ccnt[i];
-      a.cbase[i] = cnt;
-      cnt += v;
+    for (int c0 = 0; c0 < a.nchunk; c0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        v[u] = c0 + u < a.nchunk ? a.ccnt[(size_t)(c0 + u) * a.E + j] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (c0 + u < a.nchunk) {
+          a.cbase[(size_t)(c0 + u) * a.E + j] = cnt;
+          cnt += v[u];
+        }
     }
     a.expert_count[j] = cnt;
   }
@@ -1078,10 +1223,12 @@ __global__ __launch_bounds__(1024) void k_router_wmax(const uint16_t* wr, int E,
   }
 }
 
-// y = residual + the nsplit partial sums of each split tile of a kEpiY
-// launch, added in split order (deterministic): block b takes row b % BM of
-// split tile b / BM, one column per thread. Plain float accesses: y and the
-// residual are caller pointers with no alignment promise beyond float's.
+// y = residual + the NS partial sums of each split tile of a kEpiY launch,
+// added in split order (deterministic): block b takes row b % BM of split
+// tile b / BM, one column per thread; the NS loads are issued together.
+// Plain float accesses: y and the residual are caller pointers with no
+// alignment promise beyond float's.
+template <int NS>
 __global__ __launch_bounds__(256) void k_ytiles(Dense a, const float* res) {
   const int j = blockIdx.x / BM, r = blockIdx.x % BM, L = a.nfull + j;
   int mt, quad;
@@ -1090,14 +1237,19 @@ __global__ __launch_bounds__(256) void k_ytiles(Dense a, const float* res) {
   if (t >= a.T || n >= a.nvalid) return;
   const size_t tsz = (size_t)BM * 256, e = (size_t)r * 256 + threadIdx.x;
   const size_t i = (size_t)t * a.ostride + n;
+  float p[NS];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) p[k] = a.part[((size_t)k * a.nrem + j) * tsz + e];
   float v = res ? res[i] : 0.f;
-  for (int k = 0; k < a.nsplit; ++k) v += a.part[((size_t)k * a.nrem + j) * tsz + e];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) v += p[k];
   ((float*)a.out)[i] = v;
 }
 
 template <int WF, int EPI>
 int launch_dense(const Dense& a, hipStream_t st) {
-  const unsigned nblk = (unsigned)(EPI == kEpiY ? a.nfull + a.nrem * a.nsplit : a.mtiles * a.nquads);
+  const unsigned nblk = (unsigned)(EPI == kEpiY || EPI == kEpiLogits ? a.nfull + a.nrem * a.nsplit
+                                                                     : a.mtiles * a.nquads);
   if (nblk == 0) return 0;
   hipLaunchKernelGGL((k_dense<WF, EPI>), dim3(nblk), dim3(NTH), 0, st, a);
   LMOE_HIP(hipGetLastError());
@@ -1183,18 +1335,29 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     LMOE_HIP(hipEventRecord(h->ev_join, h->aux));
   }
   // router logits
+  int rsplit = 1;
   {
     Dense a{};
     a.W = WMat{h->router_m, h->g_router_m, 0, 1};
     a.A = AMat{p.xb, (size_t)2 * H, H, H};
     a.T = T; a.mtiles = mtiles; a.ntiles = h->g_router_m.tiles; a.nquads = (a.ntiles + NTW - 1) / NTW;
-    a.out = p.logits; a.ostride = Epad; a.nvalid = E;
+    a.ostride = Epad; a.nvalid = E;
+    // split k so the launch fills the chip; the partial logits go to the
+    // expert outputs' buffer, unused until the expert GEMMs
+    const int nblk0 = mtiles * a.nquads;
+    const size_t cap = (size_t)p.tmax * K * L / ((size_t)T * Epad);
+    rsplit = (int)std::max<size_t>(1, std::min<size_t>({(size_t)8, cap, (size_t)std::max(1, h->ncu / nblk0)}));
+    a.nsplit = rsplit;
+    a.nfull = rsplit == 1 ? nblk0 : 0;
+    a.nrem = rsplit == 1 ? 0 : nblk0;
+    a.out = rsplit == 1 ? p.logits : p.o;
     if (int rc = launch_dense<kBF16, kEpiLogits>(a, st)) return rc;
   }
   // selection
   {
     Select a{};
-    a.logits = p.logits; a.Epad = Epad; a.T = T; a.E = E; a.H = H; a.K = K;
+    a.logits = rsplit == 1 ? p.logits : p.o; a.nsplit = rsplit;
+    a.Epad = Epad; a.T = T; a.E = E; a.H = H; a.K = K;
     a.bias = h->bias; a.x = x; a.r = p.r; a.xnorm = p.xnorm; a.wmax = p.wmax;
     a.wr = (const uint16_t*)h->router_rm;
     // |fp32 logit - exact| <= beta: 2H bf16 x bf16 products, each exact,
@@ -1204,7 +1367,17 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     // rounded (2^-24); sum |x_i w_i| <= |x|_2 |w|_2. Margin 2%.
     a.cbeta = 1.02 * (2.0 * (2.0 * H + 1.0) * ldexp(1.0, -24) + ldexp(1.0, -15));
     a.idx = p.idx; a.w = p.w;
-    hipLaunchKernelGGL(k_select, dim3((T + 3) / 4), dim3(256), 0, st, a);
+    const dim3 g((T + 3) / 4), b(256);
+    const int nj = (H + 511) / 512;
+    if (E <= 512) {
+      if (nj <= 4) hipLaunchKernelGGL((k_select<4, 8>), g, b, 0, st, a);
+      else if (nj == 5) hipLaunchKernelGGL((k_select<5, 8>), g, b, 0, st, a);
+      else hipLaunchKernelGGL((k_select<8, 8>), g, b, 0, st, a);
+    } else {
+      if (nj <= 4) hipLaunchKernelGGL((k_select<4, 16>), g, b, 0, st, a);
+      else if (nj == 5) hipLaunchKernelGGL((k_select<5, 16>), g, b, 0, st, a);
+      else hipLaunchKernelGGL((k_select<8, 16>), g, b, 0, st, a);
+    }
     LMOE_HIP(hipGetLastError());
   }
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[1], st));
@@ -1295,7 +1468,17 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     a.part = p.o;
     if (int rc = launch_dense<kF16, kEpiY>(a, st)) return rc;
     if (a.nsplit > 1) {
-      hipLaunchKernelGGL(k_ytiles, dim3(a.nrem * BM), dim3(256), 0, st, a, norm ? x : nullptr);
+      const float* res = norm ? x : nullptr;
+      const dim3 g(a.nrem * BM), b(256);
+      switch (a.nsplit) {
+        case 2: hipLaunchKernelGGL(k_ytiles<2>, g, b, 0, st, a, res); break;
+        case 3: hipLaunchKernelGGL(k_ytiles<3>, g, b, 0, st, a, res); break;
+        case 4: hipLaunchKernelGGL(k_ytiles<4>, g, b, 0, st, a, res); break;
+        case 5: hipLaunchKernelGGL(k_ytiles<5>, g, b, 0, st, a, res); break;
+        case 6: hipLaunchKernelGGL(k_ytiles<6>, g, b, 0, st, a, res); break;
+        case 7: hipLaunchKernelGGL(k_ytiles<7>, g, b, 0, st, a, res); break;
+        default: hipLaunchKernelGGL(k_ytiles<8>, g, b, 0, st, a, res); break;
+      }
       LMOE_HIP(hipGetLastError());
     }
   }
