@@ -42,8 +42,10 @@ PREFILL_KERNELS = ["k_prep + k_dense<BF16,Logits> + k_select", "k_perm_*", "k_de
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_145b_t4_traffic.json")
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_145b_t4096_traffic.json")
 # kernel of each prefill phase as rocprofv3 names it (D and U on fp16 weights)
-PREFILL_KERNEL_IDS = ["k_select", "k_perm_scan", "k_dense<5, 1>", "k_dense<3, 2>", "k_grouped<0>",
-                      "k_grouped<1>", "k_combine", ["k_dense<5, 3>", "k_ytiles"]]
+PREFILL_KERNEL_IDS = [["k_prep", "k_dense<3, 0>", "k_select<5, 8>"],
+                      ["k_perm_mask", "k_perm_scan", "k_perm_scatter"], "k_dense<5, 1>",
+                      "k_dense<3, 2>", "k_grouped<0>", "k_grouped<1>", "k_combine",
+                      ["k_dense<5, 3>", "k_ytiles<4>"]]
 
 
 def log(*a):

@@ -212,6 +212,13 @@ __device__ __forceinline__ ARows<WF> a_rows(const AMat& A, const int* arow) {
   return R;
 }
 
+// First tile row of activation piece i (its rows are that one and the next
+// NTH / PPR - 1; the same rows in every part).
+template <int WF>
+__host__ __device__ constexpr int piece_row_lo(int i) {
+  return ((NTH * i) % (BM * Fm<WF>::PPR)) / Fm<WF>::PPR;
+}
+
 // Issues the loads of stage s: the activation pieces (all threads); for the
 // wave pair of a weight tile, alternate code slots each plus, from both, the
 // scale word of lane-chunk `lane` (row group lane/16, row lane%16). Every
@@ -223,8 +230,9 @@ __device__ __forceinline__ ARows<WF> a_rows(const AMat& A, const int* arow) {
 // issues the loads of stage nst - 1 with an empty weight resource: its weight loads
 // return zeros without a memory access and its activation loads hit the
 // lines the same thread just fetched; no branch, so the compiler's counts of
-// loads in flight stay exact.
-template <int WF, int BAUX>
+// loads in flight stay exact. Only the pieces of the first SB 32-token
+// blocks are staged (the rest of the tile is never read).
+template <int WF, int BAUX, int SB>
 __device__ __forceinline__ void fetch(const WMat& W, int tile, const AMat& A, const ARows<WF>& ar,
                                       int s, int nst, Reg<WF>& R) {
   const bool live = s < nst;
@@ -237,7 +245,8 @@ __device__ __forceinline__ void fetch(const WMat& W, int tile, const AMat& A, co
   const int col0 = sm * F::SCOLS;
   const size_t aoff = (size_t)mat * A.kmat + min(col0, A.kmat - 8 - ar.c);
 #pragma unroll
-  for (int i = 0; i < F::PPT; ++i) R.a[i] = *(const uint4*)(ar.p[i] + aoff);
+  for (int i = 0; i < F::PPT; ++i)
+    if (piece_row_lo<WF>(i) < 32 * SB) R.a[i] = *(const uint4*)(ar.p[i] + aoff);
   const int cpm = (kmat + F::CC - 1) / F::CC;
   const int ss = col0 / kSSCols, cin0 = (col0 % kSSCols) / F::CC;
   const int ncs = ss_code_slots(WF, min(kSSCols, kmat - ss * kSSCols));
@@ -258,7 +267,7 @@ __device__ __forceinline__ void fetch(const WMat& W, int tile, const AMat& A, co
   }
 }
 
-template <int WF>
+template <int WF, int SB>
 __device__ __forceinline__ void store(uint8_t* st, Reg<WF>& R, const AMat& A, const ARows<WF>& ar, int s) {
   using F = Fm<WF>;
   const int spm = (A.kmat + F::SCOLS - 1) / F::SCOLS;
@@ -267,6 +276,7 @@ __device__ __forceinline__ void store(uint8_t* st, Reg<WF>& R, const AMat& A, co
   uint16_t* As = (uint16_t*)(st + kAOff);
 #pragma unroll
   for (int i = 0; i < F::PPT; ++i) {
+    if (piece_row_lo<WF>(i) >= 32 * SB) continue;
     const int p = threadIdx.x + i * NTH;
     const int part = p / (BM * F::PPR), m = (p % (BM * F::PPR)) / F::PPR;
     // masked with an AND rather than a select: the loaded value is always
@@ -390,8 +400,10 @@ __device__ __forceinline__ void mfma_stage(const uint8_t* st, f16v (&acc)[MB][2]
 // unrolled NSET times, with one loop exit); the buffer is picked at run
 // time. Every thread of the block takes part in the staging and the
 // barriers (the range is the block's); the closing barrier also frees the
-// buffers for a following call. An empty range does nothing.
-template <int WF, int NMB, int BAUX, int NSET>
+// buffers for a following call. An empty range does nothing. Only the first
+// SB 32-token blocks of the tile are staged (SB >= the blocks any wave
+// computes on).
+template <int WF, int NMB, int BAUX, int NSET, int SB>
 __device__ __forceinline__ void gemm_loop(const WMat& W, int tile, bool b_on, const AMat& A,
                                           const int* arow, uint8_t* smem, f16v (&acc)[MB][2],
                                           int sb, int se) {
@@ -401,16 +413,16 @@ __device__ __forceinline__ void gemm_loop(const WMat& W, int tile, bool b_on, co
   const ARows<WF> ar = a_rows<WF>(A, arow);
   Reg<WF> r[NSET];
 #pragma unroll
-  for (int i = 0; i < NSET; ++i) fetch<WF, BAUX>(W, ld_tile, A, ar, sb + i, se, r[i]);
-  store<WF>(smem, r[0], A, ar, sb);
+  for (int i = 0; i < NSET; ++i) fetch<WF, BAUX, SB>(W, ld_tile, A, ar, sb + i, se, r[i]);
+  store<WF, SB>(smem, r[0], A, ar, sb);
   __syncthreads();
   // stage s: loads of s + NSET into the set stage s left, MFMAs of s, stores
   // of s + 1 (past the last stage, a stale set into the buffer no wave reads
   // again); the body has no branch
   const auto step = [&](int s, Reg<WF>& mine, Reg<WF>& next) {
-    fetch<WF, BAUX>(W, ld_tile, A, ar, s + NSET, se, mine);
+    fetch<WF, BAUX, SB>(W, ld_tile, A, ar, s + NSET, se, mine);
     if constexpr (NMB > 0) mfma_stage<WF, NMB>(smem + ((s - sb) & 1) * kStage, acc);
-    store<WF>(smem + ((s - sb + 1) & 1) * kStage, next, A, ar, min(s + 1, se - 1));
+    store<WF, SB>(smem + ((s - sb + 1) & 1) * kStage, next, A, ar, min(s + 1, se - 1));
     __syncthreads();
   };
   int s0 = sb;
@@ -437,9 +449,38 @@ __device__ __forceinline__ void gemm_wave(const WMat& W, int tile, bool b_on, in
                                           const int* arow, uint8_t* smem, f16v (&acc)[MB][2],
                                           int sb = 0, int se = -1) {
   if (se < 0) se = n_stages<WF>(W);
-  if (nmb >= 2) gemm_loop<WF, 2, BAUX, NSET>(W, tile, b_on, A, arow, smem, acc, sb, se);
-  else if (nmb == 1) gemm_loop<WF, 1, BAUX, NSET>(W, tile, b_on, A, arow, smem, acc, sb, se);
-  else gemm_loop<WF, 0, BAUX, NSET>(W, tile, b_on, A, arow, smem, acc, sb, se);
+  if (nmb >= 2) gemm_loop<WF, 2, BAUX, NSET, 4>(W, tile, b_on, A, arow, smem, acc, sb, se);
+  else if (nmb == 1) gemm_loop<WF, 1, BAUX, NSET, 4>(W, tile, b_on, A, arow, smem, acc, sb, se);
+  else gemm_loop<WF, 0, BAUX, NSET, 4>(W, tile, b_on, A, arow, smem, acc, sb, se);
+}
+
+// gemm_wave for a tile of `count` tokens (1..BM) that stages only the
+// 32-token blocks holding them: most expert pieces are short, and the
+// vector memory path is what the stages wait on. The wave of each pair that
+// covers tokens 0..63 computes min(2, blocks) blocks, the other the rest.
+template <int WF, int BAUX = 0, int NSET = 3>
+__device__ __forceinline__ void gemm_wave_count(const WMat& W, int tile, bool b_on, int count,
+                                                const AMat& A, const int* arow, uint8_t* smem,
+                                                f16v (&acc)[MB][2]) {
+  const int se = n_stages<WF>(W), blocks = min(4, (count + 31) / 32);
+  const bool lo = (wave_id() & 1) == 0;
+  switch (blocks) {
+    case 1:
+      if (lo) gemm_loop<WF, 1, BAUX, NSET, 1>(W, tile, b_on, A, arow, smem, acc, 0, se);
+      else gemm_loop<WF, 0, BAUX, NSET, 1>(W, tile, b_on, A, arow, smem, acc, 0, se);
+      break;
+    case 2:
+      if (lo) gemm_loop<WF, 2, BAUX, NSET, 2>(W, tile, b_on, A, arow, smem, acc, 0, se);
+      else gemm_loop<WF, 0, BAUX, NSET, 2>(W, tile, b_on, A, arow, smem, acc, 0, se);
+      break;
+    case 3:
+      if (lo) gemm_loop<WF, 2, BAUX, NSET, 3>(W, tile, b_on, A, arow, smem, acc, 0, se);
+      else gemm_loop<WF, 1, BAUX, NSET, 3>(W, tile, b_on, A, arow, smem, acc, 0, se);
+      break;
+    default:
+      gemm_loop<WF, 2, BAUX, NSET, 4>(W, tile, b_on, A, arow, smem, acc, 0, se);
+      break;
+  }
 }
 
 __device__ __forceinline__ void zero_acc(f16v (&acc)[MB][2]) {
@@ -623,7 +664,8 @@ template <int EPI>
 __global__ __launch_bounds__(NTH) void k_grouped(Grouped a) {
   __shared__ __align__(16) uint8_t smem[2 * kStage];
   __shared__ int arow[BM];
-  // piece p runs on XCD p % 8, all its weight-tile quads back to back
+  // piece p runs on XCD p % 8, all its weight-tile quads back to back (the
+  // pieces of a large expert spread over the XCDs, which balances them)
   const int bid = blockIdx.x, xcd = bid & 7, q = bid >> 3;
   const int p = xcd + 8 * (q / a.nquads), quad = q % a.nquads;
   if (p >= *a.npieces) return;
@@ -642,13 +684,12 @@ __global__ __launch_bounds__(NTH) void k_grouped(Grouped a) {
   const int lane = threadIdx.x & 63, wave = wave_id(), wm = wave & 1;
   const int tile = NTW * quad + (wave >> 1);
   const bool b_on = tile < a.ntiles;
-  const int nmb = min(MB, max(0, pc.count - WTOK * wm + 31) / 32);
   const uint8_t* base = a.experts + (size_t)e * a.estride;
   const WMat W{base + a.woff, a.g, 0, 1};
   f16v acc[MB][2];
   zero_acc(acc);
   // each expert's weights are streamed once per piece: non-temporal
-  gemm_wave<kFP4, kAuxNT>(W, tile, b_on, nmb, a.A, arow, smem, acc);
+  gemm_wave_count<kFP4, kAuxNT>(W, tile, b_on, pc.count, a.A, arow, smem, acc);
   if (!b_on) return;
   const float* ts = (const float*)(base + a.ts_off);
 
@@ -1054,6 +1095,8 @@ __global__ __launch_bounds__(256) void k_perm_mask(Perm a) {
 __global__ __launch_bounds__(kMaxE) void k_perm_scan(Perm a) {
   __shared__ int sc[kMaxE];
   __shared__ int sp[kMaxE];
+  __shared__ int sf[kMaxE];
+  __shared__ int sq[kMaxE];
   const int j = threadIdx.x;
   if (j < a.E) {
     // running count over the chunks, 16 chunk loads in flight at a time
@@ -1077,17 +1120,25 @@ __global__ __launch_bounds__(kMaxE) void k_perm_scan(Perm a) {
   const int e = j < a.E ? a.eorder[j] : 0;
   const int c_e = j < a.E ? a.expert_count[e] : 0;
   const int np = (c_e + BM - 1) / BM;
+  // the full pieces of all experts come first, then each expert's partial
+  // last piece: the grouped GEMMs dispatch their longest work items first
+  const int nf = c_e / BM, nq = np - nf;
   sc[j] = c_e;
   sp[j] = np;
+  sf[j] = nf;
+  sq[j] = nq;
   __syncthreads();
   for (int o = 1; o < kMaxE; o <<= 1) {
     const int x0 = j >= o ? sc[j - o] : 0, x1 = j >= o ? sp[j - o] : 0;
+    const int x2 = j >= o ? sf[j - o] : 0, x3 = j >= o ? sq[j - o] : 0;
     __syncthreads();
     sc[j] += x0;
     sp[j] += x1;
+    sf[j] += x2;
+    sq[j] += x3;
     __syncthreads();
   }
-  const int start = sc[j] - c_e, pstart = sp[j] - np;
+  const int start = sc[j] - c_e, fstart = sf[j] - nf, qstart = sf[kMaxE - 1] + sq[j] - nq;
   if (j < a.E) {
     a.seg_start[e] = start;
     for (int i = 0; i < np; ++i) {
@@ -1096,7 +1147,7 @@ __global__ __launch_bounds__(kMaxE) void k_perm_scan(Perm a) {
       p.start = start + i * BM;
       p.count = min(BM, c_e - i * BM);
       p.pad = 0;
-      a.pieces[pstart + i] = p;
+      a.pieces[i < nf ? fstart + i : qstart] = p;
     }
     // the first expert of each label opens its group's segment
     const int lab = a.labels[e];
