@@ -150,7 +150,9 @@ struct PrefillWs {
   uint16_t* xl = nullptr;          // [T][G][ell] fp16
   uint16_t* hsb = nullptr;         // [T][2][Fs] shared hidden, bf16 parts
   uint16_t* h = nullptr;           // [T*K][F] fp16 expert hidden, sorted order
-  float* o = nullptr;              // [T*K][ell] weighted expert outputs
+  float* o = nullptr;              // [T*K][ell] weighted expert outputs (held as fp16, in
+                                   // the first half); the router and U k-splits put
+                                   // their fp32 partial sums here while it is unused
   uint16_t* s = nullptr;           // [T][G][ell] fp16 per-group sums
   double* wmax = nullptr;          // [1] max_e |Wr_e|_2
   int tmax = 0;                    // tokens the buffers hold (0: no prefill path)

@@ -710,7 +710,7 @@ __global__ __launch_bounds__(NTH) void k_grouped(Grouped a) {
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg) {
           const int n = 64 * tile + 32 * rg + (lane & 31);
-          ((float*)a.out)[pos * a.ostride + n] = acc[mb][rg][v] * sc;
+          ((_Float16*)a.out)[pos * a.ostride + n] = (_Float16)(acc[mb][rg][v] * sc);
         }
       }
     }
@@ -1179,7 +1179,7 @@ struct Combine {
   const int* idx;
   const int* inv;
   const uint8_t* labels;
-  const float* o;     // [T*K][L]
+  const _Float16* o;  // [T*K][L] weighted expert outputs, fp16
   _Float16* s;        // [T][G][L]
   int K, G, L;
 };
@@ -1200,11 +1200,12 @@ __global__ __launch_bounds__(256) void k_combine(Combine a) {
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int k = 0; k < a.K; ++k) {
         if (lab[k] != g) continue;
-        const float4 v = *(const float4*)(a.o + (size_t)pos[k] * a.L + 4 * q);
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
+        const uint2 raw = *(const uint2*)(a.o + (size_t)pos[k] * a.L + 4 * q);
+        const half2v v0 = __builtin_bit_cast(half2v, raw.x), v1 = __builtin_bit_cast(half2v, raw.y);
+        acc.x += (float)v0[0];
+        acc.y += (float)v0[1];
+        acc.z += (float)v1[0];
+        acc.w += (float)v1[1];
       }
       _Float16* d = a.s + ((size_t)t * a.G + g) * a.L + 4 * q;
       half2v h0 = {(_Float16)acc.x, (_Float16)acc.y};
@@ -1483,7 +1484,7 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[6], st));
   // combine
   {
-    Combine a{p.idx, p.inv, h->labels, p.o, (_Float16*)p.s, K, G, L};
+    Combine a{p.idx, p.inv, h->labels, (const _Float16*)p.o, (_Float16*)p.s, K, G, L};
     hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, st, a);
     LMOE_HIP(hipGetLastError());
   }
