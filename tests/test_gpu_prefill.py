@@ -147,6 +147,36 @@ def test_tiny_prefill_zero_rows_tie():
     check_outputs(c, got, dbg, np.arange(40))
 
 
+def test_tiny_prefill_nonfinite_rows():
+    """Rows of NaN, +inf and -inf: their logits are not finite, so the
+    selection has fewer than K finite values and its threshold falls to
+    -inf. Every token must still get K distinct experts in [0, E) (only real
+    experts are candidates: the padded logit slots past E are never rescored,
+    so no router row past the table is read), and the finite rows keep the
+    oracle's routing and outputs."""
+    w = wl.WORKLOADS["tiny"]
+    T = 40
+    x = wl.x(w, 0, 0, tokens=T)
+    bad = [3, 7, 11]
+    x[3] = np.nan
+    x[7] = np.inf
+    x[11] = -np.inf
+    good = np.setdiff1d(np.arange(T), bad)
+    with np.errstate(invalid="ignore"):          # the oracle's logits of the bad rows
+        c = Case(w, x=x, pack_tokens=good)
+    layer = make_layer(c, T)
+    print("case tiny non-finite rows T 40", flush=True)
+    got, dbg = run(layer, w, x)
+    idx = dbg["topk_idx"]
+    for t in range(T):
+        row = idx[t].tolist()
+        assert len(set(row)) == w.top_k and min(row) >= 0 and max(row) < w.n_experts, (t, row)
+    oidx, ow = oracle.select_topk(c.logits[good], w.top_k)
+    assert np.array_equal(idx[good], oidx)
+    assert np.max(np.abs(dbg["topk_w"][good] - ow)) <= 1e-6
+    check_outputs(c, got, dbg, good)
+
+
 def test_tiny_prefill_block():
     """x += layer(RMSNorm(x)) for T > 8."""
     w = wl.WORKLOADS["tiny"]
