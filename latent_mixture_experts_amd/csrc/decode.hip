@@ -979,7 +979,7 @@ __global__ __launch_bounds__(1024) void k_phase2(P2 a) {
 // no partials leave the block. A round runs spr slots with wps waves per
 // slot; wave w of a slot takes super-steps w, w + wps, ... of the ffn width
 // into one accumulator, and the slot's wave partials are added in w order
-// (wps = nss, one super-step per wave, unless the LDS is short).
+// (the launch uses wps = 1: one wave walks all of a slot's super-steps).
 
 constexpr size_t kLdsBytes = 160 * 1024;   // LDS of one CU
 
@@ -1289,12 +1289,15 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st, i
   P3 p3{};
   p3.d = d; p3.experts = h->experts; p3.gdn = h->g_dn; p3.stride = h->expert_stride;
   p3.gu_bytes = h->g_gu.bytes(); p3.ts_off = h->ts_off; p3.labels = h->labels; p3.ws = ws;
-  // as many slots per round as 16 waves and the LDS hold; a wave per
-  // super-step unless even one slot's waves do not fit
+  // one wave per slot, walking the slot's super-steps with the next one's
+  // loads in flight: 16 slots per round, so a group that drew up to 16
+  // distinct experts takes one round (three waves per slot, one per
+  // super-step, took two rounds for groups above five: 15.6 against 14.8 us
+  // at the 145B shape); fewer slots when the LDS is short
   const int nss3 = h->g_dn.nss;
   const size_t ol_bytes = (size_t)n * 64 * sizeof(float);
   auto lds3 = [&](int spr_, int wps_) { return (size_t)spr_ * wps_ * stage_bytes_f16<T>() + ol_bytes; };
-  int spr = 16 / nss3, wps = nss3;
+  int spr = 16, wps = 1;
   while (spr > 1 && lds3(spr, wps) > kLdsBytes) --spr;
   while (wps > 1 && lds3(spr, wps) > kLdsBytes) --wps;
   if (lds3(spr, wps) > kLdsBytes) {
