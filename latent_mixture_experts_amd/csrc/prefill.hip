@@ -63,6 +63,7 @@ constexpr int WTOK = 64;       // tokens per wave
 constexpr int MB = WTOK / 32;  // 32-token MFMA blocks per wave
 constexpr int NTW = 4;         // 64-row weight tiles per workgroup (two waves each)
 constexpr int CHUNK_T = 64;    // tokens per permutation chunk
+constexpr int kShortT = 32;    // expert pieces of at most this many tokens run in k_grouped_short
 
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -650,7 +651,7 @@ struct Grouped {
   Geom g;
   AMat A;
   const Piece* pieces;
-  const int* npieces;
+  const int* npieces;   // [0] pieces, [1] the first short one
   int ntiles, nquads, G, F;
   const int* perm;      // [T*K] sorted position -> assignment t*K + k
   const float* topk_w;  // [T*K]
@@ -668,7 +669,7 @@ __global__ __launch_bounds__(NTH) void k_grouped(Grouped a) {
   // pieces of a large expert spread over the XCDs, which balances them)
   const int bid = blockIdx.x, xcd = bid & 7, q = bid >> 3;
   const int p = xcd + 8 * (q / a.nquads), quad = q % a.nquads;
-  if (p >= *a.npieces) return;
+  if (p >= a.npieces[1]) return;                     // pieces of more than kShortT tokens
   const Piece pc = a.pieces[p];
   const int e = pc.expert;
   if (threadIdx.x < BM) {
@@ -714,6 +715,189 @@ __global__ __launch_bounds__(NTH) void k_grouped(Grouped a) {
         }
       }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Short pieces of the expert GEMMs (at most kShortT = 32 tokens). Most
+// experts draw few tokens (the median of the 145B prefill input is 10), and
+// in a 128-token tile such a piece leaves half the waves without MFMAs while
+// every wave pair stages and decodes the same weight tile. Here a 512-thread
+// workgroup takes 32 tokens x 512 weight rows: each of the 8 waves owns one
+// 64-row tile and reads its weights straight from memory into the registers
+// of its MFMA operands (the tiled stream holds the v_mfma_f32_32x32x16 B
+// operand of a lane as one 16-byte lane-chunk: whole 256-byte segments per
+// load), decodes them itself, and only the 32 activation rows go through
+// LDS. Activation and weight register sets rotate separately (three each),
+// so no load targets registers the MFMAs in flight read, and each load has
+// two stages to arrive; the body has no branch (empty weight resource past
+// the last stage or tile).
+
+constexpr int kSpNtw = 8;                              // weight tiles per workgroup, one per wave
+constexpr int kSpAst = Fm<kFP4>::SCOLS + 8;            // LDS row stride of the activations
+constexpr int kSpStage = kShortT * kSpAst * 2;         // LDS bytes per stage
+static_assert(kShortT * Fm<kFP4>::PPR == NTH, "one activation piece per thread");
+static_assert(Fm<kFP4>::SC == 1, "one chunk per stage");
+
+struct SpB {
+  uint4 b[2][2];   // raw FP4 words: row block nb (rows 32 nb .. + 31 of the tile), k-half kk
+  uint2 sc[2];     // the scale words of the lane's row in each row block
+};
+
+// weights of stage s (past nst or !b_on: an empty resource, zeros). For row
+// block nb and k-half kk lane l takes lane-chunk 16 (2 kk + l / 32) + l % 16
+// of row group 2 nb + (l % 32) / 16: columns 16 ks + 8 (l / 32) .. + 7 of row
+// 32 nb + l % 32 for the k-steps ks = kk (mod 2); the scale word from the
+// same lane-chunk of the scale slot.
+template <int BAUX>
+__device__ __forceinline__ void sp_fetch_b(const WMat& W, int tile, bool b_on, int s, int nst, SpB& R) {
+  using F = Fm<kFP4>;
+  const bool live = s < nst && b_on;
+  s = min(s, nst - 1);
+  const int lane = threadIdx.x & 63;
+  const int kmat = W.g.k;
+  const int spm = (kmat + F::SCOLS - 1) / F::SCOLS;
+  const int mat = s / spm, col0 = (s % spm) * F::SCOLS;
+  const int ss = col0 / kSSCols, cin0 = (col0 % kSSCols) / F::CC;
+  const int ncs = ss_code_slots(kFP4, min(kSSCols, kmat - ss * kSSCols));
+  const rsrc_t wt = rsrc(W.base + (size_t)mat * W.mat_bytes + (size_t)tile * W.g.tile_slots * kSlot,
+                         live ? (uint32_t)(W.g.tile_slots * kSlot) : 0u);
+  const int sso = ss * W.g.full * kSlot;
+  const int vb = ((lane & 31) >> 4) * kSlot + (16 * (lane >> 5) + (lane & 15)) * 16;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      R.b[nb][kk] = ldb<BAUX>(wt, vb, sso + (cin0 * 4 + 2 * nb) * kSlot + kk * 512);
+  const int vs = (16 * ((lane & 31) >> 4) + (lane & 15)) * 16 + 8 * cin0;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+    R.sc[nb] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                             wt, vs, sso + ncs * kSlot + nb * 512, BAUX));
+}
+
+// the thread's activation piece of stage s (row m, columns c .. c + 7 of the
+// stage; ap points at column c of the row, clamped into the row past k)
+__device__ __forceinline__ uint4 sp_fetch_a(const uint16_t* ap, int c, int kmat, int s, int nst) {
+  s = min(s, nst - 1);
+  const int spm = (kmat + Fm<kFP4>::SCOLS - 1) / Fm<kFP4>::SCOLS;
+  const int col0 = (s % spm) * Fm<kFP4>::SCOLS;
+  return *(const uint4*)(ap + min(col0, kmat - 8 - c));
+}
+
+__device__ __forceinline__ void sp_store(uint8_t* st, uint4 v, int kmat, int c, int m, bool rvalid, int s) {
+  const int spm = (kmat + Fm<kFP4>::SCOLS - 1) / Fm<kFP4>::SCOLS;
+  const int col0 = (s % spm) * Fm<kFP4>::SCOLS;
+  // an AND, not a select: the load cannot be sunk down to this store
+  const uint32_t mk = (rvalid && col0 + c < kmat) ? ~0u : 0u;
+  *(uint4*)((uint16_t*)st + m * kSpAst + c) = make_uint4(v.x & mk, v.y & mk, v.z & mk, v.w & mk);
+}
+
+// one stage: per k-step the 32-token activation fragment (read one k-step
+// ahead) against the two decoded weight fragments of the wave's tile
+__device__ __forceinline__ void sp_mfma(const uint8_t* st, const SpB& R, f16v (&acc)[2]) {
+  using F = Fm<kFP4>;
+  const int lane = threadIdx.x & 63, row = lane & 31, kh = lane >> 5;
+  const uint16_t* As = (const uint16_t*)st;
+  uint4 a[2];
+  a[0] = *(const uint4*)(As + row * kSpAst + 8 * kh);
+#pragma unroll
+  for (int ks = 0; ks < F::KS; ++ks) {
+    const int kk = ks & 1, b = ks >> 1;              // k-half, 32-column block of the chunk
+    if (ks + 1 < F::KS) a[(ks + 1) & 1] = *(const uint4*)(As + row * kSpAst + 16 * (ks + 1) + 8 * kh);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const uint4 bw = decode_b<kFP4>(R.b[nb][kk], R.sc[nb], b, b, 2 * kk + kh);
+      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a[ks & 1]),
+                                                       __builtin_bit_cast(half8, bw), acc[nb], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(NTH) void k_grouped_short(Grouped a) {
+  __shared__ __align__(16) uint8_t smem[2 * kSpStage];
+  __shared__ int arow[kShortT];
+  // short piece p runs on XCD p % 8, all its weight-tile octets back to back
+  const int nocts = (a.ntiles + kSpNtw - 1) / kSpNtw;
+  const int bid = blockIdx.x, xcd = bid & 7, q = bid >> 3;
+  const int p = a.npieces[1] + xcd + 8 * (q / nocts), oct = q % nocts;
+  if (p >= a.npieces[0]) return;
+  const Piece pc = a.pieces[p];
+  const int e = pc.expert;
+  if (threadIdx.x < kShortT) {
+    const int i = threadIdx.x;
+    int row = -1;
+    if (i < pc.count) {
+      const int pos = pc.start + i;
+      row = EPI == kGateUp ? (a.perm[pos] / a.K) * a.G + a.labels[e] : pos;
+    }
+    arow[i] = row;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int tile = kSpNtw * oct + wave;
+  const bool b_on = tile < a.ntiles;
+  const uint8_t* base = a.experts + (size_t)e * a.estride;
+  const WMat W{base + a.woff, a.g, 0, 1};
+  const int nst = n_stages<kFP4>(W), kmat = a.A.kmat;
+  const int c = 8 * (threadIdx.x % Fm<kFP4>::PPR), m = threadIdx.x / Fm<kFP4>::PPR;
+  const int arw = arow[m];
+  const bool rvalid = arw >= 0;
+  const uint16_t* ap = a.A.p + (size_t)max(arw, 0) * a.A.rs + c;
+  f16v acc[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[nb][v] = 0.f;
+  uint4 ra[3];
+  SpB rb[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) ra[i] = sp_fetch_a(ap, c, kmat, i, nst);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) sp_fetch_b<kAuxNT>(W, tile, b_on, i, nst, rb[i]);
+  sp_store(smem, ra[0], kmat, c, m, rvalid, 0);
+  __syncthreads();
+  // stage s with sets i = s % 3: weights of s + 2 into the set the MFMAs of
+  // s - 1 read, activations of s + 3 into the set stored at s - 1, the
+  // activations of s + 1 stored (past the end: a stale set into the buffer
+  // no wave reads again), the MFMAs of s
+  const auto step = [&](int s, int i) {
+    sp_fetch_b<kAuxNT>(W, tile, b_on, s + 2, nst, rb[(i + 2) % 3]);
+    ra[i] = sp_fetch_a(ap, c, kmat, s + 3, nst);
+    sp_store(smem + ((s + 1) & 1) * kSpStage, ra[(i + 1) % 3], kmat, c, m, rvalid, min(s + 1, nst - 1));
+    sp_mfma(smem + (s & 1) * kSpStage, rb[i], acc);
+    __syncthreads();
+  };
+  int s0 = 0;
+  for (; s0 + 3 <= nst; s0 += 3) {
+    step(s0, 0);
+    step(s0 + 1, 1);
+    step(s0 + 2, 2);
+  }
+  if (s0 < nst) step(s0, 0);
+  if (s0 + 1 < nst) step(s0 + 1, 1);
+  if (!b_on) return;
+  const float* ts = (const float*)(base + a.ts_off);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int i = acc_tok(lane, 0, v);
+    if (i >= pc.count) continue;
+    const size_t pos = (size_t)pc.start + i;
+    if constexpr (EPI == kGateUp) {
+      const float tg = ts[0], tu = ts[1];
+      const int f = 32 * tile + (lane & 31);
+      const float hv = silu(acc[0][v] * tg) * (acc[1][v] * tu);
+      ((_Float16*)a.out)[pos * a.ostride + f] = (_Float16)hv;
+    } else {
+      const float sc = a.topk_w[a.perm[pos]] * ts[2];
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg) {
+        const int n = 64 * tile + 32 * rg + (lane & 31);
+        ((_Float16*)a.out)[pos * a.ostride + n] = (_Float16)(acc[rg][v] * sc);
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1097,6 +1281,7 @@ __global__ __launch_bounds__(kMaxE) void k_perm_scan(Perm a) {
   __shared__ int sp[kMaxE];
   __shared__ int sf[kMaxE];
   __shared__ int sq[kMaxE];
+  __shared__ int ss_[kMaxE];
   const int j = threadIdx.x;
   if (j < a.E) {
     // running count over the chunks, 16 chunk loads in flight at a time
@@ -1120,25 +1305,33 @@ __global__ __launch_bounds__(kMaxE) void k_perm_scan(Perm a) {
   const int e = j < a.E ? a.eorder[j] : 0;
   const int c_e = j < a.E ? a.expert_count[e] : 0;
   const int np = (c_e + BM - 1) / BM;
-  // the full pieces of all experts come first, then each expert's partial
-  // last piece: the grouped GEMMs dispatch their longest work items first
+  // piece order: the full pieces of all experts, then the partial last
+  // pieces of more than kShortT tokens, then the short ones (the grouped
+  // GEMMs dispatch their longest work items first; the short pieces go to
+  // k_grouped_short)
   const int nf = c_e / BM, nq = np - nf;
+  const int nqs = (nq && c_e - nf * BM <= kShortT) ? 1 : 0, nqb = nq - nqs;
   sc[j] = c_e;
   sp[j] = np;
   sf[j] = nf;
-  sq[j] = nq;
+  sq[j] = nqb;
+  ss_[j] = nqs;
   __syncthreads();
   for (int o = 1; o < kMaxE; o <<= 1) {
     const int x0 = j >= o ? sc[j - o] : 0, x1 = j >= o ? sp[j - o] : 0;
     const int x2 = j >= o ? sf[j - o] : 0, x3 = j >= o ? sq[j - o] : 0;
+    const int x4 = j >= o ? ss_[j - o] : 0;
     __syncthreads();
     sc[j] += x0;
     sp[j] += x1;
     sf[j] += x2;
     sq[j] += x3;
+    ss_[j] += x4;
     __syncthreads();
   }
-  const int start = sc[j] - c_e, fstart = sf[j] - nf, qstart = sf[kMaxE - 1] + sq[j] - nq;
+  const int nbig = sf[kMaxE - 1] + sq[kMaxE - 1];   // pieces before the short ones
+  const int start = sc[j] - c_e, fstart = sf[j] - nf;
+  const int qstart = nqs ? nbig + ss_[j] - nqs : sf[kMaxE - 1] + sq[j] - nqb;
   if (j < a.E) {
     a.seg_start[e] = start;
     for (int i = 0; i < np; ++i) {
@@ -1155,7 +1348,8 @@ __global__ __launch_bounds__(kMaxE) void k_perm_scan(Perm a) {
     for (int g = prev + 1; g <= lab; ++g) a.group_off[g] = start;
     if (j == a.E - 1) {
       for (int g = lab + 1; g <= a.G; ++g) a.group_off[g] = sc[j];
-      *a.npieces = sp[j];
+      a.npieces[0] = sp[j];
+      a.npieces[1] = nbig;
     }
   }
 }
@@ -1456,6 +1650,7 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
   }
   // experts
   const unsigned maxp = (unsigned)prefill_max_pieces(T, K, E);
+  const unsigned maxshort = (unsigned)std::min(E, T * K);   // at most one short piece per expert
   {
     Grouped a{};
     a.experts = h->experts; a.estride = h->expert_stride; a.woff = 0; a.ts_off = h->ts_off;
@@ -1466,6 +1661,9 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     a.out = p.h; a.ostride = F;
     const unsigned grid = 8u * a.nquads * ((maxp + 7) / 8);
     hipLaunchKernelGGL(k_grouped<kGateUp>, dim3(grid), dim3(NTH), 0, st, a);
+    LMOE_HIP(hipGetLastError());
+    const unsigned gs = 8u * ((a.ntiles + kSpNtw - 1) / kSpNtw) * ((maxshort + 7) / 8);
+    hipLaunchKernelGGL(k_grouped_short<kGateUp>, dim3(gs), dim3(NTH), 0, st, a);
     LMOE_HIP(hipGetLastError());
   }
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[5], st));
@@ -1479,6 +1677,9 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     a.out = p.o; a.ostride = L;
     const unsigned grid = 8u * a.nquads * ((maxp + 7) / 8);
     hipLaunchKernelGGL(k_grouped<kDown>, dim3(grid), dim3(NTH), 0, st, a);
+    LMOE_HIP(hipGetLastError());
+    const unsigned gs = 8u * ((a.ntiles + kSpNtw - 1) / kSpNtw) * ((maxshort + 7) / 8);
+    hipLaunchKernelGGL(k_grouped_short<kDown>, dim3(gs), dim3(NTH), 0, st, a);
     LMOE_HIP(hipGetLastError());
   }
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[6], st));
