@@ -155,7 +155,7 @@ int create_impl(lmoe_t* h) {
     A(p.expert_count, sizeof(int) * E);
     A(p.group_off, sizeof(int) * (G + 1));
     A(p.pieces, prefill_piece_bytes() * prefill_max_pieces(d.max_tokens, K, E));
-    A(p.npieces, 2 * sizeof(int));
+    A(p.npieces, 3 * sizeof(int));
     A(p.perm, sizeof(int) * nk);
     A(p.inv, sizeof(int) * nk);
     A(p.xl, 2 * Tp * G * L);

@@ -144,7 +144,7 @@ struct PrefillWs {
   int* expert_count = nullptr;     // [E]
   int* group_off = nullptr;        // [G+1]
   void* pieces = nullptr;          // [max pieces] grouped-GEMM work list
-  int* npieces = nullptr;          // [2] pieces, index of the first short piece
+  int* npieces = nullptr;          // [3] pieces, first of at most 64 tokens, of at most 32
   int* perm = nullptr;             // [T*K]
   int* inv = nullptr;              // [T*K] assignment -> sorted position
   uint16_t* xl = nullptr;          // [T][G][ell] fp16

@@ -63,7 +63,7 @@ constexpr int WTOK = 64;       // tokens per wave
 constexpr int MB = WTOK / 32;  // 32-token MFMA blocks per wave
 constexpr int NTW = 4;         // 64-row weight tiles per workgroup (two waves each)
 constexpr int CHUNK_T = 64;    // tokens per permutation chunk
-constexpr int kShortT = 32;    // expert pieces of at most this many tokens run in k_grouped_short
+constexpr int kShortT = 32;    // expert pieces of at most 32 (64) tokens run in k_grouped_short<1> (<2>)
 
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -651,7 +651,7 @@ struct Grouped {
   Geom g;
   AMat A;
   const Piece* pieces;
-  const int* npieces;   // [0] pieces, [1] the first short one
+  const int* npieces;   // [0] pieces, [1] the first of at most 64 tokens, [2] of at most 32
   int ntiles, nquads, G, F;
   const int* perm;      // [T*K] sorted position -> assignment t*K + k
   const float* topk_w;  // [T*K]
@@ -669,7 +669,7 @@ __global__ __launch_bounds__(NTH) void k_grouped(Grouped a) {
   // pieces of a large expert spread over the XCDs, which balances them)
   const int bid = blockIdx.x, xcd = bid & 7, q = bid >> 3;
   const int p = xcd + 8 * (q / a.nquads), quad = q % a.nquads;
-  if (p >= a.npieces[1]) return;                     // pieces of more than kShortT tokens
+  if (p >= a.npieces[1]) return;                     // pieces of more than 64 tokens
   const Piece pc = a.pieces[p];
   const int e = pc.expert;
   if (threadIdx.x < BM) {
@@ -718,25 +718,26 @@ __global__ __launch_bounds__(NTH) void k_grouped(Grouped a) {
 }
 
 // ---------------------------------------------------------------------------
-// Short pieces of the expert GEMMs (at most kShortT = 32 tokens). Most
-// experts draw few tokens (the median of the 145B prefill input is 10), and
-// in a 128-token tile such a piece leaves half the waves without MFMAs while
-// every wave pair stages and decodes the same weight tile. Here a 512-thread
-// workgroup takes 32 tokens x 512 weight rows: each of the 8 waves owns one
-// 64-row tile and reads its weights straight from memory into the registers
-// of its MFMA operands (the tiled stream holds the v_mfma_f32_32x32x16 B
-// operand of a lane as one 16-byte lane-chunk: whole 256-byte segments per
-// load), decodes them itself, and only the 32 activation rows go through
-// LDS. Activation and weight register sets rotate separately (three each),
-// so no load targets registers the MFMAs in flight read, and each load has
-// two stages to arrive; the body has no branch (empty weight resource past
-// the last stage or tile).
+// Narrow pieces of the expert GEMMs (at most 64 tokens). Most experts draw
+// few tokens (the median of the 145B prefill input is 10), and in a
+// 128-token tile such a piece leaves waves without MFMAs while every wave
+// pair stages and decodes the same weight tile. Here a workgroup of NW waves
+// takes 32 NMB tokens x 64 NW weight rows: each wave owns one 64-row tile
+// and reads its weights straight from memory into the registers of its
+// MFMA operands (the tiled stream holds the v_mfma_f32_32x32x16 B operand of
+// a lane as one 16-byte lane-chunk: whole 256-byte segments per load),
+// decodes them itself, and only the activation rows go through LDS, shared by
+// all the workgroup's tiles. Activation and weight register sets rotate separately
+// (three each), so no load targets registers the MFMAs in flight read, and
+// each load has two stages to arrive; the body has no branch (empty weight
+// resource past the last stage or tile).
 
-constexpr int kSpNtw = 8;                              // weight tiles per workgroup, one per wave
 constexpr int kSpAst = Fm<kFP4>::SCOLS + 8;            // LDS row stride of the activations
-constexpr int kSpStage = kShortT * kSpAst * 2;         // LDS bytes per stage
-static_assert(kShortT * Fm<kFP4>::PPR == NTH, "one activation piece per thread");
+static_assert(Fm<kFP4>::PPR == 16, "16 activation pieces per row");
 static_assert(Fm<kFP4>::SC == 1, "one chunk per stage");
+
+template <int NMB>
+constexpr int sp_stage_bytes() { return 32 * NMB * kSpAst * 2; }
 
 struct SpB {
   uint4 b[2][2];   // raw FP4 words: row block nb (rows 32 nb .. + 31 of the tile), k-half kk
@@ -775,60 +776,100 @@ __device__ __forceinline__ void sp_fetch_b(const WMat& W, int tile, bool b_on, i
                                              wt, vs, sso + ncs * kSlot + nb * 512, BAUX));
 }
 
-// the thread's activation piece of stage s (row m, columns c .. c + 7 of the
-// stage; ap points at column c of the row, clamped into the row past k)
-__device__ __forceinline__ uint4 sp_fetch_a(const uint16_t* ap, int c, int kmat, int s, int nst) {
+// Activation staging with NW waves: the 32 NMB x SCOLS tile of a stage is
+// 512 NMB pieces of 8 columns; thread x stages pieces x + 64 NW i, i.e.
+// columns c = 8 (x % 16) .. + 7 of rows m + 4 NW i (m = x / 16) below 32 NMB.
+template <int NMB, int NW>
+struct SpA {
+  static constexpr int PPT = (512 * NMB + 64 * NW - 1) / (64 * NW);   // pieces per thread
+  static constexpr int RS = 4 * NW;                                   // row step between them
+  static constexpr int TT = 32 * NMB;
+  __device__ static constexpr bool live(int i, int m) { return m + RS * i < TT; }
+};
+
+// the thread's activation pieces of stage s (ap[i] points at column c of its
+// row, clamped into the row past k)
+template <int NMB, int NW>
+__device__ __forceinline__ void sp_fetch_a(const uint16_t* const (&ap)[SpA<NMB, NW>::PPT], int c, int kmat,
+                                           int s, int nst, uint4 (&v)[SpA<NMB, NW>::PPT]) {
   s = min(s, nst - 1);
   const int spm = (kmat + Fm<kFP4>::SCOLS - 1) / Fm<kFP4>::SCOLS;
   const int col0 = (s % spm) * Fm<kFP4>::SCOLS;
-  return *(const uint4*)(ap + min(col0, kmat - 8 - c));
+#pragma unroll
+  for (int i = 0; i < SpA<NMB, NW>::PPT; ++i) v[i] = *(const uint4*)(ap[i] + min(col0, kmat - 8 - c));
 }
 
-__device__ __forceinline__ void sp_store(uint8_t* st, uint4 v, int kmat, int c, int m, bool rvalid, int s) {
+template <int NMB, int NW>
+__device__ __forceinline__ void sp_store(uint8_t* st, const uint4 (&v)[SpA<NMB, NW>::PPT], int kmat, int c,
+                                         int m, uint32_t rvalid, int s) {
+  using P = SpA<NMB, NW>;
   const int spm = (kmat + Fm<kFP4>::SCOLS - 1) / Fm<kFP4>::SCOLS;
   const int col0 = (s % spm) * Fm<kFP4>::SCOLS;
-  // an AND, not a select: the load cannot be sunk down to this store
-  const uint32_t mk = (rvalid && col0 + c < kmat) ? ~0u : 0u;
-  *(uint4*)((uint16_t*)st + m * kSpAst + c) = make_uint4(v.x & mk, v.y & mk, v.z & mk, v.w & mk);
+#pragma unroll
+  for (int i = 0; i < P::PPT; ++i) {
+    if (!P::live(i, m)) continue;   // only the last piece of a thread can fall past the tile
+    // an AND, not a select: the load cannot be sunk down to this store
+    const uint32_t mk = (((rvalid >> i) & 1u) && col0 + c < kmat) ? ~0u : 0u;
+    *(uint4*)((uint16_t*)st + (m + P::RS * i) * kSpAst + c) =
+        make_uint4(v[i].x & mk, v[i].y & mk, v[i].z & mk, v[i].w & mk);
+  }
 }
 
-// one stage: per k-step the 32-token activation fragment (read one k-step
-// ahead) against the two decoded weight fragments of the wave's tile
-__device__ __forceinline__ void sp_mfma(const uint8_t* st, const SpB& R, f16v (&acc)[2]) {
+// one stage: per k-step the activation fragments of the NMB token blocks
+// (read one k-step ahead) against the two decoded weight fragments of the
+// wave's tile
+template <int NMB>
+__device__ __forceinline__ void sp_mfma(const uint8_t* st, const SpB& R, f16v (&acc)[NMB][2]) {
   using F = Fm<kFP4>;
   const int lane = threadIdx.x & 63, row = lane & 31, kh = lane >> 5;
   const uint16_t* As = (const uint16_t*)st;
-  uint4 a[2];
-  a[0] = *(const uint4*)(As + row * kSpAst + 8 * kh);
+  uint4 a[2][NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) a[0][mb] = *(const uint4*)(As + (32 * mb + row) * kSpAst + 8 * kh);
 #pragma unroll
   for (int ks = 0; ks < F::KS; ++ks) {
     const int kk = ks & 1, b = ks >> 1;              // k-half, 32-column block of the chunk
-    if (ks + 1 < F::KS) a[(ks + 1) & 1] = *(const uint4*)(As + row * kSpAst + 16 * (ks + 1) + 8 * kh);
+    if (ks + 1 < F::KS)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const uint4 bw = decode_b<kFP4>(R.b[nb][kk], R.sc[nb], b, b, 2 * kk + kh);
-      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a[ks & 1]),
-                                                       __builtin_bit_cast(half8, bw), acc[nb], 0, 0, 0);
-    }
+      for (int mb = 0; mb < NMB; ++mb)
+        a[(ks + 1) & 1][mb] = *(const uint4*)(As + (32 * mb + row) * kSpAst + 16 * (ks + 1) + 8 * kh);
+    uint4 bw[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) bw[nb] = decode_b<kFP4>(R.b[nb][kk], R.sc[nb], b, b, 2 * kk + kh);
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a[ks & 1][mb]),
+                                                             __builtin_bit_cast(half8, bw[nb]), acc[mb][nb],
+                                                             0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-template <int EPI>
-__global__ __launch_bounds__(NTH) void k_grouped_short(Grouped a) {
-  __shared__ __align__(16) uint8_t smem[2 * kSpStage];
-  __shared__ int arow[kShortT];
-  // short piece p runs on XCD p % 8, all its weight-tile octets back to back
-  const int nocts = (a.ntiles + kSpNtw - 1) / kSpNtw;
+// Pieces [npieces[lo], npieces[hi]) of at most 32 NMB tokens; NW waves, one
+// 64-row weight tile each (a wave past the last tile computes on zero weights
+// and stores nothing).
+template <int EPI, int NMB, int NW>
+__global__ __launch_bounds__(64 * NW) void k_grouped_short(Grouped a, int lo, int hi) {
+  using P = SpA<NMB, NW>;
+  constexpr int TT = P::TT;                            // tokens per workgroup
+  __shared__ __align__(16) uint8_t smem[2 * sp_stage_bytes<NMB>()];
+  __shared__ int arow[TT];
+  // piece p runs on XCD p % 8, its weight-tile groups back to back
+  const int nocts = (a.ntiles + NW - 1) / NW;
   const int bid = blockIdx.x, xcd = bid & 7, q = bid >> 3;
-  const int p = a.npieces[1] + xcd + 8 * (q / nocts), oct = q % nocts;
-  if (p >= a.npieces[0]) return;
+  const int oct = q % nocts;
+  const int p = a.npieces[lo] + xcd + 8 * (q / nocts);
+  if (p >= a.npieces[hi]) return;
   const Piece pc = a.pieces[p];
+  const int cnt = min(TT, pc.count);
   const int e = pc.expert;
-  if (threadIdx.x < kShortT) {
+  static_assert(64 * NW >= TT, "one thread per token row");
+  if (threadIdx.x < TT) {
     const int i = threadIdx.x;
     int row = -1;
-    if (i < pc.count) {
+    if (i < cnt) {
       const int pos = pc.start + i;
       row = EPI == kGateUp ? (a.perm[pos] / a.K) * a.G + a.labels[e] : pos;
     }
@@ -836,27 +877,35 @@ __global__ __launch_bounds__(NTH) void k_grouped_short(Grouped a) {
   }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = wave_id();
-  const int tile = kSpNtw * oct + wave;
+  const int tile = NW * oct + wave;
   const bool b_on = tile < a.ntiles;
   const uint8_t* base = a.experts + (size_t)e * a.estride;
   const WMat W{base + a.woff, a.g, 0, 1};
   const int nst = n_stages<kFP4>(W), kmat = a.A.kmat;
-  const int c = 8 * (threadIdx.x % Fm<kFP4>::PPR), m = threadIdx.x / Fm<kFP4>::PPR;
-  const int arw = arow[m];
-  const bool rvalid = arw >= 0;
-  const uint16_t* ap = a.A.p + (size_t)max(arw, 0) * a.A.rs + c;
-  f16v acc[2];
+  const int c = 8 * (threadIdx.x % 16), m = threadIdx.x / 16;
+  const uint16_t* ap[P::PPT];
+  uint32_t rvalid = 0;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int i = 0; i < P::PPT; ++i) {
+    const int arw = P::live(i, m) ? arow[m + P::RS * i] : -1;
+    rvalid |= (arw >= 0 ? 1u : 0u) << i;
+    ap[i] = a.A.p + (size_t)max(arw, 0) * a.A.rs + c;
+  }
+  f16v acc[NMB][2];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[nb][v] = 0.f;
-  uint4 ra[3];
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+  constexpr int SB = sp_stage_bytes<NMB>();
+  uint4 ra[3][P::PPT];
   SpB rb[3];
 #pragma unroll
-  for (int i = 0; i < 3; ++i) ra[i] = sp_fetch_a(ap, c, kmat, i, nst);
+  for (int i = 0; i < 3; ++i) sp_fetch_a<NMB, NW>(ap, c, kmat, i, nst, ra[i]);
 #pragma unroll
   for (int i = 0; i < 2; ++i) sp_fetch_b<kAuxNT>(W, tile, b_on, i, nst, rb[i]);
-  sp_store(smem, ra[0], kmat, c, m, rvalid, 0);
+  sp_store<NMB, NW>(smem, ra[0], kmat, c, m, rvalid, 0);
   __syncthreads();
   // stage s with sets i = s % 3: weights of s + 2 into the set the MFMAs of
   // s - 1 read, activations of s + 3 into the set stored at s - 1, the
@@ -864,9 +913,9 @@ __global__ __launch_bounds__(NTH) void k_grouped_short(Grouped a) {
   // no wave reads again), the MFMAs of s
   const auto step = [&](int s, int i) {
     sp_fetch_b<kAuxNT>(W, tile, b_on, s + 2, nst, rb[(i + 2) % 3]);
-    ra[i] = sp_fetch_a(ap, c, kmat, s + 3, nst);
-    sp_store(smem + ((s + 1) & 1) * kSpStage, ra[(i + 1) % 3], kmat, c, m, rvalid, min(s + 1, nst - 1));
-    sp_mfma(smem + (s & 1) * kSpStage, rb[i], acc);
+    sp_fetch_a<NMB, NW>(ap, c, kmat, s + 3, nst, ra[i]);
+    sp_store<NMB, NW>(smem + ((s + 1) & 1) * SB, ra[(i + 1) % 3], kmat, c, m, rvalid, min(s + 1, nst - 1));
+    sp_mfma<NMB>(smem + (s & 1) * SB, rb[i], acc);
     __syncthreads();
   };
   int s0 = 0;
@@ -880,24 +929,56 @@ __global__ __launch_bounds__(NTH) void k_grouped_short(Grouped a) {
   if (!b_on) return;
   const float* ts = (const float*)(base + a.ts_off);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int i = acc_tok(lane, 0, v);
-    if (i >= pc.count) continue;
-    const size_t pos = (size_t)pc.start + i;
-    if constexpr (EPI == kGateUp) {
-      const float tg = ts[0], tu = ts[1];
-      const int f = 32 * tile + (lane & 31);
-      const float hv = silu(acc[0][v] * tg) * (acc[1][v] * tu);
-      ((_Float16*)a.out)[pos * a.ostride + f] = (_Float16)hv;
-    } else {
-      const float sc = a.topk_w[a.perm[pos]] * ts[2];
+  for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-      for (int rg = 0; rg < 2; ++rg) {
-        const int n = 64 * tile + 32 * rg + (lane & 31);
-        ((_Float16*)a.out)[pos * a.ostride + n] = (_Float16)(acc[rg][v] * sc);
+    for (int v = 0; v < 16; ++v) {
+      const int i = acc_tok(lane, mb, v);
+      if (i >= cnt) continue;
+      const size_t pos = (size_t)pc.start + i;
+      if constexpr (EPI == kGateUp) {
+        const float tg = ts[0], tu = ts[1];
+        const int f = 32 * tile + (lane & 31);
+        const float hv = silu(acc[mb][0][v] * tg) * (acc[mb][1][v] * tu);
+        ((_Float16*)a.out)[pos * a.ostride + f] = (_Float16)hv;
+      } else {
+        const float sc = a.topk_w[a.perm[pos]] * ts[2];
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg) {
+          const int n = 64 * tile + 32 * rg + (lane & 31);
+          ((_Float16*)a.out)[pos * a.ostride + n] = (_Float16)(acc[mb][rg][v] * sc);
+        }
       }
     }
+}
+
+// Waves per k_grouped_short workgroup: 8, or 4 for a matrix of at most four
+// 64-row tiles. Measured on the 145B prefill: 8-wave workgroups with idle
+// waves in the last group (20 and 28 tiles) beat 5- and 7-wave ones that
+// divide the tile count, which leave SIMD slots of the CU empty.
+static int short_waves(int ntiles) { return ntiles <= 4 ? 4 : 8; }
+
+template <int EPI, int NMB>
+static int launch_short(const Grouped& a, unsigned npc, int lo, int hi, hipStream_t st) {
+  const int nw = short_waves(a.ntiles);
+  const unsigned grid = 8u * ((a.ntiles + nw - 1) / nw) * ((npc + 7) / 8);
+  switch (nw) {
+    case 8: hipLaunchKernelGGL((k_grouped_short<EPI, NMB, 8>), dim3(grid), dim3(64 * 8), 0, st, a, lo, hi); break;
+    default: hipLaunchKernelGGL((k_grouped_short<EPI, NMB, 4>), dim3(grid), dim3(64 * 4), 0, st, a, lo, hi); break;
   }
+  LMOE_HIP(hipGetLastError());
+  return 0;
+}
+
+// The three grouped launches of one expert matrix: pieces of more than 64
+// tokens in 128-token tiles, then those of 33..64 and of at most 32 tokens
+// (each class holds at most one piece per expert).
+template <int EPI>
+static int launch_grouped(const Grouped& a, unsigned maxp, int E, hipStream_t st) {
+  const unsigned ncls = std::min<unsigned>(maxp, E);
+  hipLaunchKernelGGL(k_grouped<EPI>, dim3(8u * a.nquads * ((maxp + 7) / 8)), dim3(NTH), 0, st, a);
+  LMOE_HIP(hipGetLastError());
+  if (int rc = launch_short<EPI, 2>(a, ncls, 1, 2, st)) return rc;
+  return launch_short<EPI, 1>(a, ncls, 2, 0, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -1281,6 +1362,7 @@ __global__ __launch_bounds__(kMaxE) void k_perm_scan(Perm a) {
   __shared__ int sp[kMaxE];
   __shared__ int sf[kMaxE];
   __shared__ int sq[kMaxE];
+  __shared__ int sm_[kMaxE];
   __shared__ int ss_[kMaxE];
   const int j = threadIdx.x;
   if (j < a.E) {
@@ -1306,32 +1388,35 @@ __global__ __launch_bounds__(kMaxE) void k_perm_scan(Perm a) {
   const int c_e = j < a.E ? a.expert_count[e] : 0;
   const int np = (c_e + BM - 1) / BM;
   // piece order: the full pieces of all experts, then the partial last
-  // pieces of more than kShortT tokens, then the short ones (the grouped
-  // GEMMs dispatch their longest work items first; the short pieces go to
-  // k_grouped_short)
-  const int nf = c_e / BM, nq = np - nf;
-  const int nqs = (nq && c_e - nf * BM <= kShortT) ? 1 : 0, nqb = nq - nqs;
+  // pieces of more than 64 tokens, of 33 to 64, of at most 32 (the grouped
+  // GEMMs dispatch their longest work items first; the last two classes go
+  // to k_grouped_short)
+  const int nf = c_e / BM, nq = np - nf, rem = c_e - nf * BM;
+  const int cls = nq == 0 ? -1 : rem > 2 * kShortT ? 0 : rem > kShortT ? 1 : 2;
   sc[j] = c_e;
   sp[j] = np;
   sf[j] = nf;
-  sq[j] = nqb;
-  ss_[j] = nqs;
+  sq[j] = cls == 0;
+  sm_[j] = cls == 1;
+  ss_[j] = cls == 2;
   __syncthreads();
   for (int o = 1; o < kMaxE; o <<= 1) {
     const int x0 = j >= o ? sc[j - o] : 0, x1 = j >= o ? sp[j - o] : 0;
     const int x2 = j >= o ? sf[j - o] : 0, x3 = j >= o ? sq[j - o] : 0;
-    const int x4 = j >= o ? ss_[j - o] : 0;
+    const int x4 = j >= o ? sm_[j - o] : 0, x5 = j >= o ? ss_[j - o] : 0;
     __syncthreads();
     sc[j] += x0;
     sp[j] += x1;
     sf[j] += x2;
     sq[j] += x3;
-    ss_[j] += x4;
+    sm_[j] += x4;
+    ss_[j] += x5;
     __syncthreads();
   }
-  const int nbig = sf[kMaxE - 1] + sq[kMaxE - 1];   // pieces before the short ones
+  const int nbig = sf[kMaxE - 1] + sq[kMaxE - 1];   // pieces of more than 64 tokens
+  const int nmid = nbig + sm_[kMaxE - 1];           // ... and of 33 to 64
   const int start = sc[j] - c_e, fstart = sf[j] - nf;
-  const int qstart = nqs ? nbig + ss_[j] - nqs : sf[kMaxE - 1] + sq[j] - nqb;
+  const int qstart = cls == 0 ? sf[kMaxE - 1] + sq[j] - 1 : cls == 1 ? nbig + sm_[j] - 1 : nmid + ss_[j] - 1;
   if (j < a.E) {
     a.seg_start[e] = start;
     for (int i = 0; i < np; ++i) {
@@ -1350,6 +1435,7 @@ __global__ __launch_bounds__(kMaxE) void k_perm_scan(Perm a) {
       for (int g = lab + 1; g <= a.G; ++g) a.group_off[g] = sc[j];
       a.npieces[0] = sp[j];
       a.npieces[1] = nbig;
+      a.npieces[2] = nmid;
     }
   }
 }
@@ -1650,7 +1736,6 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
   }
   // experts
   const unsigned maxp = (unsigned)prefill_max_pieces(T, K, E);
-  const unsigned maxshort = (unsigned)std::min(E, T * K);   // at most one short piece per expert
   {
     Grouped a{};
     a.experts = h->experts; a.estride = h->expert_stride; a.woff = 0; a.ts_off = h->ts_off;
@@ -1659,12 +1744,7 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     a.ntiles = h->g_gu.tiles; a.nquads = (a.ntiles + NTW - 1) / NTW; a.G = G; a.F = F;
     a.perm = p.perm; a.topk_w = p.w; a.labels = h->labels; a.K = K;
     a.out = p.h; a.ostride = F;
-    const unsigned grid = 8u * a.nquads * ((maxp + 7) / 8);
-    hipLaunchKernelGGL(k_grouped<kGateUp>, dim3(grid), dim3(NTH), 0, st, a);
-    LMOE_HIP(hipGetLastError());
-    const unsigned gs = 8u * ((a.ntiles + kSpNtw - 1) / kSpNtw) * ((maxshort + 7) / 8);
-    hipLaunchKernelGGL(k_grouped_short<kGateUp>, dim3(gs), dim3(NTH), 0, st, a);
-    LMOE_HIP(hipGetLastError());
+    if (int rc = launch_grouped<kGateUp>(a, maxp, E, st)) return rc;
   }
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[5], st));
   {
@@ -1675,12 +1755,7 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     a.ntiles = h->g_dn.tiles; a.nquads = (a.ntiles + NTW - 1) / NTW; a.G = G; a.F = F;
     a.perm = p.perm; a.topk_w = p.w; a.labels = h->labels; a.K = K;
     a.out = p.o; a.ostride = L;
-    const unsigned grid = 8u * a.nquads * ((maxp + 7) / 8);
-    hipLaunchKernelGGL(k_grouped<kDown>, dim3(grid), dim3(NTH), 0, st, a);
-    LMOE_HIP(hipGetLastError());
-    const unsigned gs = 8u * ((a.ntiles + kSpNtw - 1) / kSpNtw) * ((maxshort + 7) / 8);
-    hipLaunchKernelGGL(k_grouped_short<kDown>, dim3(gs), dim3(NTH), 0, st, a);
-    LMOE_HIP(hipGetLastError());
+    if (int rc = launch_grouped<kDown>(a, maxp, E, st)) return rc;
   }
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[6], st));
   // combine

@@ -216,6 +216,28 @@ def test_prefill_u_split_along_k():
         check_outputs(c, got, dbg, np.arange(T))
 
 
+def test_prefill_expert_piece_classes():
+    """A skewed router (per-expert bias) over 32 experts: expert loads from 0
+    to 596 tokens, so the expert GEMMs get full 128-token pieces, partial
+    pieces of more than 64 tokens, of 33 to 64 and of at most 32 tokens, each
+    class on its own kernel path. Latent 512 and expert ffn 160 give 8 down
+    tiles and 5 gate/up tiles (the 8-wave narrow-piece workgroup with three
+    waves past the last tile) and a gate/up K-ragged second FP4 stage (32 of
+    128 columns). Every token is checked."""
+    w = wl.Workload("classes", 256, 512, 32, 4, 4, 160, 64, 8, 700, router_bias=True)
+    c = Case(w, seed=3, tokens=700)
+    layer = make_layer(c, 700)
+    for T in (700, 333):
+        print("case classes prefill T", T, flush=True)
+        got, dbg = run(layer, w, c.x[:T])
+        check_routing(c, dbg, T)
+        cnt = dbg["expert_count"]
+        rem = cnt % 128
+        assert (cnt >= 128).any() and (rem > 64).any()
+        assert ((rem > 32) & (rem <= 64)).any() and ((rem > 0) & (rem <= 32)).any()
+        check_outputs(c, got, dbg, np.arange(T))
+
+
 # ---------------------------------------------------------------------------
 # 145B / 120B shapes, routing over all tokens, outputs on a sample
 
