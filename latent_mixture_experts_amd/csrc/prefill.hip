@@ -951,6 +951,131 @@ __global__ __launch_bounds__(64 * NW) void k_grouped_short(Grouped a, int lo, in
     }
 }
 
+// Expert down projection with the activations resident in LDS. The down
+// matrix has K = expert ffn (640 at the 145B shapes): five FP4 stages, too
+// few for a per-tile pipeline to amortise its ramp and per-stage barriers.
+// Here a workgroup of NW waves takes one 32 NMB-token block of a piece (its
+// 32 NMB x K fp16 activations fit the LDS), stages it once, and each wave then
+// walks its weight tiles (w, w + NW, ...) as one flat sequence of
+// (tile, stage) items: weights read straight into MFMA operand registers
+// two items ahead across tile boundaries, no barrier after the staging, and
+// each tile's weighted outputs stored after its last stage.
+
+constexpr int kResMaxK = 1024;                         // largest K kept resident
+constexpr int kResAst = kResMaxK + 8;                  // LDS row stride (elements)
+
+// weights of item `it` of the wave's sequence (past n: an empty resource)
+__device__ __forceinline__ void res_fetch(const WMat& W, int wave, int nw, int it, int n, int nst, SpB& R) {
+  const int j = min(it, n - 1);
+  const int tile = wave + nw * (j / nst);
+  sp_fetch_b<kAuxNT>(W, tile, it < n, j % nst, nst, R);
+}
+
+// pieces [npieces[lo], npieces[hi]) (lo < 0: from the first one) in nsub
+// blocks of 32 NMB tokens
+template <int NW, int NMB>
+__global__ __launch_bounds__(64 * NW) void k_down_res(Grouped a, int lo, int hi, int nsub) {
+  constexpr int kResTT = 32 * NMB;                     // tokens per workgroup
+  __shared__ __align__(16) uint16_t As[kResTT * kResAst];
+  __shared__ float tsc[kResTT];
+  // piece p runs on XCD p % 8, its token blocks back to back
+  const int bid = blockIdx.x, xcd = bid & 7, q = bid >> 3;
+  const int h = q % nsub, p = (lo < 0 ? 0 : a.npieces[lo]) + xcd + 8 * (q / nsub);
+  if (p >= a.npieces[hi]) return;
+  const Piece pc = a.pieces[p];
+  const int t0 = kResTT * h, cnt = min(kResTT, pc.count - t0);
+  if (cnt <= 0) return;
+  const uint8_t* base = a.experts + (size_t)pc.expert * a.estride;
+  const float* ts = (const float*)(base + a.ts_off);
+  const WMat W{base + a.woff, a.g, 0, 1};
+  const int nst = n_stages<kFP4>(W), kmat = a.A.kmat, kpad = nst * Fm<kFP4>::SCOLS;
+  if (threadIdx.x < kResTT) {
+    const int i = threadIdx.x;
+    tsc[i] = i < cnt ? a.topk_w[a.perm[pc.start + t0 + i]] * ts[2] : 0.f;
+  }
+  // stage the block: rows past the piece and columns past K are zeros
+  {
+    const int ppr = kpad / 8, npc = kResTT * ppr;
+    for (int x = threadIdx.x; x < npc; x += 64 * NW) {
+      const int r = x / ppr, c = 8 * (x % ppr);
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (r < cnt && c < kmat) v = *(const uint4*)(a.A.p + (size_t)(pc.start + t0 + r) * a.A.rs + c);
+      *(uint4*)(As + r * kResAst + c) = v;
+    }
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int ntw = (a.ntiles - wave + NW - 1) / NW;     // the wave's tiles
+  const int n = ntw * nst;
+  if (n <= 0) return;
+  const int row = lane & 31, kh = lane >> 5;
+  f16v acc[NMB][2];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+  SpB rb[3];
+  res_fetch(W, wave, NW, 0, n, nst, rb[0]);
+  res_fetch(W, wave, NW, 1, n, nst, rb[1]);
+  // item it with set i = it % 3: weights of it + 2 into the set item it - 1
+  // read, the MFMAs of it over the stage's columns of the resident block, and
+  // after a tile's last stage its outputs
+  const auto item = [&](int it, int i) {
+    res_fetch(W, wave, NW, it + 2, n, nst, rb[(i + 2) % 3]);
+    const int st = it % nst;
+    const uint16_t* Ab = As + Fm<kFP4>::SCOLS * st + 8 * kh;
+    uint4 av[2][NMB];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) av[0][mb] = *(const uint4*)(Ab + (32 * mb + row) * kResAst);
+#pragma unroll
+    for (int ks = 0; ks < Fm<kFP4>::KS; ++ks) {
+      const int kk = ks & 1, b = ks >> 1;
+      if (ks + 1 < Fm<kFP4>::KS)
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+          av[(ks + 1) & 1][mb] = *(const uint4*)(Ab + (32 * mb + row) * kResAst + 16 * (ks + 1));
+      uint4 bw[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) bw[nb] = decode_b<kFP4>(rb[i].b[nb][kk], rb[i].sc[nb], b, b, 2 * kk + kh);
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, av[ks & 1][mb]),
+                                                               __builtin_bit_cast(half8, bw[nb]), acc[mb][nb],
+                                                               0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (st == nst - 1) {
+      const int tile = wave + NW * (it / nst);
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int t = acc_tok(lane, mb, v);
+          const float sc = tsc[t];
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            if (t < cnt)
+              ((_Float16*)a.out)[(size_t)(pc.start + t0 + t) * a.ostride + 64 * tile + 32 * nb + (lane & 31)] =
+                  (_Float16)(acc[mb][nb][v] * sc);
+            acc[mb][nb][v] = 0.f;
+          }
+        }
+    }
+  };
+  int i0 = 0;
+  for (; i0 + 3 <= n; i0 += 3) {
+    item(i0, 0);
+    item(i0 + 1, 1);
+    item(i0 + 2, 2);
+  }
+  if (i0 < n) item(i0, 0);
+  if (i0 + 1 < n) item(i0 + 1, 1);
+}
+
 // Waves per k_grouped_short workgroup: 8, or 4 for a matrix of at most four
 // 64-row tiles. Measured on the 145B prefill: 8-wave workgroups with idle
 // waves in the last group (20 and 28 tiles) beat 5- and 7-wave ones that
@@ -975,6 +1100,14 @@ static int launch_short(const Grouped& a, unsigned npc, int lo, int hi, hipStrea
 template <int EPI>
 static int launch_grouped(const Grouped& a, unsigned maxp, int E, hipStream_t st) {
   const unsigned ncls = std::min<unsigned>(maxp, E);
+  if (EPI == kDown && a.A.kmat <= kResMaxK) {
+    // pieces of more than 32 tokens in 64-token blocks, the rest in 32
+    hipLaunchKernelGGL((k_down_res<8, 2>), dim3(8u * 2 * ((maxp + 7) / 8)), dim3(512), 0, st, a, -1, 2, 2);
+    LMOE_HIP(hipGetLastError());
+    hipLaunchKernelGGL((k_down_res<8, 1>), dim3(8u * ((ncls + 7) / 8)), dim3(512), 0, st, a, 2, 0, 1);
+    LMOE_HIP(hipGetLastError());
+    return 0;
+  }
   hipLaunchKernelGGL(k_grouped<EPI>, dim3(8u * a.nquads * ((maxp + 7) / 8)), dim3(NTH), 0, st, a);
   LMOE_HIP(hipGetLastError());
   if (int rc = launch_short<EPI, 2>(a, ncls, 1, 2, st)) return rc;

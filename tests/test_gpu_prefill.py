@@ -222,8 +222,8 @@ def test_prefill_expert_piece_classes():
     pieces of more than 64 tokens, of 33 to 64 and of at most 32 tokens, each
     class on its own kernel path. Latent 512 and expert ffn 160 give 8 down
     tiles and 5 gate/up tiles (the 8-wave narrow-piece workgroup with three
-    waves past the last tile) and a gate/up K-ragged second FP4 stage (32 of
-    128 columns). Every token is checked."""
+    waves past the last tile) and a K-ragged second FP4 stage (32 of 128
+    columns) in the resident down projection. Every token is checked."""
     w = wl.Workload("classes", 256, 512, 32, 4, 4, 160, 64, 8, 700, router_bias=True)
     c = Case(w, seed=3, tokens=700)
     layer = make_layer(c, 700)
@@ -236,6 +236,24 @@ def test_prefill_expert_piece_classes():
         assert (cnt >= 128).any() and (rem > 64).any()
         assert ((rem > 32) & (rem <= 64)).any() and ((rem > 0) & (rem <= 32)).any()
         check_outputs(c, got, dbg, np.arange(T))
+
+
+def test_prefill_wide_expert_ffn():
+    """Expert ffn 1056: the down projection's K is past what the LDS holds
+    resident, so it runs on the staged 128-token and narrow-piece kernels; K
+    ends 32 columns into its ninth FP4 stage. Skewed router, every piece
+    class present, every token checked."""
+    w = wl.Workload("wide_ffn", 256, 256, 16, 4, 2, 1056, 64, 8, 400, router_bias=True)
+    c = Case(w, seed=4, tokens=400)
+    layer = make_layer(c, 400)
+    print("case wide_ffn prefill T 400", flush=True)
+    got, dbg = run(layer, w, c.x)
+    check_routing(c, dbg, 400)
+    cnt = dbg["expert_count"]
+    rem = cnt % 128
+    assert (cnt >= 128).any() and (rem > 64).any()
+    assert ((rem > 32) & (rem <= 64)).any() and ((rem > 0) & (rem <= 32)).any()
+    check_outputs(c, got, dbg, np.arange(400))
 
 
 # ---------------------------------------------------------------------------
