@@ -1711,11 +1711,173 @@ __global__ __launch_bounds__(256) void k_ytiles(Dense a, const float* res) {
   ((float*)a.out)[i] = v;
 }
 
+// ---------------------------------------------------------------------------
+// Dense GEMM on fp16 weights with 128 x 128 wave tiles (the D projection):
+// out[t][n] = sum_k A[t][k] W[n][k], fp16 out. A workgroup of 4 waves takes
+// 256 tokens x 256 weight rows (4 tiles), wave (wm, wn) 128 tokens x 128 rows
+// with its 256 accumulators in AGPRs (one wave per SIMD). Per 16-column
+// k-step a wave reads 8 KB of fragments from LDS for 16 MFMAs, half of what
+// the 64 x 64 wave tile of k_dense needs per MFMA, whose LDS bandwidth bounds
+// it. Operands reach LDS by DMA (buffer_load ... lds: no registers, no LDS
+// store instructions), 32 columns per stage in four buffers, issued three
+// stages ahead. The weights' 1 KiB slots are copied as they are; activation
+// rows are 64 B, their four 16 B pieces XOR-swizzled by (row / 2) % 4 so
+// that fragment reads of 8 consecutive rows hit distinct banks.
+
+constexpr int kWgT = 256, kWgN = 256, kWgCols = 32, kWgBuf = 4;
+constexpr int kWgA = kWgT * kWgCols * 2;                 // activation bytes per stage
+constexpr int kWgB = (kWgN / 64) * 4 * kSlot;            // weight bytes per stage
+constexpr int kWgStage = kWgA + kWgB;
+static_assert(kWgBuf * kWgStage <= 160 * 1024, "LDS");
+
+// 16 bytes per lane from r + voff + soff to LDS m0 + 16 lane. Written in
+// assembly so that the compiler, which cannot tell which LDS bytes a DMA
+// writes, does not wait for every DMA before each LDS read; the kernel waits
+// for the stage it needs (vmcnt) itself. No register is written.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               ::"s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
+}
+
+// s_waitcnt operand that waits for vmcnt <= n only (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 at their maxima)
+constexpr int vmcnt_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_dense16(Dense a) {
+  __shared__ __align__(1024) uint8_t smem[kWgBuf * kWgStage];
+  const int nq = (a.ntiles + 3) / 4, mtl = (a.T + kWgT - 1) / kWgT;
+  const int L = xcd_order(blockIdx.x, mtl * nq);
+  int mt, quad;
+  tile_of(L, mtl, nq, mt, quad);
+  const int lane = threadIdx.x & 63, wave = wave_id(), wm = wave & 1, wn = wave >> 1;
+  const int kmat = a.A.kmat, nst = kmat / kWgCols;
+  // activation DMA: wave w stages rows 16 i .. + 15 for i = w + 4 j; lane l
+  // the piece at position l % 4 of row 16 i + l / 4, which holds column
+  // piece (l % 4) ^ ((row / 2) % 4). Rows past T read zeros.
+  const rsrc_t ar = rsrc(a.A.p + (size_t)mt * kWgT * a.A.rs,
+                         (uint32_t)(min(kWgT, a.T - mt * kWgT) * a.A.rs * 2));
+  uint32_t avo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 16 * (wave + 4 * j) + (lane >> 2);
+    const int pc = (lane & 3) ^ ((r >> 1) & 3);
+    avo[j] = (uint32_t)((r * a.A.rs + 8 * pc) * 2);
+  }
+  // weight DMA: wave w copies the 4 slots of stage s of tile 4 quad + w
+  const int wt = 4 * quad + wave;
+  const rsrc_t br = rsrc(a.W.base + (size_t)min(wt, a.ntiles - 1) * a.W.g.tile_slots * kSlot,
+                         wt < a.ntiles ? (uint32_t)(a.W.g.tile_slots * kSlot) : 0u);
+  const uint32_t sbase = lds_off(smem);
+  const auto issue = [&](int s) {
+    const int b = s & (kWgBuf - 1);
+    const bool live = s < nst;
+    const uint32_t col = (uint32_t)(min(s, nst - 1) * kWgCols * 2);
+    const uint32_t st = sbase + b * kWgStage;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dma16(live ? ar : rsrc(a.A.p, 0u), st + (wave + 4 * j) * 1024, avo[j], col);
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+      dma16(live ? br : rsrc(a.W.base, 0u), st + kWgA + (wave * 4 + rg) * 1024, lane * 16,
+            (uint32_t)((4 * min(s, nst - 1) + rg) * kSlot));
+  };
+  f16v acc[4][4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mb][j][v] = 0.f;
+  const int row = lane & 31, kh = lane >> 5;
+  // fragments of k-step ks (0, 1) of stage s
+  const auto frags = [&](int s, int ks, uint4 (&af)[4], uint4 (&bf)[4]) {
+    const uint8_t* st = smem + (s & (kWgBuf - 1)) * kWgStage;
+    const uint16_t* As = (const uint16_t*)st;
+    const uint4* Bs = (const uint4*)(st + kWgA);
+    const int c = 2 * ks + kh;                       // 8-column piece of the stage
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int m = 128 * wm + 32 * mb + row;
+      af[mb] = *(const uint4*)(As + m * kWgCols + 8 * (c ^ ((m >> 1) & 3)));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tt = 2 * wn + (j >> 1), nb = j & 1;
+      bf[j] = Bs[(tt * 4 + 2 * nb + (row >> 4)) * 64 + 16 * c + (lane & 15)];
+    }
+  };
+  const auto mfmas = [&](const uint4 (&af)[4], const uint4 (&bf)[4]) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[mb][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, af[mb]),
+                                                            __builtin_bit_cast(half8, bf[j]), acc[mb][j], 0, 0, 0);
+  };
+  issue(0);
+  issue(1);
+  issue(2);
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(16));             // this wave's stage 0
+  __syncthreads();
+  uint4 a0[4], b0[4], a1[4], b1[4];
+  frags(0, 0, a0, b0);
+  // stage s: second k-step's fragments read under the first's MFMAs; then
+  // the wait for this wave's DMAs of stage s + 1 (those of s + 2, 8, may
+  // stay in flight) and the barrier that makes every wave's visible and
+  // ends all reads of stage s - 1, whose buffer stage s + 3 then refills;
+  // the next stage's first fragments are read under the second k-step's
+  // MFMAs (past the last stage they read a buffer of zeros, unused)
+  // (scheduling barriers keep this order: the compiler would otherwise read
+  // each fragment just before its MFMA and expose the LDS latency)
+  for (int s = 0; s < nst; ++s) {
+    frags(s, 1, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(8));
+    __syncthreads();
+    issue(s + 3);
+    frags(s + 1, 0, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the trailing DMAs (empty resources) write the buffers of stages past the
+  // end, which no wave reads: let them land before the workgroup's LDS is freed
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int t = mt * kWgT + 128 * wm + acc_tok(lane, mb, v);
+      if (t >= a.T) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tile = 4 * quad + 2 * wn + (j >> 1);
+        if (tile >= a.ntiles) continue;
+        const int n = 64 * tile + 32 * (j & 1) + (lane & 31);
+        if constexpr (EPI == kEpiF16) ((_Float16*)a.out)[(size_t)t * a.ostride + n] = (_Float16)acc[mb][j][v];
+      }
+    }
+}
+
 template <int WF, int EPI>
 int launch_dense(const Dense& a, hipStream_t st) {
   const unsigned nblk = (unsigned)(EPI == kEpiY || EPI == kEpiLogits ? a.nfull + a.nrem * a.nsplit
                                                                      : a.mtiles * a.nquads);
   if (nblk == 0) return 0;
+  if constexpr (WF == kF16 && EPI == kEpiF16)
+    if (a.A.kmat % kWgCols == 0 && a.A.ps == 0 && a.W.nmat == 1) {
+      const unsigned n16 = (unsigned)(((a.T + kWgT - 1) / kWgT) * ((a.ntiles + 3) / 4));
+      hipLaunchKernelGGL((k_dense16<EPI>), dim3(n16), dim3(256), 0, st, a);
+      LMOE_HIP(hipGetLastError());
+      return 0;
+    }
   hipLaunchKernelGGL((k_dense<WF, EPI>), dim3(nblk), dim3(NTH), 0, st, a);
   LMOE_HIP(hipGetLastError());
   return 0;
