@@ -718,6 +718,184 @@ __global__ __launch_bounds__(NTH) void k_grouped(Grouped a) {
 }
 
 // ---------------------------------------------------------------------------
+// LDS DMA.
+
+// 16 bytes per lane from r + voff + soff to LDS m0 + 16 lane. Written in
+// assembly so that the compiler, which cannot tell which LDS bytes a DMA
+// writes, does not wait for every DMA before each LDS read; the kernel waits
+// for the stage it needs (vmcnt) itself. No register is written.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               ::"s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
+}
+
+// s_waitcnt operand that waits for vmcnt <= n only (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 at their maxima)
+constexpr int vmcnt_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+// ---------------------------------------------------------------------------
+// Expert gate/up for pieces of more than 64 tokens, operands fed by DMA. The
+// geometry of k_grouped (128 tokens x 4 weight tiles, each wave 64 tokens x
+// one 64-row tile), but no register staging: the activation rows (gathered
+// through the permutation) and the weights' raw code and scale slots are
+// copied global -> LDS by buffer DMA, two stages ahead in three buffers, so
+// a wave's instruction stream in the loop is its LDS reads, decodes and
+// MFMAs. Activation rows are 256 B (128 fp16 columns), their sixteen 16 B
+// pieces XOR-swizzled by row % 16 through the DMA source address, so the
+// fragment reads of 16 consecutive rows hit distinct banks. K is a multiple
+// of 128 (every staged column real); rows past the piece may hold anything,
+// their outputs are not stored.
+
+constexpr int kGdA = BM * 256;                           // activation bytes per stage
+constexpr int kGdB = NTW * 4 * kSlot;                    // code slots
+constexpr int kGdS = NTW * kSlot;                        // scale slots
+constexpr int kGdStage = kGdA + kGdB + kGdS;
+constexpr int kGdBuf = 3;
+static_assert(kGdBuf * kGdStage + BM * 4 <= 160 * 1024, "LDS");
+constexpr uint32_t kOob = 0xFFFFFFF0u;                   // a DMA offset past any resource: zeros
+
+template <int EPI>
+__global__ __launch_bounds__(NTH) void k_grouped_dma(Grouped a) {
+  __shared__ __align__(1024) uint8_t smem[kGdBuf * kGdStage];
+  __shared__ int arow[BM];
+  const int bid = blockIdx.x, xcd = bid & 7, q = bid >> 3;
+  const int p = xcd + 8 * (q / a.nquads), quad = q % a.nquads;
+  if (p >= a.npieces[1]) return;                     // pieces of more than 64 tokens
+  const Piece pc = a.pieces[p];
+  const int e = pc.expert;
+  if (threadIdx.x < BM) {
+    const int i = threadIdx.x;
+    int row = -1;
+    if (i < pc.count) {
+      const int pos = pc.start + i;
+      row = EPI == kGateUp ? (a.perm[pos] / a.K) * a.G + a.labels[e] : pos;
+    }
+    arow[i] = row;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = wave_id(), wm = wave & 1, tl = wave >> 1;
+  const int tile = NTW * quad + tl;
+  const bool b_on = tile < a.ntiles;
+  const uint8_t* base = a.experts + (size_t)e * a.estride;
+  const WMat W{base + a.woff, a.g, 0, 1};
+  using F = Fm<kFP4>;
+  const int kmat = a.A.kmat, nst = n_stages<kFP4>(W);
+  // activation DMA: instruction i = wave + 8 j covers rows 4 i .. + 3; lane
+  // l the piece at position l % 16 of row 4 i + l / 16, which holds column
+  // piece (l % 16) ^ (row % 16)
+  const rsrc_t ar = rsrc(a.A.p, kOob);
+  uint32_t aro[4];
+  int acol[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 4 * (wave + 8 * j) + (lane >> 4);
+    const int arw = arow[r];
+    acol[j] = 8 * ((lane & 15) ^ (r & 15));
+    aro[j] = arw >= 0 ? (uint32_t)((size_t)arw * a.A.rs * 2) : kOob;
+  }
+  const uint32_t sbase = lds_off(smem);
+  const auto issue = [&](int s) {
+    const bool live = s < nst;
+    const uint32_t st = sbase + (uint32_t)((s % kGdBuf) * kGdStage);
+    s = min(s, nst - 1);
+    const int col0 = s * F::SCOLS;                 // one matrix: stage s covers columns col0 ..
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = col0 + acol[j];
+      const uint32_t vo = (aro[j] == kOob || c >= kmat || !live) ? kOob : aro[j] + (uint32_t)(2 * c);
+      dma16(ar, st + (wave + 8 * j) * 1024, vo, 0);
+    }
+    const int ss = col0 / kSSCols, cin0 = (col0 % kSSCols) / F::CC;
+    const int ncs = ss_code_slots(kFP4, min(kSSCols, kmat - ss * kSSCols));
+    const rsrc_t wt = rsrc(W.base + (size_t)min(tile, a.ntiles - 1) * W.g.tile_slots * kSlot,
+                           live && b_on ? (uint32_t)(W.g.tile_slots * kSlot) : 0u);
+    const uint32_t sso = (uint32_t)(ss * W.g.full * kSlot);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int rg = 2 * wm + h;
+      dma16(wt, st + kGdA + (tl * 4 + rg) * 1024, lane * 16, sso + (uint32_t)((cin0 * 4 + rg) * kSlot));
+    }
+    // the tile's scale slot, from the even wave of the pair (a DMA writes its
+    // 64 lanes to consecutive 16 B: one slot per instruction)
+    if (wm == 0) dma16(wt, st + kGdA + kGdB + tl * 1024, lane * 16, sso + (uint32_t)(ncs * kSlot));
+  };
+  f16v acc[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+  issue(0);
+  issue(1);
+  const int row = lane & 31, kh = lane >> 5;
+  for (int s = 0; s < nst; ++s) {
+    // this wave's DMAs of stage s (7 or 6) are done when at most 6 of s + 1
+    // are in flight; the barrier makes every wave's visible and ends the
+    // reads of stage s - 1, whose buffer stage s + 2 refills
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(6));
+    __syncthreads();
+    issue(s + 2);
+    const uint8_t* st = smem + (s % kGdBuf) * kGdStage;
+    const uint4* Bs = (const uint4*)(st + kGdA) + tl * 4 * 64;
+    const uint8_t* Ss = st + kGdA + kGdB + tl * 1024;
+    const int cin0 = ((s * F::SCOLS) % kSSCols) / F::CC;
+    uint4 raw[2][2];
+    uint2 sc[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) raw[nb][kk] = Bs[(2 * nb + (row >> 4)) * 64 + 16 * (2 * kk + kh) + (lane & 15)];
+      sc[nb] = *(const uint2*)(Ss + (16 * (2 * nb + (row >> 4)) + (lane & 15)) * 16 + 8 * cin0);
+    }
+    const auto afrag = [&](int ks, int mb) {
+      const int m = WTOK * wm + 32 * mb + row, c = 2 * ks + kh;
+      return *(const uint4*)(st + m * 256 + 16 * (c ^ (m & 15)));
+    };
+    uint4 av[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) av[0][mb] = afrag(0, mb);
+#pragma unroll
+    for (int ks = 0; ks < F::KS; ++ks) {
+      const int kk = ks & 1, b = ks >> 1;
+      if (ks + 1 < F::KS)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) av[(ks + 1) & 1][mb] = afrag(ks + 1, mb);
+      uint4 bw[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) bw[nb] = decode_b<kFP4>(raw[nb][kk], sc[nb], b, b, 2 * kk + kh);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, av[ks & 1][mb]),
+                                                               __builtin_bit_cast(half8, bw[nb]), acc[mb][nb],
+                                                               0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+  if (!b_on) return;
+  const float* ts = (const float*)(base + a.ts_off);
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int i = WTOK * wm + acc_tok(lane, mb, v);
+      if (i >= pc.count) continue;
+      const size_t pos = (size_t)pc.start + i;
+      const float tg = ts[0], tu = ts[1];
+      const int f = 32 * tile + (lane & 31);
+      const float hv = silu(acc[mb][0][v] * tg) * (acc[mb][1][v] * tu);
+      ((_Float16*)a.out)[pos * a.ostride + f] = (_Float16)hv;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Narrow pieces of the expert GEMMs (at most 64 tokens). Most experts draw
 // few tokens (the median of the 145B prefill input is 10), and in a
 // 128-token tile such a piece leaves waves without MFMAs while every wave
@@ -1100,6 +1278,13 @@ static int launch_short(const Grouped& a, unsigned npc, int lo, int hi, hipStrea
 template <int EPI>
 static int launch_grouped(const Grouped& a, unsigned maxp, int E, hipStream_t st) {
   const unsigned ncls = std::min<unsigned>(maxp, E);
+  if constexpr (EPI == kGateUp)
+    if (a.A.kmat % Fm<kFP4>::SCOLS == 0) {
+      hipLaunchKernelGGL(k_grouped_dma<EPI>, dim3(8u * a.nquads * ((maxp + 7) / 8)), dim3(NTH), 0, st, a);
+      LMOE_HIP(hipGetLastError());
+      if (int rc = launch_short<EPI, 2>(a, ncls, 1, 2, st)) return rc;
+      return launch_short<EPI, 1>(a, ncls, 2, 0, st);
+    }
   if (EPI == kDown && a.A.kmat <= kResMaxK) {
     // pieces of more than 32 tokens in 64-token blocks, the rest in 32
     hipLaunchKernelGGL((k_down_res<8, 2>), dim3(8u * 2 * ((maxp + 7) / 8)), dim3(512), 0, st, a, -1, 2, 2);
@@ -1729,23 +1914,6 @@ constexpr int kWgA = kWgT * kWgCols * 2;                 // activation bytes per
 constexpr int kWgB = (kWgN / 64) * 4 * kSlot;            // weight bytes per stage
 constexpr int kWgStage = kWgA + kWgB;
 static_assert(kWgBuf * kWgStage <= 160 * 1024, "LDS");
-
-// 16 bytes per lane from r + voff + soff to LDS m0 + 16 lane. Written in
-// assembly so that the compiler, which cannot tell which LDS bytes a DMA
-// writes, does not wait for every DMA before each LDS read; the kernel waits
-// for the stage it needs (vmcnt) itself. No register is written.
-__device__ __forceinline__ void dma16(rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               ::"s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
-}
-
-// s_waitcnt operand that waits for vmcnt <= n only (gfx9 encoding: vmcnt in
-// bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 at their maxima)
-constexpr int vmcnt_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
-
-__device__ __forceinline__ uint32_t lds_off(const void* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
-}
 
 template <int EPI>
 __global__ __launch_bounds__(256) void k_dense16(Dense a) {

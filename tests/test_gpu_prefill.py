@@ -256,6 +256,26 @@ def test_prefill_wide_expert_ffn():
     check_outputs(c, got, dbg, np.arange(400))
 
 
+def test_prefill_latent_not_multiple_of_128():
+    """Latent 192 (Q8 D/U): the expert gate/up's K is not a multiple of the
+    128-column FP4 stage, so its pieces of more than 64 tokens run on the
+    register-staged k_grouped (the DMA-fed kernel needs whole stages) and its
+    last stage is half real columns; the down projection (K = 96) is ragged
+    in the resident kernel. Skewed router, every piece class present, every
+    token checked."""
+    w = wl.Workload("latent192", 256, 192, 16, 4, 2, 96, 64, 8, 300, router_bias=True)
+    c = Case(w, seed=4, tokens=300)
+    layer = make_layer(c, 300)
+    print("case latent192 prefill T 300", flush=True)
+    got, dbg = run(layer, w, c.x)
+    check_routing(c, dbg, 300)
+    cnt = dbg["expert_count"]
+    rem = cnt % 128
+    assert (cnt >= 128).any() and (rem > 64).any()
+    assert ((rem > 32) & (rem <= 64)).any() and ((rem > 0) & (rem <= 32)).any()
+    check_outputs(c, got, dbg, np.arange(300))
+
+
 # ---------------------------------------------------------------------------
 # 145B / 120B shapes, routing over all tokens, outputs on a sample
 
