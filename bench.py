@@ -35,21 +35,21 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 / bf16 matrix peak, published
 PREFILL_PHASES = ["route", "permute", "d", "shared_gate_up", "expert_gate_up", "expert_down",
                   "combine", "u_shared_down"]
-PREFILL_KERNELS = ["k_prep + k_dense<BF16,Logits> + k_select", "k_perm_*",
+PREFILL_KERNELS = ["k_prep + k_dense_dma<BF16,Logits> + k_select", "k_perm_*",
                    "k_dense16<F16> (D; 128 x 128 wave tiles, LDS DMA)",
-                   "k_dense<BF16,SwigluB2> (shared gate/up)",
+                   "k_dense_dma<BF16,SwigluB2> (shared gate/up)",
                    "k_grouped_dma<GateUp> (LDS DMA) + k_grouped_short<GateUp> (64- and 32-token pieces)",
                    "k_down_res (activations resident in LDS; 64- and 32-token blocks)", "k_combine",
-                   "k_dense<F16,Y> (U + shared down, split along k) + k_ytiles (split sums)"]
+                   "k_dense_dma<F16,Y> (U + shared down, split along k; LDS DMA) + k_ytiles (split sums)"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_145b_t4_traffic.json")
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_145b_t4096_traffic.json")
 # kernel of each prefill phase as rocprofv3 names it (D and U on fp16 weights)
-PREFILL_KERNEL_IDS = [["k_prep", "k_dense<3, 0>", "k_select<5, 8>"],
+PREFILL_KERNEL_IDS = [["k_prep", "k_dense_dma<3, 0>", "k_select<5, 8>"],
                       ["k_perm_mask", "k_perm_scan", "k_perm_scatter"], "k_dense16<1>",
-                      "k_dense<3, 2>",
+                      "k_dense_dma<3, 2>",
                       ["k_grouped_dma<0>", "k_grouped_short<0, 2, 8>", "k_grouped_short<0, 1, 8>"],
                       ["k_down_res<8, 2>", "k_down_res<8, 1>"], "k_combine",
-                      ["k_dense<5, 3>", "k_ytiles<4>"]]
+                      ["k_dense_dma<5, 3>", "k_ytiles<4>"]]
 
 
 def log(*a):

@@ -549,6 +549,70 @@ __device__ __forceinline__ void tile_of(int L, int mtiles, int nquads, int& mt, 
   quad = (L % span) / gsz;
 }
 
+// ---------------------------------------------------------------------------
+// LDS DMA.
+
+// 16 bytes per lane from r + voff + soff to LDS m0 + 16 lane. Written in
+// assembly so that the compiler, which cannot tell which LDS bytes a DMA
+// writes, does not wait for every DMA before each LDS read; the kernel waits
+// for the stage it needs (vmcnt) itself. No register is written.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               ::"s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
+}
+
+// s_waitcnt operand that waits for vmcnt <= n only (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 at their maxima)
+constexpr int vmcnt_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+constexpr uint32_t kOob = 0xFFFFFFF0u;                   // a DMA offset past any resource: out of range
+
+// the k_dense epilogues for the wave's accumulators (tile row block mt,
+// weight tile `tile`, split sp of nsp of logical tile L)
+template <int EPI>
+__device__ __forceinline__ void dense_epilogue(const Dense& a, const f16v (&acc)[MB][2], int mt, int quad, int tile,
+                                               int L, int sp, int nsp, int lane, int wm) {
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int t = mt * BM + WTOK * wm + acc_tok(lane, mb, v);
+      if (t >= a.T) continue;
+      if constexpr (EPI == kEpiSwigluB2) {
+        // rows 0..31 of the tile are gate rows 32*tile + 0..31, rows 32..63
+        // the up rows of the same indices
+        const int f = 32 * tile + (lane & 31);
+        const float hv = silu(acc[mb][0][v]) * acc[mb][1][v];
+        const __bf16 h0 = (__bf16)hv;
+        const __bf16 h1 = (__bf16)(hv - (float)h0);
+        __bf16* o = (__bf16*)a.out + (size_t)t * a.ostride;
+        o[f] = h0;
+        o[a.nvalid + f] = h1;
+      } else {
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg) {
+          const int n = 64 * tile + 32 * rg + (lane & 31);
+          const float val = acc[mb][rg][v];
+          if constexpr (EPI == kEpiLogits) {
+            if (n < a.nvalid) ((float*)a.out)[((size_t)sp * a.T + t) * a.ostride + n] = val;
+          } else if constexpr (EPI == kEpiF16) {
+            ((_Float16*)a.out)[(size_t)t * a.ostride + n] = (_Float16)val;
+          } else if (nsp > 1) {
+            const size_t j = (size_t)sp * a.nrem + (L - a.nfull);
+            a.part[(j * BM + (t - mt * BM)) * 256 + (n - 256 * quad)] = val;
+          } else {
+            const size_t i = (size_t)t * a.ostride + n;
+            ((float*)a.out)[i] = a.res ? a.res[i] + val : val;
+          }
+        }
+      }
+    }
+}
+
 template <int WF, int EPI>
 __global__ __launch_bounds__(NTH) void k_dense(Dense a) {
   __shared__ __align__(16) uint8_t smem[2 * kStage];
@@ -596,42 +660,154 @@ __global__ __launch_bounds__(NTH) void k_dense(Dense a) {
     gemm_wave<WF>(a.W, tile, b_on, nmb, a.A, arow, smem, acc);
   }
   if (!b_on) return;
+  dense_epilogue<EPI>(a, acc, mt, quad, tile, L, sp, nsp, lane, wm);
+}
 
+// ---------------------------------------------------------------------------
+// The dense GEMMs of 16-bit weights (router, shared gate/up, U + shared
+// down) with DMA-fed operands: the geometry and epilogues of k_dense, but
+// 32-column stages copied global -> LDS by buffer DMA (activation rows of
+// all parts and the weights' raw slots), three stages ahead in four 32 KB
+// buffers, so the loop issues no vector loads or LDS stores of its own.
+// Activation rows are 64 B, their four 16 B pieces XOR-swizzled by
+// (row / 4) % 4: the fragment reads of 16 consecutive rows hit distinct
+// banks. K of every matrix is a multiple of 64 (k_dense's stage unit), so
+// stage s of k_dense is stages 2s and 2s + 1 here.
+
+constexpr int kDdCols = 32, kDdBuf = 4, kDdStage = 32 * 1024, kDdB = 16 * 1024;
+
+// stages [2 sb, 2 se) of W (sb, se in 64-column units); the wave's 64 tokens
+// x 64-row tile as in gemm_wave, both 32-token blocks always computed
+template <int WF>
+__device__ __forceinline__ void gemm_wave_dma(const WMat& W, int tile, bool b_on, const AMat& A,
+                                              const int* arow, uint8_t* smem, f16v (&acc)[MB][2],
+                                              int sb64, int se64) {
+  constexpr int NP = WF == kBF16 ? 2 : 1;
+  static_assert(WF == kBF16 || WF == kF16, "16-bit weights");
+  const int sb = 2 * sb64, se = 2 * se64;
+  if (se <= sb) return;
+  const int lane = threadIdx.x & 63, wave = wave_id(), wm = wave & 1, tl = wave >> 1;
+  const int row = lane & 31, kh = lane >> 5;
+  const int spm = W.g.k / kDdCols;
+  // activation DMA: instruction (part p, i = wave) covers rows 16 i .. + 15;
+  // lane l the piece at position l % 4 of row 16 i + l / 4
+  const int r = 16 * wave + (lane >> 2);
+  const int arw = arow[r];
+  const int cch = 8 * ((lane & 3) ^ ((r >> 2) & 3));
+  const uint32_t abase = arw >= 0 ? (uint32_t)((size_t)arw * A.rs * 2) : kOob;
+  const rsrc_t ar = rsrc(A.p, kOob);
+  const size_t wspan = (size_t)(W.nmat - 1) * W.mat_bytes + (size_t)W.g.tile_slots * kSlot;
+  const rsrc_t wt = rsrc(W.base + (size_t)(b_on ? tile : 0) * W.g.tile_slots * kSlot, b_on ? (uint32_t)wspan : 0u);
+  const rsrc_t wz = rsrc(W.base, 0u);
+  const uint32_t sbase = lds_off(smem);
+  const auto issue = [&](int s) {
+    const bool live = s < se;
+    const uint32_t st = sbase + (uint32_t)((s % kDdBuf) * kDdStage);
+    s = min(s, se - 1);
+    const int mat = s / spm, sm = s % spm;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+    for (int p = 0; p < NP; ++p) {
+      const uint32_t vo = (abase == kOob || !live)
+                              ? kOob
+                              : abase + (uint32_t)(2 * (p * A.ps + mat * A.kmat + sm * kDdCols + cch));
+      dma16(ar, st + p * 8192 + wave * 1024, vo, 0);
+    }
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int t = mt * BM + WTOK * wm + acc_tok(lane, mb, v);
-      if (t >= a.T) continue;
-      if constexpr (EPI == kEpiSwigluB2) {
-        // rows 0..31 of the tile are gate rows 32*tile + 0..31, rows 32..63
-        // the up rows of the same indices
-        const int f = 32 * tile + (lane & 31);
-        const float hv = silu(acc[mb][0][v]) * acc[mb][1][v];
-        const __bf16 h0 = (__bf16)hv;
-        const __bf16 h1 = (__bf16)(hv - (float)h0);
-        __bf16* o = (__bf16*)a.out + (size_t)t * a.ostride;
-        o[f] = h0;
-        o[a.nvalid + f] = h1;
-      } else {
+    for (int h = 0; h < 2; ++h) {
+      const int rg = 2 * wm + h;
+      dma16(live ? wt : wz, st + kDdB + (tl * 4 + rg) * 1024, lane * 16,
+            (uint32_t)((size_t)mat * W.mat_bytes + (size_t)(4 * sm + rg) * kSlot));
+    }
+  };
+  // the buffers may still be read by a previous range's last stage
+  __syncthreads();
+  issue(sb);
+  issue(sb + 1);
+  issue(sb + 2);
+  for (int s = sb; s < se; ++s) {
+    // this wave's DMAs of stage s are done when at most those of s + 1 and
+    // s + 2 are in flight; the barrier makes every wave's visible and ends
+    // the reads of stage s - 1, whose buffer stage s + 3 refills
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * (NP + 2)));
+    __syncthreads();
+    issue(s + 3);
+    const uint8_t* st = smem + (s % kDdBuf) * kDdStage;
 #pragma unroll
-        for (int rg = 0; rg < 2; ++rg) {
-          const int n = 64 * tile + 32 * rg + (lane & 31);
-          const float val = acc[mb][rg][v];
-          if constexpr (EPI == kEpiLogits) {
-            if (n < a.nvalid) ((float*)a.out)[((size_t)sp * a.T + t) * a.ostride + n] = val;
-          } else if constexpr (EPI == kEpiF16) {
-            ((_Float16*)a.out)[(size_t)t * a.ostride + n] = (_Float16)val;
-          } else if (nsp > 1) {
-            const size_t j = (size_t)sp * a.nrem + (L - a.nfull);
-            a.part[(j * BM + (t - mt * BM)) * 256 + (n - 256 * quad)] = val;
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c = 2 * ks + kh;
+      uint4 af[NP][2], bf[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const int m = WTOK * wm + 32 * mb + row;
+          af[p][mb] = *(const uint4*)(st + (p * BM + m) * 64 + 16 * (c ^ ((m >> 2) & 3)));
+        }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        bf[nb] = *(const uint4*)(st + kDdB + ((tl * 4 + 2 * nb + (row >> 4)) * 64 + 16 * c + (lane & 15)) * 16);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          if constexpr (WF == kBF16) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8, af[p][mb]), __builtin_bit_cast(bf16x8, bf[nb]), acc[mb][nb], 0, 0, 0);
           } else {
-            const size_t i = (size_t)t * a.ostride + n;
-            ((float*)a.out)[i] = a.res ? a.res[i] + val : val;
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(half8, af[0][mb]), __builtin_bit_cast(half8, bf[nb]), acc[mb][nb], 0, 0, 0);
           }
         }
-      }
     }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+}
+
+template <int WF, int EPI>
+__global__ __launch_bounds__(NTH) void k_dense_dma(Dense a) {
+  __shared__ __align__(1024) uint8_t smem[kDdBuf * kDdStage];
+  __shared__ int arow[BM];
+  constexpr bool SPLIT = EPI == kEpiY || EPI == kEpiLogits;
+  const int nblk0 = a.mtiles * a.nquads;
+  int L = 0, sp = 0, nsp = 1;
+  if (!SPLIT || (int)blockIdx.x < a.nfull) {
+    L = xcd_order(blockIdx.x, SPLIT ? a.nfull : nblk0);
+  } else {
+    const int Ls = xcd_order(blockIdx.x - a.nfull, a.nrem * a.nsplit);
+    sp = Ls / a.nrem;
+    L = a.nfull + Ls % a.nrem;
+    nsp = a.nsplit;
+  }
+  int mt, quad;
+  tile_of(L, a.mtiles, a.nquads, mt, quad);
+  if (threadIdx.x < BM) {
+    const int t = mt * BM + threadIdx.x;
+    arow[threadIdx.x] = t < a.T ? t : -1;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = wave_id(), wm = wave & 1;
+  const int tile = NTW * quad + (wave >> 1);
+  const bool b_on = tile < a.ntiles;
+  f16v acc[MB][2];
+  zero_acc(acc);
+  if constexpr (EPI == kEpiY) {
+    const int n1 = n_stages<WF>(a.W), n2 = n_stages<kBF16>(a.W2), units = n1 + 2 * n2;
+    const int c0 = (int)((long long)units * sp / nsp);
+    const int c1 = (int)((long long)units * (sp + 1) / nsp);
+    const auto w2_stage = [&](int c) { return min(n2, max(0, (c - n1 + 1) / 2)); };
+    gemm_wave_dma<WF>(a.W, tile, b_on, a.A, arow, smem, acc, min(c0, n1), min(c1, n1));
+    gemm_wave_dma<kBF16>(a.W2, tile, b_on, a.A2, arow, smem, acc, w2_stage(c0), w2_stage(c1));
+  } else if constexpr (EPI == kEpiLogits) {
+    const int n1 = n_stages<WF>(a.W);
+    gemm_wave_dma<WF>(a.W, tile, b_on, a.A, arow, smem, acc,
+                      (int)((long long)n1 * sp / nsp), (int)((long long)n1 * (sp + 1) / nsp));
+  } else {
+    gemm_wave_dma<WF>(a.W, tile, b_on, a.A, arow, smem, acc, 0, n_stages<WF>(a.W));
+  }
+  if (!b_on) return;
+  dense_epilogue<EPI>(a, acc, mt, quad, tile, L, sp, nsp, lane, wm);
 }
 
 // ---------------------------------------------------------------------------
@@ -718,26 +894,6 @@ __global__ __launch_bounds__(NTH) void k_grouped(Grouped a) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS DMA.
-
-// 16 bytes per lane from r + voff + soff to LDS m0 + 16 lane. Written in
-// assembly so that the compiler, which cannot tell which LDS bytes a DMA
-// writes, does not wait for every DMA before each LDS read; the kernel waits
-// for the stage it needs (vmcnt) itself. No register is written.
-__device__ __forceinline__ void dma16(rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               ::"s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
-}
-
-// s_waitcnt operand that waits for vmcnt <= n only (gfx9 encoding: vmcnt in
-// bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 at their maxima)
-constexpr int vmcnt_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
-
-__device__ __forceinline__ uint32_t lds_off(const void* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
-}
-
-// ---------------------------------------------------------------------------
 // Expert gate/up for pieces of more than 64 tokens, operands fed by DMA. The
 // geometry of k_grouped (128 tokens x 4 weight tiles, each wave 64 tokens x
 // one 64-row tile), but no register staging: the activation rows (gathered
@@ -756,7 +912,6 @@ constexpr int kGdS = NTW * kSlot;                        // scale slots
 constexpr int kGdStage = kGdA + kGdB + kGdS;
 constexpr int kGdBuf = 3;
 static_assert(kGdBuf * kGdStage + BM * 4 <= 160 * 1024, "LDS");
-constexpr uint32_t kOob = 0xFFFFFFF0u;                   // a DMA offset past any resource: zeros
 
 template <int EPI>
 __global__ __launch_bounds__(NTH) void k_grouped_dma(Grouped a) {
@@ -2043,6 +2198,12 @@ int launch_dense(const Dense& a, hipStream_t st) {
     if (a.A.kmat % kWgCols == 0 && a.A.ps == 0 && a.W.nmat == 1) {
       const unsigned n16 = (unsigned)(((a.T + kWgT - 1) / kWgT) * ((a.ntiles + 3) / 4));
       hipLaunchKernelGGL((k_dense16<EPI>), dim3(n16), dim3(256), 0, st, a);
+      LMOE_HIP(hipGetLastError());
+      return 0;
+    }
+  if constexpr (WF == kF16 || WF == kBF16)
+    if (a.W.g.k % 64 == 0 && (EPI != kEpiY || a.W2.g.k % 64 == 0)) {
+      hipLaunchKernelGGL((k_dense_dma<WF, EPI>), dim3(nblk), dim3(NTH), 0, st, a);
       LMOE_HIP(hipGetLastError());
       return 0;
     }
