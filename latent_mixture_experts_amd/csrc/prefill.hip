@@ -2259,12 +2259,13 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     hipLaunchKernelGGL(k_prep, dim3(T), dim3(256), 0, st, a);
     LMOE_HIP(hipGetLastError());
   }
-  // D and the shared gate/up need only the staged rows: they run on the aux
-  // stream while the routing chain runs on the caller's. When phases are
-  // timed everything runs on the caller's stream in phase order, so that
-  // each phase is measured alone.
-  auto dense_front = [&](hipStream_t sd) -> int {
-    {
+  // D and the shared gate/up need only the staged rows: D runs on the aux
+  // stream while the routing chain and then the shared gate/up run on the
+  // caller's (D alone is longer than both). When phases are timed everything
+  // runs on the caller's stream in phase order, so that each phase is
+  // measured alone.
+  auto dense_front = [&](hipStream_t sd, bool d_part, bool s_part) -> int {
+    if (d_part) {
       Dense a{};
       a.W = WMat{h->dmat16, h->g_d16, 0, 1};
       a.A = AMat{p.xh, (size_t)H, 0, H};
@@ -2273,7 +2274,7 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
       if (int rc = launch_dense<kF16, kEpiF16>(a, sd)) return rc;
       if (ev) LMOE_HIP(hipEventRecord(h->phase_events[3], sd));
     }
-    {
+    if (s_part) {
       Dense a{};
       a.W = WMat{h->sgu, h->g_sgu, 0, 1};
       a.A = AMat{p.xb, (size_t)2 * H, H, H};
@@ -2287,7 +2288,7 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
   if (!ev) {
     LMOE_HIP(hipEventRecord(h->ev_fork, st));
     LMOE_HIP(hipStreamWaitEvent(h->aux, h->ev_fork, 0));
-    if (int rc = dense_front(h->aux)) return rc;
+    if (int rc = dense_front(h->aux, true, false)) return rc;
     LMOE_HIP(hipEventRecord(h->ev_join, h->aux));
   }
   // router logits
@@ -2354,8 +2355,9 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
   }
   if (ev) {
     LMOE_HIP(hipEventRecord(h->phase_events[2], st));
-    if (int rc = dense_front(st)) return rc;
+    if (int rc = dense_front(st, true, true)) return rc;
   } else {
+    if (int rc = dense_front(st, false, true)) return rc;
     LMOE_HIP(hipStreamWaitEvent(st, h->ev_join, 0));
   }
   // experts
