@@ -1479,28 +1479,41 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
   return s;
 }
 
+// One block per token, 8 columns per thread and step (H is a multiple of 256).
 __global__ __launch_bounds__(256) void k_prep(Prep a) {
   __shared__ double red[4];
   const int t = blockIdx.x;
   const float* xr = a.x + (size_t)t * a.H;
+  const int nc = a.H / 8;
   float r = 1.0f;
   if (a.norm) {
     double s = 0.0;
-    for (int i = threadIdx.x; i < a.H; i += blockDim.x) {
-      const double v = xr[i];
-      s += v * v;
+    for (int c = threadIdx.x; c < nc; c += blockDim.x) {
+      const float4 u0 = *(const float4*)(xr + 8 * c), u1 = *(const float4*)(xr + 8 * c + 4);
+      const float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s += (double)v[j] * v[j];
     }
     s = block_sum(s, red);
     r = (float)(1.0 / sqrt(s / a.H + (double)a.eps));
   }
   double s2 = 0.0;
-  for (int i = threadIdx.x; i < a.H; i += blockDim.x) {
-    const float v = a.norm ? xr[i] * r : xr[i];
-    a.xh[(size_t)t * a.H + i] = (_Float16)v;
-    const __bf16 b0 = (__bf16)v;
-    a.xb[(size_t)t * 2 * a.H + i] = b0;
-    a.xb[(size_t)t * 2 * a.H + a.H + i] = (__bf16)(v - (float)b0);
-    s2 += (double)v * v;
+  for (int c = threadIdx.x; c < nc; c += blockDim.x) {
+    const float4 u0 = *(const float4*)(xr + 8 * c), u1 = *(const float4*)(xr + 8 * c + 4);
+    float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    half8 h;
+    bf16x8 b0, b1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (a.norm) v[j] *= r;
+      h[j] = (_Float16)v[j];
+      b0[j] = (__bf16)v[j];
+      b1[j] = (__bf16)(v[j] - (float)b0[j]);
+      s2 += (double)v[j] * v[j];
+    }
+    *(half8*)(a.xh + (size_t)t * a.H + 8 * c) = h;
+    *(bf16x8*)(a.xb + (size_t)t * 2 * a.H + 8 * c) = b0;
+    *(bf16x8*)(a.xb + (size_t)t * 2 * a.H + a.H + 8 * c) = b1;
   }
   s2 = block_sum(s2, red);
   if (threadIdx.x == 0) {
@@ -1937,9 +1950,18 @@ struct Combine {
   int K, G, L;
 };
 
+// One block per token; a thread owns 8 columns (one 16-byte chunk) of the
+// ell outputs. The token's K assignments are put in (group, k) order (each
+// ranked by its own thread, in LDS); a thread loads its chunk of up to
+// 16 of them at once and walks them in that order with one running fp32
+// sum, writing each group's sum (zeros for groups the token skips) when the
+// walk passes it: every group's sum is over ascending k.
+constexpr int kCombBatch = 16;
+
 __global__ __launch_bounds__(256) void k_combine(Combine a) {
   __shared__ int pos[64];
   __shared__ int lab[64];
+  __shared__ int ord[64];                  // assignment k in (group, k) order
   const int t = blockIdx.x;
   if (threadIdx.x < a.K) {
     const size_t i = (size_t)t * a.K + threadIdx.x;
@@ -1947,25 +1969,45 @@ __global__ __launch_bounds__(256) void k_combine(Combine a) {
     lab[threadIdx.x] = a.labels[a.idx[i]];
   }
   __syncthreads();
-  const int nq = a.L / 4;
-  for (int g = 0; g < a.G; ++g) {
-    for (int q = threadIdx.x; q < nq; q += blockDim.x) {
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int k = 0; k < a.K; ++k) {
-        if (lab[k] != g) continue;
-        const uint2 raw = *(const uint2*)(a.o + (size_t)pos[k] * a.L + 4 * q);
-        const half2v v0 = __builtin_bit_cast(half2v, raw.x), v1 = __builtin_bit_cast(half2v, raw.y);
-        acc.x += (float)v0[0];
-        acc.y += (float)v0[1];
-        acc.z += (float)v1[0];
-        acc.w += (float)v1[1];
+  if (threadIdx.x < a.K) {
+    // rank of assignment k: those of lower labels, then those of its label before it
+    const int k = threadIdx.x, lk = lab[k];
+    int rank = 0;
+    for (int j = 0; j < a.K; ++j) rank += (lab[j] < lk) || (lab[j] == lk && j < k);
+    ord[rank] = k;
+  }
+  __syncthreads();
+  const int nc = a.L / 8;
+  for (int q = threadIdx.x; q < nc; q += blockDim.x) {
+    _Float16* out = a.s + (size_t)t * a.G * a.L + 8 * q;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int g = 0;
+    const auto flush = [&]() {
+      half8 h;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        h[j] = (_Float16)acc[j];
+        acc[j] = 0.f;
       }
-      _Float16* d = a.s + ((size_t)t * a.G + g) * a.L + 4 * q;
-      half2v h0 = {(_Float16)acc.x, (_Float16)acc.y};
-      half2v h1 = {(_Float16)acc.z, (_Float16)acc.w};
-      *(half2v*)d = h0;
-      *(half2v*)(d + 2) = h1;
+      *(half8*)(out + (size_t)g * a.L) = h;
+      ++g;
+    };
+    for (int k0 = 0; k0 < a.K; k0 += kCombBatch) {
+      uint4 raw[kCombBatch];
+#pragma unroll
+      for (int u = 0; u < kCombBatch; ++u)
+        if (k0 + u < a.K) raw[u] = *(const uint4*)(a.o + (size_t)pos[ord[k0 + u]] * a.L + 8 * q);
+#pragma unroll
+      for (int u = 0; u < kCombBatch; ++u) {
+        if (k0 + u >= a.K) break;
+        const int gi = lab[ord[k0 + u]];
+        while (g < gi) flush();
+        const half8 v = __builtin_bit_cast(half8, raw[u]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += (float)v[j];
+      }
     }
+    while (g < a.G) flush();
   }
 }
 
