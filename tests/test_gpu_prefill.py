@@ -276,6 +276,21 @@ def test_prefill_latent_not_multiple_of_128():
     check_outputs(c, got, dbg, np.arange(300))
 
 
+def test_prefill_shared_ffn_not_multiple_of_64():
+    """Shared ffn 96: the shared down projection's K is not a multiple of the
+    64-column unit the DMA-fed dense GEMM splits by, so U + shared down runs
+    on the register-staged k_dense (its other users always qualify). Every
+    token checked."""
+    w = wl.Workload("shared96", 256, 128, 16, 2, 2, 64, 96, 8, 200)
+    c = Case(w, seed=5, tokens=200)
+    layer = make_layer(c, 200)
+    for T in (200, 77):
+        print("case shared96 prefill T", T, flush=True)
+        got, dbg = run(layer, w, c.x[:T])
+        check_routing(c, dbg, T)
+        check_outputs(c, got, dbg, np.arange(T))
+
+
 # ---------------------------------------------------------------------------
 # 145B / 120B shapes, routing over all tokens, outputs on a sample
 
