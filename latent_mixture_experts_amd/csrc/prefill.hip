@@ -1030,7 +1030,6 @@ __global__ __launch_bounds__(NTH) void k_grouped_dma(Grouped a) {
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, av[ks & 1][mb]),
                                                                __builtin_bit_cast(half8, bw[nb]), acc[mb][nb],
                                                                0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
     }
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
