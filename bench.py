@@ -16,8 +16,8 @@ prefill layer (T = 4096, router bias N(0, 1) skewing expert loads) on the
 prefill path, with its per-kernel MFMA roofline. --workload 145b_prefill makes
 that the primary line.
 
-Prints one JSON line (rank 0). --gpus above 1 is refused: this build runs on
-one GPU.
+Prints one JSON line (rank 0). --gpus above 1 is refused: the library runs
+on one GPU.
 """
 
 import argparse
@@ -291,7 +291,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(--gpus %d refused)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
