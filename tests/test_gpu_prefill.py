@@ -291,6 +291,40 @@ def test_prefill_shared_ffn_not_multiple_of_64():
         check_outputs(c, got, dbg, np.arange(T))
 
 
+# expert loads on both sides of every piece-class boundary (pieces of 32 /
+# 33, 64 / 65 tokens; a whole 128-token piece; 128 + 1) plus idle experts
+BOUNDARY_COUNTS = [32, 33, 64, 65, 128, 129, 1, 0, 127, 96, 31, 63, 0, 2, 97, 30]
+
+
+@pytest.mark.parametrize("latent,ffn", [(128, 64), (512, 160)])
+def test_prefill_piece_class_boundaries(latent, ffn):
+    """Exact expert loads by construction: the router is the identity on the
+    first 16 hidden dimensions and token t's row carries 4 and 3.9 on its two
+    experts (small noise elsewhere), so top-2 picks them with a wide margin;
+    the sorted assignment list, split in halves, gives every token two
+    distinct experts. Latent 128 / ffn 64 runs the narrow-piece kernels with
+    4 waves, latent 512 / ffn 160 with 8 (three of them past the last gate/up
+    tile). Every token checked."""
+    T = sum(BOUNDARY_COUNTS) // 2
+    w = wl.Workload("bounds", 256, latent, 16, 2, 2, ffn, 64, 8, T)
+    m = wl.masters(w, seed=6)
+    r = np.zeros((16, 256), np.float32)
+    r[np.arange(16), np.arange(16)] = 1.0
+    m["router"] = r
+    lst = np.repeat(np.arange(16), BOUNDARY_COUNTS)
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((T, 256)) * 0.05).astype(np.float32)
+    x[np.arange(T), lst[:T]] += 4.0
+    x[np.arange(T), lst[T:]] += 3.9
+    c = Case(w, x=x, masters=m, tokens=T)
+    layer = make_layer(c, T)
+    print("case bounds latent %d ffn %d prefill T %d" % (latent, ffn, T), flush=True)
+    got, dbg = run(layer, w, c.x)
+    check_routing(c, dbg, T)
+    assert dbg["expert_count"].tolist() == BOUNDARY_COUNTS
+    check_outputs(c, got, dbg, np.arange(T))
+
+
 # ---------------------------------------------------------------------------
 # 145B / 120B shapes, routing over all tokens, outputs on a sample
 
