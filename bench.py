@@ -275,6 +275,34 @@ def cpu_baseline(w, seed, tokens):
                           tokens, w.name, seed, len(m["expert_ids"]), dt)}
 
 
+def calibrate_hbm(torch, copy_bytes=256 << 20, reps=4, read_bytes=1 << 30):
+    """Reference runs for the profiler's HBM counters (--calibrate-hbm):
+    a device-to-device copy of exactly 256 MiB, repeated (each copy reads
+    and writes 268,435,456 bytes: the scale for FETCH_SIZE / WRITE_SIZE), and
+    the read bandwidth of a plain streaming reduction over 1 GiB (the
+    achievable-bandwidth reference beside the published peak)."""
+    src = torch.ones(copy_bytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    big = torch.ones(read_bytes // 4, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        big.sum()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 20
+    start.record()
+    for _ in range(n):
+        big.sum()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / n
+    print(json.dumps({"copy_bytes_per_launch": copy_bytes, "copies": reps,
+                      "sum_read_bytes": read_bytes, "sum_ms": ms,
+                      "sum_read_GBps": read_bytes / (ms * 1e-3) / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -289,6 +317,8 @@ def main():
     ap.add_argument("--prefill-warmup", type=int, default=3)
     ap.add_argument("--prefill-copies", type=int, default=2)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--calibrate-hbm", action="store_true",
+                    help="only run the reference copy and read for the HBM counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
@@ -296,6 +326,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_hbm:
+        calibrate_hbm(torch)
+        return
     from latent_mixture_experts_amd import lmoe as lm
     from latent_mixture_experts_amd import workloads as wl
 

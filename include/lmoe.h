@@ -111,6 +111,9 @@ typedef struct lmoe_debug {
   float*   topk_w;         /* [T][K] renormalized softmax weights */
   int32_t* perm;           /* [T*K]: stable sort of a = t*K+k by (label, expert) */
   int32_t* expert_count;   /* [E] assignments per expert */
+  int32_t* expert_off;     /* [E+1] exclusive scan of expert_count in expert-id
+                              order: expert_off[e] = sum of expert_count[e']
+                              over e' < e, expert_off[E] = T*K */
   int32_t* group_off;      /* [G+1] start of each group's segment in perm */
   float*   latent;         /* [T][G][ell] D_g x; entries of (t, g) pairs that
                               token t does not use are unspecified. For

@@ -185,6 +185,23 @@ struct DeviceGuard {
   }
 };
 
+// Exclusive scan of n counts into off[0..n] by one block (n <= 1024).
+__global__ __launch_bounds__(1024) void k_exclusive_scan(const int* __restrict__ cnt, int n,
+                                                         int* __restrict__ off) {
+  __shared__ int buf[1024];
+  const int i = threadIdx.x;
+  buf[i] = i < n ? cnt[i] : 0;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {      // inclusive Hillis-Steele scan
+    const int v = i >= d ? buf[i - d] : 0;
+    __syncthreads();
+    buf[i] += v;
+    __syncthreads();
+  }
+  if (i < n) off[i + 1] = buf[i];
+  if (i == 0) off[0] = 0;
+}
+
 int copy_debug(lmoe_t* h, const lmoe_debug* dbg, int T, hipStream_t st) {
   const lmoe_dims& d = h->d;
   const Workspace& w = h->ws;
@@ -198,6 +215,12 @@ int copy_debug(lmoe_t* h, const lmoe_debug* dbg, int T, hipStream_t st) {
   if (dbg->expert_count)
     LMOE_HIP(hipMemcpyAsync(dbg->expert_count, pre ? p.expert_count : w.expert_count,
                             4 * (size_t)d.n_experts, D2D, st));
+  if (dbg->expert_off) {
+    hipLaunchKernelGGL(k_exclusive_scan, dim3(1), dim3(1024), 0, st,
+                       (const int*)(pre ? p.expert_count : w.expert_count), d.n_experts,
+                       dbg->expert_off);
+    LMOE_HIP(hipGetLastError());
+  }
   if (dbg->group_off)
     LMOE_HIP(hipMemcpyAsync(dbg->group_off, pre ? p.group_off : w.group_off,
                             4 * (size_t)(d.n_groups + 1), D2D, st));

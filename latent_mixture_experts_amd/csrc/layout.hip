@@ -414,6 +414,10 @@ int load_weights_impl(lmoe_t* h, const lmoe_weights* w, hipStream_t st) {
       set_error("lmoe_load_weights: a group label is >= n_groups");
       return LMOE_EINVAL;
     }
+  // From here on the device copies are overwritten: the handle refuses
+  // forwards until every part of the new weights is in place, so a load that
+  // fails midway cannot leave a mix of old and new weights in use.
+  h->loaded = false;
 
   // router, bias, labels
   {

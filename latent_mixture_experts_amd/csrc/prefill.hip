@@ -555,11 +555,17 @@ __device__ __forceinline__ void tile_of(int L, int mtiles, int nquads, int& mt, 
 // 16 bytes per lane from r + voff + soff to LDS m0 + 16 lane. Written in
 // assembly so that the compiler, which cannot tell which LDS bytes a DMA
 // writes, does not wait for every DMA before each LDS read; the kernel waits
-// for the stage it needs (vmcnt) itself. No register is written.
+// for the stage it needs (vmcnt) itself. No vector register is written; m0
+// (the LDS address) is, and is declared clobbered: the compiler reserves m0
+// and sets it itself before each of its own uses, so it warns that a
+// reserved register is listed (silenced here).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               ::"s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
+               ::"s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // s_waitcnt operand that waits for vmcnt <= n only (gfx9 encoding: vmcnt in
 // bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 at their maxima)

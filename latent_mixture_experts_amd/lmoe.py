@@ -43,7 +43,7 @@ class Weights(ctypes.Structure):
 
 class Debug(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "topk_idx", "topk_w", "perm", "expert_count", "group_off", "latent")]
+        "topk_idx", "topk_w", "perm", "expert_count", "expert_off", "group_off", "latent")]
 
 
 class LmoeError(RuntimeError):
@@ -160,7 +160,7 @@ class Layer:
         dbg = None
         if debug is not None:
             dbg = Debug(*[_ptr(debug.get(k)) for k in (
-                "topk_idx", "topk_w", "perm", "expert_count", "group_off", "latent")])
+                "topk_idx", "topk_w", "perm", "expert_count", "expert_off", "group_off", "latent")])
         _check(_lib.lmoe_forward(self._h, _ptr(x), T, _ptr(y),
                                  ctypes.byref(dbg) if dbg is not None else None, _stream(stream)),
                "lmoe_forward")

@@ -34,5 +34,5 @@ from .formats import (  # noqa: F401
 )
 from .layer import (  # noqa: F401
     LayerDims, pack_layer, decode_layer, router_logits, select_topk,
-    permute, layer_forward, rmsnorm, stack_forward,
+    permute, expert_offsets, layer_forward, rmsnorm, stack_forward,
 )

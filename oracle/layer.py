@@ -18,8 +18,8 @@ layer has G groups of D/U, chosen by each expert's group label). Readings:
 * w_e: softmax over all E router logits, keep the top K, renormalize. The
   E-way denominator cancels, so w is the softmax of the K kept logits.
   Ordering of the kept experts: descending logit, ties to the lower index.
-* The router reads the full-width x (TEARDOWN: the router still reads the
-  full 2,560-wide hidden state); logits are exact dot products of the fp32
+* The router reads the full-width x, not the latent (TEARDOWN, "A latent in
+  front of the experts"); logits are exact dot products of the fp32
   x with the bf16 weights, plus an optional per-expert bias.
 * SwiGLU: h = silu(W_gate z) * (W_up z), out = W_down h, silu(v) = v/(1+e^-v).
 * The shared expert is a full-width SwiGLU on x (LAYER: only the 512 experts
@@ -154,6 +154,12 @@ def permute(idx, labels, n_experts, n_groups):
     return perm, count, group_off
 
 
+def expert_offsets(count):
+    """Exclusive scan of the per-expert counts in expert-id order: off[e] is
+    the number of assignments to experts below e, off[E] = T*K."""
+    return np.concatenate([[0], np.cumsum(np.asarray(count, dtype=np.int64))]).astype(np.int32)
+
+
 # ---------------------------------------------------------------------------
 # Forward.
 
@@ -225,7 +231,7 @@ def layer_forward(dims, blobs, x, dec=None, intermediates=False):
     if not intermediates:
         return y
     return dict(y=y, logits=logits, idx=idx, w=w, perm=perm, expert_count=count,
-                group_off=group_off, xl=xl, h=h, o=o, s=s, used=used,
+                expert_off=expert_offsets(count), group_off=group_off, xl=xl, h=h, o=o, s=s, used=used,
                 y_routed=y_routed, y_shared=y_shared)
 
 

@@ -42,6 +42,7 @@ def run(layer, case, T):
         topk_w=torch.empty(T, w.top_k, dtype=torch.float32, device=dev),
         perm=torch.empty(T * w.top_k, dtype=torch.int32, device=dev),
         expert_count=torch.empty(w.n_experts, dtype=torch.int32, device=dev),
+        expert_off=torch.empty(w.n_experts + 1, dtype=torch.int32, device=dev),
         group_off=torch.empty(w.n_groups + 1, dtype=torch.int32, device=dev),
         latent=torch.full((T, w.n_groups, w.latent), float("nan"), device=dev),
     )
@@ -57,6 +58,7 @@ def check(case, layer, T, label):
     assert np.array_equal(dbg["topk_idx"], r["idx"]), "top-K indices differ"
     assert np.array_equal(dbg["perm"], r["perm"]), "permutation differs"
     assert np.array_equal(dbg["expert_count"], r["expert_count"])
+    assert np.array_equal(dbg["expert_off"], r["expert_off"])
     assert np.array_equal(dbg["group_off"], r["group_off"])
     assert np.max(np.abs(dbg["topk_w"] - r["w"])) <= 1e-6
     used = r["used"]

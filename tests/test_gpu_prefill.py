@@ -47,6 +47,7 @@ def run(layer, w, x):
         topk_w=torch.empty(T, w.top_k, dtype=torch.float32, device=dev),
         perm=torch.empty(T * w.top_k, dtype=torch.int32, device=dev),
         expert_count=torch.empty(w.n_experts, dtype=torch.int32, device=dev),
+        expert_off=torch.empty(w.n_experts + 1, dtype=torch.int32, device=dev),
         group_off=torch.empty(w.n_groups + 1, dtype=torch.int32, device=dev),
         latent=torch.full((T, w.n_groups, w.latent), float("nan"), device=dev),
     )
@@ -66,6 +67,7 @@ def check_routing(case, dbg, T):
     assert np.array_equal(dbg["topk_idx"], idx), "top-K indices differ"
     assert np.array_equal(dbg["perm"], perm), "permutation differs"
     assert np.array_equal(dbg["expert_count"], count)
+    assert np.array_equal(dbg["expert_off"], oracle.expert_offsets(count))
     assert np.array_equal(dbg["group_off"], goff)
     assert np.max(np.abs(dbg["topk_w"] - w)) <= 1e-6
 

@@ -16,6 +16,7 @@ import torch
 
 import oracle
 from oracle import formats as fm
+from oracle import layer as ol
 from oracle.layer import LayerDims, layer_forward, pack_layer, decode_layer
 
 # Tiny, deliberately non-square shapes: H != ell != F != Fs, K < G < E.
@@ -254,6 +255,16 @@ def test_permute_matches_counting_sort_and_invariants():
         assert np.all(labels[flat[seg]] == g)
 
 
+def test_expert_offsets_count_lower_experts():
+    rng = np.random.default_rng(41)
+    idx = rng.integers(0, 9, size=(6, 3)).astype(np.int32)
+    _, count, _ = oracle.permute(idx, rng.integers(0, 2, 9).astype(np.uint8), 9, 2)
+    off = oracle.expert_offsets(count)
+    assert off.shape == (10,) and off.dtype == np.int32
+    for e in range(10):      # brute force: assignments to experts below e
+        assert off[e] == sum(1 for v in idx.ravel().tolist() if v < e)
+
+
 def test_permute_empty():
     perm, count, goff = oracle.permute(np.zeros((0, 3), np.int32), np.zeros(4, np.uint8), 4, 2)
     assert perm.size == 0 and count.sum() == 0 and goff.tolist() == [0, 0, 0]
@@ -281,6 +292,34 @@ def test_stack_is_residual_of_layers():
         xn = xd / np.sqrt((xd ** 2).mean(axis=1, keepdims=True) + 1e-6)
         xd = xd + layer_forward(d, blobs, xn)
     assert np.array_equal(out, xd)
+
+
+def _identity_layer(dims, blobs, x, dec=None, intermediates=False):
+    return np.asarray(x, dtype=np.float64)
+
+
+def stack_closed_form_holds():
+    """Pins stack_forward by hand-computed closed forms, with every layer
+    replaced by the identity map (pre-norm residual: x + x / rms(x)):
+    a constant row of 3s over two layers, and a ragged row over one."""
+    x0 = np.full((1, 8), 3.0, dtype=np.float32)
+    x1 = 3.0 + 3.0 / math.sqrt(9.0 + 1e-6)
+    x2 = x1 + x1 / math.sqrt(x1 * x1 + 1e-6)
+    got = ol.stack_forward(SMALL, [None, None], x0)
+    ok = got.shape == (1, 8) and np.allclose(got, x2, rtol=1e-15, atol=0)
+    v = np.array([[1.0, -2.0, 4.0, 0.5]], dtype=np.float32)
+    ms = (1.0 + 4.0 + 16.0 + 0.25) / 4.0
+    want = v.astype(np.float64) * (1.0 + 1.0 / math.sqrt(ms + 1e-6))
+    got1 = ol.stack_forward(SMALL, [None], v)
+    return ok and np.allclose(got1, want, rtol=1e-15, atol=0)
+
+
+def test_stack_closed_form(monkeypatch):
+    monkeypatch.setattr(ol, "layer_forward", _identity_layer)
+    assert stack_closed_form_holds()
+    # zero layers leave x as it is
+    x = _x(SMALL, 2, seed=5)
+    assert np.array_equal(oracle.stack_forward(SMALL, [], x), x.astype(np.float64))
 
 
 def test_normalized_input_scales_logits():

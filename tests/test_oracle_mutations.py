@@ -8,7 +8,8 @@ import torch
 from oracle import formats as fm
 from oracle import layer as ol
 
-from test_oracle_layer import SMALL, _brute_layer, _masters, _x
+from test_oracle_layer import (SMALL, _brute_layer, _identity_layer, _masters, _x,
+                               stack_closed_form_holds)
 
 _ORIG = {"select_topk": ol.select_topk, "unpack_expert_record": fm.unpack_expert_record,
          "e4m3_decode": fm.e4m3_decode, "unpack_nibbles": fm.unpack_nibbles}
@@ -108,3 +109,42 @@ def test_nibble_order_mistake_caught_by_byte_pin(monkeypatch):
     blob = fm.pack_du(w, 4)
     codes, _ = fm.quantize_blocks(w, 4)
     assert blob[0] != (codes[0, 0] | (codes[0, 1] << 4))
+
+
+def _post_norm_stack(dims, layers, x, eps=1e-6):
+    xd = np.asarray(x, dtype=np.float64)
+    for blobs in layers:
+        xd = ol.rmsnorm(xd + ol.layer_forward(dims, blobs, xd), eps)
+    return xd
+
+
+def _no_residual_stack(dims, layers, x, eps=1e-6):
+    xd = np.asarray(x, dtype=np.float64)
+    for blobs in layers:
+        xd = ol.layer_forward(dims, blobs, ol.rmsnorm(xd, eps))
+    return xd
+
+
+STACK_MUTATIONS = {
+    "post-norm instead of pre-norm": (ol, "stack_forward", _post_norm_stack),
+    "residual dropped": (ol, "stack_forward", _no_residual_stack),
+    "rmsnorm without eps": (ol, "rmsnorm", lambda v, eps=1e-6: np.asarray(v, np.float64) / np.sqrt(
+        np.mean(np.asarray(v, np.float64) ** 2, axis=-1, keepdims=True))),
+    "rmsnorm without the square root": (ol, "rmsnorm", lambda v, eps=1e-6: np.asarray(v, np.float64) / (
+        np.mean(np.asarray(v, np.float64) ** 2, axis=-1, keepdims=True) + eps)),
+    "rmsnorm over the sum, not the mean": (ol, "rmsnorm", lambda v, eps=1e-6: np.asarray(v, np.float64) / np.sqrt(
+        np.sum(np.asarray(v, np.float64) ** 2, axis=-1, keepdims=True) + eps)),
+}
+
+
+def test_unmutated_stack_pin_holds(monkeypatch):
+    monkeypatch.setattr(ol, "layer_forward", _identity_layer)
+    assert stack_closed_form_holds()
+
+
+@pytest.mark.parametrize("name", sorted(STACK_MUTATIONS))
+def test_stack_mutation_is_caught(name, monkeypatch):
+    monkeypatch.setattr(ol, "layer_forward", _identity_layer)
+    mod, attr, repl = STACK_MUTATIONS[name]
+    monkeypatch.setattr(mod, attr, repl)
+    assert not stack_closed_form_holds()
