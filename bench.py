@@ -11,10 +11,15 @@ same seeded generator as the tests). Steps rotate over --copies independently
 seeded layers so that the 256 MB Infinity Cache cannot hold the weights a
 step reads; inputs are resident in HBM before the timed region.
 
-The default line also carries a "prefill" object: the Edge0-145B-shaped
-prefill layer (T = 4096, router bias N(0, 1) skewing expert loads) on the
-prefill path, with its per-kernel MFMA roofline. --workload 145b_prefill makes
-that the primary line.
+The default line also carries nested objects, each with its own roofline and
+oracle CPU baseline: "decode_t1" (the same layers at T = 1, with the byte
+counts of reading D and U for used groups only and for all groups),
+"decode_120b" (the Edge0-120B-shaped layer, Q4 D/U, latent 1280, T = 5),
+"stack_145b" (48 independently seeded 145B-shaped layers as pre-norm
+residual blocks, T = 4: whole-stack tokens/s and sustained HBM bandwidth) and
+"prefill" (the 145B-shaped layer at T = 4096 with a router bias skewing expert
+loads, on the prefill path, with its per-kernel MFMA roofline).
+--workload picks another primary line.
 
 Prints one JSON line (rank 0). --gpus above 1 is refused: the library runs
 on one GPU.
@@ -41,7 +46,7 @@ PREFILL_KERNELS = ["k_prep + k_dense_dma<BF16,Logits> + k_select", "k_perm_*",
                    "k_grouped_dma<GateUp> (LDS DMA) + k_grouped_short<GateUp> (64- and 32-token pieces)",
                    "k_down_res (activations resident in LDS; 64- and 32-token blocks)", "k_combine",
                    "k_dense_dma<F16,Y> (U + shared down, split along k; LDS DMA) + k_ytiles (split sums)"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_145b_t4_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_145b_t4096_traffic.json")
 # kernel of each prefill phase as rocprofv3 names it (D and U on fp16 weights)
 PREFILL_KERNEL_IDS = [["k_prep", "k_dense_dma<3, 0>", "k_select<5, 8>"],
@@ -98,28 +103,40 @@ def build_layer(lm, wl, w, seed, layer_idx, torch):
     return layer, labels
 
 
-def phase_bytes(w, idx, labels):
-    """Algorithmic HBM bytes of each of the four decode kernels for one
-    forward with routing idx [T][K]: every weight the step must read once,
-    plus the activations it must read and write."""
-    T, H, L, E, K, G, F, Fs = (w.tokens, w.hidden, w.latent, w.n_experts, w.top_k, w.n_groups,
-                               w.expert_ffn, w.shared_ffn)
+def decode_bytes(w, idx, labels):
+    """Algorithmic HBM bytes of one decode forward with routing idx [T][K]:
+    every weight the forward must read once (router, D of every group as the
+    layer computes it, U of the groups the tokens use, each distinct expert's
+    record, the shared expert) plus the activations read and written. Also
+    the two variants of the T = 1 accounting: D and U of the used groups
+    only, and of all groups."""
+    T, H, L, E, K, G, F, Fs = (idx.shape[0], w.hidden, w.latent, w.n_experts, w.top_k,
+                               w.n_groups, w.expert_ffn, w.shared_ffn)
     du = (w.du_bits / 8.0) * (34.0 / 32.0 if w.du_bits == 8 else 18.0 / 16.0)  # bytes / weight
     distinct = len(set(idx.ravel().tolist()))
-    used_groups = len(set(labels[idx.ravel()].tolist()))
+    used = len(set(labels[idx.ravel()].tolist()))
     fp4 = 0.5 + 1.0 / 16.0
-    p1 = E * H * 2 + G * L * H * du + 2 * Fs * H * 2 + T * H * 4 + T * G * L * 4 + T * Fs * 4
-    p2 = distinct * 2 * F * L * fp4 + T * K * (L + F) * 4
-    p3 = distinct * L * F * fp4 + T * K * (F + L) * 4
-    p4 = used_groups * H * L * du + H * Fs * 2 + T * (G * L + Fs + H) * 4
-    return [p1, p2, p3, p4], distinct, used_groups
+    common = E * H * 2 + distinct * 3 * F * L * fp4 + 3 * Fs * H * 2 + 2 * T * H * 4
+    phases = [E * H * 2 + G * L * H * du + 2 * Fs * H * 2 + T * H * 4 + T * G * L * 4 + T * Fs * 4,
+              distinct * 2 * F * L * fp4 + T * K * (L + F) * 4,
+              distinct * L * F * fp4 + T * K * (F + L) * 4,
+              used * H * L * du + H * Fs * 2 + T * (G * L + Fs + H) * 4]
+    out = {
+        "phases": phases,
+        "bytes": common + (G + used) * L * H * du,
+        "bytes_used_groups": common + 2 * used * L * H * du,
+        "bytes_all_groups": common + 2 * G * L * H * du,
+        "distinct_experts": distinct,
+        "used_groups": used,
+    }
+    return out
 
 
 def measured_traffic(kernel, workload, path=TRAFFIC_FILE):
     """HBM bytes per launch of `kernel` (a name, or a list of names whose
     launches make up one phase: their bytes add) from the committed rocprofv3
-    counter summary, or None when there is none or the kernel source has
-    changed since the counters were taken."""
+    counter summary for `workload`, or None when there is none or the kernel
+    source has changed since the counters were taken."""
     import hashlib
     try:
         with open(path) as f:
@@ -127,10 +144,14 @@ def measured_traffic(kernel, workload, path=TRAFFIC_FILE):
         src = open(os.path.join(ROOT, t["source"]), "rb").read()
     except (OSError, ValueError, KeyError):
         return None
-    if t.get("workload") != workload or hashlib.sha256(src).hexdigest() != t["source_sha256"]:
+    if hashlib.sha256(src).hexdigest() != t["source_sha256"]:
+        return None
+    entry = t.get("workloads", {}).get(workload) if "workloads" in t else \
+        (t if t.get("workload") == workload else None)
+    if entry is None:
         return None
     names = kernel if isinstance(kernel, list) else [kernel]
-    ks = [t["kernels"].get(n) for n in names]
+    ks = [entry["kernels"].get(n) for n in names]
     return None if any(k is None for k in ks) else sum(k["traffic_bytes"] for k in ks)
 
 
@@ -218,6 +239,7 @@ def bench_prefill(lm, wl, w, args, torch):
         "tokens": T,
         "value": T / (ms * 1e-3),
         "unit": "tokens/s",
+        "dtype": "f16",
         "ms_per_step": ms,
         "steps": args.prefill_steps,
         "warmup": args.prefill_warmup,
@@ -247,20 +269,35 @@ def bench_prefill(lm, wl, w, args, torch):
     return out
 
 
-def cpu_baseline(w, seed, tokens):
-    """The fp64 oracle timed on the host on a bounded sample: one forward of
-    `tokens` tokens of layer 0 (including its on-the-fly dequantization of
-    D, U and the experts it touches; excluding weight drawing and packing)."""
-    import oracle
-    from latent_mixture_experts_amd import workloads as wl
+def host_cores():
+    """Threads the oracle can use on this host: os.cpu_count(), the
+    affinity-mask size and the BLAS thread count."""
     try:
         from threadpoolctl import threadpool_info
         blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas = 1
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = os.cpu_count()
+    return {"cpu_count": os.cpu_count(), "affinity": aff, "blas_threads": int(blas)}
+
+
+def cpu_baseline(w, seed, tokens, layers=1):
+    """The fp64 oracle timed on the host on a bounded sample: one forward of
+    `tokens` tokens of layer 0 (including its on-the-fly dequantization of
+    D, U and the experts it touches; excluding weight drawing and packing).
+    For a stack of `layers` layers the sample is one layer, and the rate is
+    scaled by the layer count."""
+    import oracle
+    from latent_mixture_experts_amd import workloads as wl
+    cores = host_cores()
     d = oracle.LayerDims(w.hidden, w.latent, w.n_experts, w.top_k, w.n_groups, w.expert_ffn,
                          w.shared_ffn, w.du_bits)
     x = wl.x(w, seed, 0, tokens=tokens)
+    if layers > 1:
+        x = oracle.rmsnorm(x)
     m = wl.masters(w, seed, 0)
     lg = oracle.router_logits(x, oracle.f32_to_bf16_bits(m["router"]), m["router_bias"])
     idx, _ = oracle.select_topk(lg, w.top_k)
@@ -269,38 +306,182 @@ def cpu_baseline(w, seed, tokens):
     t0 = time.perf_counter()
     oracle.layer_forward(d, blobs, x)
     dt = time.perf_counter() - t0
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
-            "sample": "one fp64 NumPy forward of %d tokens of the %s layer (seed %d), including "
-                      "dequantization of D, U and the %d experts it touches; %.1f s" % (
-                          tokens, w.name, seed, len(m["expert_ids"]), dt)}
+    what = ("one fp64 NumPy forward of %d tokens of the %s layer (seed %d), including "
+            "dequantization of D, U and the %d experts it touches; %.1f s" % (
+                tokens, w.name, seed, len(m["expert_ids"]), dt))
+    if layers > 1:
+        what = ("layer 0 of the %d-layer stack: " % layers) + what + \
+               "; the stack's rate is this layer's divided by %d" % layers
+    return {"value": tokens / (dt * layers), "unit": "tokens/s", "cores": cores["blas_threads"],
+            "cpu_count": cores["cpu_count"], "affinity": cores["affinity"], "kind": "oracle",
+            "sample": what}
 
 
-def calibrate_hbm(torch, copy_bytes=256 << 20, reps=4, read_bytes=1 << 30):
-    """Reference runs for the profiler's HBM counters (--calibrate-hbm):
-    a device-to-device copy of exactly 256 MiB, repeated (each copy reads
-    and writes 268,435,456 bytes: the scale for FETCH_SIZE / WRITE_SIZE), and
-    the read bandwidth of a plain streaming reduction over 1 GiB (the
-    achievable-bandwidth reference beside the published peak)."""
-    src = torch.ones(copy_bytes // 4, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(reps):
-        dst.copy_(src)
+def phase_times(lm, layers, x, y, T, torch, stack):
+    """Per-kernel durations in ms with HIP events on the stream the kernels
+    run on. Single layer: each phase is launched alone, back to back over the
+    weight copies (cold, as in the forward), one event pair around the run,
+    so a figure is one kernel's launch-to-launch time. Stack (block
+    forwards): events between the phases of each forward, which add their
+    own gaps."""
+    nph = lm.lib().lmoe_phase_count(T)
+    n = len(layers)
+    if not stack:
+        for L_, _ in layers:
+            L_.forward(x, y)               # the workspace state each phase reads
+        nrep = max(n * 8, 64)
+        out = []
+        for k in range(1, nph + 1):
+            for i in range(n):
+                layers[i][0].run_phase(x, y, k)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(nrep):
+                layers[i % n][0].run_phase(x, y, k)
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) / nrep)
+        return np.array(out)
+    nprof = max(n * 2, 32)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)] for _ in range(nprof)]
+    for row in evs:
+        for e in row:
+            e.record()
     torch.cuda.synchronize()
-    big = torch.ones(read_bytes // 4, dtype=torch.float32, device="cuda")
-    for _ in range(3):
-        big.sum()
+    for i in range(nprof):
+        L_ = layers[i % n][0]
+        L_.set_phase_events([e.cuda_event for e in evs[i]])
+        L_.forward_block(x)
+    for L_, _ in layers:
+        L_.set_phase_events(None)
+    torch.cuda.synchronize()
+    ms = np.array([[row[k].elapsed_time(row[k + 1]) for k in range(nph)] for row in evs])
+    return ms.mean(axis=0)
+
+
+def bench_decode(lm, wl, w, args, torch, T=None, layers=None, steps=None, warmup=None):
+    """Times decode forwards (block forwards through a stack for a workload
+    with n_layers > 1); returns the result dict (value, timing percentiles,
+    bytes, roofline, stage spans) and the layers for reuse."""
+    T = w.tokens if T is None else T
+    stack = w.n_layers > 1
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
+    if layers is None:
+        n_handles = w.n_layers if stack else args.copies
+        t_build = time.time()
+        layers = [build_layer(lm, wl, w, args.seed, r, torch) for r in range(n_handles)]
+        log("%s: built %d layers in %.1f s" % (w.name, n_handles, time.time() - t_build))
+    n_handles = len(layers)
+    x0 = torch.from_numpy(wl.x(w, args.seed, 0, tokens=T)).cuda()
+    x = x0.clone()
+    y = torch.empty(T, w.hidden, device="cuda")
+
+    def step(i):
+        if stack:
+            for L_, _ in layers:
+                L_.forward_block(x)
+        else:
+            layers[i % n_handles][0].forward(x, y)
+
+    # routing of each layer, for the algorithmic byte counts
+    per = []
+    xr = x0.clone()
+    for L_, lab in layers:
+        idx = torch.empty(T, w.top_k, dtype=torch.int32, device="cuda")
+        if stack:
+            # the routing a block sees is that of its normalized input
+            xn = xr / torch.sqrt((xr.double() ** 2).mean(dim=1, keepdim=True) + 1e-6).float()
+            L_.forward(xn, y, debug=dict(topk_idx=idx))
+            xr = xr + y
+        else:
+            L_.forward(x, y, debug=dict(topk_idx=idx))
+        torch.cuda.synchronize()
+        per.append(decode_bytes(w, idx.cpu().numpy(), lab))
+    keys = ["bytes", "bytes_used_groups", "bytes_all_groups", "distinct_experts", "used_groups"]
+    mean = {k: float(np.mean([p[k] for p in per])) for k in keys}
+    layer_bytes = mean["bytes"]
+    step_bytes = layer_bytes * (len(layers) if stack else 1)
+
+    for i in range(warmup):
+        step(i)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n = 20
     start.record()
-    for _ in range(n):
-        big.sum()
+    for i in range(steps):
+        step(i)
     end.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / n
-    print(json.dumps({"copy_bytes_per_launch": copy_bytes, "copies": reps,
-                      "sum_read_bytes": read_bytes, "sum_ms": ms,
-                      "sum_read_GBps": read_bytes / (ms * 1e-3) / 1e9}), flush=True)
+    ms = start.elapsed_time(end) / steps
+    # per-step distribution: an event pair around each step
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        step(i)
+        b.record()
+    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(b) for a, b in ev])
+    p10, p50, p90 = (float(v) for v in np.percentile(per_step, [10, 50, 90]))
+    x.copy_(x0)
+    pt = phase_times(lm, layers, x, y, T, torch, stack)
+    x.copy_(x0)
+    pbytes = np.mean(np.array([p["phases"] for p in per]), axis=0)
+    gbps = step_bytes / (ms * 1e-3) / 1e9
+    dom = int(np.argmax(pt))
+    kern_us = float(pt[dom] * 1e3)
+    kbytes = float(pbytes[dom])
+    log("%s T=%d: %.2f us/step (p10 %.2f, median %.2f, p90 %.2f us); %.0f GB/s over %.1f MB; "
+        "%.1f distinct experts, %.1f groups used; kernels (us): %s; kernel GB/s: %s" % (
+            w.name, T, ms * 1e3, p10 * 1e3, p50 * 1e3, p90 * 1e3, gbps, step_bytes / 1e6,
+            mean["distinct_experts"], mean["used_groups"],
+            " ".join("%.2f" % (v * 1e3) for v in pt),
+            " ".join("%.0f" % (b / (v * 1e-3) / 1e9) for b, v in zip(pbytes, pt))))
+    out = {
+        "workload": w.name,
+        "tokens": T,
+        "layers": len(layers) if stack else 1,
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "ms_per_step": ms,
+        "step_us_p10": p10 * 1e3, "step_us_median": p50 * 1e3, "step_us_p90": p90 * 1e3,
+        "steps": steps, "warmup": warmup,
+        "weight_copies": None if stack else n_handles,
+        "step_algorithmic_bytes": step_bytes,
+        "step_GBps": gbps,
+        "hbm_frac": gbps / HBM_PEAK_GBS,
+        "distinct_experts": mean["distinct_experts"],
+        "used_groups": mean["used_groups"],
+        "roofline": {"bound": "hbm", "achieved": kbytes / (kern_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": kbytes / (kern_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("k_phase%d" % (dom + 1), "%s_t%d" % (w.name, T)),
+                     "kernel": "k_phase%d" % (dom + 1), "kernel_us": kern_us,
+                     "kernel_algorithmic_bytes": kbytes},
+        "kernels_us": {"k_phase%d" % (k + 1): float(v * 1e3) for k, v in enumerate(pt)},
+        "kernels_GBps": {"k_phase%d" % (k + 1): float(b / (v * 1e-3) / 1e9)
+                         for k, (b, v) in enumerate(zip(pbytes, pt))},
+        "kernels_algorithmic_bytes": {"k_phase%d" % (k + 1): float(b) for k, b in enumerate(pbytes)},
+    }
+    if T == 1 and not stack:
+        out["t1_bytes"] = {"used_groups_only": mean["bytes_used_groups"],
+                           "all_groups": mean["bytes_all_groups"],
+                           "read_by_kernel": mean["bytes"],
+                           "GBps_used_groups_only": mean["bytes_used_groups"] / (ms * 1e-3) / 1e9,
+                           "GBps_all_groups": mean["bytes_all_groups"] / (ms * 1e-3) / 1e9}
+    return out, layers
+
+
+def close_layers(layers):
+    for L_, _ in layers:
+        L_.close()
+
+
+def config_of(w, T, copies):
+    return {"workload": w.name, "tokens": T, "hidden": w.hidden, "latent": w.latent,
+            "experts": w.n_experts, "top_k": w.top_k, "groups": w.n_groups,
+            "expert_ffn": w.expert_ffn, "shared_ffn": w.shared_ffn,
+            "du_format": "Q%d" % w.du_bits, "expert_format": "NVFP4",
+            "router_bias": w.router_bias, "layers": w.n_layers, "weight_copies": copies}
 
 
 def main():
@@ -316,7 +497,10 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--prefill-warmup", type=int, default=3)
     ap.add_argument("--prefill-copies", type=int, default=2)
+    ap.add_argument("--stack-steps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="only the primary line: no T = 1, 120B, stack or prefill objects")
     ap.add_argument("--calibrate-hbm", action="store_true",
                     help="only run the reference copy and read for the HBM counters")
     args = ap.parse_args()
@@ -334,6 +518,7 @@ def main():
 
     w = wl.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
+    cpu = not args.no_cpu_baseline
     if w.tokens > 8:
         pre = bench_prefill(lm, wl, w, args, torch)
         out = {
@@ -342,155 +527,68 @@ def main():
             "steps": args.prefill_steps, "warmup": args.prefill_warmup,
             "ms_per_step": pre["ms_per_step"], "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-            "config": {"workload": w.name, "tokens": w.tokens, "hidden": w.hidden,
-                       "latent": w.latent, "experts": w.n_experts, "top_k": w.top_k,
-                       "groups": w.n_groups, "expert_ffn": w.expert_ffn,
-                       "shared_ffn": w.shared_ffn, "du_format": "Q%d" % w.du_bits,
-                       "expert_format": "NVFP4", "router_bias": w.router_bias,
-                       "weight_copies": args.prefill_copies},
+            "config": config_of(w, w.tokens, args.prefill_copies),
             "roofline": pre["roofline"],
             "prefill": pre,
         }
-        if not args.no_cpu_baseline:
-            out["cpu_baseline"] = cpu_baseline(w, args.seed, 16)
+        if cpu:
+            out["cpu_baseline"] = pre.get("cpu_baseline") or cpu_baseline(w, args.seed, 8)
         print(json.dumps(out), flush=True)
         return
+
     stack = w.n_layers > 1
-    n_handles = w.n_layers if stack else args.copies
-    t_build = time.time()
-    layers, labels = [], []
-    for r in range(n_handles):
-        L_, lab = build_layer(lm, wl, w, args.seed, r, torch)
-        layers.append(L_)
-        labels.append(lab)
-    log("built %d layers in %.1f s" % (n_handles, time.time() - t_build))
-
-    T = w.tokens
-    x0 = torch.from_numpy(wl.x(w, args.seed, 0)).cuda()
-    x = x0.clone()
-    y = torch.empty(T, w.hidden, device="cuda")
-
-    def step(i):
-        if stack:
-            for L_ in layers:
-                L_.forward_block(x)
-        else:
-            layers[i % n_handles].forward(x, y)
-
-    # routing of each layer, for the algorithmic byte counts
-    bytes_per_layer, distinct, groups = [], [], []
-    xr = x0.clone()
-    for r, L_ in enumerate(layers):
-        idx = torch.empty(T, w.top_k, dtype=torch.int32, device="cuda")
-        if stack:
-            # the routing a block sees is that of its normalized input
-            xn = xr / torch.sqrt((xr.double() ** 2).mean(dim=1, keepdim=True) + 1e-6).float()
-            L_.forward(xn, y, debug=dict(topk_idx=idx))
-            xr = xr + y
-        else:
-            L_.forward(x, y, debug=dict(topk_idx=idx))
-        torch.cuda.synchronize()
-        pb, dn, ug = phase_bytes(w, idx.cpu().numpy(), labels[r])
-        bytes_per_layer.append(pb)
-        distinct.append(dn)
-        groups.append(ug)
-    pbytes = np.mean(np.array(bytes_per_layer), axis=0)
-    layer_bytes = float(np.sum(pbytes))
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(args.steps):
-        step(i)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-
-    # per-kernel durations, with HIP events on the stream the kernels run on.
-    # Single layer: each phase is launched alone, back to back over the weight
-    # copies (cold, as in the forward), one event pair around the run, so a
-    # figure is one kernel's launch-to-launch time. Stack (block forwards):
-    # events between the phases of each forward, which add their own gaps.
-    nph = lm.lib().lmoe_phase_count(T)
-    if not stack:
-        for L_ in layers:
-            L_.forward(x, y)               # the workspace state each phase reads
-        nrep = max(n_handles * 8, 64)
-        phase_avg = []
-        for k in range(1, nph + 1):
-            for i in range(n_handles):
-                layers[i].run_phase(x, y, k)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for i in range(nrep):
-                layers[i % n_handles].run_phase(x, y, k)
-            e1.record()
-            torch.cuda.synchronize()
-            phase_avg.append(e0.elapsed_time(e1) / nrep)
-        phase_avg = np.array(phase_avg)
-    else:
-        nprof = max(n_handles * 2, 32)
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)] for _ in range(nprof)]
-        for row in evs:
-            for e in row:
-                e.record()
-        torch.cuda.synchronize()
-        for i in range(nprof):
-            L_ = layers[i % n_handles]
-            L_.set_phase_events([e.cuda_event for e in evs[i]])
-            L_.forward_block(x)
-        for L_ in layers:
-            L_.set_phase_events(None)
-        torch.cuda.synchronize()
-        phase_ms = np.array([[row[k].elapsed_time(row[k + 1]) for k in range(nph)] for row in evs])
-        phase_avg = phase_ms.mean(axis=0)
-    dom = int(np.argmax(phase_avg))
-    achieved = pbytes[dom] / (phase_avg[dom] * 1e-3) / 1e9
-    step_bytes = layer_bytes * (w.n_layers if stack else 1)
-    log("step %.2f us; phases (us): %s; phase GB/s: %s; whole-step %.0f GB/s over %.1f MB" % (
-        ms * 1e3, " ".join("%.2f" % (p * 1e3) for p in phase_avg),
-        " ".join("%.0f" % (b / (p * 1e-3) / 1e9) for b, p in zip(pbytes, phase_avg)),
-        step_bytes / (ms * 1e-3) / 1e9, step_bytes / 1e6))
-    log("distinct experts per layer %.1f, groups used %.1f" % (np.mean(distinct), np.mean(groups)))
-
+    res, layers = bench_decode(lm, wl, w, args, torch,
+                               steps=args.stack_steps if stack else args.steps)
     out = {
         "metric": ("latent-MoE %d-layer stack tokens/s (decode; HBM roofline)" % w.n_layers) if stack
                   else "latent-MoE layer tokens/s (decode; HBM roofline)",
-        "value": T / (ms * 1e-3),
+        "value": res["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
+        "steps": res["steps"],
+        "warmup": res["warmup"],
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "tokens": T, "hidden": w.hidden, "latent": w.latent,
-                   "experts": w.n_experts, "top_k": w.top_k, "groups": w.n_groups,
-                   "expert_ffn": w.expert_ffn, "shared_ffn": w.shared_ffn,
-                   "du_format": "Q%d" % w.du_bits, "expert_format": "NVFP4",
-                   "layers": w.n_layers,
-                   "weight_copies": None if stack else args.copies,
-                   "step_algorithmic_bytes": step_bytes,
-                   "step_GBps": step_bytes / (ms * 1e-3) / 1e9},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("k_phase%d" % (dom + 1), w.name),
-                     "kernel": "k_phase%d" % (dom + 1),
-                     "kernel_us": phase_avg[dom] * 1e3,
-                     "kernel_algorithmic_bytes": pbytes[dom]},
+        "config": dict(config_of(w, w.tokens, None if stack else args.copies),
+                       step_algorithmic_bytes=res["step_algorithmic_bytes"],
+                       step_GBps=res["step_GBps"]),
+        "roofline": res["roofline"],
+        "decode": res,
     }
-    for L_ in layers:
-        L_.close()
+    if cpu:
+        out["cpu_baseline"] = cpu_baseline(w, args.seed, w.tokens, layers=w.n_layers)
+    if not stack and not args.no_extra:
+        r1, _ = bench_decode(lm, wl, w, args, torch, T=1, layers=layers)
+        if cpu:
+            r1["cpu_baseline"] = cpu_baseline(w, args.seed, 1)
+        out["decode_t1"] = r1
+    close_layers(layers)
     del layers
-    if not args.no_prefill and not stack:
-        out["prefill"] = bench_prefill(lm, wl, wl.WORKLOADS[args.prefill_workload], args, torch)
-    if not args.no_cpu_baseline and not stack:
-        out["cpu_baseline"] = cpu_baseline(w, args.seed, T)
+    if not stack and not args.no_extra:
+        w120 = wl.WORKLOADS["120b_decode"]
+        r120, l120 = bench_decode(lm, wl, w120, args, torch)
+        close_layers(l120)
+        del l120
+        if cpu:
+            r120["cpu_baseline"] = cpu_baseline(w120, args.seed, w120.tokens)
+        out["decode_120b"] = r120
+        ws = wl.WORKLOADS["145b_stack"]
+        rs, ls = bench_decode(lm, wl, ws, args, torch, steps=args.stack_steps,
+                              warmup=min(args.warmup, 3))
+        close_layers(ls)
+        del ls
+        if cpu:
+            rs["cpu_baseline"] = cpu_baseline(ws, args.seed, ws.tokens, layers=ws.n_layers)
+        out["stack_145b"] = rs
+    if not stack and not args.no_extra and not args.no_prefill:
+        pre = bench_prefill(lm, wl, wl.WORKLOADS[args.prefill_workload], args, torch)
+        if cpu:
+            pre["cpu_baseline"] = cpu_baseline(wl.WORKLOADS[args.prefill_workload], args.seed, 8)
+        out["prefill"] = pre
     print(json.dumps(out), flush=True)
 
 

@@ -44,6 +44,11 @@ int check_dims(const lmoe_dims& d) {
   if (d.n_experts > 1024 || d.top_k > 64 || d.n_groups > 64)
     return unsup("n_experts <= 1024, top_k <= 64, n_groups <= 64");
   if (d.max_tokens > kMaxTokens) return unsup("max_tokens above 1048576");
+  // the decode kernels keep activations, partial sums, expert outputs and the
+  // routing tables in LDS: refuse shapes whose blocks would not fit a CU
+  const int Td = d.max_tokens < kMaxDecodeT ? d.max_tokens : kMaxDecodeT;
+  if (decode_lds_bytes(d, Td) > 160 * 1024)
+    return unsup("decode path: n_groups, T * top_k or the expert count too large for the LDS of a CU");
   return 0;
 }
 
@@ -116,6 +121,7 @@ int create_impl(lmoe_t* h) {
   A(w.group_off, sizeof(int) * (G + 1));
   A(w.expert_count, sizeof(int) * E);
   A(w.rms, sizeof(float) * T);
+  A(w.rms64, sizeof(double) * T);
   A(w.xl, sizeof(float) * T * G * L);
   A(w.hs, sizeof(float) * T * Fs);
   A(w.hsp, sizeof(float) * h->g_sgu.nss * T * 2 * Fs);
@@ -144,6 +150,7 @@ int create_impl(lmoe_t* h) {
     A(p.xb, 4 * Tp * H);
     A(p.xnorm, sizeof(double) * Tp);
     A(p.r, sizeof(float) * Tp);
+    A(p.r64, sizeof(double) * Tp);
     A(p.logits, sizeof(float) * Tp * Epm);
     A(p.idx, sizeof(int) * nk);
     A(p.w, sizeof(float) * nk);

@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "internal.h"
 
 namespace lm {
@@ -91,19 +93,70 @@ __device__ __forceinline__ void x_load(XRegs<NT>& r, const float* const (&src)[N
   }
 }
 
-// fp16 hi/lo parts: xs[part][i][col], part 0 = hi, 1 = lo.
+// Maximum of a non-negative int over the wavefront, by DPP: row shifts give
+// each row's maximum in its lane 15, two row broadcasts carry it to lane 63
+// (lanes a shift or mask leaves out contribute 0).
+__device__ __forceinline__ int wave_max_nonneg(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true));   // row_shr:1
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true));   // row_shr:2
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true));   // row_shr:4
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true));   // row_shr:8
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// fp16 hi/lo parts: xs[part][i][col], part 0 = hi, 1 = lo, of each vector
+// scaled by an exact power of two 2^s_i chosen from its largest magnitude in
+// this super-step (to [2^14, 2^15)) when that magnitude lies outside
+// [2^-4, 2^14), so that neither part overflows or loses precision to the
+// fp16 subnormals; inv[i] = 2^-s_i undoes it on the fp32 products.
+// A vector whose largest magnitude is zero, subnormal, infinite or NaN is
+// staged as is (inf and NaN then reach y, as in exact arithmetic).
 template <int NT>
-__device__ __forceinline__ void x_stage_f16(const XRegs<NT>& r, _Float16* xs, int lane) {
+__device__ __forceinline__ void x_stage_f16(const XRegs<NT>& r, _Float16* xs, int lane,
+                                            float (&inv)[NT]) {
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
     const float v[4] = {r.v[i].x, r.v[i].y, r.v[i].z, r.v[i].w};
+    // largest |v| by its bit pattern (NaN sorts above inf)
+    int mb = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mb = max(mb, (int)(__float_as_uint(v[j]) & 0x7FFFFFFFu));
+    // A vector whose largest magnitude lies in [2^-4, 2^14) needs no scale
+    // (its hi part cannot overflow, and the lo parts' absolute error of at
+    // most 2^-25 is below 2^-21 of that magnitude): two ballots decide it,
+    // and only other vectors pay for the exact wave maximum.
+    const bool over = __ballot(mb >= 0x46800000) != 0ull;      // some |v| >= 2^14 (or inf, NaN)
+    const bool some = __ballot(mb >= 0x3D800000) != 0ull;      // some |v| >= 2^-4
+    int sh = 0;
+    if (over || !some) {
+      mb = wave_max_nonneg(mb);
+      const int e = (mb >> 23) & 0xFF;                          // biased exponent of the maximum
+      sh = (e == 0 || e == 255) ? 0 : max(-126, min(126, 141 - e));
+    }
+    const float sc = __int_as_float((127 + sh) << 23);
+    inv[i] = __int_as_float((127 - sh) << 23);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const _Float16 hi = (_Float16)v[j];
+      const float u = v[j] * sc;
+      const _Float16 hi = (_Float16)u;
       xs[(0 * NT + i) * kXStr + 4 * lane + j] = hi;
-      xs[(1 * NT + i) * kXStr + 4 * lane + j] = (_Float16)(v[j] - (float)hi);
+      xs[(1 * NT + i) * kXStr + 4 * lane + j] = (_Float16)(u - (float)hi);
     }
   }
+}
+
+// The inverse scales of the tokens a lane holds in the MFMA D layout
+// (tokens 4 (l / 16) + 0..3); 1 past NT.
+template <int NT>
+__device__ __forceinline__ f4 lane_inv(const float (&inv)[NT], int lane) {
+  const int q = lane >> 4;
+  f4 r = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    if (t / 4 == q) r[t % 4] = inv[t];
+  return r;
 }
 
 // Three bf16 parts whose sum is the fp32 value exactly.
@@ -266,9 +319,19 @@ __device__ __forceinline__ void wave_compute(const WRegs<FMT, NT, SL>& R, int nc
   const int tok = lane & 15, qg = lane >> 4;
   const uint4 (&sc)[4] = R.sc;
   const uint4 (&q)[SL] = R.q;
+  float inv[NT];
   if (FMT == kBF16) x_stage_bf16<NT>(R.xr, (__bf16*)xs, lane);
-  else x_stage_f16<NT>(R.xr, (_Float16*)xs, lane);
+  else x_stage_f16<NT>(R.xr, (_Float16*)xs, lane, inv);
   __builtin_amdgcn_wave_barrier();
+  f4 iv = {1.f, 1.f, 1.f, 1.f};
+  if (FMT != kBF16) iv = lane_inv<NT>(inv, lane);
+  // NVFP4: this super-step's products in their own accumulators, unscaled
+  // into acc at the end
+  f4 dss[4];
+  if (FMT == kFP4) {
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) dss[rg] = (f4){0.f, 0.f, 0.f, 0.f};
+  }
 
   const int nch = ncs / 4;
 #pragma unroll
@@ -306,8 +369,8 @@ __device__ __forceinline__ void wave_compute(const WRegs<FMT, NT, SL>& R, int nc
             const uint32_t sb = (word(sc[rg], k >> 1) >> (16 * (k & 1) + 8 * (qg >> 1))) & 0xFFu;
             const _Float16 s = (_Float16)__builtin_amdgcn_cvt_f32_fp8(sb, 0);
             const half8 bw = dec_fp4(word(w, b), s);
-            acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahb, bw, acc[rg], 0, 0, 0);
-            acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alb, bw, acc[rg], 0, 0, 0);
+            dss[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahb, bw, dss[rg], 0, 0, 0);
+            dss[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alb, bw, dss[rg], 0, 0, 0);
           } else {
             const half8 bw = FMT == kQ8 ? dec_q8(word(w, 2 * b), word(w, 2 * b + 1))
                                         : dec_q4(word(w, b));
@@ -316,11 +379,15 @@ __device__ __forceinline__ void wave_compute(const WRegs<FMT, NT, SL>& R, int nc
             d = __builtin_amdgcn_mfma_f32_16x16x32_f16(alb, bw, d, 0, 0, 0);
             const int blk = NB * c + b;                  // fp16 scale of this 32-column block
             const float s = h2f(word(sc[rg], blk >> 1) >> (16 * (blk & 1)));
-            acc[rg] += s * d;
+            acc[rg] += (s * iv) * d;
           }
         }
       }
     }
+  }
+  if (FMT == kFP4) {
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) acc[rg] += dss[rg] * iv;
   }
 }
 
@@ -455,6 +522,7 @@ struct P1 {
   Dims d;
   const float* x;          // [T][H]
   const float* rms;        // [T] or null: multiply dot products by rms[t]
+  const double* rms64;     // [T] the same in fp64 (router logits)
   const uint8_t* router; Geom gr;
   const float* bias;
   const uint8_t* labels;
@@ -554,7 +622,7 @@ __device__ void routing(const P1& a, char* smem) {
           double l = 0.0;
 #pragma unroll
           for (int c = 0; c < kRouterChunks; ++c) l += part[u][c];
-          if (a.rms) l *= (double)a.rms[t];
+          if (a.rms) l *= a.rms64[t];
           lg[t * Epad + e] = l + (double)a.bias[e];
           if (t == 0) elab[e] = lab[u];
         }
@@ -1193,7 +1261,8 @@ __global__ __launch_bounds__(64 * W) void k_phase4(P4 a) {
 }
 
 // 1/sqrt(mean(x^2) + eps) per row, fp64 sum.
-__global__ void k_rms(const float* __restrict__ x, int H, float eps, float* __restrict__ out) {
+__global__ void k_rms(const float* __restrict__ x, int H, float eps, float* __restrict__ out,
+                      double* __restrict__ out64) {
   const int t = blockIdx.x;
   double s = 0.0;
   for (int i = threadIdx.x; i < H; i += blockDim.x) {
@@ -1206,7 +1275,9 @@ __global__ void k_rms(const float* __restrict__ x, int H, float eps, float* __re
   if (threadIdx.x == 0) {
     double z = 0.0;
     for (int i = 0; i < (int)blockDim.x; ++i) z += red[i];
-    out[t] = (float)(1.0 / sqrt(z / H + (double)eps));
+    const double r = 1.0 / sqrt(z / H + (double)eps);
+    out[t] = (float)r;
+    out64[t] = r;
   }
 }
 
@@ -1241,6 +1312,7 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st, i
   p1.d = d;
   p1.x = x;
   p1.rms = norm ? ws.rms : nullptr;
+  p1.rms64 = norm ? ws.rms64 : nullptr;
   p1.router = h->router; p1.gr = h->g_router;
   p1.bias = h->bias;
   p1.labels = h->labels;
@@ -1347,10 +1419,41 @@ int launch_t(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st, int
                            : launch_all<T, kQ4>(h, x, y, norm, st, only);
 }
 
+// Largest dynamic LDS any of the four kernels asks for at T tokens (the
+// same sizes launch_all computes).
+template <int T>
+size_t lds_need(const lmoe_dims& d) {
+  const int nssH = (d.hidden + kSSCols - 1) / kSSCols, nssL = (d.latent + kSSCols - 1) / kSSCols;
+  const int Epad = (d.n_experts + 63) / 64 * 64, n = T * d.top_k;
+  size_t m = (size_t)nssH * (stage_bytes<T>() + red_bytes_per_wave<T>());
+  m = std::max(m, (size_t)nssH * T * 64 * sizeof(double));
+  m = std::max(m, routing_lds_bytes(T, d.n_experts, Epad, n, nssH));
+  m = std::max(m, (size_t)nssL * (stage_bytes<T>() + 2 * red_bytes_per_wave<T>()));
+  m = std::max(m, (size_t)stage_bytes_f16<T>() + (size_t)n * 64 * sizeof(float));   // phase 3, one slot
+  const int hu = (nssL + 1) / 2, nhs = (d.shared_ffn + 127) / 128, nsb = (nhs + hu - 1) / hu;
+  m = std::max(m, (size_t)hu * (stage_bytes<T>() + red_bytes_per_wave<T>()));
+  m = std::max(m, (size_t)(2 * d.n_groups + nsb) * T * 64 * sizeof(float));
+  return m;
+}
+
 }  // namespace
 
+size_t decode_lds_bytes(const lmoe_dims& d, int T) {
+  switch (T) {
+    case 1: return lds_need<1>(d);
+    case 2: return lds_need<2>(d);
+    case 3: return lds_need<3>(d);
+    case 4: return lds_need<4>(d);
+    case 5: return lds_need<5>(d);
+    case 6: return lds_need<6>(d);
+    case 7: return lds_need<7>(d);
+    default: return lds_need<8>(d);
+  }
+}
+
 int rms_rows(lmoe_t* h, const float* x, int T, float eps, hipStream_t st) {
-  hipLaunchKernelGGL(k_rms, dim3(T), dim3(256), 0, st, x, h->d.hidden, eps, h->ws.rms);
+  hipLaunchKernelGGL(k_rms, dim3(T), dim3(256), 0, st, x, h->d.hidden, eps, h->ws.rms,
+                     h->ws.rms64);
   LMOE_HIP(hipGetLastError());
   return 0;
 }

@@ -115,6 +115,7 @@ struct Workspace {
   int* group_off = nullptr;      // [G+1]
   int* expert_count = nullptr;   // [E]
   float* rms = nullptr;          // [T] 1/rms of the input rows (block forward)
+  double* rms64 = nullptr;       // [T] the same in fp64, for the router logits
   float* xl = nullptr;           // [T][G][ell]
   float* hs = nullptr;           // [T][Fs] shared-expert hidden
   float* hsp = nullptr;          // [H/256][T][2 Fs] shared gate/up partials per super-step
@@ -133,6 +134,7 @@ struct PrefillWs {
   uint16_t* xb = nullptr;          // [T][2][H] bf16 parts (router, shared gate/up)
   double* xnorm = nullptr;         // [T] 2-norm of the staged rows
   float* r = nullptr;              // [T] row scale (1/rms in the block forward, else 1)
+  double* r64 = nullptr;           // [T] the same in fp64 (the fp64 rescoring of the logits)
   float* logits = nullptr;         // [T][Epad] fp32 router logits
   int* idx = nullptr;              // [T][K]
   float* w = nullptr;              // [T][K]
@@ -212,6 +214,9 @@ int pack_experts_impl(const float* gate, const float* up, const float* down, int
 int forward_decode(lmoe_t* h, const float* x, int T, float* y, bool norm, hipStream_t stream,
                    int only = 0);
 int rms_rows(lmoe_t* h, const float* x, int T, float eps, hipStream_t stream);
+// Largest dynamic LDS a decode kernel needs for T tokens (a handle whose
+// decode path would need more than a CU has is refused at create).
+size_t decode_lds_bytes(const lmoe_dims& d, int T);
 
 // prefill.hip
 int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float eps,

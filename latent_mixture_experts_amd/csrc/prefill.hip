@@ -1471,6 +1471,7 @@ struct Prep {
   __bf16* xb;       // [T][2][H]
   double* xnorm;    // [T] |staged row|_2
   float* r;         // [T] the row scale (1/rms, or 1)
+  double* r64;      // [T] the same in fp64 (exact 1/rms for the fp64 logits)
 };
 
 __device__ __forceinline__ double block_sum(double v, double* red) {
@@ -1491,6 +1492,7 @@ __global__ __launch_bounds__(256) void k_prep(Prep a) {
   const float* xr = a.x + (size_t)t * a.H;
   const int nc = a.H / 8;
   float r = 1.0f;
+  double r64 = 1.0;
   if (a.norm) {
     double s = 0.0;
     for (int c = threadIdx.x; c < nc; c += blockDim.x) {
@@ -1500,7 +1502,8 @@ __global__ __launch_bounds__(256) void k_prep(Prep a) {
       for (int j = 0; j < 8; ++j) s += (double)v[j] * v[j];
     }
     s = block_sum(s, red);
-    r = (float)(1.0 / sqrt(s / a.H + (double)a.eps));
+    r64 = 1.0 / sqrt(s / a.H + (double)a.eps);
+    r = (float)r64;
   }
   double s2 = 0.0;
   for (int c = threadIdx.x; c < nc; c += blockDim.x) {
@@ -1524,6 +1527,7 @@ __global__ __launch_bounds__(256) void k_prep(Prep a) {
   if (threadIdx.x == 0) {
     a.xnorm[t] = sqrt(s2);
     a.r[t] = r;
+    a.r64[t] = r64;
   }
 }
 
@@ -1536,7 +1540,7 @@ struct Select {
   int Epad, T, E, H, K;
   const float* bias;         // [E]
   const float* x;            // [T][H] raw input rows
-  const float* r;            // [T] row scale
+  const double* r;           // [T] row scale (fp64)
   const double* xnorm;       // [T]
   const double* wmax;        // max_e |Wr_e|_2
   const uint16_t* wr;        // router bf16 [E][H] row-major
@@ -1677,7 +1681,7 @@ __global__ __launch_bounds__(256) void k_select(Select a) {
   // within 2 beta of the K-th largest (|fp32 - exact| <= beta for all e)
   const double beta = a.cbeta * a.xnorm[t] * *a.wmax + 1e-30;
   const double thr = vk - 2.0 * beta;
-  const double rt = (double)a.r[t];
+  const double rt = a.r[t];
   const XRow<NJ> X = load_xrow<NJ>(a.x + (size_t)t * a.H, a.H);   // read once for every candidate
   unsigned long long cm[EPL];                              // candidates, per slot (uniform)
   int nc = 0;
@@ -2302,7 +2306,7 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
 
   // staging
   {
-    Prep a{x, T, H, norm ? 1 : 0, eps, (_Float16*)p.xh, (__bf16*)p.xb, p.xnorm, p.r};
+    Prep a{x, T, H, norm ? 1 : 0, eps, (_Float16*)p.xh, (__bf16*)p.xb, p.xnorm, p.r, p.r64};
     hipLaunchKernelGGL(k_prep, dim3(T), dim3(256), 0, st, a);
     LMOE_HIP(hipGetLastError());
   }
@@ -2362,7 +2366,7 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     Select a{};
     a.logits = rsplit == 1 ? p.logits : p.o; a.nsplit = rsplit;
     a.Epad = Epad; a.T = T; a.E = E; a.H = H; a.K = K;
-    a.bias = h->bias; a.x = x; a.r = p.r; a.xnorm = p.xnorm; a.wmax = p.wmax;
+    a.bias = h->bias; a.x = x; a.r = p.r64; a.xnorm = p.xnorm; a.wmax = p.wmax;
     a.wr = (const uint16_t*)h->router_rm;
     // |fp32 logit - exact| <= beta: 2H bf16 x bf16 products, each exact,
     // summed in fp32 in any order (each addition within 2 ulp, allowing

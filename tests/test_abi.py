@@ -63,6 +63,8 @@ def _create(lib, **kw):
     (dict(du_bits=6), -1), (dict(top_k=17), -1), (dict(hidden=0), -1), (dict(max_tokens=0), -1),
     (dict(has_router_bias=2), -1), (dict(hidden=200), -5), (dict(latent=96), -5),
     (dict(expert_ffn=48), -5), (dict(n_experts=2048), -5), (dict(n_groups=65), -5),
+    # 64 groups at T 8: the decode U kernel's partial sums need more LDS than a CU has
+    (dict(n_groups=64, max_tokens=8), -5),
 ])
 def test_create_rejects_bad_dims_on_host(lib, kw, code):
     rc, h = _create(lib, **kw)

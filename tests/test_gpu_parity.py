@@ -222,3 +222,36 @@ def test_run_phase_repeats_the_forward():
     with pytest.raises(lm.LmoeError) as e:
         layer.run_phase(x[:2], y[:2], 1)               # last forward was of 4 tokens
     assert e.value.code == lm.ESTATE
+
+
+def _per_token_close(got, r, what):
+    """The bar per token: rows of very different magnitude each meet it."""
+    for t in range(got.shape[0]):
+        rel, mx = assert_close(got[t], r["y"][t], "%s token %d" % (what, t))
+        rel_r, _ = rel_errors(got[t] - r["y_shared"][t], r["y_routed"][t])
+        print("  token %d (max |x| %.3g): y rel L2 %.3g max/rms %.3g; routed part %.3g" % (
+            t, float(np.max(np.abs(r["x"][t]))), rel, mx, rel_r), flush=True)
+        assert rel_r <= 1e-4, "token %d routed part relative error %.3g" % (t, rel_r)
+
+
+@pytest.mark.parametrize("name", ["tiny", "145b_decode"])
+def test_decode_activation_range(name):
+    """Token rows far from unit scale: x scaled by 1e-3 and by 1e2, a row of
+    elements around 1e-6 with every seventh element near 1e5, and a row at
+    3e3. The fp16 staging of every activation is scaled per token by a power
+    of two, so each token meets the bar on its own."""
+    w = wl.WORKLOADS[name]
+    x = wl.x(w, 11, tokens=5)
+    x[0] *= 1e-3
+    x[1] *= 1e2
+    x[2] *= 1e-6
+    x[2, ::7] = x[2, ::7] * 1e11
+    x[4] *= 3e3
+    c = Case(w, seed=11, x=x)
+    layer = make_layer(c)
+    got, dbg = run(layer, c, 5)
+    r = c.expect(5)
+    r["x"] = x
+    assert np.array_equal(dbg["topk_idx"], r["idx"])
+    assert np.array_equal(dbg["perm"], r["perm"])
+    _per_token_close(got, r, name)

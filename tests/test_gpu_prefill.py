@@ -330,10 +330,41 @@ def test_prefill_piece_class_boundaries(latent, ffn):
 # ---------------------------------------------------------------------------
 # 145B / 120B shapes, routing over all tokens, outputs on a sample
 
+def piece_class_tokens(idx, labels, E, G, T, n_total, seed=1234):
+    """Tokens whose assignments land on every piece class of the grouped
+    GEMMs (an expert's assignments are cut into pieces of 128 in sorted
+    order; the last piece has 1..128): the last and the first assignment of
+    the largest expert, the last assignment of an expert whose last piece
+    holds 65..127, 33..64 and 1..32, the last token of the batch and one in
+    its last 64-token chunk; then seeded random tokens up to n_total."""
+    perm, count, goff = oracle.permute(idx, labels, E, G)
+    K = idx.shape[1]
+    lab = np.asarray(labels, np.int64)
+    order = np.lexsort((np.arange(E), lab))           # (label, expert) order of the segments
+    start = np.concatenate([[0], np.cumsum(count[order])])[:-1]
+    seg = {int(e): int(s0) for e, s0 in zip(order, start)}
+    picks = []
+    big = int(np.argmax(count))
+    picks += [int(perm[seg[big] + count[big] - 1]) // K, int(perm[seg[big]]) // K]
+    last = np.where(count > 0, count - 128 * ((count - 1) // 128), 0)
+    for lo, hi in ((65, 127), (33, 64), (1, 32)):
+        es = np.where((last >= lo) & (last <= hi))[0]
+        if len(es):
+            e = int(es[0])
+            picks.append(int(perm[seg[e] + count[e] - 1]) // K)
+    picks += [T - 1, T - 1 - int(np.random.default_rng(seed).integers(1, min(64, T)))]
+    rng = np.random.default_rng(seed)
+    tokens = set(picks)
+    while len(tokens) < n_total:
+        tokens.add(int(rng.integers(0, T)))
+    return np.array(sorted(tokens))
+
+
 def _sampled(name, T, n_sample, seed=0):
     w = wl.WORKLOADS[name]
-    rng = np.random.default_rng(1234)
-    tokens = np.unique(np.concatenate([[0, T - 1], rng.choice(T, n_sample - 2, replace=False)]))
+    pre = Case(w, seed=seed, tokens=T, pack_tokens=[0])          # routing of every token
+    labels = np.asarray(pre.blobs["labels"])
+    tokens = piece_class_tokens(pre.idx, labels, w.n_experts, w.n_groups, T, n_sample)
     print("case %s prefill T %d, packing experts of tokens %s" % (name, T, tokens.tolist()),
           flush=True)
     c = Case(w, seed=seed, tokens=T, pack_tokens=tokens)
@@ -345,8 +376,8 @@ def _sampled(name, T, n_sample, seed=0):
 
 
 def test_145b_prefill_4096():
-    _sampled("145b_prefill", 4096, 6)
+    _sampled("145b_prefill", 4096, 16)
 
 
 def test_120b_prefill_q4():
-    _sampled("120b_decode", 600, 4)
+    _sampled("120b_decode", 600, 16)
