@@ -149,6 +149,19 @@ int lmoe_load_weights(lmoe_t* h, const lmoe_weights* w, void* hip_stream);
 int lmoe_forward(lmoe_t* h, const float* x_dev, int32_t T, float* y_dev,
                  const lmoe_debug* dbg, void* hip_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * forward as lmoe_forward for T <= 8 tokens (the decode path, same kernels,
+ * bit-identical y), with its workspace in a static device array of 16 MiB per
+ * GPU instead of the handle's. It calls no allocator. All calls on one GPU
+ * share that array: calls that overlap on one GPU (other streams, other
+ * handles) race and must be ordered by the caller. x and y are device fp32
+ * [T][H], not aliased. LMOE_EUNSUPPORTED for T > 8 or when the layer's
+ * workspace at this T exceeds the array (it holds the 145B shapes at T 8
+ * several times over); LMOE_EINVAL / LMOE_ESTATE as lmoe_forward. No debug
+ * outputs. */
+int lmoe_forward_noalloc(lmoe_t* h, const float* x, int32_t T, float* y, void* hip_stream);
+
 /* One block of a pre-norm residual stack, in place on device memory:
  *   x += layer(RMSNorm(x)),  RMSNorm(v) = v / sqrt(mean(v^2) + eps), unit gain.
  * (The stack arrangement is this library's reading; the pages give none.) */

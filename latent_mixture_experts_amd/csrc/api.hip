@@ -2,8 +2,10 @@
 // validation, device memory, and dispatch to the decode path.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <new>
 #include <string>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -75,6 +77,56 @@ void free_all(lmoe_t* h) {
   h->aux = nullptr;
 }
 
+}  // namespace
+
+// Lays out the decode workspace for up to T tokens at `base` (nullptr: only
+// sizes it); returns its bytes. Each array starts on a 256-byte boundary.
+size_t decode_ws_layout(const lmoe_t* h, int T, char* base, Workspace* out) {
+  const lmoe_dims& d = h->d;
+  const int E = d.n_experts, H = d.hidden, L = d.latent, G = d.n_groups, F = d.expert_ffn,
+            Fs = d.shared_ffn, K = d.top_k;
+  const int nss_d = (H + kSSCols - 1) / kSSCols, nss_s = nss_d;
+  const int Epad = (E + 63) / 64 * 64;
+  const int n = T * K;
+  Workspace w;
+  w.tmax = T;
+  w.nch = (H + 64 * nss_d - 1) / (64 * nss_d);
+  size_t off = 0;
+  auto take = [&](auto*& p, size_t bytes) {
+    off = (off + 255) / 256 * 256;
+    p = base ? reinterpret_cast<std::remove_reference_t<decltype(p)>>(base + off) : nullptr;
+    off += bytes ? bytes : 1;
+  };
+  take(w.part64, sizeof(double) * w.nch * T * Epad);
+  take(w.topk_idx, sizeof(int) * n);
+  take(w.topk_w, sizeof(float) * n);
+  take(w.perm, sizeof(int) * n);
+  take(w.tg_cnt, sizeof(int) * T * G);
+  take(w.tg_pos, sizeof(int) * T * G * K);
+  take(w.slot_expert, sizeof(int) * n);
+  take(w.slot_start, sizeof(int) * n);
+  take(w.slot_count, sizeof(int) * n);
+  take(w.n_slots, sizeof(int));
+  take(w.gslot_off, sizeof(int) * (G + 1));
+  take(w.group_off, sizeof(int) * (G + 1));
+  take(w.expert_count, sizeof(int) * E);
+  take(w.rms, sizeof(float) * T);
+  take(w.rms64, sizeof(double) * T);
+  take(w.xl, sizeof(float) * T * G * L);
+  take(w.hs, sizeof(float) * T * Fs);
+  take(w.hsp, sizeof(float) * nss_s * T * 2 * Fs);
+  take(w.hbuf, sizeof(float) * n * F);
+  take(w.s, sizeof(float) * T * G * L);
+  // 2G + shared-down blocks (at most one per half-step)
+  take(w.ypart, sizeof(float) * (2 * G + (Fs + 127) / 128) * T * H);
+  take(w.ctr_router, sizeof(unsigned));
+  take(w.ctr_y, sizeof(unsigned) * (H / 64));
+  if (out) *out = w;
+  return (off + 255) / 256 * 256;
+}
+
+namespace {
+
 int create_impl(lmoe_t* h) {
   const lmoe_dims& d = h->d;
   const int E = d.n_experts, H = d.hidden, L = d.latent, G = d.n_groups, F = d.expert_ffn,
@@ -101,35 +153,12 @@ int create_impl(lmoe_t* h) {
   A(h->sgu, h->g_sgu.bytes());
   A(h->sdn, h->g_sdn.bytes());
 
-  Workspace& w = h->ws;
-  const int T = d.max_tokens < kMaxDecodeT ? d.max_tokens : kMaxDecodeT;
-  w.tmax = T;
-  w.nch = (H + 64 * h->g_d.nss - 1) / (64 * h->g_d.nss);
-  const int Epad = h->g_router.tiles * 64;
-  const int n = T * K;
-  A(w.part64, sizeof(double) * w.nch * T * Epad);
-  A(w.topk_idx, sizeof(int) * n);
-  A(w.topk_w, sizeof(float) * n);
-  A(w.perm, sizeof(int) * n);
-  A(w.tg_cnt, sizeof(int) * T * G);
-  A(w.tg_pos, sizeof(int) * T * G * K);
-  A(w.slot_expert, sizeof(int) * n);
-  A(w.slot_start, sizeof(int) * n);
-  A(w.slot_count, sizeof(int) * n);
-  A(w.n_slots, sizeof(int));
-  A(w.gslot_off, sizeof(int) * (G + 1));
-  A(w.group_off, sizeof(int) * (G + 1));
-  A(w.expert_count, sizeof(int) * E);
-  A(w.rms, sizeof(float) * T);
-  A(w.rms64, sizeof(double) * T);
-  A(w.xl, sizeof(float) * T * G * L);
-  A(w.hs, sizeof(float) * T * Fs);
-  A(w.hsp, sizeof(float) * h->g_sgu.nss * T * 2 * Fs);
-  A(w.hbuf, sizeof(float) * n * F);
-  A(w.s, sizeof(float) * T * G * L);
-  A(w.ypart, sizeof(float) * (2 * G + (Fs + 127) / 128) * T * H);   // 2G + shared-down blocks (at most one per half-step)
-  A(w.ctr_router, sizeof(unsigned));
-  A(w.ctr_y, sizeof(unsigned) * (H / 64));
+  {
+    const int T = d.max_tokens < kMaxDecodeT ? d.max_tokens : kMaxDecodeT;
+    char* base = nullptr;
+    A(base, decode_ws_layout(h, T, nullptr, nullptr));
+    decode_ws_layout(h, T, base, &h->ws);
+  }
 
   // prefill path (T > kMaxDecodeT): router copies and GEMM workspace
   if (d.max_tokens > kMaxDecodeT) {
@@ -175,8 +204,8 @@ int create_impl(lmoe_t* h) {
     LMOE_HIP(hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming));
   }
 #undef A
-  LMOE_HIP(hipMemset(w.ctr_router, 0, sizeof(unsigned)));
-  LMOE_HIP(hipMemset(w.ctr_y, 0, sizeof(unsigned) * (H / 64)));
+  LMOE_HIP(hipMemset(h->ws.ctr_router, 0, sizeof(unsigned)));
+  LMOE_HIP(hipMemset(h->ws.ctr_y, 0, sizeof(unsigned) * (H / 64)));
   LMOE_HIP(hipDeviceSynchronize());
   return 0;
 }
@@ -258,6 +287,48 @@ int check_forward(lmoe_t* h, const void* x, int T, const void* y) {
   return 0;
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free decode forwards: the workspace lives in one static device
+// array per GPU (allocated by the loader with the code object, kept until the
+// process ends). Host code never passes `scratch` itself to a kernel (its
+// host-side name is only a stand-in): each device's address is looked up once
+// with hipGetSymbolAddress and kept here.
+constexpr size_t kScratchBytes = (size_t)16 << 20;   // 16 MiB per GPU
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+char* g_scratch[kMaxDevices] = {};
+
+// Looks up this device's copy of `scratch` (the device must be current).
+int scratch_setup(int device) {
+  if (device < 0 || device >= kMaxDevices) {
+    set_error("scratch: device index above the supported count");
+    return LMOE_EUNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch[device]) return 0;
+  void* p = nullptr;
+  LMOE_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+  if (!p) {
+    set_error("scratch: hipGetSymbolAddress returned no address");
+    return LMOE_EHIP;
+  }
+  g_scratch[device] = (char*)p;
+  return 0;
+}
+
+char* scratch_of(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  return g_scratch[device];
+}
+
+// Zeroes n 32-bit words (the kernels' arrival counters must start at 0).
+__global__ void k_fill_zero(unsigned* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
 }  // namespace
 }  // namespace lm
 
@@ -286,6 +357,10 @@ int lmoe_create(const lmoe_dims* dims, int hip_device, lmoe_t** out) {
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, hip_device) == hipSuccess &&
       ncu > 0)
     h->ncu = ncu;
+  if (int rc = scratch_setup(hip_device)) {
+    delete h;
+    return rc;
+  }
   if (int rc = create_impl(h)) {
     free_all(h);
     delete h;
@@ -319,6 +394,41 @@ int lmoe_forward(lmoe_t* h, const float* x, int32_t T, float* y, const lmoe_debu
   h->last_decode_T = T > kMaxDecodeT ? h->last_decode_T : T;
   if (dbg) return copy_debug(h, dbg, T, st);
   return 0;
+}
+
+int lmoe_forward_noalloc(lmoe_t* h, const float* x, int32_t T, float* y, void* stream) {
+  if (!h || !x || !y || x == y || T <= 0 || T > h->d.max_tokens) {
+    set_error("lmoe_forward_noalloc: NULL or aliased x / y, or T outside [1, max_tokens]");
+    return LMOE_EINVAL;
+  }
+  if (T > kMaxDecodeT) {
+    set_error("lmoe_forward_noalloc: serves the decode path only (T <= 8)");
+    return LMOE_EUNSUPPORTED;
+  }
+  const size_t need = decode_ws_layout(h, T, nullptr, nullptr);
+  if (need > kScratchBytes) {
+    set_error("lmoe_forward_noalloc: the layer needs " + std::to_string(need) +
+              " bytes of workspace at this T, above the " + std::to_string(kScratchBytes) +
+              "-byte static scratch");
+    return LMOE_EUNSUPPORTED;
+  }
+  if (int rc = check_forward(h, x, T, y)) return rc;
+  DeviceGuard g(h->device);
+  char* base = scratch_of(h->device);
+  if (!base) {
+    set_error("lmoe_forward_noalloc: no scratch address for this device");
+    return LMOE_EHIP;
+  }
+  Workspace ws;
+  decode_ws_layout(h, T, base, &ws);
+  hipStream_t st = (hipStream_t)stream;
+  // the counters reset themselves at the end of a forward; clear them anyway,
+  // in case another handle's forward on this device stopped short
+  const int nctr = h->d.hidden / 64;
+  hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(64), 0, st, ws.ctr_router, 1);
+  hipLaunchKernelGGL(k_fill_zero, dim3((nctr + 255) / 256), dim3(256), 0, st, ws.ctr_y, nctr);
+  LMOE_HIP(hipGetLastError());
+  return forward_decode(h, x, T, y, false, st, 0, &ws);
 }
 
 int lmoe_forward_block(lmoe_t* h, float* x, int32_t T, float eps, void* stream) {

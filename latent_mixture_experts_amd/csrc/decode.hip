@@ -1299,11 +1299,11 @@ int resident_blocks(lmoe_t* h, const void* kernel, int threads, size_t lds) {
 // only: 0 launches every phase, k in 1..4 phase k alone (its inputs are in
 // the workspace from an earlier forward of T tokens)
 template <int T, int DU>
-int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st, int only) {
+int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st, int only,
+               const Workspace& ws) {
   const lmoe_dims& dd = h->d;
   Dims d{T, dd.hidden, dd.latent, dd.n_experts, dd.top_k, dd.n_groups, dd.expert_ffn,
          dd.shared_ffn};
-  Workspace ws = h->ws;
   const bool ev = only == 0 && h->phase_events.size() == (size_t)kDecodePhases + 1;
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[0], st));
 
@@ -1414,9 +1414,10 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st, i
 }
 
 template <int T>
-int launch_t(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st, int only) {
-  return h->d.du_bits == 8 ? launch_all<T, kQ8>(h, x, y, norm, st, only)
-                           : launch_all<T, kQ4>(h, x, y, norm, st, only);
+int launch_t(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st, int only,
+             const Workspace& ws) {
+  return h->d.du_bits == 8 ? launch_all<T, kQ8>(h, x, y, norm, st, only, ws)
+                           : launch_all<T, kQ4>(h, x, y, norm, st, only, ws);
 }
 
 // Largest dynamic LDS any of the four kernels asks for at T tokens (the
@@ -1458,16 +1459,18 @@ int rms_rows(lmoe_t* h, const float* x, int T, float eps, hipStream_t st) {
   return 0;
 }
 
-int forward_decode(lmoe_t* h, const float* x, int T, float* y, bool norm, hipStream_t st, int only) {
+int forward_decode(lmoe_t* h, const float* x, int T, float* y, bool norm, hipStream_t st, int only,
+                   const Workspace* ws) {
+  const Workspace& w = ws ? *ws : h->ws;
   switch (T) {
-    case 1: return launch_t<1>(h, x, y, norm, st, only);
-    case 2: return launch_t<2>(h, x, y, norm, st, only);
-    case 3: return launch_t<3>(h, x, y, norm, st, only);
-    case 4: return launch_t<4>(h, x, y, norm, st, only);
-    case 5: return launch_t<5>(h, x, y, norm, st, only);
-    case 6: return launch_t<6>(h, x, y, norm, st, only);
-    case 7: return launch_t<7>(h, x, y, norm, st, only);
-    case 8: return launch_t<8>(h, x, y, norm, st, only);
+    case 1: return launch_t<1>(h, x, y, norm, st, only, w);
+    case 2: return launch_t<2>(h, x, y, norm, st, only, w);
+    case 3: return launch_t<3>(h, x, y, norm, st, only, w);
+    case 4: return launch_t<4>(h, x, y, norm, st, only, w);
+    case 5: return launch_t<5>(h, x, y, norm, st, only, w);
+    case 6: return launch_t<6>(h, x, y, norm, st, only, w);
+    case 7: return launch_t<7>(h, x, y, norm, st, only, w);
+    case 8: return launch_t<8>(h, x, y, norm, st, only, w);
     default: return LMOE_EUNSUPPORTED;
   }
 }

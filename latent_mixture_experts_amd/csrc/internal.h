@@ -211,8 +211,9 @@ int pack_experts_impl(const float* gate, const float* up, const float* down, int
 
 // decode.hip
 // only: 0 runs the whole forward, 1..4 that phase alone
+// ws: the workspace to run on (nullptr: the handle's)
 int forward_decode(lmoe_t* h, const float* x, int T, float* y, bool norm, hipStream_t stream,
-                   int only = 0);
+                   int only = 0, const Workspace* ws = nullptr);
 int rms_rows(lmoe_t* h, const float* x, int T, float eps, hipStream_t stream);
 // Largest dynamic LDS a decode kernel needs for T tokens (a handle whose
 // decode path would need more than a CU has is refused at create).
@@ -230,6 +231,7 @@ int prefill_debug_latent(lmoe_t* h, int T, float* dst, hipStream_t stream);
 
 // api.hip
 void set_error(const std::string& msg);
+size_t decode_ws_layout(const lmoe_t* h, int T, char* base, Workspace* out);
 int hip_fail(hipError_t e, const char* what);
 
 }  // namespace lm

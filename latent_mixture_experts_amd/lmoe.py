@@ -64,6 +64,7 @@ def _load():
         "lmoe_load_weights": (ctypes.c_int, [vp, ctypes.POINTER(Weights), vp]),
         "lmoe_forward": (ctypes.c_int, [vp, vp, i32, vp, ctypes.POINTER(Debug), vp]),
         "lmoe_forward_block": (ctypes.c_int, [vp, vp, i32, ctypes.c_float, vp]),
+        "lmoe_forward_noalloc": (ctypes.c_int, [vp, vp, i32, vp, vp]),
         "lmoe_destroy": (None, [vp]),
         "lmoe_set_phase_events": (ctypes.c_int, [vp, ctypes.POINTER(vp), i32]),
         "lmoe_phase_count": (i32, [i32]),
@@ -164,6 +165,13 @@ class Layer:
         _check(_lib.lmoe_forward(self._h, _ptr(x), T, _ptr(y),
                                  ctypes.byref(dbg) if dbg is not None else None, _stream(stream)),
                "lmoe_forward")
+        return y
+
+    def forward_noalloc(self, x, y, T=None, stream=None):
+        """lmoe_forward_noalloc: the decode forward on the static scratch."""
+        T = x.shape[0] if T is None else T
+        _check(_lib.lmoe_forward_noalloc(self._h, _ptr(x), T, _ptr(y), _stream(stream)),
+               "lmoe_forward_noalloc")
         return y
 
     def forward_block(self, x, eps=1e-6, T=None, stream=None):
