@@ -269,6 +269,34 @@ def bench_prefill(lm, wl, w, args, torch):
     return out
 
 
+def calibrate_hbm(torch, copy_bytes=256 << 20, reps=4, read_bytes=1 << 30):
+    """Reference runs for the profiler's HBM counters (--calibrate-hbm):
+    a device-to-device copy of exactly 256 MiB, repeated (each copy reads
+    and writes 268,435,456 bytes: the scale for FETCH_SIZE / WRITE_SIZE), and
+    the read bandwidth of a plain streaming reduction over 1 GiB (the
+    achievable-bandwidth reference beside the published peak)."""
+    src = torch.ones(copy_bytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    big = torch.ones(read_bytes // 4, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        big.sum()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 20
+    start.record()
+    for _ in range(n):
+        big.sum()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / n
+    print(json.dumps({"copy_bytes_per_launch": copy_bytes, "copies": reps,
+                      "sum_read_bytes": read_bytes, "sum_ms": ms,
+                      "sum_read_GBps": read_bytes / (ms * 1e-3) / 1e9}), flush=True)
+
+
 def host_cores():
     """Threads the oracle can use on this host: os.cpu_count(), the
     affinity-mask size and the BLAS thread count."""

@@ -114,8 +114,9 @@ __device__ __forceinline__ int wave_max_nonneg(int v) {
 // A vector whose largest magnitude is zero, subnormal, infinite or NaN is
 // staged as is (inf and NaN then reach y, as in exact arithmetic).
 template <int NT>
-__device__ __forceinline__ void x_stage_f16(const XRegs<NT>& r, _Float16* xs, int lane,
+__device__ __forceinline__ bool x_stage_f16(const XRegs<NT>& r, _Float16* xs, int lane,
                                             float (&inv)[NT]) {
+  bool any = false;
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
     const float v[4] = {r.v[i].x, r.v[i].y, r.v[i].z, r.v[i].w};
@@ -137,6 +138,7 @@ __device__ __forceinline__ void x_stage_f16(const XRegs<NT>& r, _Float16* xs, in
     }
     const float sc = __int_as_float((127 + sh) << 23);
     inv[i] = __int_as_float((127 - sh) << 23);
+    any = any || sh != 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float u = v[j] * sc;
@@ -145,6 +147,7 @@ __device__ __forceinline__ void x_stage_f16(const XRegs<NT>& r, _Float16* xs, in
       xs[(1 * NT + i) * kXStr + 4 * lane + j] = (_Float16)(u - (float)hi);
     }
   }
+  return any;
 }
 
 // The inverse scales of the tokens a lane holds in the MFMA D layout
@@ -320,18 +323,10 @@ __device__ __forceinline__ void wave_compute(const WRegs<FMT, NT, SL>& R, int nc
   const uint4 (&sc)[4] = R.sc;
   const uint4 (&q)[SL] = R.q;
   float inv[NT];
+  bool scaled = false;
   if (FMT == kBF16) x_stage_bf16<NT>(R.xr, (__bf16*)xs, lane);
-  else x_stage_f16<NT>(R.xr, (_Float16*)xs, lane, inv);
+  else scaled = x_stage_f16<NT>(R.xr, (_Float16*)xs, lane, inv);
   __builtin_amdgcn_wave_barrier();
-  f4 iv = {1.f, 1.f, 1.f, 1.f};
-  if (FMT != kBF16) iv = lane_inv<NT>(inv, lane);
-  // NVFP4: this super-step's products in their own accumulators, unscaled
-  // into acc at the end
-  f4 dss[4];
-  if (FMT == kFP4) {
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) dss[rg] = (f4){0.f, 0.f, 0.f, 0.f};
-  }
 
   const int nch = ncs / 4;
 #pragma unroll
@@ -369,8 +364,15 @@ __device__ __forceinline__ void wave_compute(const WRegs<FMT, NT, SL>& R, int nc
             const uint32_t sb = (word(sc[rg], k >> 1) >> (16 * (k & 1) + 8 * (qg >> 1))) & 0xFFu;
             const _Float16 s = (_Float16)__builtin_amdgcn_cvt_f32_fp8(sb, 0);
             const half8 bw = dec_fp4(word(w, b), s);
-            dss[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahb, bw, dss[rg], 0, 0, 0);
-            dss[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alb, bw, dss[rg], 0, 0, 0);
+            if (!scaled) {                               // wave-uniform
+              acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahb, bw, acc[rg], 0, 0, 0);
+              acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alb, bw, acc[rg], 0, 0, 0);
+            } else {                                     // undo the token scales per block
+              f4 d = {0.f, 0.f, 0.f, 0.f};
+              d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahb, bw, d, 0, 0, 0);
+              d = __builtin_amdgcn_mfma_f32_16x16x32_f16(alb, bw, d, 0, 0, 0);
+              acc[rg] += d * lane_inv<NT>(inv, lane);
+            }
           } else {
             const half8 bw = FMT == kQ8 ? dec_q8(word(w, 2 * b), word(w, 2 * b + 1))
                                         : dec_q4(word(w, b));
@@ -379,15 +381,12 @@ __device__ __forceinline__ void wave_compute(const WRegs<FMT, NT, SL>& R, int nc
             d = __builtin_amdgcn_mfma_f32_16x16x32_f16(alb, bw, d, 0, 0, 0);
             const int blk = NB * c + b;                  // fp16 scale of this 32-column block
             const float s = h2f(word(sc[rg], blk >> 1) >> (16 * (blk & 1)));
-            acc[rg] += (s * iv) * d;
+            if (!scaled) acc[rg] += s * d;
+            else acc[rg] += (s * lane_inv<NT>(inv, lane)) * d;
           }
         }
       }
     }
-  }
-  if (FMT == kFP4) {
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) acc[rg] += dss[rg] * iv;
   }
 }
 
