@@ -180,6 +180,8 @@ int create_impl(lmoe_t* h) {
     A(p.xnorm, sizeof(double) * Tp);
     A(p.r, sizeof(float) * Tp);
     A(p.r64, sizeof(double) * Tp);
+    A(p.xsc, sizeof(float) * Tp);
+    A(p.psc, sizeof(float) * nk);
     A(p.logits, sizeof(float) * Tp * Epm);
     A(p.idx, sizeof(int) * nk);
     A(p.w, sizeof(float) * nk);

@@ -135,6 +135,8 @@ struct PrefillWs {
   double* xnorm = nullptr;         // [T] 2-norm of the staged rows
   float* r = nullptr;              // [T] row scale (1/rms in the block forward, else 1)
   double* r64 = nullptr;           // [T] the same in fp64 (the fp64 rescoring of the logits)
+  float* xsc = nullptr;            // [T] power-of-two range scale of the fp16 activations
+  float* psc = nullptr;            // [T*K] the same per sorted assignment
   float* logits = nullptr;         // [T][Epad] fp32 router logits
   int* idx = nullptr;              // [T][K]
   float* w = nullptr;              // [T][K]

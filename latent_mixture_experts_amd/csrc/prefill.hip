@@ -69,6 +69,10 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
+// 1 / v for v a power of two in [2^-126, 2^127]: exact, from the exponent
+__device__ __forceinline__ float inv_pow2(float v) {
+  return __builtin_bit_cast(float, 0x7F000000u - __builtin_bit_cast(uint32_t, v));
+}
 
 // ---------------------------------------------------------------------------
 // Weight decoding: the 8 columns one lane holds of one 32-column block.
@@ -520,6 +524,7 @@ struct Dense {
   size_t ostride;
   int nvalid;
   const float* res;   // kEpiY: residual rows [T][ostride] or null
+  const float* xsc;   // kEpiSwigluB2, kEpiY: range scale c per token (h gets c^2, y c^-2)
   // kEpiY and kEpiLogits: the first nfull logical tiles run whole; each of
   // the remaining nrem runs as nsplit blocks along k. Split sp covers a
   // balanced share of the stages of W (kEpiY: then W2, a W2 stage, bf16 in
@@ -592,7 +597,8 @@ __device__ __forceinline__ void dense_epilogue(const Dense& a, const f16v (&acc)
         // rows 0..31 of the tile are gate rows 32*tile + 0..31, rows 32..63
         // the up rows of the same indices
         const int f = 32 * tile + (lane & 31);
-        const float hv = silu(acc[mb][0][v]) * acc[mb][1][v];
+        const float c = a.xsc[t];
+        const float hv = silu(acc[mb][0][v]) * acc[mb][1][v] * c * c;
         const __bf16 h0 = (__bf16)hv;
         const __bf16 h1 = (__bf16)(hv - (float)h0);
         __bf16* o = (__bf16*)a.out + (size_t)t * a.ostride;
@@ -612,7 +618,8 @@ __device__ __forceinline__ void dense_epilogue(const Dense& a, const f16v (&acc)
             a.part[(j * BM + (t - mt * BM)) * 256 + (n - 256 * quad)] = val;
           } else {
             const size_t i = (size_t)t * a.ostride + n;
-            ((float*)a.out)[i] = a.res ? a.res[i] + val : val;
+            const float ic = inv_pow2(a.xsc[t]), yv = val * ic * ic;
+            ((float*)a.out)[i] = a.res ? a.res[i] + yv : yv;
           }
         }
       }
@@ -837,6 +844,7 @@ struct Grouped {
   int ntiles, nquads, G, F;
   const int* perm;      // [T*K] sorted position -> assignment t*K + k
   const float* topk_w;  // [T*K]
+  const float* psc;     // [T*K] range scale of each sorted assignment's token
   const uint8_t* labels;
   int K;
   void* out;
@@ -886,7 +894,9 @@ __global__ __launch_bounds__(NTH) void k_grouped(Grouped a) {
       if constexpr (EPI == kGateUp) {
         const float tg = ts[0], tu = ts[1];
         const int f = 32 * tile + (lane & 31);
-        const float hv = silu(acc[mb][0][v] * tg) * (acc[mb][1][v] * tu);
+        // gate and up carry the token's range scale c: h = silu(g) u c^2
+        const float c = a.psc[pos];
+        const float hv = silu(acc[mb][0][v] * tg * inv_pow2(c)) * (acc[mb][1][v] * tu * c);
         ((_Float16*)a.out)[pos * a.ostride + f] = (_Float16)hv;
       } else {
         const float sc = a.topk_w[a.perm[pos]] * ts[2];
@@ -1050,7 +1060,9 @@ __global__ __launch_bounds__(NTH) void k_grouped_dma(Grouped a) {
       const size_t pos = (size_t)pc.start + i;
       const float tg = ts[0], tu = ts[1];
       const int f = 32 * tile + (lane & 31);
-      const float hv = silu(acc[mb][0][v] * tg) * (acc[mb][1][v] * tu);
+      // gate and up carry the token's range scale c: h = silu(g) u c^2
+      const float c = a.psc[pos];
+      const float hv = silu(acc[mb][0][v] * tg * inv_pow2(c)) * (acc[mb][1][v] * tu * c);
       ((_Float16*)a.out)[pos * a.ostride + f] = (_Float16)hv;
     }
 }
@@ -1276,7 +1288,9 @@ __global__ __launch_bounds__(64 * NW) void k_grouped_short(Grouped a, int lo, in
       if constexpr (EPI == kGateUp) {
         const float tg = ts[0], tu = ts[1];
         const int f = 32 * tile + (lane & 31);
-        const float hv = silu(acc[mb][0][v] * tg) * (acc[mb][1][v] * tu);
+        // gate and up carry the token's range scale c: h = silu(g) u c^2
+        const float c = a.psc[pos];
+        const float hv = silu(acc[mb][0][v] * tg * inv_pow2(c)) * (acc[mb][1][v] * tu * c);
         ((_Float16*)a.out)[pos * a.ostride + f] = (_Float16)hv;
       } else {
         const float sc = a.topk_w[a.perm[pos]] * ts[2];
@@ -1472,7 +1486,25 @@ struct Prep {
   double* xnorm;    // [T] |staged row|_2
   float* r;         // [T] the row scale (1/rms, or 1)
   double* r64;      // [T] the same in fp64 (exact 1/rms for the fp64 logits)
+  float* xsc;       // [T] power-of-two scale of the fp16 rows
 };
+
+// Range of the fp16 activations. A staged row whose largest magnitude m lies
+// outside [2^-3, 2^6) is multiplied by the power of two c that brings m into
+// [4, 8) (|log2 c| <= 60), so that the fp16 copies of x, D x and of what
+// follows neither overflow nor lose bits to subnormals. The path is linear in
+// x up to the SwiGLU: D x, the gate and up rows carry c, h = silu(g) u is
+// formed from the unscaled gate and carries c^2 (so do the expert outputs,
+// the per-group sums and the shared expert's hidden row), and U's
+// accumulators are multiplied by c^-2. Powers of two make every one of these
+// steps exact, and c = 1 (every unit-scale and every normalized row) leaves
+// the arithmetic as it is without them.
+__device__ __forceinline__ float range_scale(float m) {
+  if (!(m > 0.f) || !(m < 3.0e38f) || (m >= 0.125f && m < 64.f)) return 1.f;
+  int ex;
+  frexpf(m, &ex);                                       // m = f 2^ex, f in [0.5, 1)
+  return ldexpf(1.f, max(-60, min(60, 3 - ex)));
+}
 
 __device__ __forceinline__ double block_sum(double v, double* red) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -1491,20 +1523,32 @@ __global__ __launch_bounds__(256) void k_prep(Prep a) {
   const int t = blockIdx.x;
   const float* xr = a.x + (size_t)t * a.H;
   const int nc = a.H / 8;
+  __shared__ float redm[4];
   float r = 1.0f;
   double r64 = 1.0;
-  if (a.norm) {
-    double s = 0.0;
-    for (int c = threadIdx.x; c < nc; c += blockDim.x) {
-      const float4 u0 = *(const float4*)(xr + 8 * c), u1 = *(const float4*)(xr + 8 * c + 4);
-      const float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+  double s = 0.0;
+  float m = 0.f;
+  for (int c = threadIdx.x; c < nc; c += blockDim.x) {
+    const float4 u0 = *(const float4*)(xr + 8 * c), u1 = *(const float4*)(xr + 8 * c + 4);
+    const float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s += (double)v[j] * v[j];
+    for (int j = 0; j < 8; ++j) {
+      if (a.norm) s += (double)v[j] * v[j];
+      m = fmaxf(m, fabsf(v[j]));
     }
+  }
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) redm[threadIdx.x >> 6] = m;
+  if (a.norm) {
     s = block_sum(s, red);
     r64 = 1.0 / sqrt(s / a.H + (double)a.eps);
     r = (float)r64;
+  } else {
+    __syncthreads();
   }
+  m = fmaxf(fmaxf(redm[0], redm[1]), fmaxf(redm[2], redm[3]));
+  // the largest staged magnitude, up to rounding (enough to pick the scale)
+  const float xs = range_scale(m * r);
   double s2 = 0.0;
   for (int c = threadIdx.x; c < nc; c += blockDim.x) {
     const float4 u0 = *(const float4*)(xr + 8 * c), u1 = *(const float4*)(xr + 8 * c + 4);
@@ -1514,7 +1558,7 @@ __global__ __launch_bounds__(256) void k_prep(Prep a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (a.norm) v[j] *= r;
-      h[j] = (_Float16)v[j];
+      h[j] = (_Float16)(v[j] * xs);
       b0[j] = (__bf16)v[j];
       b1[j] = (__bf16)(v[j] - (float)b0[j]);
       s2 += (double)v[j] * v[j];
@@ -1528,6 +1572,7 @@ __global__ __launch_bounds__(256) void k_prep(Prep a) {
     a.xnorm[t] = sqrt(s2);
     a.r[t] = r;
     a.r64[t] = r64;
+    a.xsc[t] = xs;
   }
 }
 
@@ -1831,6 +1876,8 @@ struct Perm {
   int* npieces;
   int* perm;             // [T*K]
   int* inv;              // [T*K]
+  const float* xsc;      // [T] range scale per token
+  float* psc;            // [T*K] the same per sorted position
 };
 
 __global__ __launch_bounds__(256) void k_perm_mask(Perm a) {
@@ -1945,6 +1992,7 @@ __global__ __launch_bounds__(256) void k_perm_scatter(Perm a) {
   const int pos = a.seg_start[e] + a.cbase[ci] + __popcll(a.cmask[ci] & below);
   a.perm[pos] = i;
   a.inv[i] = pos;
+  a.psc[pos] = a.xsc[t];
 }
 
 // ---------------------------------------------------------------------------
@@ -2051,9 +2099,10 @@ __global__ void k_dequant_du(const uint8_t* src, Geom gs, int fmt, uint8_t* dst,
 }
 
 // fp16 latent rows to fp32 (debug copy)
-__global__ void k_f16_to_f32(const _Float16* src, size_t n, float* dst) {
+// fp16 rows of `row` elements to fp32, the row's range scale taken out
+__global__ void k_f16_to_f32(const _Float16* src, size_t n, size_t row, const float* xsc, float* dst) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) dst[i] = (float)src[i];
+  if (i < n) dst[i] = (float)src[i] * inv_pow2(xsc[i / row]);
 }
 
 // max_e |Wr_e|_2 of the row-major bf16 router, fp64, one block
@@ -2096,10 +2145,12 @@ __global__ __launch_bounds__(256) void k_ytiles(Dense a, const float* res) {
   float p[NS];
 #pragma unroll
   for (int k = 0; k < NS; ++k) p[k] = a.part[((size_t)k * a.nrem + j) * tsz + e];
-  float v = res ? res[i] : 0.f;
+  float v = p[0];
 #pragma unroll
-  for (int k = 0; k < NS; ++k) v += p[k];
-  ((float*)a.out)[i] = v;
+  for (int k = 1; k < NS; ++k) v += p[k];
+  const float ic = inv_pow2(a.xsc[t]);
+  v = v * ic * ic;
+  ((float*)a.out)[i] = res ? res[i] + v : v;
 }
 
 // ---------------------------------------------------------------------------
@@ -2306,7 +2357,7 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
 
   // staging
   {
-    Prep a{x, T, H, norm ? 1 : 0, eps, (_Float16*)p.xh, (__bf16*)p.xb, p.xnorm, p.r, p.r64};
+    Prep a{x, T, H, norm ? 1 : 0, eps, (_Float16*)p.xh, (__bf16*)p.xb, p.xnorm, p.r, p.r64, p.xsc};
     hipLaunchKernelGGL(k_prep, dim3(T), dim3(256), 0, st, a);
     LMOE_HIP(hipGetLastError());
   }
@@ -2331,6 +2382,7 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
       a.A = AMat{p.xb, (size_t)2 * H, H, H};
       a.T = T; a.mtiles = mtiles; a.ntiles = h->g_sgu.tiles; a.nquads = (a.ntiles + NTW - 1) / NTW;
       a.out = p.hsb; a.ostride = (size_t)2 * Fs; a.nvalid = Fs;
+      a.xsc = p.xsc;
       if (int rc = launch_dense<kBF16, kEpiSwigluB2>(a, sd)) return rc;
       if (ev) LMOE_HIP(hipEventRecord(h->phase_events[4], sd));
     }
@@ -2396,7 +2448,7 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     a.cmask = p.cmask; a.ccnt = p.ccnt; a.cbase = p.cbase; a.eorder = p.eorder;
     a.labels = h->labels; a.seg_start = p.seg_start; a.expert_count = p.expert_count;
     a.group_off = p.group_off; a.pieces = (Piece*)p.pieces; a.npieces = p.npieces;
-    a.perm = p.perm; a.inv = p.inv;
+    a.perm = p.perm; a.inv = p.inv; a.xsc = p.xsc; a.psc = p.psc;
     hipLaunchKernelGGL(k_perm_mask, dim3(a.nchunk), dim3(256), 0, st, a);
     LMOE_HIP(hipGetLastError());
     hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(kMaxE), 0, st, a);
@@ -2419,7 +2471,7 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     a.g = h->g_gu; a.A = AMat{p.xl, (size_t)L, 0, L};
     a.pieces = (const Piece*)p.pieces; a.npieces = p.npieces;
     a.ntiles = h->g_gu.tiles; a.nquads = (a.ntiles + NTW - 1) / NTW; a.G = G; a.F = F;
-    a.perm = p.perm; a.topk_w = p.w; a.labels = h->labels; a.K = K;
+    a.perm = p.perm; a.topk_w = p.w; a.psc = p.psc; a.labels = h->labels; a.K = K;
     a.out = p.h; a.ostride = F;
     if (int rc = launch_grouped<kGateUp>(a, maxp, E, st)) return rc;
   }
@@ -2430,7 +2482,7 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     a.ts_off = h->ts_off; a.g = h->g_dn; a.A = AMat{p.h, (size_t)F, 0, F};
     a.pieces = (const Piece*)p.pieces; a.npieces = p.npieces;
     a.ntiles = h->g_dn.tiles; a.nquads = (a.ntiles + NTW - 1) / NTW; a.G = G; a.F = F;
-    a.perm = p.perm; a.topk_w = p.w; a.labels = h->labels; a.K = K;
+    a.perm = p.perm; a.topk_w = p.w; a.psc = p.psc; a.labels = h->labels; a.K = K;
     a.out = p.o; a.ostride = L;
     if (int rc = launch_grouped<kDown>(a, maxp, E, st)) return rc;
   }
@@ -2450,7 +2502,7 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     a.W2 = WMat{h->sdn, h->g_sdn, 0, 1};
     a.A2 = AMat{p.hsb, (size_t)2 * Fs, Fs, Fs};
     a.T = T; a.mtiles = mtiles; a.ntiles = h->g_u16.tiles; a.nquads = (a.ntiles + NTW - 1) / NTW;
-    a.out = y; a.ostride = H; a.nvalid = H; a.res = norm ? x : nullptr;
+    a.out = y; a.ostride = H; a.nvalid = H; a.res = norm ? x : nullptr; a.xsc = p.xsc;
     // One block per CU at a time. Every tile is split along k into ns
     // blocks, ns minimising rounds of the chip per split plus a small charge
     // per split for writing and re-reading its partial sums (as many as the
@@ -2494,7 +2546,7 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
 int prefill_debug_latent(lmoe_t* h, int T, float* dst, hipStream_t st) {
   const size_t n = (size_t)T * h->d.n_groups * h->d.latent;
   hipLaunchKernelGGL(k_f16_to_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                     (const _Float16*)h->pw.xl, n, dst);
+                     (const _Float16*)h->pw.xl, n, (size_t)h->d.n_groups * h->d.latent, h->pw.xsc, dst);
   LMOE_HIP(hipGetLastError());
   return 0;
 }

@@ -17,6 +17,10 @@ model page, "Model profile" and architecture tables):
 * ``145b_prefill``: as 145b_decode with T 4096 and a per-expert router bias
   N(0, 1) that skews expert loads.
 * ``145b_stack``: 48 independently seeded 145b_decode layers, T 4.
+* ``mtp_draft``: the MoE of the multi-token-prediction draft layer ("MTP
+  head" row of the architecture tables: 1.26B parameters in 512 experts,
+  i.e. 2,457,600 = 3 x 1280 x 640 per expert): ell 1280, F 640 NVFP4, top-10,
+  8 groups, Q8 D/U, shared 640 bf16, H 2560, T 1 (one drafted token).
 
 Every non-router weight is N(0, 0.02); router weights N(0, 1/sqrt(H));
 activations N(0, 1). Each tensor (and each expert, each group's D and U) has
@@ -62,6 +66,7 @@ WORKLOADS = {
     "145b_prefill": Workload("145b_prefill", 2560, 1792, 512, 10, 8, 640, 640, 8, 4096,
                              router_bias=True),
     "145b_stack": Workload("145b_stack", 2560, 1792, 512, 10, 8, 640, 640, 8, 4, n_layers=48),
+    "mtp_draft": Workload("mtp_draft", 2560, 1280, 512, 10, 8, 640, 640, 8, 1),
 }
 
 # stream identifiers

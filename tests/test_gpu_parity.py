@@ -116,6 +116,20 @@ def test_120b_decode(l120, T):
     check(case, layer, T, "120b_decode")
 
 
+@pytest.fixture(scope="module")
+def lmtp():
+    c = Case(wl.WORKLOADS["mtp_draft"], tokens=4)
+    return c, make_layer(c, 4)
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_mtp_draft_layer(lmtp, T):
+    """The draft layer's MoE (512 experts of 3 x 1280 x 640, Q8 D/U): one
+    drafted token, and the four tokens of a verify window."""
+    case, layer = lmtp
+    check(case, layer, T, "mtp_draft")
+
+
 def test_same_token_repeated_shares_experts():
     """All tokens identical: every routed expert serves T tokens at once."""
     w = wl.WORKLOADS["tiny"]

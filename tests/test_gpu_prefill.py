@@ -381,3 +381,35 @@ def test_145b_prefill_4096():
 
 def test_120b_prefill_q4():
     _sampled("120b_decode", 600, 16)
+
+
+@pytest.mark.parametrize("name", ["tiny", "145b_decode"])
+def test_prefill_activation_range(name):
+    """Prefill rows far from unit scale: x scaled by 1e-3, 1e2, 3e3, 1e-9 and
+    1e4, and a row of elements around 1e-6 with every seventh element near
+    1e5 (fp16 alone would lose the first rows to subnormals and overflow on
+    the last ones). Each token's fp16 activations carry an exact power-of-two
+    scale, so each token meets the bar on its own, and its latent D x too."""
+    w = wl.WORKLOADS[name]
+    T = 16
+    x = wl.x(w, 12, tokens=T)
+    for t, f in ((0, 1e-3), (1, 1e2), (2, 1e-6), (3, 3e3), (4, 1e-9), (5, 1e4),
+                 (8, 1e-3), (9, 1e2), (10, 1e-6), (11, 3e3), (12, 1e-9), (13, 1e4)):
+        x[t] *= np.float32(f)
+    x[2, ::7] *= np.float32(1e11)
+    x[10, ::7] *= np.float32(1e11)
+    c = Case(w, seed=12, x=x)
+    layer = make_layer(c, T)
+    print("case %s prefill activation range T %d" % (name, T), flush=True)
+    got, dbg = run(layer, w, x)
+    check_routing(c, dbg, T)
+    r = oracle.layer_forward(c.d, c.blobs, x, dec=c.dec, intermediates=True)
+    for t in range(T):
+        rel, mx = assert_close(got[t], r["y"][t], "token %d" % t)
+        rel_r, _ = rel_errors(got[t] - r["y_shared"][t], r["y_routed"][t])
+        u = r["used"][t]
+        rel_l, _ = rel_errors(dbg["latent"][t][u], r["xl"][t][u])
+        print("  token %d (max |x| %.3g): y rel L2 %.3g max/rms %.3g; routed part %.3g; latent %.3g" % (
+            t, float(np.max(np.abs(x[t]))), rel, mx, rel_r, rel_l), flush=True)
+        assert rel_r <= ROUTED_BAR, "token %d routed part relative error %.3g" % (t, rel_r)
+        assert rel_l <= LATENT_BAR, "token %d latent relative error %.3g" % (t, rel_l)
