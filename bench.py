@@ -15,6 +15,8 @@ The default line also carries nested objects, each with its own roofline and
 oracle CPU baseline: "decode_t1" (the same layers at T = 1, with the byte
 counts of reading D and U for used groups only and for all groups),
 "decode_120b" (the Edge0-120B-shaped layer, Q4 D/U, latent 1280, T = 5),
+"mtp_draft" (the draft layer's MoE: 512 experts of 3 x 1280 x 640, Q8 D/U,
+T = 1, one drafted token),
 "stack_145b" (48 independently seeded 145B-shaped layers as pre-norm
 residual blocks, T = 4: whole-stack tokens/s and sustained HBM bandwidth) and
 "prefill" (the 145B-shaped layer at T = 4096 with a router bias skewing expert
@@ -604,6 +606,13 @@ def main():
         if cpu:
             r120["cpu_baseline"] = cpu_baseline(w120, args.seed, w120.tokens)
         out["decode_120b"] = r120
+        wm = wl.WORKLOADS["mtp_draft"]
+        rm, lmm = bench_decode(lm, wl, wm, args, torch)
+        close_layers(lmm)
+        del lmm
+        if cpu:
+            rm["cpu_baseline"] = cpu_baseline(wm, args.seed, wm.tokens)
+        out["mtp_draft"] = rm
         ws = wl.WORKLOADS["145b_stack"]
         rs, ls = bench_decode(lm, wl, ws, args, torch, steps=args.stack_steps,
                               warmup=min(args.warmup, 3))

@@ -544,7 +544,6 @@ struct P2 {
 
 struct P3 {
   Dims d;
-  int spr, wps;            // slots per round of a block, waves per slot
   const uint8_t* experts; Geom gdn; size_t stride, gu_bytes, ts_off;
   const uint8_t* labels;
   Workspace ws;
@@ -1039,14 +1038,11 @@ __global__ __launch_bounds__(1024) void k_phase2(P2 a) {
 // Phase 3: routed-expert down, scaled by the routing weight, and the
 // per-group sums s[t][g] = sum over token t's experts in group g, ascending k.
 //
-// One block per (group g, row tile r of ell). The group's slots are
-// contiguous in slot order and their assignments occupy one contiguous run
-// of sorted positions [P0, P1), so the block keeps every weighted expert
-// output of the group for its 64 rows in LDS and adds them per token there:
-// no partials leave the block. A round runs spr slots with wps waves per
-// slot; wave w of a slot takes super-steps w, w + wps, ... of the ffn width
-// into one accumulator, and the slot's wave partials are added in w order
-// (the launch uses wps = 1: one wave walks all of a slot's super-steps).
+// One block per (slot, 64-row tile r of ell), one wave per super-step of the
+// ffn width, so that every block's loads are in flight at once and the
+// blocks spread over the whole chip whatever the group sizes. The weighted
+// outputs go to obuf with coherent stores; the last of group g's slots to
+// finish tile r adds, per token, the group's outputs in ascending k.
 
 constexpr size_t kLdsBytes = 160 * 1024;   // LDS of one CU
 
@@ -1054,94 +1050,72 @@ constexpr size_t kLdsBytes = 160 * 1024;   // LDS of one CU
 template <int NT>
 constexpr int stage_bytes_f16() { return 2 * NT * kXStr * 2; }
 
+// waves of a phase-3 block: one per super-step, fewer if the LDS is short
 template <int T>
-__global__ __launch_bounds__(1024) void k_phase3(P3 a) {
+constexpr int phase3_waves(int nss) {
+  int n = nss < 16 ? nss : 16;
+  while (n > 1 && (size_t)n * (stage_bytes_f16<T>() + red_bytes_per_wave<T>()) > kLdsBytes) --n;
+  return n;
+}
+
+template <int T, int W>
+__global__ __launch_bounds__(64 * W) void k_phase3(P3 a) {
   extern __shared__ __align__(16) char smem[];
+  __shared__ int flag;
   const Dims& d = a.d;
   const int tiles = a.gdn.tiles;                     // ell / 64
-  const int g = blockIdx.x / tiles, r = blockIdx.x % tiles;
-  ci_t gso = ci(a.ws.gslot_off);
-  const int j0 = gso[g], ng = gso[g + 1] - j0;
-  if (ng == 0) return;                               // group unused: phase 4 skips it
+  const int j = blockIdx.x / tiles, r = blockIdx.x % tiles;
+  if (j >= ci(a.ws.n_slots)[0]) return;
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6), nw = blockDim.x >> 6;
-  const int nss = a.gdn.nss, spr = a.spr, wps = a.wps;
-  ci_t sstart = ci(a.ws.slot_start);
-  ci_t scount = ci(a.ws.slot_count);
-  ci_t sexp = ci(a.ws.slot_expert);
   ci_t perm = ci(a.ws.perm);
-  const int P0 = sstart[j0];
-  char* xs = smem + wave * stage_bytes_f16<T>();     // staging, then this wave's partial
-  float* ol = (float*)(smem + nw * stage_bytes_f16<T>());   // [P1 - P0][64]
-  constexpr int LN = 16 * ((T + 3) / 4);             // lanes holding tokens < T
-  const rsrc_t hr = rsrc(a.ws.hbuf, (uint32_t)((size_t)T * d.K * d.F * sizeof(float)));
-  const int u_in = wave / wps, sw = wave % wps;
-  // This wave's tasks, in order: slot u0 + u_in of each round, its
-  // super-steps sw, sw + wps, ... The loads of the next task are issued as
-  // soon as the MFMAs of the current one have consumed its registers, so a
-  // second round does not wait a full load latency.
-  WRegs<kFP4, T> R;
-  auto issue = [&](int u, int ss) {
-    const int j = j0 + u;
-    const int start = sstart[j], cnt = scount[j];
+  const int e = ci(a.ws.slot_expert)[j], start = ci(a.ws.slot_start)[j];
+  const int cnt = ci(a.ws.slot_count)[j];
+  const int g = label_of(a.labels, e);
+  const uint8_t* rec = a.experts + (size_t)e * a.stride;
+  char* xs = smem + wave * stage_bytes_f16<T>();
+  f4* red = (f4*)(smem + nw * stage_bytes_f16<T>());
+  f4 acc[4];
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg) acc[rg] = (f4){0.f, 0.f, 0.f, 0.f};
+  // wave w takes super-steps w, w + nw, ... (nw = all of them unless the
+  // LDS is short)
+  for (int ss = wave; ss < a.gdn.nss; ss += nw) {
     int xoff[T];
 #pragma unroll
     for (int i = 0; i < T; ++i)
       xoff[i] = (int)(((size_t)(start + (i < cnt ? i : 0)) * d.F + ss * kSSCols) * sizeof(float));
     const int ncs = ss_codes(kFP4, a.gdn, ss);
-    const uint8_t* base = a.experts + (size_t)sexp[j] * a.stride + a.gu_bytes;
-    wave_load_b<kFP4, T>(R, rsrc(ss_ptr(base, a.gdn, r, ss), (ncs + scale_slots(kFP4)) * kSlot),
-                         ncs, hr, xoff, cnt, ss_cols(a.gdn, ss), lane);
-  };
-  if (u_in < spr && u_in < ng) issue(u_in, sw);
-  for (int u0 = 0; u0 < ng; u0 += spr) {
-    const int u = u0 + u_in;
-    const bool valid = u_in < spr && u < ng;
-    const int j = j0 + (valid ? u : 0);
-    const int start = sstart[j], cnt = scount[j];
-    f4 acc[4];
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) acc[rg] = (f4){0.f, 0.f, 0.f, 0.f};
-    if (valid) {
-      for (int ss = sw; ss < nss; ss += wps) {
-        wave_compute<kFP4, T>(R, ss_codes(kFP4, a.gdn, ss), cnt, xs, lane, acc);
-        __builtin_amdgcn_sched_barrier(0);   // the next loads reuse these registers
-        if (ss + wps < nss) issue(u, ss + wps);
-        else if (u + spr < ng) issue(u + spr, sw);
-      }
-    }
-    f4* red = (f4*)xs;                               // this wave's staging is free again
-    if (valid && lane < LN) {
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) red[rg * LN + lane] = acc[rg];
-    }
-    __syncthreads();
-    if (valid && sw == 0 && lane < LN) {
-      cf_t ts = cf((const float*)(a.experts + (size_t)sexp[j] * a.stride + a.ts_off));
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        f4 v = acc[rg];
-        for (int k = 1; k < wps; ++k) v += ((const f4*)(smem + (wave + k) * stage_bytes_f16<T>()))[rg * LN + lane];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int i = 4 * (lane >> 4) + q;
-          if (i < cnt) {
-            const float w = a.ws.topk_w[perm[start + i]];
-            ol[(start + i - P0) * 64 + rg * 16 + (lane & 15)] = v[q] * ts[2] * w;
-          }
-        }
-      }
-    }
-    __syncthreads();
+    WRegs<kFP4, T> R;
+    wave_load_b<kFP4, T>(R, rsrc(ss_ptr(rec + a.gu_bytes, a.gdn, r, ss), (ncs + scale_slots(kFP4)) * kSlot),
+                         ncs, rsrc(a.ws.hbuf, (uint32_t)((size_t)T * d.K * d.F * sizeof(float))), xoff, cnt,
+                         ss_cols(a.gdn, ss), lane);
+    wave_compute<kFP4, T>(R, ncs, cnt, xs, lane, acc);
   }
-  // s[t][g][row] for every token (0 where token t has no expert in g)
+  if (block_reduce_mf<T>(acc, red, wave, lane, nw)) {
+    cf_t ts = cf((const float*)(rec + a.ts_off));
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int i = 4 * (lane >> 4) + v;
+        const int row = r * 64 + rg * 16 + (lane & 15);
+        if (i < cnt && row < d.L)
+          st_co(a.ws.obuf + (size_t)(start + i) * d.L + row, acc[rg][v] * ts[2] * a.ws.topk_w[perm[start + i]]);
+      }
+  }
+  ci_t gso = ci(a.ws.gslot_off);
+  if (!arrive_last(a.ws.ctr_g + g * tiles + r, (unsigned)(gso[g + 1] - gso[g]), &flag)) return;
+  // s[t][g][rows of r] for every token (0 where token t has no expert in g)
   ci_t cnt_tab = ci(a.ws.tg_cnt);
   ci_t pos_tab = ci(a.ws.tg_pos);
+  const int row = r * 64 + lane;
+  if (row >= d.L) return;
   for (int t = wave; t < T; t += nw) {
     const int q = t * d.G + g;
     const int c = cnt_tab[q];
     float v = 0.f;
-    for (int i = 0; i < c; ++i) v += ol[(pos_tab[q * d.K + i] - P0) * 64 + lane];
-    a.ws.s[(size_t)q * d.L + r * 64 + lane] = v;
+    for (int i = 0; i < c; ++i) v += ld_co(a.ws.obuf + (size_t)pos_tab[q * d.K + i] * d.L + row);
+    a.ws.s[(size_t)q * d.L + row] = v;
   }
 }
 
@@ -1360,27 +1334,17 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st, i
   P3 p3{};
   p3.d = d; p3.experts = h->experts; p3.gdn = h->g_dn; p3.stride = h->expert_stride;
   p3.gu_bytes = h->g_gu.bytes(); p3.ts_off = h->ts_off; p3.labels = h->labels; p3.ws = ws;
-  // one wave per slot, walking the slot's super-steps with the next one's
-  // loads in flight: 16 slots per round, so a group that drew up to 16
-  // distinct experts takes one round (three waves per slot, one per
-  // super-step, took two rounds for groups above five: 15.6 against 14.8 us
-  // at the 145B shape); fewer slots when the LDS is short
-  const int nss3 = h->g_dn.nss;
-  const size_t ol_bytes = (size_t)n * 64 * sizeof(float);
-  auto lds3 = [&](int spr_, int wps_) { return (size_t)spr_ * wps_ * stage_bytes_f16<T>() + ol_bytes; };
-  int spr = 16, wps = 1;
-  while (spr > 1 && lds3(spr, wps) > kLdsBytes) --spr;
-  while (wps > 1 && lds3(spr, wps) > kLdsBytes) --wps;
-  if (lds3(spr, wps) > kLdsBytes) {
-    set_error("decode phase 3: T * top_k too large for the LDS");
-    return LMOE_EUNSUPPORTED;
+  // Blocks of at most eight waves are compiled for 512 threads: they then
+  // fit in 94 registers, five waves per SIMD, and every item of the 145B
+  // shape is resident at once (at four waves per SIMD the items past 1024
+  // waited a whole round)
+  const int nw3 = phase3_waves<T>(h->g_dn.nss);
+  const size_t sm3 = (size_t)nw3 * (stage_bytes_f16<T>() + red_bytes_per_wave<T>());
+  const dim3 grid3((unsigned)(maxslots * h->g_dn.tiles)), block3(nw3 * 64);
+  if (only == 0 || only == 3) {
+    if (nw3 <= 8) hipLaunchKernelGGL((k_phase3<T, 8>), grid3, block3, sm3, st, p3);
+    else hipLaunchKernelGGL((k_phase3<T, 16>), grid3, block3, sm3, st, p3);
   }
-  p3.spr = spr;
-  p3.wps = wps;
-  const int nw3 = spr * wps;
-  if (only == 0 || only == 3)
-    hipLaunchKernelGGL(k_phase3<T>, dim3(d.G * h->g_dn.tiles), dim3(nw3 * 64),
-                     (size_t)nw3 * stage_bytes_f16<T>() + ol_bytes, st, p3);
   LMOE_HIP(hipGetLastError());
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[3], st));
 
@@ -1429,7 +1393,8 @@ size_t lds_need(const lmoe_dims& d) {
   m = std::max(m, (size_t)nssH * T * 64 * sizeof(double));
   m = std::max(m, routing_lds_bytes(T, d.n_experts, Epad, n, nssH));
   m = std::max(m, (size_t)nssL * (stage_bytes<T>() + 2 * red_bytes_per_wave<T>()));
-  m = std::max(m, (size_t)stage_bytes_f16<T>() + (size_t)n * 64 * sizeof(float));   // phase 3, one slot
+  const int nssF = (d.expert_ffn + kSSCols - 1) / kSSCols;
+  m = std::max(m, (size_t)phase3_waves<T>(nssF) * (stage_bytes_f16<T>() + red_bytes_per_wave<T>()));
   const int hu = (nssL + 1) / 2, nhs = (d.shared_ffn + 127) / 128, nsb = (nhs + hu - 1) / hu;
   m = std::max(m, (size_t)hu * (stage_bytes<T>() + red_bytes_per_wave<T>()));
   m = std::max(m, (size_t)(2 * d.n_groups + nsb) * T * 64 * sizeof(float));
