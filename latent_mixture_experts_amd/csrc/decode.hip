@@ -1114,7 +1114,15 @@ __global__ __launch_bounds__(64 * W) void k_phase3(P3 a) {
     const int q = t * d.G + g;
     const int c = cnt_tab[q];
     float v = 0.f;
-    for (int i = 0; i < c; ++i) v += ld_co(a.ws.obuf + (size_t)pos_tab[q * d.K + i] * d.L + row);
+    for (int i0 = 0; i0 < c; i0 += 4) {               // four loads in flight, added in k order
+      float u[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        u[k] = i0 + k < c ? ld_co(a.ws.obuf + (size_t)pos_tab[q * d.K + i0 + k] * d.L + row) : 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (i0 + k < c) v += u[k];
+    }
     a.ws.s[(size_t)q * d.L + row] = v;
   }
 }
@@ -1198,22 +1206,26 @@ __global__ __launch_bounds__(64 * W) void k_phase4(P4 a) {
   }
   const int np = 2 * d.G + a.nsb;
   if (!arrive_last(a.ws.ctr_y + r, (unsigned)np, &flag)) return;
-  // Ordered sum of the partials: wave w fetches parts w, w + nw, ... (all
-  // loads in flight together), wave 0 adds them in part order.
+  // Ordered sum of the partials: wave w fetches parts w, w + nw, ..., up to
+  // eight per pass with all their loads in flight together (one pass at the
+  // 145B shape), then wave 0 adds them in part order.
   const int row = r * 64 + lane;
   float* stage = (float*)smem;                       // [np][T][64]
-  for (int p0 = wave; p0 < np; p0 += 2 * nw) {
-    const int p1 = min(p0 + nw, np - 1);
-    float v0[T], v1[T];
+  constexpr int PW = 8;
+  for (int base = 0; base < np; base += PW * nw) {
+    float v[PW][T];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      v0[t] = ld_co(a.ws.ypart + ((size_t)p0 * T + t) * d.H + row);
-      v1[t] = ld_co(a.ws.ypart + ((size_t)p1 * T + t) * d.H + row);
+    for (int k = 0; k < PW; ++k) {
+      const int p = base + wave + k * nw;
+#pragma unroll
+      for (int t = 0; t < T; ++t) v[k][t] = p < np ? ld_co(a.ws.ypart + ((size_t)p * T + t) * d.H + row) : 0.f;
     }
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      stage[(p0 * T + t) * 64 + lane] = v0[t];
-      if (p0 + nw < np) stage[(p1 * T + t) * 64 + lane] = v1[t];
+    for (int k = 0; k < PW; ++k) {
+      const int p = base + wave + k * nw;
+      if (p < np)
+#pragma unroll
+        for (int t = 0; t < T; ++t) stage[(p * T + t) * 64 + lane] = v[k][t];
     }
   }
   __syncthreads();
@@ -1364,9 +1376,9 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st, i
   sm4 = sm4 > sm4r ? sm4 : sm4r;
   const int grid4 = (2 * d.G + p4.nsb) * h->g_u.tiles;
   if (only == 0 || only == 4) {
-    if (nw4 <= 4)
-      hipLaunchKernelGGL((k_phase4<T, DU, 4>), dim3(grid4), dim3(nw4 * 64), sm4, st, p4);
-    else if (nw4 <= 8)
+    // blocks of up to eight waves compiled for 512 threads: 4-wave bounds
+    // let the compiler spend AGPRs and drop to three waves per SIMD
+    if (nw4 <= 8)
       hipLaunchKernelGGL((k_phase4<T, DU, 8>), dim3(grid4), dim3(nw4 * 64), sm4, st, p4);
     else
       hipLaunchKernelGGL((k_phase4<T, DU, 16>), dim3(grid4), dim3(nw4 * 64), sm4, st, p4);
