@@ -16,6 +16,8 @@ What it follows (cited by page title, then section / equation / table):
   base, byte for byte" (bf16 router, 2,621,440 B per layer).
 * README = the Edge0 README ("Architecture": 10 of 512 experts plus one
   shared expert).
+* PLE = TEARDOWN, section "The 51.2B the GPU never holds" (the n-gram
+  embedding gather, module ``ple``; its hash is a reading, see there).
 
 Where the pages leave a step open, the reading taken is stated at the
 function that takes it. Numeric parity of the layer output has no printed
