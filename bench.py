@@ -17,7 +17,8 @@ counts of reading D and U for used groups only and for all groups),
 "decode_120b" (the Edge0-120B-shaped layer, Q4 D/U, latent 1280, T = 5),
 "mtp_draft" (the draft layer's MoE: 512 experts of 3 x 1280 x 640, Q8 D/U,
 T = 1, one drafted token),
-"stack_145b" (48 independently seeded 145B-shaped layers as pre-norm
+"ple_gather" (the n-gram embedding gather on the full 51.2 GB table at
+T = 4096 and T = 4), "stack_145b" (48 independently seeded 145B-shaped layers as pre-norm
 residual blocks, T = 4: whole-stack tokens/s and sustained HBM bandwidth) and
 "prefill" (the 145B-shaped layer at T = 4096 with a router bias skewing expert
 loads, on the prefill path, with its per-kernel MFMA roofline).
@@ -172,6 +173,80 @@ def prefill_flops(w, idx, labels):
     executed = [4.0 * T * E * H, 0.0, 2.0 * T * G * L * H, 4.0 * T * 2 * Fs * H, None, None, 0.0,
                 2.0 * T * G * H * L + 4.0 * T * H * Fs]
     return fl, executed, pairs
+
+
+PLE_ROW_BYTES = 160
+
+
+def ple_head_rows():
+    """Rows per hash head of the n-gram table: 20,000,003 for the first (as
+    printed) and the rest of the 320,001,536 rows split evenly, the first
+    three of the others taking one row more."""
+    total, first, n = 320001536, 20000003, 15
+    base, extra = divmod(total - first, n)
+    return [first] + [base + (1 if h <= extra else 0) for h in range(1, 16)]
+
+
+def bench_ple(lm, args, torch, cpu):
+    """The PLE n-gram gather on the full table (51.2 GB of E4M3 rows, drawn
+    on the device) at T = 4096 (a prefill batch) and T = 4 (a verify window).
+    Each step gathers one of 8 pre-drawn token batches; HIP events on the
+    stream the kernel runs on time the steps."""
+    dev = "cuda"
+    sizes = ple_head_rows()
+    n = sum(sizes)
+    table = torch.empty(n, PLE_ROW_BYTES, dtype=torch.uint8, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed * 7919 + 11)
+    for r0 in range(0, n, 1 << 22):
+        r1 = min(n, r0 + (1 << 22))
+        table[r0:r1] = torch.randint(0, 256, (r1 - r0, PLE_ROW_BYTES), generator=g, device=dev,
+                                     dtype=torch.uint8)
+    res = {"table_bytes": n * PLE_ROW_BYTES, "head_rows": sizes}
+    per_tok = 16 * PLE_ROW_BYTES * 3           # E4M3 rows read, bf16 rows written
+    for T, steps in ((4096, 200), (4, 400)):
+        toks = [torch.randint(-1, 248000, (T + 2,), generator=g, device=dev, dtype=torch.int32)
+                for _ in range(8)]
+        out = torch.empty(T, 16, PLE_ROW_BYTES, dtype=torch.int16, device=dev)
+        for i in range(20):
+            lm.ple_gather(toks[i % 8], table, sizes, out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            lm.ple_gather(toks[i % 8], table, sizes, out)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        algo = T * (per_tok + 4) + 8
+        gbs = algo / (us * 1e-6) / 1e9
+        res["t%d" % T] = {
+            "tokens": T, "us_per_step": us, "value": T / (us * 1e-6), "unit": "tokens/s",
+            "steps": steps, "algorithmic_bytes": algo,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "k_ple",
+                         "kernel_us": us, "kernel_algorithmic_bytes": algo},
+        }
+        log("ple gather T=%d: %.2f us/step, %.0f GB/s algorithmic" % (T, us, gbs))
+    del table
+    torch.cuda.empty_cache()
+    if cpu:
+        import oracle.ple as ople
+        rng = np.random.default_rng(args.seed)
+        small = [100003] * 16
+        tab = rng.integers(0, 256, (sum(small), PLE_ROW_BYTES), dtype=np.uint8)
+        T = 2048
+        toks = rng.integers(-1, 248000, T + 2)
+        t0 = time.perf_counter()
+        ople.ple_gather(toks, tab, small)
+        dt = time.perf_counter() - t0
+        cores = host_cores()
+        res["cpu_baseline"] = {
+            "value": T / dt, "unit": "tokens/s", "cores": 1, "cpu_count": cores["cpu_count"],
+            "affinity": cores["affinity"], "kind": "oracle",
+            "sample": "the oracle's hash and gather of %d tokens over a table of 16 x 100,003 rows "
+                      "(Python integer hashing, one core); %.2f s" % (T, dt)}
+    return res
 
 
 def bench_prefill(lm, wl, w, args, torch):
@@ -621,6 +696,8 @@ def main():
         if cpu:
             rs["cpu_baseline"] = cpu_baseline(ws, args.seed, ws.tokens, layers=ws.n_layers)
         out["stack_145b"] = rs
+    if not stack and not args.no_extra:
+        out["ple_gather"] = bench_ple(lm, args, torch, cpu)
     if not stack and not args.no_extra and not args.no_prefill:
         pre = bench_prefill(lm, wl, wl.WORKLOADS[args.prefill_workload], args, torch)
         if cpu:

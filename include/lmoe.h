@@ -199,6 +199,30 @@ const char* lmoe_last_error(void);
 size_t lmoe_expert_record_bytes(int32_t latent, int32_t expert_ffn);
 size_t lmoe_du_matrix_bytes(int32_t rows, int32_t cols, int32_t du_bits);
 
+/* ---- PLE n-gram embedding gather --------------------------------------------
+ * "Edge0-145B: a Qwen MoE with its experts squeezed, and a 51B table left on
+ * the SSD", section "The 51.2B the GPU never holds": 16 hash heads, heads
+ * 0..7 over each token's 2-gram (previous token, token) and heads 8..15 over
+ * its 3-gram, each naming one row of row_bytes E4M3 (OCP E4M3FN) values in
+ * one table (160 bytes a row, 2,560 bytes a token at the Edge0 shapes).
+ * The hash is this library's reading (the pages do not give it): head h's
+ * row is mix64(key) mod head_rows[h], key = sum over the n-gram's ids, oldest
+ * first, of (id + 1) * K[h][j] mod 2^64, where mix64 is the SplitMix64
+ * output function and K[h][j] its output number 3h + j + 1 from seed 0;
+ * head h's rows follow those of heads 0..h-1 in the table.
+ *   tokens     DEVICE int32 [T + 2]: the two ids before the batch (-1 where
+ *              the sequence has not started), then the T ids of the batch
+ *   table      DEVICE bytes [sum of head_rows][row_bytes]
+ *   head_rows  HOST int64 [16], each >= 1
+ *   row_bytes  multiple of 16 in [16, 1024]
+ *   out        DEVICE bf16 bit patterns [T][16][row_bytes]: the decoded
+ *              values (exact; NaN codes give NaN)
+ * Asynchronous on hip_stream; no handle, the calling thread's device.
+ * EINVAL for a bad argument (T == 0 is a no-op). Ids are hashed as given. */
+int lmoe_ple_gather(const int32_t* tokens, int32_t T, const uint8_t* table,
+                    const int64_t* head_rows, int32_t row_bytes, uint16_t* out,
+                    void* hip_stream);
+
 /* ---- Device-side packing of fp32 masters into the formats above ----------
  * For callers holding unquantized weights on the GPU. All pointers are
  * DEVICE memory; asynchronous on `hip_stream`. Rounding is to nearest, ties

@@ -76,6 +76,7 @@ def _load():
         "lmoe_pack_bf16": (ctypes.c_int, [vp, sz, vp, vp]),
         "lmoe_pack_blocks": (ctypes.c_int, [vp, i32, i32, i32, vp, vp]),
         "lmoe_pack_expert_records": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp, vp]),
+        "lmoe_ple_gather": (ctypes.c_int, [vp, i32, vp, vp, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -225,3 +226,14 @@ def pack_expert_records(gate, up, down, dst, stream=None):
     _check(_lib.lmoe_pack_expert_records(_ptr(gate), _ptr(up), _ptr(down), n, ell, f, _ptr(dst),
                                          _stream(stream)), "lmoe_pack_expert_records")
     return dst
+
+
+def ple_gather(tokens, table, head_rows, out, row_bytes=160, stream=None):
+    """lmoe_ple_gather: tokens int32 [T + 2] (the two ids before the batch
+    first), table uint8 [rows][row_bytes], head_rows 16 ints, out [T][16][row_bytes]
+    in a 2-byte dtype (bf16 bit patterns), all device tensors but head_rows."""
+    T = tokens.numel() - 2
+    hr = (ctypes.c_int64 * 16)(*[int(v) for v in head_rows])
+    _check(_lib.lmoe_ple_gather(_ptr(tokens), T, _ptr(table), hr, row_bytes, _ptr(out), _stream(stream)),
+           "lmoe_ple_gather")
+    return out

@@ -77,3 +77,23 @@ def test_null_arguments(lib):
     assert lib.lmoe_forward(None, None, 1, None, None, None) == -1
     assert lib.lmoe_load_weights(None, None, None) == -1
     lib.lmoe_destroy(None)
+
+
+def test_ple_gather_argument_checks_on_host(lib):
+    """lmoe_ple_gather validates on the host before touching the device:
+    bad row widths, negative T, a head without rows and NULL pointers are
+    EINVAL; T == 0 is a no-op."""
+    from latent_mixture_experts_amd import lmoe
+    rows = (ctypes.c_int64 * 16)(*([5] * 16))
+    dummy = ctypes.c_void_p(16)                     # never dereferenced on these paths
+    f = lib.lmoe_ple_gather
+    assert f(dummy, 0, dummy, rows, 160, dummy, None) == lmoe.OK
+    assert f(None, 0, None, rows, 160, None, None) == lmoe.OK
+    assert f(dummy, -1, dummy, rows, 160, dummy, None) == lmoe.EINVAL
+    assert f(dummy, 4, dummy, rows, 100, dummy, None) == lmoe.EINVAL
+    assert f(dummy, 4, dummy, rows, 0, dummy, None) == lmoe.EINVAL
+    assert f(dummy, 4, dummy, rows, 2048, dummy, None) == lmoe.EINVAL
+    assert f(None, 4, dummy, rows, 160, dummy, None) == lmoe.EINVAL
+    assert f(dummy, 4, dummy, None, 160, dummy, None) == lmoe.EINVAL
+    bad = (ctypes.c_int64 * 16)(*([5] * 15 + [0]))
+    assert f(dummy, 4, dummy, bad, 160, dummy, None) == lmoe.EINVAL
