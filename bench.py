@@ -389,7 +389,7 @@ def host_cores():
     return {"cpu_count": os.cpu_count(), "affinity": aff, "blas_threads": int(blas)}
 
 
-def cpu_baseline(w, seed, tokens, layers=1):
+def cpu_baseline(w, seed, tokens, layers=1, min_seconds=0.0):
     """The fp64 oracle timed on the host on a bounded sample: one forward of
     `tokens` tokens of layer 0 (including its on-the-fly dequantization of
     D, U and the experts it touches; excluding weight drawing and packing).
@@ -409,11 +409,16 @@ def cpu_baseline(w, seed, tokens, layers=1):
     m["expert_ids"] = sorted(set(idx.ravel().tolist()))
     blobs = oracle.pack_layer(d, m)
     t0 = time.perf_counter()
-    oracle.layer_forward(d, blobs, x)
-    dt = time.perf_counter() - t0
-    what = ("one fp64 NumPy forward of %d tokens of the %s layer (seed %d), including "
-            "dequantization of D, U and the %d experts it touches; %.1f s" % (
-                tokens, w.name, seed, len(m["expert_ids"]), dt))
+    reps = 0
+    while True:
+        oracle.layer_forward(d, blobs, x)
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    what = ("%d fp64 NumPy forward%s of %d tokens of the %s layer (seed %d), each including "
+            "dequantization of D, U and the %d experts it touches; %.1f s each" % (
+                reps, "s" if reps > 1 else "", tokens, w.name, seed, len(m["expert_ids"]), dt))
     if layers > 1:
         what = ("layer 0 of the %d-layer stack: " % layers) + what + \
                "; the stack's rate is this layer's divided by %d" % layers
@@ -665,7 +670,7 @@ def main():
         "decode": res,
     }
     if cpu:
-        out["cpu_baseline"] = cpu_baseline(w, args.seed, w.tokens, layers=w.n_layers)
+        out["cpu_baseline"] = cpu_baseline(w, args.seed, w.tokens, layers=w.n_layers, min_seconds=10.0)
     if not stack and not args.no_extra:
         r1, _ = bench_decode(lm, wl, w, args, torch, T=1, layers=layers)
         if cpu:
