@@ -106,6 +106,7 @@ size_t decode_ws_layout(const lmoe_t* h, int T, char* base, Workspace* out) {
   take(w.slot_expert, sizeof(int) * n);
   take(w.slot_start, sizeof(int) * n);
   take(w.slot_count, sizeof(int) * n);
+  take(w.slot_xrow, sizeof(int) * n * kMaxDecodeT);
   take(w.n_slots, sizeof(int));
   take(w.gslot_off, sizeof(int) * (G + 1));
   take(w.group_off, sizeof(int) * (G + 1));

@@ -800,6 +800,9 @@ __device__ void routing(const P1& a, char* smem) {
       ws.slot_expert[s0] = aexp[sperm[j]];
       ws.slot_start[s0] = j;
       ws.slot_count[s0] = end - j;
+      // the xl rows (t * G + g) of the slot's tokens, padded with the first
+      for (int i = 0; i < kMaxDecodeT; ++i)
+        ws.slot_xrow[s0 * kMaxDecodeT + i] = (sperm[j + (j + i < end ? i : 0)] / d.K) * d.G + slab[j];
     }
     const int lo = j == 0 ? 0 : slab[j - 1] + 1;
     for (int g = lo; g <= slab[j]; ++g) {
@@ -945,7 +948,6 @@ __global__ __launch_bounds__(1024) void k_phase2(P2 a) {
   ci_t ns = ci(a.ws.n_slots);
   const int nvalid = ns[0] * tiles;            // items of real slots come first
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6), nw = blockDim.x >> 6;
-  ci_t perm = ci(a.ws.perm);
   char* xs = smem + wave * stage_bytes<T>();
   f4* red0 = (f4*)(smem + nw * stage_bytes<T>());
   const int red_len = nw * red_bytes_per_wave<T>() / (int)sizeof(f4);
@@ -954,17 +956,16 @@ __global__ __launch_bounds__(1024) void k_phase2(P2 a) {
   // activations: xl [T][G][L] fp32; item (slot j, tile r)
   const rsrc_t xr = rsrc(a.ws.xl, (uint32_t)((size_t)T * d.G * d.L * sizeof(float)));
   const int wbytes = (ss_codes(kFP4, a.ggu, wave) + scale_slots(kFP4)) * kSlot;
+  // Item (slot j, tile r): every table entry it needs comes in one round of
+  // scalar loads (expert, count, the xl rows of its tokens written by the
+  // routing), so its weight and activation loads start one load latency in.
   auto issue = [&](int item, WRegs<kFP4, T>& R) {
     const int j = item / tiles;
-    const int e = ci(a.ws.slot_expert)[j], start = ci(a.ws.slot_start)[j];
-    const int cnt = ci(a.ws.slot_count)[j];
-    const int g = label_of(a.labels, e);
+    const int e = ci(a.ws.slot_expert)[j], cnt = ci(a.ws.slot_count)[j];
+    ci_t xrow = ci(a.ws.slot_xrow + j * kMaxDecodeT);
     int xoff[T];
 #pragma unroll
-    for (int i = 0; i < T; ++i) {
-      const int t = i < cnt ? perm[start + i] / d.K : 0;
-      xoff[i] = (int)(((t * d.G + g) * d.L + wave * kSSCols) * sizeof(float));
-    }
+    for (int i = 0; i < T; ++i) xoff[i] = (int)((xrow[i] * d.L + wave * kSSCols) * sizeof(float));
     const uint8_t* base = a.experts + (size_t)e * a.stride;
     wave_load_b<kFP4, T>(R, rsrc(ss_ptr(base, a.ggu, item % tiles, wave), wbytes),
                          ss_codes(kFP4, a.ggu, wave), xr, xoff, cnt, ss_cols(a.ggu, wave), lane);
@@ -1065,11 +1066,13 @@ __global__ __launch_bounds__(64 * W) void k_phase3(P3 a) {
   const Dims& d = a.d;
   const int tiles = a.gdn.tiles;                     // ell / 64
   const int j = blockIdx.x / tiles, r = blockIdx.x % tiles;
+  // the slot's entries are read with the slot count (j < T * K: in bounds,
+  // stale past the count), so the loads below wait one round, not two
+  const int e = ci(a.ws.slot_expert)[j], start = ci(a.ws.slot_start)[j];
+  const int cnt = ci(a.ws.slot_count)[j];
   if (j >= ci(a.ws.n_slots)[0]) return;
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6), nw = blockDim.x >> 6;
   ci_t perm = ci(a.ws.perm);
-  const int e = ci(a.ws.slot_expert)[j], start = ci(a.ws.slot_start)[j];
-  const int cnt = ci(a.ws.slot_count)[j];
   const int g = label_of(a.labels, e);
   const uint8_t* rec = a.experts + (size_t)e * a.stride;
   char* xs = smem + wave * stage_bytes_f16<T>();

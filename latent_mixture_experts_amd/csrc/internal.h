@@ -110,6 +110,7 @@ struct Workspace {
   int* slot_expert = nullptr;    // [T*K] distinct experts in (label, expert) order
   int* slot_start = nullptr;     // [T*K]
   int* slot_count = nullptr;     // [T*K]
+  int* slot_xrow = nullptr;      // [T*K][8] xl rows t * G + g of each slot's tokens (padded)
   int* n_slots = nullptr;        // [1]
   int* gslot_off = nullptr;      // [G+1] first slot of each group
   int* group_off = nullptr;      // [G+1]
