@@ -16,6 +16,9 @@ What it follows (cited by page title, then section / equation / table):
   base, byte for byte" (bf16 router, 2,621,440 B per layer).
 * README = the Edge0 README ("Architecture": 10 of 512 experts plus one
   shared expert).
+* Q3_K builds = TEARDOWN "What is 4-bit" (Q3_K gate/up, IQ4_NL down, the
+  record sizes), module ``kquants`` (block layouts restated from GGML's
+  published definitions; the quantizer is ours).
 * PLE = TEARDOWN, section "The 51.2B the GPU never holds" (the n-gram
   embedding gather, module ``ple``; its hash is a reading, see there).
 

@@ -36,6 +36,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from . import formats as fm
+from . import kquants as kq
 
 
 @dataclass(frozen=True)
@@ -48,10 +49,23 @@ class LayerDims:
     expert_ffn: int   # F
     shared_ffn: int   # F_s
     du_bits: int      # 8 (Q8) or 4 (Q4)
+    expert_format: int = 0   # 0 NVFP4; 1 Q3_K gate/up + IQ4_NL down (oracle/kquants.py)
 
     @property
     def record_bytes(self):
+        if self.expert_format == 1:
+            return kq.q3k_record_bytes(self.latent, self.expert_ffn)
         return fm.expert_record_bytes(self.latent, self.expert_ffn)
+
+    def pack_record(self, gate, up, down):
+        if self.expert_format == 1:
+            return kq.pack_q3k_record(gate, up, down)
+        return fm.pack_expert_record(gate, up, down)
+
+    def unpack_record(self, rec):
+        if self.expert_format == 1:
+            return kq.unpack_q3k_record(rec, self.latent, self.expert_ffn)
+        return fm.unpack_expert_record(rec, self.latent, self.expert_ffn)
 
 
 # ---------------------------------------------------------------------------
@@ -78,7 +92,7 @@ def pack_layer(dims, m):
     ids = range(d.n_experts) if ids is None else ids
     for e in ids:
         g_, u_, w_ = m["experts"](e)
-        experts[e] = fm.pack_expert_record(g_, u_, w_)
+        experts[e] = d.pack_record(g_, u_, w_)
     out["experts"] = experts
     out["shared"] = tuple(fm.f32_to_bf16_bits(a) for a in m["shared"])
     return out
@@ -203,7 +217,7 @@ def layer_forward(dims, blobs, x, dec=None, intermediates=False):
         for k in range(d.top_k):
             e = int(idx[t, k])
             if e not in cache:
-                cache[e] = fm.unpack_expert_record(blobs["experts"][e], d.latent, d.expert_ffn)
+                cache[e] = d.unpack_record(blobs["experts"][e])
             wg, wu, wd = cache[e]
             z = xl[t, labels[e]]
             a = t * d.top_k + k

@@ -17,6 +17,7 @@ import torch
 import oracle
 from oracle import formats as fm
 from oracle import layer as ol
+from oracle import kquants as kq
 from oracle.layer import LayerDims, layer_forward, pack_layer, decode_layer
 
 # Tiny, deliberately non-square shapes: H != ell != F != Fs, K < G < E.
@@ -84,8 +85,8 @@ def _brute_layer(d, blobs, x):
         y = [0.0] * d.hidden
         for wk, e in zip(w, top):
             g = labels[e]
-            gate, up, down = (a.tolist() for a in fm.unpack_expert_record(blobs["experts"][e], d.latent,
-                                                                          d.expert_ffn))
+            unpack = kq.unpack_q3k_record if d.expert_format == 1 else fm.unpack_expert_record
+            gate, up, down = (a.tolist() for a in unpack(blobs["experts"][e], d.latent, d.expert_ffn))
             xl = _matvec(D[g], xt)
             hid = [_silu(a) * b for a, b in zip(_matvec(gate, xl), _matvec(up, xl))]
             out = _matvec(U[g], _matvec(down, hid))
@@ -104,6 +105,20 @@ def test_layer_matches_brute_force(bits, bias):
         m["router_bias"] = np.random.default_rng(3).standard_normal(d.n_experts).astype(np.float32)
     blobs = pack_layer(d, m)
     x = _x(d, 3)
+    got = layer_forward(d, blobs, x, intermediates=True)
+    want, idx = _brute_layer(d, blobs, x)
+    assert np.array_equal(got["idx"], idx)
+    assert np.max(np.abs(got["y"] - want)) <= 1e-12 * np.max(np.abs(want))
+
+
+def test_q3k_layer_matches_brute_force():
+    """The layer with Q3_K gate/up and IQ4_NL down expert records (latent
+    256, one Q3_K super-block per row) against the brute force."""
+    d = LayerDims(hidden=96, latent=256, n_experts=5, top_k=2, n_groups=2, expert_ffn=32,
+                  shared_ffn=48, du_bits=8, expert_format=1)
+    blobs = pack_layer(d, _masters(d, seed=5))
+    assert blobs["experts"].shape == (5, kq.q3k_record_bytes(256, 32))
+    x = _x(d, 2)
     got = layer_forward(d, blobs, x, intermediates=True)
     want, idx = _brute_layer(d, blobs, x)
     assert np.array_equal(got["idx"], idx)
