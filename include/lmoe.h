@@ -72,6 +72,19 @@ extern "C" {
 #define LMOE_ESTATE       -4   /* forward before load_weights */
 #define LMOE_EUNSUPPORTED -5   /* dimensions the kernels do not cover */
 
+/* Expert record formats ("Edge0 145B and Edge0 120B", "Model profile" row
+ * "Expert formats"; teardown "What is 4-bit"):
+ *   LMOE_EXPERTS_NVFP4  the NVFP4 record described below
+ *   LMOE_EXPERTS_Q3K    Q3_K gate and up, IQ4_NL down: gate blocks [F][latent/256]
+ *                       then up blocks (GGML Q3_K, 110 bytes a 256-weight block:
+ *                       high-bit mask, low bits, 12 bytes of 6-bit sub-block scales,
+ *                       fp16 d), then down blocks [latent][F/32] (GGML IQ4_NL, 18
+ *                       bytes a 32-weight block: fp16 d, 16 bytes of table
+ *                       indices); 1,630,720 bytes at latent 1792, F 640. Decode
+ *                       path only (max_tokens <= 8), latent % 256 == 0. */
+#define LMOE_EXPERTS_NVFP4 0
+#define LMOE_EXPERTS_Q3K   1
+
 /* Layer dimensions, validated by lmoe_create.
  * Constraints: hidden % 256 == 0, latent % 64 == 0, expert_ffn % 32 == 0,
  * shared_ffn % 32 == 0, hidden <= 4096, latent <= 4096, expert_ffn <= 4096,
@@ -88,6 +101,7 @@ typedef struct lmoe_dims {
   int32_t du_bits;         /* 8 = Q8, 4 = Q4 ("D/U formats", LAYER) */
   int32_t max_tokens;      /* largest T a forward may take; sizes the workspace */
   int32_t has_router_bias; /* 1: lmoe_weights.router_bias is read */
+  int32_t expert_format;   /* LMOE_EXPERTS_NVFP4 (0) or LMOE_EXPERTS_Q3K */
 } lmoe_dims;
 
 /* Packed weights (layouts above). Pointers may be host or device memory;
@@ -197,6 +211,8 @@ const char* lmoe_last_error(void);
 
 /* Bytes of one packed NVFP4 expert record and of one packed D_g / U_g. */
 size_t lmoe_expert_record_bytes(int32_t latent, int32_t expert_ffn);
+/* Bytes of one record in expert format `fmt` (0 for an unknown format). */
+size_t lmoe_expert_record_bytes_fmt(int32_t latent, int32_t expert_ffn, int32_t fmt);
 size_t lmoe_du_matrix_bytes(int32_t rows, int32_t cols, int32_t du_bits);
 
 /* ---- PLE n-gram embedding gather --------------------------------------------

@@ -37,6 +37,12 @@ int check_dims(const lmoe_dims& d) {
   if (d.du_bits != 8 && d.du_bits != 4) return bad("du_bits must be 8 or 4");
   if (d.top_k > d.n_experts) return bad("top_k exceeds n_experts");
   if (d.has_router_bias != 0 && d.has_router_bias != 1) return bad("has_router_bias must be 0 or 1");
+  if (d.expert_format != LMOE_EXPERTS_NVFP4 && d.expert_format != LMOE_EXPERTS_Q3K)
+    return bad("expert_format must be LMOE_EXPERTS_NVFP4 or LMOE_EXPERTS_Q3K");
+  if (d.expert_format == LMOE_EXPERTS_Q3K && d.latent % 256)
+    return unsup("Q3_K experts need latent % 256 == 0 (one super-block per 256 columns)");
+  if (d.expert_format == LMOE_EXPERTS_Q3K && d.max_tokens > kMaxDecodeT)
+    return unsup("Q3_K experts run on the decode path only (max_tokens <= 8)");
   if (d.hidden % 256) return unsup("hidden must be a multiple of 256");
   if (d.latent % 64) return unsup("latent must be a multiple of 64");
   if (d.expert_ffn % 32 || d.shared_ffn % 32) return unsup("expert_ffn and shared_ffn must be multiples of 32");
@@ -138,8 +144,9 @@ int create_impl(lmoe_t* h) {
   h->g_router = make_geom(kBF16R, E, H);
   h->g_d = make_geom(du, L, H);
   h->g_u = make_geom(du, H, L);
-  h->g_gu = make_geom(kFP4, 2 * F, L);   // tiles of 32 gate + 32 up rows
-  h->g_dn = make_geom(kFP4, L, F);
+  const bool q3k = d.expert_format == LMOE_EXPERTS_Q3K;
+  h->g_gu = make_geom(q3k ? kQ3K : kFP4, 2 * F, L);   // tiles of 32 gate + 32 up rows
+  h->g_dn = make_geom(q3k ? kIQ4 : kFP4, L, F);
   h->g_sgu = make_geom(kBF16, 2 * Fs, H);
   h->g_sdn = make_geom(kBF16, H, Fs);
   h->ts_off = h->g_gu.bytes() + h->g_dn.bytes();
@@ -508,6 +515,12 @@ const char* lmoe_strerror(int code) {
 }
 
 const char* lmoe_last_error(void) { return g_last_error.c_str(); }
+
+size_t lmoe_expert_record_bytes_fmt(int32_t latent, int32_t expert_ffn, int32_t fmt) {
+  if (fmt == LMOE_EXPERTS_NVFP4) return lmoe_expert_record_bytes(latent, expert_ffn);
+  if (fmt != LMOE_EXPERTS_Q3K || latent <= 0 || expert_ffn <= 0 || latent % 256 || expert_ffn % 32) return 0;
+  return 2 * (size_t)expert_ffn * (latent / 256) * 110 + (size_t)latent * (expert_ffn / 32) * 18;
+}
 
 size_t lmoe_expert_record_bytes(int32_t latent, int32_t expert_ffn) {
   size_t n = (size_t)latent * expert_ffn;

@@ -242,6 +242,59 @@ __device__ __forceinline__ half8 dec_fp4(uint32_t w, _Float16 s) {
   return r;
 }
 
+// IQ4_NL: 8 indices into the format's 16-value table, in the Q4 nibble
+// order. Four lookups per byte permute (indices 0..7 from the first half of
+// the table, 8..15 from the second, picked by bit 3), the int8 values then
+// offset-binary as for Q8; exact in fp16.
+__device__ __forceinline__ uint32_t iq4_look(uint32_t ix) {
+  constexpr uint32_t kT0 = 0xBFAD9881u, kT1 = 0xF6EADDCFu;     // -127 -104 -83 -65 | -49 -35 -22 -10
+  constexpr uint32_t kT2 = 0x26190D01u, kT3 = 0x71594535u;     //    1   13  25  38 |  53  69  89 113
+  const uint32_t sel = ix & 0x07070707u;
+  const uint32_t lo = __builtin_amdgcn_perm(kT1, kT0, sel), hi = __builtin_amdgcn_perm(kT3, kT2, sel);
+  const uint32_t m = ((ix >> 3) & 0x01010101u) * 0xFFu;
+  return ((hi & m) | (lo & ~m)) ^ 0x80808080u;
+}
+__device__ __forceinline__ half8 dec_iq4(uint32_t w) {
+  const half2v off = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const uint32_t a = iq4_look(w & 0x0F0F0F0Fu), b = iq4_look((w >> 4) & 0x0F0F0F0Fu);
+  const uint32_t d[4] = {__builtin_amdgcn_perm(0x64646464u, a, 0x05010400u),
+                         __builtin_amdgcn_perm(0x64646464u, a, 0x05030402u),
+                         __builtin_amdgcn_perm(0x64646464u, b, 0x05010400u),
+                         __builtin_amdgcn_perm(0x64646464u, b, 0x05030402u)};
+  half8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const half2v h = __builtin_bit_cast(half2v, d[i]) - off;
+    r[2 * i] = h[0];
+    r[2 * i + 1] = h[1];
+  }
+  return r;
+}
+
+// Q3_K: 8 weights of one 16-column run of a 32-column block: two low bits at
+// bit sq of each byte of q0, q1, the high bit at bit sm of m0, m1; code
+// u = low + 4 high in 0..7, weight (u - 4) times the run's integer scale
+// s = scale - 32 (|product| <= 128: exact in fp16; the block's fp16 d is
+// applied to the MFMA result).
+__device__ __forceinline__ half8 dec_q3k(uint32_t q0, uint32_t q1, uint32_t m0, uint32_t m1, int sq,
+                                         int sm, _Float16 s) {
+  const half2v off = {(_Float16)1028.0f, (_Float16)1028.0f}, ss = {s, s};
+  const uint32_t u0 = ((q0 >> sq) & 0x03030303u) | (((m0 >> sm) & 0x01010101u) << 2);
+  const uint32_t u1 = ((q1 >> sq) & 0x03030303u) | (((m1 >> sm) & 0x01010101u) << 2);
+  const uint32_t d[4] = {__builtin_amdgcn_perm(0x64646464u, u0, 0x05010400u),
+                         __builtin_amdgcn_perm(0x64646464u, u0, 0x05030402u),
+                         __builtin_amdgcn_perm(0x64646464u, u1, 0x05010400u),
+                         __builtin_amdgcn_perm(0x64646464u, u1, 0x05030402u)};
+  half8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const half2v h = (__builtin_bit_cast(half2v, d[i]) - off) * ss;
+    r[2 * i] = h[0];
+    r[2 * i + 1] = h[1];
+  }
+  return r;
+}
+
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
@@ -257,11 +310,13 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
 //
 // xs: this wave's staging area; src[i]: vector i at the super-step's first
 // column; n: valid vectors; ncs: code slots present.
-__host__ __device__ constexpr int cc_of(int fmt) { return fmt == kQ8 ? 64 : (fmt == kBF16 ? 32 : 128); }
+__host__ __device__ constexpr int cc_of(int fmt) {
+  return fmt == kQ8 ? 64 : (fmt == kBF16 ? 32 : (fmt == kQ3K ? 256 : 128));
+}
 
 // SL: code slots the registers hold (a full super-step by default; fewer
 // for waves that take only the first columns of one).
-template <int FMT, int NT, int SL = 4 * (kSSCols / cc_of(FMT))>
+template <int FMT, int NT, int SL = FMT == kQ3K ? 6 : 4 * (kSSCols / cc_of(FMT))>
 struct WRegs {
   static constexpr int CC = cc_of(FMT);   // columns per chunk
   static constexpr int NSL = SL;
@@ -328,6 +383,45 @@ __device__ __forceinline__ void wave_compute(const WRegs<FMT, NT, SL>& R, int nc
   else scaled = x_stage_f16<NT>(R.xr, (_Float16*)xs, lane, inv);
   __builtin_amdgcn_wave_barrier();
 
+  if constexpr (FMT == kQ3K) {
+    // one super-block per row: slots 0..3 the low bits of row group rg,
+    // slots 4, 5 the high-bit masks of row groups 0, 1 and 2, 3; the scale
+    // slot the row's sub-block scales and d. The lane's k-group is half of
+    // run qg / 2 of each 32-column block 4h + j, whose scale is number
+    // 8h + 2j + qg / 2; d multiplies the chain of the super-step.
+    const _Float16* x = (const _Float16*)xs;
+    const int run = qg >> 1;
+    f4 ch[4];
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) ch[rg] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int B = 0; B < 8; ++B) {
+      const int h = B >> 2, j = B & 3;
+      const int col = 32 * B + 8 * qg;
+      const half8 ahb = a_read<NT, _Float16, half8>(x, 0, tok, n, col);
+      const half8 alb = a_read<NT, _Float16, half8>(x, 1, tok, n, col);
+      const int bsh = 8 * (2 * (j & 1) + run);       // the scale bytes' position for this run
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const uint32_t lo4 = (word(sc[rg], j >> 1) >> (bsh + 4 * h)) & 0xFu;
+        const uint32_t hi2 = (sc[rg].z >> (bsh + 2 * (2 * h + (j >> 1)))) & 3u;
+        const _Float16 s = (_Float16)((int)(lo4 | (hi2 << 4)) - 32);
+        const uint4& m = q[4 + (rg >> 1)];
+        const half8 bw = dec_q3k(word(q[rg], 2 * h), word(q[rg], 2 * h + 1), word(m, 2 * (rg & 1)),
+                                 word(m, 2 * (rg & 1) + 1), 2 * j, 4 * h + j, s);
+        ch[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahb, bw, ch[rg], 0, 0, 0);
+        ch[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alb, bw, ch[rg], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const float dd = h2f(sc[rg].w);
+      if (!scaled) acc[rg] += dd * ch[rg];
+      else acc[rg] += (dd * lane_inv<NT>(inv, lane)) * ch[rg];
+    }
+    return;
+  }
+
   const int nch = ncs / 4;
 #pragma unroll
   for (int c = 0; c < MAXCH; ++c) {
@@ -375,7 +469,7 @@ __device__ __forceinline__ void wave_compute(const WRegs<FMT, NT, SL>& R, int nc
             }
           } else {
             const half8 bw = FMT == kQ8 ? dec_q8(word(w, 2 * b), word(w, 2 * b + 1))
-                                        : dec_q4(word(w, b));
+                                        : FMT == kIQ4 ? dec_iq4(word(w, b)) : dec_q4(word(w, b));
             f4 d = {0.f, 0.f, 0.f, 0.f};
             d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahb, bw, d, 0, 0, 0);
             d = __builtin_amdgcn_mfma_f32_16x16x32_f16(alb, bw, d, 0, 0, 0);
@@ -940,7 +1034,8 @@ __global__ __launch_bounds__(64 * W) void k_phase1(P1 a) {
 
 // Phase 2: routed-expert gate/up + SwiGLU, item = (slot, tile).
 
-template <int T>
+// GU: the gate/up format (kFP4, or kQ3K for the Q3_K records)
+template <int T, int GU>
 __global__ __launch_bounds__(1024) void k_phase2(P2 a) {
   extern __shared__ __align__(16) char smem[];
   const Dims& d = a.d;
@@ -955,11 +1050,11 @@ __global__ __launch_bounds__(1024) void k_phase2(P2 a) {
 
   // activations: xl [T][G][L] fp32; item (slot j, tile r)
   const rsrc_t xr = rsrc(a.ws.xl, (uint32_t)((size_t)T * d.G * d.L * sizeof(float)));
-  const int wbytes = (ss_codes(kFP4, a.ggu, wave) + scale_slots(kFP4)) * kSlot;
+  const int wbytes = (ss_codes(GU, a.ggu, wave) + scale_slots(GU)) * kSlot;
   // Item (slot j, tile r): every table entry it needs comes in one round of
   // scalar loads (expert, count, the xl rows of its tokens written by the
   // routing), so its weight and activation loads start one load latency in.
-  auto issue = [&](int item, WRegs<kFP4, T>& R) {
+  auto issue = [&](int item, WRegs<GU, T>& R) {
     const int j = item / tiles;
     const int e = ci(a.ws.slot_expert)[j], cnt = ci(a.ws.slot_count)[j];
     ci_t xrow = ci(a.ws.slot_xrow + j * kMaxDecodeT);
@@ -967,10 +1062,10 @@ __global__ __launch_bounds__(1024) void k_phase2(P2 a) {
 #pragma unroll
     for (int i = 0; i < T; ++i) xoff[i] = (int)((xrow[i] * d.L + wave * kSSCols) * sizeof(float));
     const uint8_t* base = a.experts + (size_t)e * a.stride;
-    wave_load_b<kFP4, T>(R, rsrc(ss_ptr(base, a.ggu, item % tiles, wave), wbytes),
-                         ss_codes(kFP4, a.ggu, wave), xr, xoff, cnt, ss_cols(a.ggu, wave), lane);
+    wave_load_b<GU, T>(R, rsrc(ss_ptr(base, a.ggu, item % tiles, wave), wbytes),
+                         ss_codes(GU, a.ggu, wave), xr, xoff, cnt, ss_cols(a.ggu, wave), lane);
   };
-  WRegs<kFP4, T> R;
+  WRegs<GU, T> R;
   int it = blockIdx.x;
   if (it < nvalid && active) issue(it, R);
   for (int par = 0; it < nvalid; it += gridDim.x, par ^= 1) {
@@ -980,7 +1075,7 @@ __global__ __launch_bounds__(1024) void k_phase2(P2 a) {
     f4 acc[4];
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) acc[rg] = (f4){0.f, 0.f, 0.f, 0.f};
-    if (active) wave_compute<kFP4, T>(R, ss_codes(kFP4, a.ggu, wave), cnt, xs, lane, acc);
+    if (active) wave_compute<GU, T>(R, ss_codes(GU, a.ggu, wave), cnt, xs, lane, acc);
     __builtin_amdgcn_sched_barrier(0);   // the next loads reuse this item's registers
     const int nx = it + gridDim.x;
     if (nx < nvalid && active) issue(nx, R);
@@ -1059,7 +1154,8 @@ constexpr int phase3_waves(int nss) {
   return n;
 }
 
-template <int T, int W>
+// DN: the down format (kFP4, or kIQ4 for the Q3_K records)
+template <int T, int W, int DN>
 __global__ __launch_bounds__(64 * W) void k_phase3(P3 a) {
   extern __shared__ __align__(16) char smem[];
   __shared__ int flag;
@@ -1087,12 +1183,12 @@ __global__ __launch_bounds__(64 * W) void k_phase3(P3 a) {
 #pragma unroll
     for (int i = 0; i < T; ++i)
       xoff[i] = (int)(((size_t)(start + (i < cnt ? i : 0)) * d.F + ss * kSSCols) * sizeof(float));
-    const int ncs = ss_codes(kFP4, a.gdn, ss);
-    WRegs<kFP4, T> R;
-    wave_load_b<kFP4, T>(R, rsrc(ss_ptr(rec + a.gu_bytes, a.gdn, r, ss), (ncs + scale_slots(kFP4)) * kSlot),
+    const int ncs = ss_codes(DN, a.gdn, ss);
+    WRegs<DN, T> R;
+    wave_load_b<DN, T>(R, rsrc(ss_ptr(rec + a.gu_bytes, a.gdn, r, ss), (ncs + scale_slots(DN)) * kSlot),
                          ncs, rsrc(a.ws.hbuf, (uint32_t)((size_t)T * d.K * d.F * sizeof(float))), xoff, cnt,
                          ss_cols(a.gdn, ss), lane);
-    wave_compute<kFP4, T>(R, ncs, cnt, xs, lane, acc);
+    wave_compute<DN, T>(R, ncs, cnt, xs, lane, acc);
   }
   if (block_reduce_mf<T>(acc, red, wave, lane, nw)) {
     cf_t ts = cf((const float*)(rec + a.ts_off));
@@ -1338,10 +1434,15 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st, i
   const int nw2 = h->g_gu.nss;
   const size_t sm2 = (size_t)nw2 * (stage_bytes<T>() + 2 * red_bytes_per_wave<T>());
   const int items2 = maxslots * h->g_gu.tiles;
-  const int res2 = resident_blocks(h, (const void*)k_phase2<T>, nw2 * 64, sm2);
+  const bool q3k = dd.expert_format == LMOE_EXPERTS_Q3K;
+  const void* k2 = q3k ? (const void*)k_phase2<T, kQ3K> : (const void*)k_phase2<T, kFP4>;
+  const int res2 = resident_blocks(h, k2, nw2 * 64, sm2);
   if (res2 <= 0) { set_error("phase 2: occupancy query failed"); return LMOE_EHIP; }
-  if (only == 0 || only == 2)
-    hipLaunchKernelGGL(k_phase2<T>, dim3(items2 < res2 ? items2 : res2), dim3(nw2 * 64), sm2, st, p2);
+  if (only == 0 || only == 2) {
+    const dim3 g2(items2 < res2 ? items2 : res2), b2(nw2 * 64);
+    if (q3k) hipLaunchKernelGGL((k_phase2<T, kQ3K>), g2, b2, sm2, st, p2);
+    else hipLaunchKernelGGL((k_phase2<T, kFP4>), g2, b2, sm2, st, p2);
+  }
   LMOE_HIP(hipGetLastError());
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[2], st));
 
@@ -1357,8 +1458,13 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st, i
   const size_t sm3 = (size_t)nw3 * (stage_bytes_f16<T>() + red_bytes_per_wave<T>());
   const dim3 grid3((unsigned)(maxslots * h->g_dn.tiles)), block3(nw3 * 64);
   if (only == 0 || only == 3) {
-    if (nw3 <= 8) hipLaunchKernelGGL((k_phase3<T, 8>), grid3, block3, sm3, st, p3);
-    else hipLaunchKernelGGL((k_phase3<T, 16>), grid3, block3, sm3, st, p3);
+    if (q3k) {
+      if (nw3 <= 8) hipLaunchKernelGGL((k_phase3<T, 8, kIQ4>), grid3, block3, sm3, st, p3);
+      else hipLaunchKernelGGL((k_phase3<T, 16, kIQ4>), grid3, block3, sm3, st, p3);
+    } else {
+      if (nw3 <= 8) hipLaunchKernelGGL((k_phase3<T, 8, kFP4>), grid3, block3, sm3, st, p3);
+      else hipLaunchKernelGGL((k_phase3<T, 16, kFP4>), grid3, block3, sm3, st, p3);
+    }
   }
   LMOE_HIP(hipGetLastError());
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[3], st));

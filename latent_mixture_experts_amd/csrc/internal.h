@@ -47,12 +47,21 @@ __device__ __forceinline__ uint4 ldb(rsrc_t r, int voff, int soff) {
 //   FP4     128     4 blocks x 8 E2M1 codes (pairs per byte, low nibble first)
 //                                                         16 E4M3 scales of row r (per 16 cols)
 //   BF16    32      8 bf16                                none
+//   IQ4     128     as Q4, the nibbles holding IQ4_NL table indices
+//                                                         8 fp16 scales of row r (per 32 cols)
+//   Q3K     256     (K a multiple of 256: one super-step is one Q3_K super-block
+//                   per row; six code slots) slots 0..3, row group j: lane
+//                   (r, k-group q) holds the 8 low-bit bytes 16 b + 8 (q % 2) + 0..7
+//                   of half 0, then of half 1 (b = q / 2: the 16-column run of
+//                   its k-group); slots 4, 5: row groups 2s and 2s + 1, each the
+//                   lane's 8 high-bit-mask bytes 16 b + 8 (q % 2) + 0..7
+//                                                         row r's 12 scale bytes and fp16 d
 //
 // The router keeps a plainer layout (BF16R) for its fp64 dot products: lane
 // l of a slot holds 8 consecutive bf16 columns of row l of the tile. F16 is
 // the BF16 layout holding fp16 values: the prefill path keeps D and U
 // dequantized to fp16(q * d) in it.
-enum Fmt : int { kQ8 = 0, kQ4 = 1, kFP4 = 2, kBF16 = 3, kBF16R = 4, kF16 = 5 };
+enum Fmt : int { kQ8 = 0, kQ4 = 1, kFP4 = 2, kBF16 = 3, kBF16R = 4, kF16 = 5, kIQ4 = 6, kQ3K = 7 };
 constexpr int kSSCols = 256;
 constexpr int kSlot = 1024;
 constexpr int kMaxDecodeT = 8;     // tokens the GEMV (decode) path takes per forward
@@ -63,7 +72,7 @@ constexpr int kMaxTokens = 1 << 20;   // largest max_tokens a handle accepts
 constexpr int kRouterChunks = 4;  // router column chunks: H / (64 * H/256)
 
 __host__ __device__ constexpr int chunk_cols(int f) {      // columns of one chunk
-  return f == kQ8 ? 64 : ((f == kBF16 || f == kF16) ? 32 : (f == kBF16R ? 8 : 128));
+  return f == kQ8 ? 64 : ((f == kBF16 || f == kF16) ? 32 : (f == kBF16R ? 8 : (f == kQ3K ? 256 : 128)));
 }
 __host__ __device__ constexpr int scale_slots(int f) {
   return (f == kBF16 || f == kBF16R || f == kF16) ? 0 : 1;
@@ -72,7 +81,7 @@ __host__ __device__ constexpr int scale_slots(int f) {
 // (one slot per chunk for the router layout); a partial last chunk is
 // padded with zero codes.
 __host__ __device__ constexpr int ss_code_slots(int f, int cols) {
-  return f == kBF16R ? cols / 8 : 4 * ((cols + chunk_cols(f) - 1) / chunk_cols(f));
+  return f == kBF16R ? cols / 8 : (f == kQ3K ? 6 : 4 * ((cols + chunk_cols(f) - 1) / chunk_cols(f)));
 }
 
 struct Geom {

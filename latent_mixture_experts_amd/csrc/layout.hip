@@ -21,10 +21,42 @@ namespace {
 
 // Where the rows of one source matrix live in packed form.
 struct Src {
-  const uint8_t* codes;   // row-major codes in the packed format
-  const uint8_t* scales;  // Q8/Q4: fp16 [rows][k/32]; FP4: E4M3 [rows][k/16]; BF16: unused
+  const uint8_t* codes;   // row-major codes in the packed format; Q3K / IQ4: the blocks
+  const uint8_t* scales;  // Q8/Q4: fp16 [rows][k/32]; FP4: E4M3 [rows][k/16]; else unused
   int rows;
 };
+
+constexpr int kQ3KBlock = 110, kIQ4Block = 18;   // bytes of a Q3_K (256) / IQ4_NL (32) block
+
+// One 16-byte lane chunk of a Q3K super-step (layout in internal.h): slot j
+// of super-step ss, lane (r16, qg) of the tile's row group(s).
+__device__ void q3k_chunk(const Src& a, const Src& b, int pair, int k, int tile, int ss, int j,
+                          int lane, uint8_t (&out)[16]) {
+  const int r16 = lane % 16, qg = lane / 16, run = qg >> 1, part = qg & 1;
+  const auto block = [&](int rg, int& rows_ok) -> const uint8_t* {
+    const Src* s = (pair && rg >= 2) ? &b : &a;
+    const int row = pair ? 32 * tile + 16 * (rg & 1) + r16 : 64 * tile + 16 * rg + r16;
+    rows_ok = row < s->rows;
+    return s->codes + ((size_t)row * (k / 256) + ss) * kQ3KBlock;
+  };
+  int ok;
+  if (j < 4) {                                  // low bits, halves 0 and 1
+    const uint8_t* p = block(j, ok);
+    if (ok)
+      for (int h = 0; h < 2; ++h)
+        for (int i = 0; i < 8; ++i) out[8 * h + i] = p[32 + 32 * h + 16 * run + 8 * part + i];
+  } else if (j < 6) {                           // high-bit masks of two row groups
+    for (int t = 0; t < 2; ++t) {
+      const uint8_t* p = block(2 * (j - 4) + t, ok);
+      if (ok)
+        for (int i = 0; i < 8; ++i) out[8 * t + i] = p[16 * run + 8 * part + i];
+    }
+  } else {                                      // lane-chunk 16 rg + r: scales and d of that row
+    const uint8_t* p = block(lane / 16, ok);
+    if (ok)
+      for (int i = 0; i < 14; ++i) out[i] = p[96 + i];
+  }
+}
 
 __device__ inline size_t code_offset(int fmt, int row, int k, int col) {
   size_t e = (size_t)row * k + col;
@@ -50,7 +82,9 @@ __global__ void k_tile(int fmt, Src a, Src b, int pair, int k, Geom g, uint8_t* 
   uint8_t out[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) out[i] = 0;
-  if (fmt == kBF16R) {
+  if (fmt == kQ3K) {
+    q3k_chunk(a, b, pair, k, tile, ss, j, lane, out);
+  } else if (fmt == kBF16R) {
     const int row = 64 * tile + lane;
     if (row < a.rows) {
       const uint8_t* p = a.codes + code_offset(fmt, row, k, ss * kSSCols + j * 8);
@@ -88,6 +122,20 @@ __global__ void k_tile(int fmt, Src a, Src b, int pair, int k, Geom g, uint8_t* 
                 for (int i = 0; i < 4; ++i) out[4 * bb + i] = 0x88;         // q = 0
               continue;
             }
+            if (fmt == kIQ4) {
+              // block col / 32 holds element o < 16 in the low nibble of
+              // byte 2 + o, element 16 + o in its high nibble; the device
+              // keeps element i low and element i + 4 high in byte i
+              const uint8_t* blk = s->codes + ((size_t)row * (k / 32) + col / 32) * kIQ4Block;
+              const int o = col % 32;
+              uint8_t e[8];
+              for (int i = 0; i < 8; ++i) {
+                const int oo = o + i;
+                e[i] = oo < 16 ? (blk[2 + oo] & 0xF) : (blk[2 + oo - 16] >> 4);
+              }
+              for (int i = 0; i < 4; ++i) out[4 * bb + i] = (uint8_t)(e[i] | (e[i + 4] << 4));
+              continue;
+            }
             const uint8_t* p = s->codes + code_offset(fmt, row, k, col);
             if (fmt == kFP4) {
               for (int i = 0; i < 4; ++i) out[4 * bb + i] = p[i];
@@ -106,6 +154,12 @@ __global__ void k_tile(int fmt, Src a, Src b, int pair, int k, Geom g, uint8_t* 
         if (fmt == kFP4) {
           const uint8_t* p = s->scales + (size_t)row * (k / 16) + ss * 16;
           for (int i = 0; i < cols / 16; ++i) out[i] = p[i];
+        } else if (fmt == kIQ4) {
+          const uint8_t* blk = s->codes + ((size_t)row * (k / 32) + ss * 8) * kIQ4Block;
+          for (int i = 0; i < cols / 32; ++i) {
+            out[2 * i] = blk[i * kIQ4Block];
+            out[2 * i + 1] = blk[i * kIQ4Block + 1];
+          }
         } else {
           const uint8_t* p = s->scales + ((size_t)row * (k / 32) + ss * 8) * 2;
           for (int i = 0; i < 2 * (cols / 32); ++i) out[i] = p[i];
@@ -157,6 +211,15 @@ __global__ void k_copy_ts(const uint8_t* __restrict__ recs, size_t rec_bytes, si
     uint32_t v = p[4 * i] | (p[4 * i + 1] << 8) | (p[4 * i + 2] << 16) | ((uint32_t)p[4 * i + 3] << 24);
     q[i] = __uint_as_float(v);
   }
+  q[3] = 0.f;
+}
+
+// Q3_K records carry no tensor scales: the device record's three are 1.
+__global__ void k_unit_ts(int n, uint8_t* __restrict__ dst, size_t stride, size_t ts_off) {
+  int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  float* q = (float*)(dst + (size_t)e * stride + ts_off);
+  q[0] = q[1] = q[2] = 1.f;
   q[3] = 0.f;
 }
 
@@ -402,9 +465,10 @@ int load_weights_impl(lmoe_t* h, const lmoe_weights* w, hipStream_t st) {
     set_error("lmoe_load_weights: d_bytes/u_bytes do not match G packed matrices");
     return LMOE_EINVAL;
   }
-  const size_t rec = lmoe_expert_record_bytes(L, F);
+  const bool q3k = d.expert_format == LMOE_EXPERTS_Q3K;
+  const size_t rec = lmoe_expert_record_bytes_fmt(L, F, d.expert_format);
   if (w->expert_record_bytes != rec) {
-    set_error("lmoe_load_weights: expert_record_bytes does not match the NVFP4 record size");
+    set_error("lmoe_load_weights: expert_record_bytes does not match the expert format's record size");
     return LMOE_EINVAL;
   }
   std::vector<uint8_t> lab(E);
@@ -489,14 +553,26 @@ int load_weights_impl(lmoe_t* h, const lmoe_weights* w, hipStream_t st) {
       for (int i = 0; i < cnt; ++i) {
         const uint8_t* r = (const uint8_t*)t.p + (size_t)i * rec;
         uint8_t* dst = h->experts + (size_t)(e0 + i) * h->expert_stride;
+        if (q3k) {
+          // gate blocks [F][L/256], up blocks, down blocks [L][F/32]
+          const size_t n1 = (size_t)F * (L / 256) * kQ3KBlock;
+          Src ga{r, nullptr, F}, ua{r + n1, nullptr, F}, da{r + 2 * n1, nullptr, L};
+          if (int rc = launch_tile(kQ3K, ga, ua, 1, L, h->g_gu, dst, st)) return rc;
+          if (int rc = launch_tile(kIQ4, da, da, 0, F, h->g_dn, dst + h->g_gu.bytes(), st)) return rc;
+          continue;
+        }
         Src ga{r + ro.gate_c, r + ro.gate_s, F}, ua{r + ro.up_c, r + ro.up_s, F};
         if (int rc = launch_tile(kFP4, ga, ua, 1, L, h->g_gu, dst, st)) return rc;
         Src da{r + ro.down_c, r + ro.down_s, L};
         if (int rc = launch_tile(kFP4, da, da, 0, F, h->g_dn, dst + h->g_gu.bytes(), st)) return rc;
       }
-      hipLaunchKernelGGL(k_copy_ts, dim3((cnt + 63) / 64), dim3(64), 0, st, (const uint8_t*)t.p,
-                         rec, ro.tail, cnt, h->experts + (size_t)e0 * h->expert_stride,
-                         h->expert_stride, h->ts_off);
+      if (q3k)
+        hipLaunchKernelGGL(k_unit_ts, dim3((cnt + 63) / 64), dim3(64), 0, st, cnt,
+                           h->experts + (size_t)e0 * h->expert_stride, h->expert_stride, h->ts_off);
+      else
+        hipLaunchKernelGGL(k_copy_ts, dim3((cnt + 63) / 64), dim3(64), 0, st, (const uint8_t*)t.p,
+                           rec, ro.tail, cnt, h->experts + (size_t)e0 * h->expert_stride,
+                           h->expert_stride, h->ts_off);
       LMOE_HIP(hipGetLastError());
       LMOE_HIP(hipStreamSynchronize(st));
     }

@@ -26,7 +26,9 @@ OK, EINVAL, ENOMEM, EHIP, ESTATE, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
 class Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "hidden", "latent", "n_experts", "top_k", "n_groups", "expert_ffn", "shared_ffn",
-        "du_bits", "max_tokens", "has_router_bias")]
+        "du_bits", "max_tokens", "has_router_bias", "expert_format")]
+
+EXPERTS_NVFP4, EXPERTS_Q3K = 0, 1
 
 
 class Weights(ctypes.Structure):
@@ -77,6 +79,7 @@ def _load():
         "lmoe_pack_blocks": (ctypes.c_int, [vp, i32, i32, i32, vp, vp]),
         "lmoe_pack_expert_records": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp, vp]),
         "lmoe_ple_gather": (ctypes.c_int, [vp, i32, vp, vp, i32, vp, vp]),
+        "lmoe_expert_record_bytes_fmt": (sz, [i32, i32, i32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -117,8 +120,8 @@ def _stream(stream):
     return getattr(stream, "cuda_stream", stream)
 
 
-def expert_record_bytes(latent, ffn):
-    return _lib.lmoe_expert_record_bytes(latent, ffn)
+def expert_record_bytes(latent, ffn, expert_format=0):
+    return _lib.lmoe_expert_record_bytes_fmt(latent, ffn, expert_format)
 
 
 def du_matrix_bytes(rows, cols, bits):
@@ -129,9 +132,9 @@ class Layer:
     """One latent-MoE layer on one GPU."""
 
     def __init__(self, hidden, latent, n_experts, top_k, n_groups, expert_ffn, shared_ffn,
-                 du_bits, max_tokens, has_router_bias=False, device=0):
+                 du_bits, max_tokens, has_router_bias=False, device=0, expert_format=0):
         self.dims = Dims(hidden, latent, n_experts, top_k, n_groups, expert_ffn, shared_ffn,
-                         du_bits, max_tokens, int(bool(has_router_bias)))
+                         du_bits, max_tokens, int(bool(has_router_bias)), int(expert_format))
         h = ctypes.c_void_p()
         _check(_lib.lmoe_create(ctypes.byref(self.dims), device, ctypes.byref(h)), "lmoe_create")
         self._h = h
@@ -144,7 +147,7 @@ class Layer:
         def nbytes(a):
             return a.nbytes if isinstance(a, np.ndarray) else a.numel() * a.element_size()
         ex = blobs["experts"]
-        rec = expert_record_bytes(self.dims.latent, self.dims.expert_ffn)
+        rec = expert_record_bytes(self.dims.latent, self.dims.expert_ffn, self.dims.expert_format)
         sg, su, sd = blobs["shared"]
         w = Weights(_ptr(blobs["router_bf16"]), _ptr(blobs.get("router_bias")),
                     _ptr(blobs["labels"]),

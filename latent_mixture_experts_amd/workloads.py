@@ -17,6 +17,8 @@ model page, "Model profile" and architecture tables):
 * ``145b_prefill``: as 145b_decode with T 4096 and a per-expert router bias
   N(0, 1) that skews expert loads.
 * ``145b_stack``: 48 independently seeded 145b_decode layers, T 4.
+* ``145b_q3k_decode``: 145b_decode with the Q3_K build's expert records (Q3_K
+  gate/up, IQ4_NL down: 1,630,720 bytes an expert).
 * ``mtp_draft``: the MoE of the multi-token-prediction draft layer ("MTP
   head" row of the architecture tables: 1.26B parameters in 512 experts,
   i.e. 2,457,600 = 3 x 1280 x 640 per expert): ell 1280, F 640 NVFP4, top-10,
@@ -50,6 +52,7 @@ class Workload:
     router_bias: bool = False
     labels_mod: bool = False     # label = e mod G instead of uniform random
     n_layers: int = 1
+    expert_format: int = 0       # 0 NVFP4 records, 1 Q3_K gate/up + IQ4_NL down
 
     @property
     def router_std(self):
@@ -67,6 +70,8 @@ WORKLOADS = {
                              router_bias=True),
     "145b_stack": Workload("145b_stack", 2560, 1792, 512, 10, 8, 640, 640, 8, 4, n_layers=48),
     "mtp_draft": Workload("mtp_draft", 2560, 1280, 512, 10, 8, 640, 640, 8, 1),
+    "145b_q3k_decode": Workload("145b_q3k_decode", 2560, 1792, 512, 10, 8, 640, 640, 8, 4,
+                                expert_format=1),
 }
 
 # stream identifiers

@@ -14,7 +14,7 @@ MAX_ABS_OF_RMS = 1e-2
 
 def dims_of(w):
     return oracle.LayerDims(w.hidden, w.latent, w.n_experts, w.top_k, w.n_groups, w.expert_ffn,
-                            w.shared_ffn, w.du_bits)
+                            w.shared_ffn, w.du_bits, getattr(w, "expert_format", 0))
 
 
 class Case:

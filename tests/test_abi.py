@@ -52,7 +52,7 @@ def test_du_bytes_match_oracle(lib, rows, cols, bits):
 def _create(lib, **kw):
     from latent_mixture_experts_amd import lmoe
     base = dict(hidden=256, latent=128, n_experts=16, top_k=2, n_groups=2, expert_ffn=64,
-                shared_ffn=64, du_bits=8, max_tokens=4, has_router_bias=0)
+                shared_ffn=64, du_bits=8, max_tokens=4, has_router_bias=0, expert_format=0)
     base.update(kw)
     d = lmoe.Dims(*[base[f] for f, _ in lmoe.Dims._fields_])
     h = ctypes.c_void_p()
@@ -97,3 +97,22 @@ def test_ple_gather_argument_checks_on_host(lib):
     assert f(dummy, 4, dummy, None, 160, dummy, None) == lmoe.EINVAL
     bad = (ctypes.c_int64 * 16)(*([5] * 15 + [0]))
     assert f(dummy, 4, dummy, bad, 160, dummy, None) == lmoe.EINVAL
+
+
+def test_q3k_record_sizes_and_refusals(lib):
+    """The Q3_K record sizes the pages print, and the shapes lmoe_create
+    refuses for Q3_K experts (a latent not a multiple of 256, the prefill
+    path)."""
+    from latent_mixture_experts_amd import lmoe
+    assert lmoe.expert_record_bytes(1792, 640, 1) == 1630720
+    assert lmoe.expert_record_bytes(1280, 640, 1) == 1164800
+    assert lmoe.expert_record_bytes(1792, 640, 0) == lmoe.expert_record_bytes(1792, 640)
+    assert lmoe.expert_record_bytes(1792, 640, 7) == 0
+    for kw, code in ((dict(latent=128), lmoe.EUNSUPPORTED), (dict(max_tokens=16), lmoe.EUNSUPPORTED),
+                     (dict(expert_format=2), lmoe.EINVAL)):
+        a = dict(hidden=256, latent=256, n_experts=16, top_k=2, n_groups=2, expert_ffn=64,
+                 shared_ffn=64, du_bits=8, max_tokens=4, has_router_bias=0, expert_format=1)
+        a.update(kw)
+        d = lmoe.Dims(**a)
+        h = ctypes.c_void_p()
+        assert lib.lmoe_create(ctypes.byref(d), 0, ctypes.byref(h)) == code, kw

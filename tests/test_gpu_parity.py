@@ -27,7 +27,8 @@ def make_layer(case, max_tokens=8):
     lm = _lmoe()
     w = case.w
     layer = lm.Layer(w.hidden, w.latent, w.n_experts, w.top_k, w.n_groups, w.expert_ffn,
-                     w.shared_ffn, w.du_bits, max_tokens, has_router_bias=w.router_bias)
+                     w.shared_ffn, w.du_bits, max_tokens, has_router_bias=w.router_bias,
+                     expert_format=w.expert_format)
     layer.load(case.blobs)
     return layer
 
@@ -128,6 +129,66 @@ def test_mtp_draft_layer(lmtp, T):
     drafted token, and the four tokens of a verify window."""
     case, layer = lmtp
     check(case, layer, T, "mtp_draft")
+
+
+# ---------------------------------------------------------------------------
+# Q3_K gate/up + IQ4_NL down expert records (decode path)
+
+Q3K_TINY = wl.Workload("q3k_tiny", 256, 256, 16, 2, 2, 64, 64, 8, 8, labels_mod=True,
+                       expert_format=1)
+
+
+@pytest.fixture(scope="module")
+def q3k_tiny():
+    c = Case(Q3K_TINY, tokens=8)
+    return c, make_layer(c)
+
+
+@pytest.mark.parametrize("T", range(1, 9))
+def test_q3k_tiny_all_token_counts(q3k_tiny, T):
+    case, layer = q3k_tiny
+    check(case, layer, T, "q3k tiny")
+
+
+@pytest.fixture(scope="module")
+def l145q3k():
+    c = Case(wl.WORKLOADS["145b_q3k_decode"], tokens=8)
+    return c, make_layer(c)
+
+
+@pytest.mark.parametrize("T", [4, 1, 8])
+def test_145b_q3k_decode(l145q3k, T):
+    case, layer = l145q3k
+    check(case, layer, T, "145b q3k")
+
+
+def test_120b_q3k_decode():
+    """The 120B shapes (latent 1280, Q4 D/U) with Q3_K records: 1,164,800
+    bytes an expert, as the model page prints."""
+    w = wl.Workload("120b_q3k", 2560, 1280, 512, 10, 8, 640, 640, 4, 5, expert_format=1)
+    c = Case(w, tokens=5)
+    assert c.blobs["experts"].shape[1] == 1164800
+    layer = make_layer(c, 5)
+    check(c, layer, 5, "120b q3k")
+
+
+def test_q3k_decode_activation_range():
+    """Rows at 1e-3, 1e2, 1e-6 with every seventh element near 1e5, and 3e3
+    through the Q3_K / IQ4_NL decoders (the token scales are undone on the
+    super-step's chain and on each 32-column block)."""
+    x = wl.x(Q3K_TINY, 11, tokens=5)
+    x[0] *= 1e-3
+    x[1] *= 1e2
+    x[2] *= 1e-6
+    x[2, ::7] = x[2, ::7] * 1e11
+    x[4] *= 3e3
+    c = Case(Q3K_TINY, seed=11, x=x)
+    layer = make_layer(c)
+    got, dbg = run(layer, c, 5)
+    r = c.expect(5)
+    r["x"] = x
+    assert np.array_equal(dbg["topk_idx"], r["idx"])
+    _per_token_close(got, r, "q3k tiny")
 
 
 def test_same_token_repeated_shares_experts():
