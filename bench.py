@@ -16,7 +16,8 @@ oracle CPU baseline: "decode_t1" (the same layers at T = 1, with the byte
 counts of reading D and U for used groups only and for all groups),
 "decode_120b" (the Edge0-120B-shaped layer, Q4 D/U, latent 1280, T = 5),
 "mtp_draft" (the draft layer's MoE: 512 experts of 3 x 1280 x 640, Q8 D/U,
-T = 1, one drafted token),
+T = 1, one drafted token), "decode_q3k" (the 145B layer at T = 4 with the
+Q3_K build's expert records: Q3_K gate/up, IQ4_NL down),
 "ple_gather" (the n-gram embedding gather on the full 51.2 GB table at
 T = 4096 and T = 4), "stack_145b" (48 independently seeded 145B-shaped layers as pre-norm
 residual blocks, T = 4: whole-stack tokens/s and sustained HBM bandwidth) and
@@ -69,7 +70,7 @@ def build_layer(lm, wl, w, seed, layer_idx, torch):
     dev = "cuda"
     E, H, L, G, F, Fs = w.n_experts, w.hidden, w.latent, w.n_groups, w.expert_ffn, w.shared_ffn
     layer = lm.Layer(H, L, E, w.top_k, G, F, Fs, w.du_bits, max(w.tokens, 1),
-                     has_router_bias=w.router_bias)
+                     has_router_bias=w.router_bias, expert_format=w.expert_format)
     router = torch.from_numpy(wl.router(w, seed, layer_idx)).to(dev)
     router_bf16 = torch.empty(E, H, dtype=torch.int16, device=dev)
     lm.pack_bf16(router, router_bf16)
@@ -90,14 +91,25 @@ def build_layer(lm, wl, w, seed, layer_idx, torch):
         t = torch.empty(*shp, dtype=torch.int16, device=dev)
         lm.pack_bf16(rnd(*shp), t)
         shared.append(t)
-    rec = lm.expert_record_bytes(L, F)
+    rec = lm.expert_record_bytes(L, F, w.expert_format)
     experts = torch.empty(E, rec, dtype=torch.uint8, device=dev)
-    chunk = 64
-    for e0 in range(0, E, chunk):
-        n = min(chunk, E - e0)
-        g_, u_, d_ = wl.torch_expert_masters(w, seed, layer_idx, e0, n, dev)
-        lm.pack_expert_records(g_, u_, d_, experts[e0:e0 + n])
-        del g_, u_, d_
+    if w.expert_format == 1:
+        # Q3_K / IQ4_NL records of random codes and scales (the library has no
+        # device packer for them): every fp16 d set to a value of the size a
+        # quantizer gives N(0, 0.02) weights
+        experts.copy_(torch.randint(0, 256, (E, rec), generator=gen, device=dev, dtype=torch.uint8))
+        n1 = F * (L // 256) * 110
+        def set_d(view, off):
+            d = (torch.rand(view.shape[:-1], generator=gen, device=dev) * 3e-4 + 3e-4).to(torch.float16)
+            view[..., off:off + 2] = d.view(torch.uint8).view(*view.shape[:-1], 2)
+        set_d(experts[:, :2 * n1].reshape(E, 2 * F * (L // 256), 110), 108)
+        set_d(experts[:, 2 * n1:].reshape(E, L * (F // 32), 18), 0)
+    else:
+        for e0 in range(0, E, 64):
+            n = min(64, E - e0)
+            g_, u_, d_ = wl.torch_expert_masters(w, seed, layer_idx, e0, n, dev)
+            lm.pack_expert_records(g_, u_, d_, experts[e0:e0 + n])
+            del g_, u_, d_
     layer.load(dict(router_bf16=router_bf16,
                     router_bias=None if bias is None else torch.from_numpy(bias).to(dev),
                     labels=torch.from_numpy(labels).to(dev), d_blob=d_blob, u_blob=u_blob,
@@ -118,11 +130,14 @@ def decode_bytes(w, idx, labels):
     du = (w.du_bits / 8.0) * (34.0 / 32.0 if w.du_bits == 8 else 18.0 / 16.0)  # bytes / weight
     distinct = len(set(idx.ravel().tolist()))
     used = len(set(labels[idx.ravel()].tolist()))
-    fp4 = 0.5 + 1.0 / 16.0
-    common = E * H * 2 + distinct * 3 * F * L * fp4 + 3 * Fs * H * 2 + 2 * T * H * 4
+    if getattr(w, "expert_format", 0) == 1:
+        gu_w, dn_w = 110.0 / 256.0, 18.0 / 32.0      # Q3_K gate/up, IQ4_NL down: bytes / weight
+    else:
+        gu_w = dn_w = 0.5 + 1.0 / 16.0              # NVFP4
+    common = E * H * 2 + distinct * F * L * (2 * gu_w + dn_w) + 3 * Fs * H * 2 + 2 * T * H * 4
     phases = [E * H * 2 + G * L * H * du + 2 * Fs * H * 2 + T * H * 4 + T * G * L * 4 + T * Fs * 4,
-              distinct * 2 * F * L * fp4 + T * K * (L + F) * 4,
-              distinct * L * F * fp4 + T * K * (F + L) * 4,
+              distinct * 2 * F * L * gu_w + T * K * (L + F) * 4,
+              distinct * L * F * dn_w + T * K * (F + L) * 4,
               used * H * L * du + H * Fs * 2 + T * (G * L + Fs + H) * 4]
     out = {
         "phases": phases,
@@ -590,7 +605,8 @@ def config_of(w, T, copies):
     return {"workload": w.name, "tokens": T, "hidden": w.hidden, "latent": w.latent,
             "experts": w.n_experts, "top_k": w.top_k, "groups": w.n_groups,
             "expert_ffn": w.expert_ffn, "shared_ffn": w.shared_ffn,
-            "du_format": "Q%d" % w.du_bits, "expert_format": "NVFP4",
+            "du_format": "Q%d" % w.du_bits,
+            "expert_format": "Q3_K+IQ4_NL" if w.expert_format == 1 else "NVFP4",
             "router_bias": w.router_bias, "layers": w.n_layers, "weight_copies": copies}
 
 
@@ -693,6 +709,13 @@ def main():
         if cpu:
             rm["cpu_baseline"] = cpu_baseline(wm, args.seed, wm.tokens)
         out["mtp_draft"] = rm
+        wq = wl.WORKLOADS["145b_q3k_decode"]
+        rq, lq = bench_decode(lm, wl, wq, args, torch)
+        close_layers(lq)
+        del lq
+        if cpu:
+            rq["cpu_baseline"] = cpu_baseline(wq, args.seed, wq.tokens)
+        out["decode_q3k"] = rq
         ws = wl.WORKLOADS["145b_stack"]
         rs, ls = bench_decode(lm, wl, ws, args, torch, steps=args.stack_steps,
                               warmup=min(args.warmup, 3))
