@@ -285,34 +285,38 @@ def bench_prefill(lm, wl, w, args, torch):
         fl.append(f_); ex.append(e_); pairs.append(p_); counts.append(cnt.cpu().numpy())
     flops = np.mean(np.array(fl), axis=0)
     n = len(layers)
-    for i in range(args.prefill_warmup):
-        layers[i % n][0].forward(x, y)
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(args.prefill_steps):
-        layers[i % n][0].forward(x, y)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.prefill_steps
-
     nph = lm.lib().lmoe_phase_count(T)
     assert nph == len(PREFILL_PHASES)
-    nprof = max(2 * n, 8)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)] for _ in range(nprof)]
-    for row in evs:          # torch creates the HIP event at its first record
-        for e in row:
-            e.record()
-    torch.cuda.synchronize()
-    for i in range(nprof):
-        L_ = layers[i % n][0]
-        L_.set_phase_events([e.cuda_event for e in evs[i]])
-        L_.forward(x, y)
-    for L_, _ in layers:
-        L_.set_phase_events(None)
-    torch.cuda.synchronize()
-    phase_ms = np.array([[row[k].elapsed_time(row[k + 1]) for k in range(nph)] for row in evs])
-    phase_avg = phase_ms.mean(axis=0)
+
+    def timed():
+        """Step time over the timed steps, then per-phase times (events)."""
+        for i in range(args.prefill_warmup):
+            layers[i % n][0].forward(x, y)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(args.prefill_steps):
+            layers[i % n][0].forward(x, y)
+        end.record()
+        torch.cuda.synchronize()
+        step_ms = start.elapsed_time(end) / args.prefill_steps
+        nprof = max(2 * n, 8)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)] for _ in range(nprof)]
+        for row in evs:          # torch creates the HIP event at its first record
+            for e in row:
+                e.record()
+        torch.cuda.synchronize()
+        for i in range(nprof):
+            L_ = layers[i % n][0]
+            L_.set_phase_events([e.cuda_event for e in evs[i]])
+            L_.forward(x, y)
+        for L_, _ in layers:
+            L_.set_phase_events(None)
+        torch.cuda.synchronize()
+        pm = np.array([[row[k].elapsed_time(row[k + 1]) for k in range(nph)] for row in evs])
+        return step_ms, pm.mean(axis=0)
+
+    ms, phase_avg = timed()
     tflops = [f / (p * 1e-3) / 1e12 if f else 0.0 for f, p in zip(flops, phase_avg)]
     dom = int(np.argmax(phase_avg))
     log("prefill step %.3f ms (%.0f tokens/s); phases (us): %s" % (
@@ -355,6 +359,21 @@ def bench_prefill(lm, wl, w, args, torch):
                      "phase": PREFILL_PHASES[dom], "kernel_us": float(phase_avg[dom] * 1e3),
                      "kernel_algorithmic_flop": float(flops[dom]),
                      "kernel_executed_flop": ex[0][dom]},
+    }
+    # the variant with D over the routed (token, group) pairs only: it waits
+    # for the routing, the shared gate/up takes its place beside it
+    for L_, _ in layers:
+        L_.set_prefill_d(1)
+    ms_r, phase_r = timed()
+    log("prefill, D over routed pairs: step %.3f ms; D %.1f us (all groups: %.1f us)" % (
+        ms_r, phase_r[2] * 1e3, phase_avg[2] * 1e3))
+    out["d_routed"] = {
+        "ms_per_step": ms_r, "value": T / (ms_r * 1e-3), "unit": "tokens/s",
+        "phases_us": {nm: float(p * 1e3) for nm, p in zip(PREFILL_PHASES, phase_r)},
+        "d_executed_tflop": flops[2] / 1e12,
+        "d_tflops": flops[2] / (phase_r[2] * 1e-3) / 1e12,
+        "all_groups_d_executed_tflop": ex[0][2] / 1e12,
+        "all_groups_d_tflops_executed": ex[0][2] / (phase_avg[2] * 1e-3) / 1e12,
     }
     for L_, _ in layers:
         L_.close()

@@ -211,6 +211,8 @@ int create_impl(lmoe_t* h) {
     A(p.h, 2 * nk * F);
     A(p.o, sizeof(float) * nk * L);
     A(p.s, 2 * Tp * G * L);
+    A(p.gl_tok, sizeof(int) * Tp * G);
+    A(p.gl_cnt, sizeof(int) * G);
     LMOE_HIP(hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking));
     LMOE_HIP(hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming));
     LMOE_HIP(hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming));
@@ -559,3 +561,12 @@ int lmoe_pack_expert_records(const float* gate, const float* up, const float* do
 }
 
 }  // extern "C"
+
+int lmoe_set_prefill_d(lmoe_t* h, int32_t routed_only) {
+  if (!h || (routed_only != 0 && routed_only != 1)) {
+    set_error("lmoe_set_prefill_d: NULL handle or a value other than 0 and 1");
+    return LMOE_EINVAL;
+  }
+  h->prefill_d_routed = routed_only == 1;
+  return LMOE_OK;
+}

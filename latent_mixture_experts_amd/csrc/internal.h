@@ -170,6 +170,8 @@ struct PrefillWs {
                                    // the first half); the router and U k-splits put
                                    // their fp32 partial sums here while it is unused
   uint16_t* s = nullptr;           // [T][G][ell] fp16 per-group sums
+  int* gl_tok = nullptr;           // [G][T] each group's routed tokens (routed-pairs D)
+  int* gl_cnt = nullptr;           // [G]
   double* wmax = nullptr;          // [1] max_e |Wr_e|_2
   int tmax = 0;                    // tokens the buffers hold (0: no prefill path)
 };
@@ -181,6 +183,7 @@ struct lmoe {
   int device = 0;
   int ncu = 1;                // compute units of the device
   bool loaded = false;
+  bool prefill_d_routed = false;  // prefill D over the routed (t, g) pairs only
   lm::Geom g_router, g_d, g_u, g_gu, g_dn, g_sgu, g_sdn;
   lm::Geom g_router_m;        // router in the MFMA layout (prefill)
   lm::Geom g_d16, g_u16;      // D_g, U_g dequantized to fp16 (prefill)

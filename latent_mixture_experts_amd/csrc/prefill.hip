@@ -534,6 +534,12 @@ struct Dense {
   // out + sp * T * ostride (k_select adds them up).
   int nfull, nrem, nsplit;
   float* part;
+  // D over the routed (token, group) pairs only: group g's rows are the
+  // tokens gl_tok[g * gcap + i], i < gl_cnt[g]; its output goes to columns
+  // g * gL .. of the token's row
+  const int* gl_tok;
+  const int* gl_cnt;
+  int G, gcap, gL;
 };
 
 // XCD-aware order: block b of n runs on XCD b % 8; each XCD takes a
@@ -2172,30 +2178,60 @@ constexpr int kWgB = (kWgN / 64) * 4 * kSlot;            // weight bytes per sta
 constexpr int kWgStage = kWgA + kWgB;
 static_assert(kWgBuf * kWgStage <= 160 * 1024, "LDS");
 
-template <int EPI>
+// GATHER: D over the routed (token, group) pairs only. Blocks then take
+// (group, 256-token tile of the group's tokens, quad), gather their rows by
+// the DMA's per-lane source offsets and write each result row to its token's
+// group columns; blocks past the last tile exit.
+template <int EPI, bool GATHER>
 __global__ __launch_bounds__(256) void k_dense16(Dense a) {
   __shared__ __align__(1024) uint8_t smem[kWgBuf * kWgStage];
-  const int nq = (a.ntiles + 3) / 4, mtl = (a.T + kWgT - 1) / kWgT;
-  const int L = xcd_order(blockIdx.x, mtl * nq);
-  int mt, quad;
-  tile_of(L, mtl, nq, mt, quad);
+  __shared__ int toks[GATHER ? kWgT : 1];
+  const int nq = (a.ntiles + 3) / 4;
+  int mt, quad, g = 0, nrows;
+  const uint8_t* wbase = a.W.base;
+  if constexpr (!GATHER) {
+    const int mtl = (a.T + kWgT - 1) / kWgT;
+    const int L = xcd_order(blockIdx.x, mtl * nq);
+    tile_of(L, mtl, nq, mt, quad);
+    nrows = min(kWgT, a.T - mt * kWgT);
+  } else {
+    const int L = xcd_order(blockIdx.x, gridDim.x);
+    quad = L % nq;
+    int lt = L / nq, c = 0;
+    for (; g < a.G; ++g) {
+      c = a.gl_cnt[g];
+      const int nt = (c + kWgT - 1) / kWgT;
+      if (lt < nt) break;
+      lt -= nt;
+    }
+    if (g >= a.G) return;
+    mt = lt;
+    nrows = min(kWgT, c - mt * kWgT);
+    wbase = a.W.base + (size_t)g * a.W.g.bytes();
+    for (int i = threadIdx.x; i < kWgT; i += blockDim.x)
+      toks[i] = i < nrows ? a.gl_tok[(size_t)g * a.gcap + (size_t)mt * kWgT + i] : 0;
+    __syncthreads();
+  }
   const int lane = threadIdx.x & 63, wave = wave_id(), wm = wave & 1, wn = wave >> 1;
   const int kmat = a.A.kmat, nst = kmat / kWgCols;
   // activation DMA: wave w stages rows 16 i .. + 15 for i = w + 4 j; lane l
   // the piece at position l % 4 of row 16 i + l / 4, which holds column
-  // piece (l % 4) ^ ((row / 2) % 4). Rows past T read zeros.
-  const rsrc_t ar = rsrc(a.A.p + (size_t)mt * kWgT * a.A.rs,
-                         (uint32_t)(min(kWgT, a.T - mt * kWgT) * a.A.rs * 2));
+  // piece (l % 4) ^ ((row / 2) % 4). Rows past the tile's last read zeros.
+  const rsrc_t ar = GATHER ? rsrc(a.A.p, (uint32_t)((size_t)a.T * a.A.rs * 2))
+                           : rsrc(a.A.p + (size_t)mt * kWgT * a.A.rs, (uint32_t)(nrows * a.A.rs * 2));
   uint32_t avo[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = 16 * (wave + 4 * j) + (lane >> 2);
     const int pc = (lane & 3) ^ ((r >> 1) & 3);
-    avo[j] = (uint32_t)((r * a.A.rs + 8 * pc) * 2);
+    if constexpr (GATHER)
+      avo[j] = r < nrows ? (uint32_t)(((size_t)toks[r] * a.A.rs + 8 * pc) * 2) : kOob;
+    else
+      avo[j] = (uint32_t)((r * a.A.rs + 8 * pc) * 2);
   }
   // weight DMA: wave w copies the 4 slots of stage s of tile 4 quad + w
   const int wt = 4 * quad + wave;
-  const rsrc_t br = rsrc(a.W.base + (size_t)min(wt, a.ntiles - 1) * a.W.g.tile_slots * kSlot,
+  const rsrc_t br = rsrc(wbase + (size_t)min(wt, a.ntiles - 1) * a.W.g.tile_slots * kSlot,
                          wt < a.ntiles ? (uint32_t)(a.W.g.tile_slots * kSlot) : 0u);
   const uint32_t sbase = lds_off(smem);
   const auto issue = [&](int s) {
@@ -2279,16 +2315,46 @@ __global__ __launch_bounds__(256) void k_dense16(Dense a) {
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int t = mt * kWgT + 128 * wm + acc_tok(lane, mb, v);
-      if (t >= a.T) continue;
+      const int r = 128 * wm + acc_tok(lane, mb, v);
+      if (r >= nrows) continue;
+      const size_t orow = GATHER ? (size_t)toks[r] * a.ostride + (size_t)g * a.gL
+                                 : (size_t)(mt * kWgT + r) * a.ostride;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int tile = 4 * quad + 2 * wn + (j >> 1);
         if (tile >= a.ntiles) continue;
         const int n = 64 * tile + 32 * (j & 1) + (lane & 31);
-        if constexpr (EPI == kEpiF16) ((_Float16*)a.out)[(size_t)t * a.ostride + n] = (_Float16)acc[mb][j][v];
+        if constexpr (EPI == kEpiF16) ((_Float16*)a.out)[orow + n] = (_Float16)acc[mb][j][v];
       }
     }
+}
+
+// Per group g, its tokens in ascending order (those with an assignment
+// labelled g): one block per group, a ballot and a wave-offset scan per
+// 1024 tokens.
+__global__ __launch_bounds__(1024) void k_group_lists(const int* idx, const uint8_t* labels, int T, int K,
+                                                      int gcap, int* gl_tok, int* gl_cnt) {
+  __shared__ int wsum[16];
+  const int g = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int run = 0;
+  for (int t0 = 0; t0 < T; t0 += 1024) {
+    const int t = t0 + (int)threadIdx.x;
+    bool used = false;
+    if (t < T)
+      for (int k = 0; k < K; ++k) used = used || labels[idx[(size_t)t * K + k]] == g;
+    const unsigned long long m = __ballot(used);
+    if (lane == 0) wsum[w] = __popcll(m);
+    __syncthreads();
+    int off = run, tot = 0;
+    for (int i = 0; i < 16; ++i) {
+      if (i < w) off += wsum[i];
+      tot += wsum[i];
+    }
+    if (used) gl_tok[(size_t)g * gcap + off + __popcll(m & ((1ull << lane) - 1ull))] = t;
+    run += tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) gl_cnt[g] = run;
 }
 
 template <int WF, int EPI>
@@ -2299,7 +2365,7 @@ int launch_dense(const Dense& a, hipStream_t st) {
   if constexpr (WF == kF16 && EPI == kEpiF16)
     if (a.A.kmat % kWgCols == 0 && a.A.ps == 0 && a.W.nmat == 1) {
       const unsigned n16 = (unsigned)(((a.T + kWgT - 1) / kWgT) * ((a.ntiles + 3) / 4));
-      hipLaunchKernelGGL((k_dense16<EPI>), dim3(n16), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_dense16<EPI, false>), dim3(n16), dim3(256), 0, st, a);
       LMOE_HIP(hipGetLastError());
       return 0;
     }
@@ -2366,6 +2432,27 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
   // caller's (D alone is longer than both). When phases are timed everything
   // runs on the caller's stream in phase order, so that each phase is
   // measured alone.
+  // D over the routed (token, group) pairs (the handle's prefill-D option):
+  // per-group token lists, then the gathered GEMM; it needs the routing
+  const bool routed = h->prefill_d_routed && (size_t)T * H * 2 < (1ull << 31);
+  auto routed_d = [&](hipStream_t sd) -> int {
+    hipLaunchKernelGGL(k_group_lists, dim3(G), dim3(1024), 0, sd, p.idx, h->labels, T, K, p.tmax,
+                       p.gl_tok, p.gl_cnt);
+    LMOE_HIP(hipGetLastError());
+    Dense a{};
+    a.W = WMat{h->dmat16, h->g_d16, 0, 1};
+    a.A = AMat{p.xh, (size_t)H, 0, H};
+    a.T = T; a.ntiles = h->g_d16.tiles;
+    a.out = p.xl; a.ostride = (size_t)G * L;
+    a.gl_tok = p.gl_tok; a.gl_cnt = p.gl_cnt; a.G = G; a.gcap = p.tmax; a.gL = L;
+    // at most sum_g ceil(cnt_g / 256) <= T min(K, G) / 256 + G tiles
+    const size_t nt = (size_t)T * std::min(K, G) / kWgT + G;
+    const size_t nb = nt * ((a.ntiles + 3) / 4);
+    hipLaunchKernelGGL((k_dense16<kEpiF16, true>), dim3((unsigned)nb), dim3(256), 0, sd, a);
+    LMOE_HIP(hipGetLastError());
+    if (ev) LMOE_HIP(hipEventRecord(h->phase_events[3], sd));
+    return 0;
+  };
   auto dense_front = [&](hipStream_t sd, bool d_part, bool s_part) -> int {
     if (d_part) {
       Dense a{};
@@ -2389,9 +2476,11 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     return 0;
   };
   if (!ev) {
+    // the second stream takes D over all groups, or (routed D, which waits
+    // for the routing) the shared gate/up
     LMOE_HIP(hipEventRecord(h->ev_fork, st));
     LMOE_HIP(hipStreamWaitEvent(h->aux, h->ev_fork, 0));
-    if (int rc = dense_front(h->aux, true, false)) return rc;
+    if (int rc = dense_front(h->aux, !routed, routed)) return rc;
     LMOE_HIP(hipEventRecord(h->ev_join, h->aux));
   }
   // router logits
@@ -2458,9 +2547,16 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
   }
   if (ev) {
     LMOE_HIP(hipEventRecord(h->phase_events[2], st));
-    if (int rc = dense_front(st, true, true)) return rc;
+    if (routed) {
+      if (int rc = routed_d(st)) return rc;
+    }
+    if (int rc = dense_front(st, !routed, true)) return rc;
   } else {
-    if (int rc = dense_front(st, false, true)) return rc;
+    if (routed) {
+      if (int rc = routed_d(st)) return rc;
+    } else if (int rc = dense_front(st, false, true)) {
+      return rc;
+    }
     LMOE_HIP(hipStreamWaitEvent(st, h->ev_join, 0));
   }
   // experts

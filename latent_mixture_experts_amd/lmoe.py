@@ -80,6 +80,7 @@ def _load():
         "lmoe_pack_expert_records": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp, vp]),
         "lmoe_ple_gather": (ctypes.c_int, [vp, i32, vp, vp, i32, vp, vp]),
         "lmoe_expert_record_bytes_fmt": (sz, [i32, i32, i32]),
+        "lmoe_set_prefill_d": (ctypes.c_int, [vp, i32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -139,6 +140,10 @@ class Layer:
         _check(_lib.lmoe_create(ctypes.byref(self.dims), device, ctypes.byref(h)), "lmoe_create")
         self._h = h
         self.device = device
+
+    def set_prefill_d(self, routed_only):
+        """0: prefill D over all groups (default); 1: over the routed pairs only."""
+        _check(_lib.lmoe_set_prefill_d(self._h, int(routed_only)), "lmoe_set_prefill_d")
 
     def load(self, blobs, stream=None):
         """blobs: router_bf16, router_bias (or None), labels, d_blob, u_blob,

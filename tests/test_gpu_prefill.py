@@ -360,7 +360,7 @@ def piece_class_tokens(idx, labels, E, G, T, n_total, seed=1234):
     return np.array(sorted(tokens))
 
 
-def _sampled(name, T, n_sample, seed=0):
+def _sampled(name, T, n_sample, seed=0, routed_d=False):
     w = wl.WORKLOADS[name]
     pre = Case(w, seed=seed, tokens=T, pack_tokens=[0])          # routing of every token
     labels = np.asarray(pre.blobs["labels"])
@@ -369,6 +369,8 @@ def _sampled(name, T, n_sample, seed=0):
           flush=True)
     c = Case(w, seed=seed, tokens=T, pack_tokens=tokens)
     layer = make_layer(c, T)
+    if routed_d:
+        layer.set_prefill_d(1)
     got, dbg = run(layer, w, c.x)
     check_routing(c, dbg, T)
     check_outputs(c, got, dbg, tokens)
@@ -381,6 +383,50 @@ def test_145b_prefill_4096():
 
 def test_120b_prefill_q4():
     _sampled("120b_decode", 600, 16)
+
+
+# ---------------------------------------------------------------------------
+# D over the routed (token, group) pairs only (lmoe_set_prefill_d(h, 1))
+
+def test_145b_prefill_4096_routed_d():
+    _sampled("145b_prefill", 4096, 16, routed_d=True)
+
+
+@pytest.mark.parametrize("T", [9, 64, 300])
+def test_tiny_prefill_routed_d(tiny, T):
+    c, layer = tiny
+    layer.set_prefill_d(1)
+    try:
+        print("case tiny prefill routed D T", T, flush=True)
+        got, dbg = run(layer, c.w, c.x[:T])
+        check_routing(c, dbg, T)
+        check_outputs(c, got, dbg, np.arange(T))
+    finally:
+        layer.set_prefill_d(0)
+
+
+def test_prefill_routed_d_skewed_groups():
+    """A skewed router over 32 experts in 4 groups (some groups draw most of
+    the 700 tokens, their lists span several 256-token tiles; others few):
+    every token checked, the routed and the all-groups D agree on y."""
+    w = wl.Workload("classes", 256, 512, 32, 4, 4, 160, 64, 8, 700, router_bias=True)
+    c = Case(w, seed=3, tokens=700)
+    layer = make_layer(c, 700)
+    print("case skewed groups prefill routed D T 700", flush=True)
+    dense, _ = run(layer, w, c.x)
+    layer.set_prefill_d(1)
+    got, dbg = run(layer, w, c.x)
+    check_routing(c, dbg, 700)
+    check_outputs(c, got, dbg, np.arange(700))
+    rel, _ = rel_errors(got, dense)
+    assert rel <= 1e-6, rel
+
+
+def test_set_prefill_d_rejects_bad_values(tiny):
+    from latent_mixture_experts_amd import lmoe
+    c, layer = tiny
+    with pytest.raises(lmoe.LmoeError):
+        layer.set_prefill_d(2)
 
 
 @pytest.mark.parametrize("name", ["tiny", "145b_decode"])
