@@ -661,9 +661,24 @@ def main():
     from latent_mixture_experts_amd import lmoe as lm
     from latent_mixture_experts_amd import workloads as wl
 
-    w = wl.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     cpu = not args.no_cpu_baseline
+    if args.workload == "ple_gather":
+        res = bench_ple(lm, args, torch, cpu)
+        r = res["t4096"]
+        out = {
+            "metric": "PLE n-gram embedding gather tokens/s (HBM roofline)",
+            "value": r["value"], "unit": "tokens/s", "n_gpus": 1, "steps": r["steps"], "warmup": 20,
+            "ms_per_step": r["us_per_step"] * 1e-3, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "e4m3->bf16", "data": "synthetic",
+            "config": {"workload": "ple_gather", "tokens": 4096, "table_bytes": res["table_bytes"]},
+            "roofline": r["roofline"], "ple_gather": res,
+        }
+        if cpu:
+            out["cpu_baseline"] = res["cpu_baseline"]
+        print(json.dumps(out), flush=True)
+        return
+    w = wl.WORKLOADS[args.workload]
     if w.tokens > 8:
         pre = bench_prefill(lm, wl, w, args, torch)
         out = {
