@@ -54,7 +54,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_145b_t4096_traffic.json")
 # kernel of each prefill phase as rocprofv3 names it (D and U on fp16 weights)
 PREFILL_KERNEL_IDS = [["k_prep", "k_dense_dma<3, 0>", "k_select<5, 8>"],
-                      ["k_perm_mask", "k_perm_scan", "k_perm_scatter"], "k_dense16<1>",
+                      ["k_perm_mask", "k_perm_scan", "k_perm_scatter"], "k_dense16<1, false>",
                       "k_dense_dma<3, 2>",
                       ["k_grouped_dma<0>", "k_grouped_short<0, 2, 8>", "k_grouped_short<0, 1, 8>"],
                       ["k_down_res<8, 2>", "k_down_res<8, 1>"], "k_combine",
