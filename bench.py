@@ -45,7 +45,7 @@ MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 / bf16 matrix peak, published
 PREFILL_PHASES = ["route", "permute", "d", "shared_gate_up", "expert_gate_up", "expert_down",
                   "combine", "u_shared_down"]
 PREFILL_KERNELS = ["k_prep + k_dense_dma<BF16,Logits> + k_select", "k_perm_*",
-                   "k_dense16<F16> (D; 128 x 128 wave tiles, LDS DMA)",
+                   "k_group_lists + k_dense16<F16, gather> (D over the routed (t, g) pairs; 128 x 128 wave tiles, LDS DMA)",
                    "k_dense_dma<BF16,SwigluB2> (shared gate/up)",
                    "k_grouped_dma<GateUp> (LDS DMA) + k_grouped_short<GateUp> (64- and 32-token pieces)",
                    "k_down_res (activations resident in LDS; 64- and 32-token blocks)", "k_combine",
@@ -54,7 +54,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_145b_t4096_traffic.json")
 # kernel of each prefill phase as rocprofv3 names it (D and U on fp16 weights)
 PREFILL_KERNEL_IDS = [["k_prep", "k_dense_dma<3, 0>", "k_select<5, 8>"],
-                      ["k_perm_mask", "k_perm_scan", "k_perm_scatter"], "k_dense16<1, false>",
+                      ["k_perm_mask", "k_perm_scan", "k_perm_scatter"], ["k_group_lists", "k_dense16<1, true>"],
                       "k_dense_dma<3, 2>",
                       ["k_grouped_dma<0>", "k_grouped_short<0, 2, 8>", "k_grouped_short<0, 1, 8>"],
                       ["k_down_res<8, 2>", "k_down_res<8, 1>"], "k_combine",
@@ -175,9 +175,10 @@ def measured_traffic(kernel, workload, path=TRAFFIC_FILE):
 
 def prefill_flops(w, idx, labels):
     """Algorithmic flops of each prefill phase for routing idx [T][K]: D and
-    U count the (token, group) pairs the tokens route into (the kernels run
-    all G groups; that figure is reported beside it), the router one pass of
-    bf16 products (the kernel runs two)."""
+    U count the (token, group) pairs the tokens route into (D runs over
+    those pairs; U, and D in its all-groups form, over all G groups: that
+    figure is reported beside it), the router one pass of bf16 products (the
+    kernel runs two)."""
     T, H, L, E, K, G, F, Fs = (idx.shape[0], w.hidden, w.latent, w.n_experts, w.top_k,
                                w.n_groups, w.expert_ffn, w.shared_ffn)
     lab = labels[idx]
@@ -185,7 +186,7 @@ def prefill_flops(w, idx, labels):
     fl = [2.0 * T * E * H, 0.0, 2.0 * pairs * L * H, 2.0 * T * 2 * Fs * H,
           2.0 * T * K * 2 * F * L, 2.0 * T * K * L * F, 0.0,
           2.0 * pairs * H * L + 2.0 * T * H * Fs]
-    executed = [4.0 * T * E * H, 0.0, 2.0 * T * G * L * H, 4.0 * T * 2 * Fs * H, None, None, 0.0,
+    executed = [4.0 * T * E * H, 0.0, 2.0 * pairs * L * H, 4.0 * T * 2 * Fs * H, None, None, 0.0,
                 2.0 * T * G * H * L + 4.0 * T * H * Fs]
     return fl, executed, pairs
 
@@ -360,20 +361,23 @@ def bench_prefill(lm, wl, w, args, torch):
                      "kernel_algorithmic_flop": float(flops[dom]),
                      "kernel_executed_flop": ex[0][dom]},
     }
-    # the variant with D over the routed (token, group) pairs only: it waits
-    # for the routing, the shared gate/up takes its place beside it
+    # the variant with D over all G groups of every token (the reference
+    # engine's form), on the second stream beside the routing
+    for L_, _ in layers:
+        L_.set_prefill_d(0)
+    ms_a, phase_a = timed()
     for L_, _ in layers:
         L_.set_prefill_d(1)
-    ms_r, phase_r = timed()
-    log("prefill, D over routed pairs: step %.3f ms; D %.1f us (all groups: %.1f us)" % (
-        ms_r, phase_r[2] * 1e3, phase_avg[2] * 1e3))
-    out["d_routed"] = {
-        "ms_per_step": ms_r, "value": T / (ms_r * 1e-3), "unit": "tokens/s",
-        "phases_us": {nm: float(p * 1e3) for nm, p in zip(PREFILL_PHASES, phase_r)},
-        "d_executed_tflop": flops[2] / 1e12,
-        "d_tflops": flops[2] / (phase_r[2] * 1e-3) / 1e12,
-        "all_groups_d_executed_tflop": ex[0][2] / 1e12,
-        "all_groups_d_tflops_executed": ex[0][2] / (phase_avg[2] * 1e-3) / 1e12,
+    d_all = 2.0 * T * w.n_groups * w.latent * w.hidden
+    log("prefill, D over all groups: step %.3f ms; D %.1f us (routed pairs: %.1f us)" % (
+        ms_a, phase_a[2] * 1e3, phase_avg[2] * 1e3))
+    out["d_all_groups"] = {
+        "ms_per_step": ms_a, "value": T / (ms_a * 1e-3), "unit": "tokens/s",
+        "phases_us": {nm: float(p * 1e3) for nm, p in zip(PREFILL_PHASES, phase_a)},
+        "d_executed_tflop": d_all / 1e12,
+        "d_tflops_executed": d_all / (phase_a[2] * 1e-3) / 1e12,
+        "routed_d_executed_tflop": flops[2] / 1e12,
+        "routed_d_tflops": flops[2] / (phase_avg[2] * 1e-3) / 1e12,
     }
     for L_, _ in layers:
         L_.close()

@@ -206,15 +206,15 @@ int lmoe_run_phase(lmoe_t* h, const float* x, int32_t T, int32_t phase, float* y
 
 /* Prefill D variant ("Edge0-145B: a Qwen MoE with its experts squeezed, and
  * a 51B table left on the SSD", section "A latent in front of the experts":
- * the reference engine runs D for every group): 0 (the default) computes
- * D_g x for all G groups of every token, on a second stream beside the
- * routing; 1 only for the (token, group) pairs the routing uses, after the
+ * the reference engine runs D for every group): 1 (the default) computes
+ * D_g x only for the (token, group) pairs the routing uses, after the
  * routing (per-group token lists, a gathered GEMM), with the shared gate/up
- * on the second stream instead. y is the same up to fp32 rounding order; the
- * debug latent rows of unused pairs are then not written. Applies to
- * forwards of T > 8 on a handle created with max_tokens > 8 (and to batches
- * with T * hidden * 2 < 2^31; larger ones use the default). EINVAL for a
- * NULL handle or another value. */
+ * on a second stream; the debug latent rows of unused pairs are then not
+ * written. 0 computes D_g x for all G groups of every token, on the second
+ * stream beside the routing (the reference engine's form). y is the same up
+ * to fp32 rounding order. Applies to forwards of T > 8 on a handle created
+ * with max_tokens > 8; batches with T * hidden * 2 >= 2^31 always take the
+ * all-groups form. EINVAL for a NULL handle or another value. */
 int lmoe_set_prefill_d(lmoe_t* h, int32_t routed_only);
 
 void lmoe_destroy(lmoe_t* h);

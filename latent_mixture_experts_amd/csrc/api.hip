@@ -196,6 +196,7 @@ int create_impl(lmoe_t* h) {
     A(p.idx, sizeof(int) * nk);
     A(p.w, sizeof(float) * nk);
     A(p.cmask, sizeof(unsigned long long) * nchunk * E);
+    A(p.gmask, sizeof(unsigned long long) * nchunk * G);
     A(p.ccnt, sizeof(int) * nchunk * E);
     A(p.cbase, sizeof(int) * nchunk * E);
     A(p.eorder, sizeof(int) * E);

@@ -153,6 +153,7 @@ struct PrefillWs {
   int* idx = nullptr;              // [T][K]
   float* w = nullptr;              // [T][K]
   unsigned long long* cmask = nullptr;  // [nchunk][E] tokens of a 64-token chunk per expert
+  unsigned long long* gmask = nullptr;  // [nchunk][G] the same per group
   int* ccnt = nullptr;             // [nchunk][E]
   int* cbase = nullptr;            // [nchunk][E]
   int* eorder = nullptr;           // [E] experts in (label, expert) order
@@ -183,7 +184,7 @@ struct lmoe {
   int device = 0;
   int ncu = 1;                // compute units of the device
   bool loaded = false;
-  bool prefill_d_routed = false;  // prefill D over the routed (t, g) pairs only
+  bool prefill_d_routed = true;   // prefill D over the routed (t, g) pairs only (else all groups)
   lm::Geom g_router, g_d, g_u, g_gu, g_dn, g_sgu, g_sdn;
   lm::Geom g_router_m;        // router in the MFMA layout (prefill)
   lm::Geom g_d16, g_u16;      // D_g, U_g dequantized to fp16 (prefill)

@@ -1642,6 +1642,7 @@ __device__ __forceinline__ void wave_argmax(double& v, int& i) {
 }
 
 constexpr int kMaxE = 1024;
+constexpr int kMaxG = 64;     // groups (the create-time limit)
 
 // Sum over the wave, every lane gets it: DPP exchanges within each row of
 // 16 lanes (xor 1, xor 2, half-row mirror, row mirror), then the four row
@@ -1871,6 +1872,7 @@ struct Perm {
   const int* idx;        // [T][K]
   int T, K, E, G, nchunk;
   unsigned long long* cmask;   // [nchunk][E]
+  unsigned long long* gmask;   // [nchunk][G]: the chunk's tokens with an assignment in group g
   int* ccnt;             // [nchunk][E] tokens of the chunk per expert
   int* cbase;            // [nchunk][E] tokens of earlier chunks per expert
   const int* eorder;     // [E] experts in (label, expert) order
@@ -1888,8 +1890,10 @@ struct Perm {
 
 __global__ __launch_bounds__(256) void k_perm_mask(Perm a) {
   __shared__ unsigned long long m[kMaxE];
+  __shared__ unsigned long long gm[kMaxG];
   const int c = blockIdx.x;
   for (int e = threadIdx.x; e < a.E; e += blockDim.x) m[e] = 0ull;
+  for (int g = threadIdx.x; g < a.G; g += blockDim.x) gm[g] = 0ull;
   __syncthreads();
   const int n = CHUNK_T * a.K;
   for (int j = threadIdx.x; j < n; j += blockDim.x) {
@@ -1900,7 +1904,10 @@ __global__ __launch_bounds__(256) void k_perm_mask(Perm a) {
   for (int e = threadIdx.x; e < a.E; e += blockDim.x) {
     a.cmask[(size_t)c * a.E + e] = m[e];
     a.ccnt[(size_t)c * a.E + e] = __popcll(m[e]);
+    if (m[e]) atomicOr(&gm[a.labels[e]], m[e]);
   }
+  __syncthreads();
+  for (int g = threadIdx.x; g < a.G; g += blockDim.x) a.gmask[(size_t)c * a.G + g] = gm[g];
 }
 
 // one block of kMaxE threads: chunk prefixes, segment starts, group offsets
@@ -2195,7 +2202,14 @@ __global__ __launch_bounds__(256) void k_dense16(Dense a) {
     tile_of(L, mtl, nq, mt, quad);
     nrows = min(kWgT, a.T - mt * kWgT);
   } else {
-    const int L = xcd_order(blockIdx.x, gridDim.x);
+    // the grid is an upper bound; the work items (256-token tiles of the
+    // groups' lists x quads) are ordered over the XCDs by their own count,
+    // so that every XCD gets its share whatever the lists hold
+    int nw = 0;
+    for (int gg = 0; gg < a.G; ++gg) nw += (a.gl_cnt[gg] + kWgT - 1) / kWgT;
+    nw *= nq;
+    if ((int)blockIdx.x >= nw) return;
+    const int L = xcd_order(blockIdx.x, nw);
     quad = L % nq;
     int lt = L / nq, c = 0;
     for (; g < a.G; ++g) {
@@ -2330,31 +2344,46 @@ __global__ __launch_bounds__(256) void k_dense16(Dense a) {
 }
 
 // Per group g, its tokens in ascending order (those with an assignment
-// labelled g): one block per group, a ballot and a wave-offset scan per
-// 1024 tokens.
-__global__ __launch_bounds__(1024) void k_group_lists(const int* idx, const uint8_t* labels, int T, int K,
+// labelled g), from the per-chunk group masks of the permutation: one block
+// per group, 1024 chunks of 64 tokens per pass; a block scan of the chunks'
+// popcounts gives each chunk's first position, then wave w writes the tokens
+// of chunks w, w + 16, ... (lane l: token 64 c + l).
+__global__ __launch_bounds__(1024) void k_group_lists(const unsigned long long* gmask, int nchunk, int G,
                                                       int gcap, int* gl_tok, int* gl_cnt) {
+  __shared__ unsigned long long ms[1024];
+  __shared__ int base[1024];
   __shared__ int wsum[16];
-  const int g = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int run = 0;
-  for (int t0 = 0; t0 < T; t0 += 1024) {
-    const int t = t0 + (int)threadIdx.x;
-    bool used = false;
-    if (t < T)
-      for (int k = 0; k < K; ++k) used = used || labels[idx[(size_t)t * K + k]] == g;
-    const unsigned long long m = __ballot(used);
-    if (lane == 0) wsum[w] = __popcll(m);
+  for (int c0 = 0; c0 < nchunk; c0 += 1024) {
+    const int c = c0 + tid;
+    const unsigned long long m = c < nchunk ? gmask[(size_t)c * G + g] : 0ull;
+    const int n = __popcll(m);
+    int v = n;                                        // inclusive scan over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(v, o);
+      if (lane >= o) v += u;
+    }
+    if (lane == 63) wsum[w] = v;
+    ms[tid] = m;
     __syncthreads();
     int off = run, tot = 0;
     for (int i = 0; i < 16; ++i) {
       if (i < w) off += wsum[i];
       tot += wsum[i];
     }
-    if (used) gl_tok[(size_t)g * gcap + off + __popcll(m & ((1ull << lane) - 1ull))] = t;
+    base[tid] = off + v - n;
+    __syncthreads();
+    for (int cc = w; cc < 1024 && c0 + cc < nchunk; cc += 16) {
+      const unsigned long long mm = ms[cc];
+      if ((mm >> lane) & 1ull)
+        gl_tok[(size_t)g * gcap + base[cc] + __popcll(mm & ((1ull << lane) - 1ull))] = (c0 + cc) * 64 + lane;
+    }
     run += tot;
     __syncthreads();
   }
-  if (threadIdx.x == 0) gl_cnt[g] = run;
+  if (tid == 0) gl_cnt[g] = run;
 }
 
 template <int WF, int EPI>
@@ -2436,8 +2465,8 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
   // per-group token lists, then the gathered GEMM; it needs the routing
   const bool routed = h->prefill_d_routed && (size_t)T * H * 2 < (1ull << 31);
   auto routed_d = [&](hipStream_t sd) -> int {
-    hipLaunchKernelGGL(k_group_lists, dim3(G), dim3(1024), 0, sd, p.idx, h->labels, T, K, p.tmax,
-                       p.gl_tok, p.gl_cnt);
+    hipLaunchKernelGGL(k_group_lists, dim3(G), dim3(1024), 0, sd, (const unsigned long long*)p.gmask,
+                       prefill_chunks(T), G, p.tmax, p.gl_tok, p.gl_cnt);
     LMOE_HIP(hipGetLastError());
     Dense a{};
     a.W = WMat{h->dmat16, h->g_d16, 0, 1};
@@ -2534,7 +2563,7 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
   {
     Perm a{};
     a.idx = p.idx; a.T = T; a.K = K; a.E = E; a.G = G; a.nchunk = prefill_chunks(T);
-    a.cmask = p.cmask; a.ccnt = p.ccnt; a.cbase = p.cbase; a.eorder = p.eorder;
+    a.cmask = p.cmask; a.gmask = p.gmask; a.ccnt = p.ccnt; a.cbase = p.cbase; a.eorder = p.eorder;
     a.labels = h->labels; a.seg_start = p.seg_start; a.expert_count = p.expert_count;
     a.group_off = p.group_off; a.pieces = (Piece*)p.pieces; a.npieces = p.npieces;
     a.perm = p.perm; a.inv = p.inv; a.xsc = p.xsc; a.psc = p.psc;

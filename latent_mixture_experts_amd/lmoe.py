@@ -142,7 +142,7 @@ class Layer:
         self.device = device
 
     def set_prefill_d(self, routed_only):
-        """0: prefill D over all groups (default); 1: over the routed pairs only."""
+        """1: prefill D over the routed (token, group) pairs only (default); 0: over all groups."""
         _check(_lib.lmoe_set_prefill_d(self._h, int(routed_only)), "lmoe_set_prefill_d")
 
     def load(self, blobs, stream=None):

@@ -360,7 +360,7 @@ def piece_class_tokens(idx, labels, E, G, T, n_total, seed=1234):
     return np.array(sorted(tokens))
 
 
-def _sampled(name, T, n_sample, seed=0, routed_d=False):
+def _sampled(name, T, n_sample, seed=0, all_groups_d=False):
     w = wl.WORKLOADS[name]
     pre = Case(w, seed=seed, tokens=T, pack_tokens=[0])          # routing of every token
     labels = np.asarray(pre.blobs["labels"])
@@ -369,8 +369,8 @@ def _sampled(name, T, n_sample, seed=0, routed_d=False):
           flush=True)
     c = Case(w, seed=seed, tokens=T, pack_tokens=tokens)
     layer = make_layer(c, T)
-    if routed_d:
-        layer.set_prefill_d(1)
+    if all_groups_d:
+        layer.set_prefill_d(0)
     got, dbg = run(layer, w, c.x)
     check_routing(c, dbg, T)
     check_outputs(c, got, dbg, tokens)
@@ -386,23 +386,24 @@ def test_120b_prefill_q4():
 
 
 # ---------------------------------------------------------------------------
-# D over the routed (token, group) pairs only (lmoe_set_prefill_d(h, 1))
+# D over all groups of every token (lmoe_set_prefill_d(h, 0)); the default,
+# D over the routed (token, group) pairs, runs in every other prefill test
 
-def test_145b_prefill_4096_routed_d():
-    _sampled("145b_prefill", 4096, 16, routed_d=True)
+def test_145b_prefill_4096_all_groups_d():
+    _sampled("145b_prefill", 4096, 16, all_groups_d=True)
 
 
 @pytest.mark.parametrize("T", [9, 64, 300])
-def test_tiny_prefill_routed_d(tiny, T):
+def test_tiny_prefill_all_groups_d(tiny, T):
     c, layer = tiny
-    layer.set_prefill_d(1)
+    layer.set_prefill_d(0)
     try:
-        print("case tiny prefill routed D T", T, flush=True)
+        print("case tiny prefill all-groups D T", T, flush=True)
         got, dbg = run(layer, c.w, c.x[:T])
         check_routing(c, dbg, T)
         check_outputs(c, got, dbg, np.arange(T))
     finally:
-        layer.set_prefill_d(0)
+        layer.set_prefill_d(1)
 
 
 def test_prefill_routed_d_skewed_groups():
@@ -413,6 +414,7 @@ def test_prefill_routed_d_skewed_groups():
     c = Case(w, seed=3, tokens=700)
     layer = make_layer(c, 700)
     print("case skewed groups prefill routed D T 700", flush=True)
+    layer.set_prefill_d(0)
     dense, _ = run(layer, w, c.x)
     layer.set_prefill_d(1)
     got, dbg = run(layer, w, c.x)
