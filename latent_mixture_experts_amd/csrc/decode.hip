@@ -1233,10 +1233,10 @@ __global__ __launch_bounds__(64 * W) void k_phase3(P3 a) {
 // (group g, half h, row tile r) or (shared down block k, row tile r): small
 // blocks, several per CU, so that every item's loads are in flight in one
 // round. Item (g, h) writes partial 2g + h of row tile r, shared down block
-// k partial 2G + k; the last of a row tile's items to finish adds the
-// partials in that order.
+// k partial 2G + k; the partials are added in that order, by k_ysum after
+// the kernel (SUMK) or by the last of a row tile's items to finish.
 
-template <int T, int DU, int W>
+template <int T, int DU, int W, bool SUMK>
 __global__ __launch_bounds__(64 * W) void k_phase4(P4 a) {
   extern __shared__ __align__(16) char smem[];
   __shared__ int flag;
@@ -1299,10 +1299,14 @@ __global__ __launch_bounds__(64 * W) void k_phase4(P4 a) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int t = 4 * (lane >> 4) + v;
-        if (t < T)
-          st_co(a.ws.ypart + ((size_t)part * T + t) * d.H + r * 64 + rg * 16 + (lane & 15), acc[rg][v]);
+        if (t < T) {
+          float* q = a.ws.ypart + ((size_t)part * T + t) * d.H + r * 64 + rg * 16 + (lane & 15);
+          if constexpr (SUMK) *q = acc[rg][v];
+          else st_co(q, acc[rg][v]);
+        }
       }
   }
+  if constexpr (SUMK) return;                        // k_ysum adds the partials
   const int np = 2 * d.G + a.nsb;
   if (!arrive_last(a.ws.ctr_y + r, (unsigned)np, &flag)) return;
   // Ordered sum of the partials: wave w fetches parts w, w + nw, ..., up to
@@ -1344,6 +1348,34 @@ __global__ __launch_bounds__(64 * W) void k_phase4(P4 a) {
   }
 }
 
+// The ordered sum of phase 4's partials as a kernel of its own: block r
+// takes row tile r, thread (t, lane) row 64 r + lane of token t, all its
+// partials' loads in flight, added in part order (used groups only).
+template <int T>
+__global__ __launch_bounds__(512) void k_ysum(P4 a) {
+  const Dims& d = a.d;
+  const int r = blockIdx.x, lane = threadIdx.x & 63, t = threadIdx.x >> 6;
+  if (t >= T) return;
+  ci_t gso = ci(a.ws.gslot_off);
+  const int np = 2 * d.G + a.nsb, row = r * 64 + lane;
+  float y = 0.f;
+  for (int p0 = 0; p0 < np; p0 += 8) {
+    float v[8];
+    bool use[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int p = p0 + k;
+      use[k] = p < np && (p >= 2 * d.G || gso[p / 2 + 1] > gso[p / 2]);
+      v[k] = use[k] ? a.ws.ypart[((size_t)p * T + t) * d.H + row] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (use[k]) y += v[k];
+  }
+  float* dst = a.y + (size_t)t * d.H + row;
+  *dst = a.accumulate ? *dst + y : y;
+}
+
 // 1/sqrt(mean(x^2) + eps) per row, fp64 sum.
 __global__ void k_rms(const float* __restrict__ x, int H, float eps, float* __restrict__ out,
                       double* __restrict__ out64) {
@@ -1382,6 +1414,14 @@ int resident_blocks(lmoe_t* h, const void* kernel, int threads, size_t lds) {
 
 // only: 0 launches every phase, k in 1..4 phase k alone (its inputs are in
 // the workspace from an earlier forward of T tokens)
+// Phase 4's ordered sum: from four tokens on, a kernel of its own after
+// phase 4 (no store-completion waits, arrival counters or coherent loads:
+// 145B T 4 phase 4 18.1 -> 17.0 us, 120B T 5 17.9 -> 15.8); for fewer
+// tokens the last-arriving block of each row tile (MTP T 1: 11.7 against
+// 12.5 us as a kernel).
+template <int T>
+constexpr bool ysum_kernel() { return T >= 4; }
+
 template <int T, int DU>
 int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st, int only,
                const Workspace& ws) {
@@ -1487,10 +1527,17 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st, i
   if (only == 0 || only == 4) {
     // blocks of up to eight waves compiled for 512 threads: 4-wave bounds
     // let the compiler spend AGPRs and drop to three waves per SIMD
-    if (nw4 <= 8)
-      hipLaunchKernelGGL((k_phase4<T, DU, 8>), dim3(grid4), dim3(nw4 * 64), sm4, st, p4);
-    else
-      hipLaunchKernelGGL((k_phase4<T, DU, 16>), dim3(grid4), dim3(nw4 * 64), sm4, st, p4);
+    if (ysum_kernel<T>()) {
+      if (nw4 <= 8)
+        hipLaunchKernelGGL((k_phase4<T, DU, 8, true>), dim3(grid4), dim3(nw4 * 64), sm4, st, p4);
+      else
+        hipLaunchKernelGGL((k_phase4<T, DU, 16, true>), dim3(grid4), dim3(nw4 * 64), sm4, st, p4);
+      hipLaunchKernelGGL((k_ysum<T>), dim3(h->g_u.tiles), dim3(64 * T), 0, st, p4);
+    } else if (nw4 <= 8) {
+      hipLaunchKernelGGL((k_phase4<T, DU, 8, false>), dim3(grid4), dim3(nw4 * 64), sm4, st, p4);
+    } else {
+      hipLaunchKernelGGL((k_phase4<T, DU, 16, false>), dim3(grid4), dim3(nw4 * 64), sm4, st, p4);
+    }
   }
   LMOE_HIP(hipGetLastError());
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[4], st));
