@@ -119,6 +119,7 @@ size_t decode_ws_layout(const lmoe_t* h, int T, char* base, Workspace* out) {
   take(w.expert_count, sizeof(int) * E);
   take(w.rms, sizeof(float) * T);
   take(w.rms64, sizeof(double) * T);
+  take(w.sqp, sizeof(double) * w.nch * T);
   take(w.xl, sizeof(float) * T * G * L);
   take(w.hs, sizeof(float) * T * Fs);
   take(w.hsp, sizeof(float) * nss_s * T * 2 * Fs);
@@ -457,7 +458,7 @@ int lmoe_forward_block(lmoe_t* h, float* x, int32_t T, float eps, void* stream) 
   DeviceGuard g(h->device);
   hipStream_t st = (hipStream_t)stream;
   if (T > kMaxDecodeT) return forward_prefill(h, x, T, x, true, eps, st);
-  if (int rc = rms_rows(h, x, T, eps, st)) return rc;
+  h->rms_eps = eps;                                // phase 1 normalizes the rows itself
   h->last_decode_T = 0;                            // the decode workspace now holds a block forward
   return forward_decode(h, x, T, x, true, st);
 }

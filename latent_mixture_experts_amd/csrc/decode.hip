@@ -614,8 +614,9 @@ struct Dims {
 struct P1 {
   Dims d;
   const float* x;          // [T][H]
-  const float* rms;        // [T] or null: multiply dot products by rms[t]
-  const double* rms64;     // [T] the same in fp64 (router logits)
+  float* rms;              // [T] or null (plain forward): block forward, 1/rms of
+  double* rms64;           // each row, written by the routing for phase 2
+  float eps;               // RMSNorm eps (block forward)
   const uint8_t* router; Geom gr;
   const float* bias;
   const uint8_t* labels;
@@ -657,6 +658,13 @@ struct P4 {
 // ---------------------------------------------------------------------------
 // Routing, done by the last router block.
 
+// Sum of a double over the wavefront (butterfly: every lane gets it).
+__device__ __forceinline__ double wave_sum64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
 // LDS of the routing block: logits [T][Epad] (fp64, -inf past E), per-wave
 // top-K scratch,
 // then per assignment (at least 64 entries) key, sorted order, inverse,
@@ -688,6 +696,20 @@ __device__ void routing(const P1& a, char* smem) {
   int* elab = ecnt + d.E;          // [E] group label of each expert
   int* nslot = elab + d.E;         // [1]
 
+  // block forward: 1/rms of each row from the router chunks' sums of x^2
+  // (added in chunk order, fp64), kept for the logits and written for phase 2
+  __shared__ double rr[kMaxDecodeT];
+  if (a.rms) {
+    if (tid < T) {
+      double q = 0.0;
+      for (int c = 0; c < a.nch; ++c) q += ld_co(ws.sqp + (size_t)c * T + tid);
+      const double r = 1.0 / sqrt(q / d.H + (double)a.eps);
+      rr[tid] = r;
+      a.rms64[tid] = r;
+      a.rms[tid] = (float)r;
+    }
+    __syncthreads();
+  }
   // logits = the chunk partials summed in chunk order (scaled by 1/rms in the
   // block forward) + bias; the labels come in with the token-0 entries.
   // Every thread issues all its loads before summing.
@@ -714,7 +736,7 @@ __device__ void routing(const P1& a, char* smem) {
           double l = 0.0;
 #pragma unroll
           for (int c = 0; c < kRouterChunks; ++c) l += part[u][c];
-          if (a.rms) l *= a.rms64[t];
+          if (a.rms) l *= rr[t];
           lg[t * Epad + e] = l + (double)a.bias[e];
           if (t == 0) elab[e] = lab[u];
         }
@@ -982,6 +1004,27 @@ __global__ __launch_bounds__(64 * W) void k_phase1(P1 a) {
       for (int t = 0; t < T; ++t)
         st_co(a.ws.part64 + ((size_t)c * T + t) * Epad + r * 64 + lane, acc[t]);
     }
+    if (a.rms && r == 0) {
+      // block forward: sum of x^2 over this chunk's columns (one a thread),
+      // per token, fp64, for the routing's 1/rms
+      __shared__ double sqw[16][kMaxDecodeT];
+      const int col = c * a.cw + (int)threadIdx.x;
+      double q[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const double v = (int)threadIdx.x < a.cw && col < d.H ? (double)a.x[(size_t)t * d.H + col] : 0.0;
+        q[t] = wave_sum64(v * v);
+      }
+      if (lane == 0)
+#pragma unroll
+        for (int t = 0; t < T; ++t) sqw[wave][t] = q[t];
+      __syncthreads();
+      if ((int)threadIdx.x < T) {
+        double sq = 0.0;
+        for (int w = 0; w < nw; ++w) sq += sqw[w][threadIdx.x];
+        st_co(a.ws.sqp + (size_t)c * T + threadIdx.x, sq);
+      }
+    }
     if (arrive_last(a.ws.ctr_router, (unsigned)a.nrb, &flag)) routing<T>(a, smem);
     return;
   }
@@ -1002,7 +1045,33 @@ __global__ __launch_bounds__(64 * W) void k_phase1(P1 a) {
     if (wave < a.gd.nss)
       wave_ss<DU, T>(ss_ptr(a.dmat + (size_t)g * a.gd.bytes(), a.gd, r, wave),
                      ss_codes(DU, a.gd, wave), ss_cols(a.gd, wave), src, T, xs, lane, acc);
+    // block forward: the block's waves cover every column (wave w: super-step
+    // w), so the block forms each row's sum of x^2 itself (fp64)
+    __shared__ double sqd[16][kMaxDecodeT];
+    if (a.rms) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        double q = 0.0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = wave * kSSCols + 4 * lane + j;
+          const double v = col < d.H ? (double)a.x[(size_t)t * d.H + col] : 0.0;
+          q += v * v;
+        }
+        q = wave_sum64(q);
+        if (lane == 0) sqd[wave][t] = q;
+      }
+    }
     if (block_reduce_mf<T>(acc, red, wave, lane, nw)) {
+      float rt[T];
+      if (a.rms) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          double q = 0.0;
+          for (int w = 0; w < nw; ++w) q += sqd[w][t];
+          rt[t] = (float)(1.0 / sqrt(q / d.H + (double)a.eps));
+        }
+      }
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg)
 #pragma unroll
@@ -1010,7 +1079,7 @@ __global__ __launch_bounds__(64 * W) void k_phase1(P1 a) {
           const int t = 4 * (lane >> 4) + v;
           if (t < T) {
             float y = acc[rg][v];
-            if (a.rms) y *= a.rms[t];
+            if (a.rms) y *= rt[t];
             a.ws.xl[((size_t)t * d.G + g) * d.L + r * 64 + rg * 16 + (lane & 15)] = y;
           }
         }
@@ -1376,26 +1445,6 @@ __global__ __launch_bounds__(512) void k_ysum(P4 a) {
   *dst = a.accumulate ? *dst + y : y;
 }
 
-// 1/sqrt(mean(x^2) + eps) per row, fp64 sum.
-__global__ void k_rms(const float* __restrict__ x, int H, float eps, float* __restrict__ out,
-                      double* __restrict__ out64) {
-  const int t = blockIdx.x;
-  double s = 0.0;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) {
-    double v = x[(size_t)t * H + i];
-    s += v * v;
-  }
-  __shared__ double red[1024];
-  red[threadIdx.x] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double z = 0.0;
-    for (int i = 0; i < (int)blockDim.x; ++i) z += red[i];
-    const double r = 1.0 / sqrt(z / H + (double)eps);
-    out[t] = (float)r;
-    out64[t] = r;
-  }
-}
 
 
 // Blocks of `kernel` the device holds at once with `threads` threads and
@@ -1437,6 +1486,7 @@ int launch_all(lmoe_t* h, const float* x, float* y, bool norm, hipStream_t st, i
   p1.x = x;
   p1.rms = norm ? ws.rms : nullptr;
   p1.rms64 = norm ? ws.rms64 : nullptr;
+  p1.eps = h->rms_eps;
   p1.router = h->router; p1.gr = h->g_router;
   p1.bias = h->bias;
   p1.labels = h->labels;
@@ -1584,12 +1634,6 @@ size_t decode_lds_bytes(const lmoe_dims& d, int T) {
   }
 }
 
-int rms_rows(lmoe_t* h, const float* x, int T, float eps, hipStream_t st) {
-  hipLaunchKernelGGL(k_rms, dim3(T), dim3(256), 0, st, x, h->d.hidden, eps, h->ws.rms,
-                     h->ws.rms64);
-  LMOE_HIP(hipGetLastError());
-  return 0;
-}
 
 int forward_decode(lmoe_t* h, const float* x, int T, float* y, bool norm, hipStream_t st, int only,
                    const Workspace* ws) {

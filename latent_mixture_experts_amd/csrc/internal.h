@@ -126,6 +126,7 @@ struct Workspace {
   int* expert_count = nullptr;   // [E]
   float* rms = nullptr;          // [T] 1/rms of the input rows (block forward)
   double* rms64 = nullptr;       // [T] the same in fp64, for the router logits
+  double* sqp = nullptr;         // [nch][T] sums of x^2 over the router's column chunks
   float* xl = nullptr;           // [T][G][ell]
   float* hs = nullptr;           // [T][Fs] shared-expert hidden
   float* hsp = nullptr;          // [H/256][T][2 Fs] shared gate/up partials per super-step
@@ -212,6 +213,7 @@ struct lmoe {
   std::vector<void*> allocations;
   std::vector<hipEvent_t> phase_events;   // empty: no phase timing
   int last_decode_T = 0;                  // T of the last plain decode forward (0: none)
+  float rms_eps = 0.f;                    // eps of the block forward being launched
   // blocks of a kernel resident at once, by (kernel, threads, LDS bytes)
   struct Resident { const void* kernel; int threads; size_t lds; int blocks; };
   std::vector<Resident> resident;
@@ -232,7 +234,6 @@ int pack_experts_impl(const float* gate, const float* up, const float* down, int
 // ws: the workspace to run on (nullptr: the handle's)
 int forward_decode(lmoe_t* h, const float* x, int T, float* y, bool norm, hipStream_t stream,
                    int only = 0, const Workspace* ws = nullptr);
-int rms_rows(lmoe_t* h, const float* x, int T, float eps, hipStream_t stream);
 // Largest dynamic LDS a decode kernel needs for T tokens (a handle whose
 // decode path would need more than a CU has is refused at create).
 size_t decode_lds_bytes(const lmoe_dims& d, int T);
