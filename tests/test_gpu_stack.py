@@ -66,6 +66,13 @@ def test_tiny_stack_8_layers():
         run_stack(w, 8, T)
 
 
+@pytest.mark.parametrize("T", [1, 2, 5, 8])
+def test_tiny_stack_block_t(T):
+    """Three block forwards at the other decode token counts (the 1/rms is
+    formed inside the decode kernels for every T)."""
+    run_stack(wl.WORKLOADS["tiny"], 3, T, seed=T)
+
+
 def test_145b_stack_2_layers():
     w = wl.WORKLOADS["145b_stack"]
     run_stack(w, 2, w.tokens)
