@@ -80,8 +80,12 @@ extern "C" {
  *                       high-bit mask, low bits, 12 bytes of 6-bit sub-block scales,
  *                       fp16 d), then down blocks [latent][F/32] (GGML IQ4_NL, 18
  *                       bytes a 32-weight block: fp16 d, 16 bytes of table
- *                       indices); 1,630,720 bytes at latent 1792, F 640. Decode
- *                       path only (max_tokens <= 8), latent % 256 == 0. */
+ *                       indices); 1,630,720 bytes at latent 1792, F 640.
+ *                       latent % 256 == 0. Batches of T > 8 run as decode
+ *                       forwards of 8 tokens each (no prefill workspace is
+ *                       allocated); their lmoe_debug perm, expert_count,
+ *                       expert_off and group_off are refused
+ *                       (LMOE_EUNSUPPORTED). */
 #define LMOE_EXPERTS_NVFP4 0
 #define LMOE_EXPERTS_Q3K   1
 
@@ -130,9 +134,9 @@ typedef struct lmoe_debug {
                               over e' < e, expert_off[E] = T*K */
   int32_t* group_off;      /* [G+1] start of each group's segment in perm */
   float*   latent;         /* [T][G][ell] D_g x; entries of (t, g) pairs that
-                              token t does not use are unspecified. For
-                              T > 8 these are the fp16 values the experts
-                              read, widened to fp32 */
+                              token t does not use are unspecified. On the
+                              prefill path (T > 8, NVFP4 records) these are
+                              the fp16 values the experts read, widened */
 } lmoe_debug;
 
 typedef struct lmoe lmoe_t;
@@ -142,7 +146,7 @@ typedef struct lmoe lmoe_t;
  * Two paths serve a forward: T <= 8 tokens run the decode path (weights
  * streamed once per call through a GEMV on matrix cores); T > 8 the prefill
  * path (MFMA GEMMs over the sorted assignments). The prefill workspace
- * exists only when max_tokens > 8; it takes about
+ * exists only when max_tokens > 8 (and the records are NVFP4); it takes about
  *   T * (6H + 4 Epad + 8 G ell + K (2F + 4 ell + 48) + 4 Fs) bytes
  * for T = max_tokens (Epad = E rounded up to 64), e.g. 0.68 GB at T 4096
  * for the 145B shapes, plus a bf16 copy of the router in two layouts. */

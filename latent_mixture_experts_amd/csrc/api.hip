@@ -41,8 +41,6 @@ int check_dims(const lmoe_dims& d) {
     return bad("expert_format must be LMOE_EXPERTS_NVFP4 or LMOE_EXPERTS_Q3K");
   if (d.expert_format == LMOE_EXPERTS_Q3K && d.latent % 256)
     return unsup("Q3_K experts need latent % 256 == 0 (one super-block per 256 columns)");
-  if (d.expert_format == LMOE_EXPERTS_Q3K && d.max_tokens > kMaxDecodeT)
-    return unsup("Q3_K experts run on the decode path only (max_tokens <= 8)");
   if (d.hidden % 256) return unsup("hidden must be a multiple of 256");
   if (d.latent % 64) return unsup("latent must be a multiple of 64");
   if (d.expert_ffn % 32 || d.shared_ffn % 32) return unsup("expert_ffn and shared_ffn must be multiples of 32");
@@ -171,8 +169,9 @@ int create_impl(lmoe_t* h) {
     decode_ws_layout(h, T, base, &h->ws);
   }
 
-  // prefill path (T > kMaxDecodeT): router copies and GEMM workspace
-  if (d.max_tokens > kMaxDecodeT) {
+  // prefill path (T > kMaxDecodeT): router copies and GEMM workspace (NVFP4
+  // records; Q3_K records run larger batches as decode forwards of 8 tokens)
+  if (d.max_tokens > kMaxDecodeT && !q3k) {
     PrefillWs& p = h->pw;
     const size_t Tp = (size_t)d.max_tokens, nk = Tp * K;
     const size_t nchunk = (size_t)prefill_chunks(d.max_tokens);
@@ -396,6 +395,34 @@ int lmoe_load_weights(lmoe_t* h, const lmoe_weights* w, void* stream) {
   return load_weights_impl(h, w, (hipStream_t)stream);
 }
 
+// Q3_K records, T > 8: decode forwards of up to 8 tokens each (every output
+// row depends on its own input row only); the debug outputs that describe
+// the whole batch's permutation are refused.
+static int forward_chunked(lmoe_t* h, const float* x, int T, float* y, bool norm, float eps,
+                           const lmoe_debug* dbg, hipStream_t st) {
+  if (dbg && (dbg->perm || dbg->expert_count || dbg->expert_off || dbg->group_off)) {
+    set_error("Q3_K records, T > 8: perm, expert_count, expert_off and group_off are not produced "
+              "(the batch runs as decode forwards of 8 tokens)");
+    return LMOE_EUNSUPPORTED;
+  }
+  const lmoe_dims& d = h->d;
+  const size_t H = d.hidden, K = d.top_k, GL = (size_t)d.n_groups * d.latent;
+  const auto D2D = hipMemcpyDeviceToDevice;
+  h->rms_eps = eps;
+  for (int t0 = 0; t0 < T; t0 += kMaxDecodeT) {
+    const int n = T - t0 < kMaxDecodeT ? T - t0 : kMaxDecodeT;
+    if (int rc = forward_decode(h, x + t0 * H, n, y + t0 * H, norm, st)) return rc;
+    if (dbg && dbg->topk_idx)
+      LMOE_HIP(hipMemcpyAsync(dbg->topk_idx + t0 * K, h->ws.topk_idx, 4 * n * K, D2D, st));
+    if (dbg && dbg->topk_w)
+      LMOE_HIP(hipMemcpyAsync(dbg->topk_w + t0 * K, h->ws.topk_w, 4 * n * K, D2D, st));
+    if (dbg && dbg->latent)
+      LMOE_HIP(hipMemcpyAsync(dbg->latent + t0 * GL, h->ws.xl, 4 * n * GL, D2D, st));
+  }
+  h->last_decode_T = 0;                            // the workspace holds the last chunk only
+  return 0;
+}
+
 int lmoe_forward(lmoe_t* h, const float* x, int32_t T, float* y, const lmoe_debug* dbg,
                  void* stream) {
   if (int rc = check_forward(h, x, T, y)) return rc;
@@ -405,6 +432,8 @@ int lmoe_forward(lmoe_t* h, const float* x, int32_t T, float* y, const lmoe_debu
   }
   DeviceGuard g(h->device);
   hipStream_t st = (hipStream_t)stream;
+  if (T > kMaxDecodeT && h->d.expert_format == LMOE_EXPERTS_Q3K)
+    return forward_chunked(h, x, T, y, false, 0.0f, dbg, st);
   const int rc = T > kMaxDecodeT ? forward_prefill(h, x, T, y, false, 0.0f, st)
                                  : forward_decode(h, x, T, y, false, st);
   if (rc) return rc;
@@ -457,6 +486,8 @@ int lmoe_forward_block(lmoe_t* h, float* x, int32_t T, float eps, void* stream) 
   }
   DeviceGuard g(h->device);
   hipStream_t st = (hipStream_t)stream;
+  if (T > kMaxDecodeT && h->d.expert_format == LMOE_EXPERTS_Q3K)
+    return forward_chunked(h, x, T, x, true, eps, nullptr, st);
   if (T > kMaxDecodeT) return forward_prefill(h, x, T, x, true, eps, st);
   h->rms_eps = eps;                                // phase 1 normalizes the rows itself
   h->last_decode_T = 0;                            // the decode workspace now holds a block forward

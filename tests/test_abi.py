@@ -101,15 +101,13 @@ def test_ple_gather_argument_checks_on_host(lib):
 
 def test_q3k_record_sizes_and_refusals(lib):
     """The Q3_K record sizes the pages print, and the shapes lmoe_create
-    refuses for Q3_K experts (a latent not a multiple of 256, the prefill
-    path)."""
+    refuses for Q3_K experts (a latent not a multiple of 256)."""
     from latent_mixture_experts_amd import lmoe
     assert lmoe.expert_record_bytes(1792, 640, 1) == 1630720
     assert lmoe.expert_record_bytes(1280, 640, 1) == 1164800
     assert lmoe.expert_record_bytes(1792, 640, 0) == lmoe.expert_record_bytes(1792, 640)
     assert lmoe.expert_record_bytes(1792, 640, 7) == 0
-    for kw, code in ((dict(latent=128), lmoe.EUNSUPPORTED), (dict(max_tokens=16), lmoe.EUNSUPPORTED),
-                     (dict(expert_format=2), lmoe.EINVAL)):
+    for kw, code in ((dict(latent=128), lmoe.EUNSUPPORTED), (dict(expert_format=2), lmoe.EINVAL)):
         a = dict(hidden=256, latent=256, n_experts=16, top_k=2, n_groups=2, expert_ffn=64,
                  shared_ffn=64, du_bits=8, max_tokens=4, has_router_bias=0, expert_format=1)
         a.update(kw)

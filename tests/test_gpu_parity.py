@@ -172,6 +172,38 @@ def test_120b_q3k_decode():
     check(c, layer, 5, "120b q3k")
 
 
+def test_q3k_batches_above_8_tokens():
+    """Q3_K records, T = 20 and 12: the batch runs as decode forwards of 8
+    tokens each; every token's routing, weights, latent and output against
+    the oracle, and the whole-batch debug outputs refused."""
+    from latent_mixture_experts_amd import lmoe
+    c = Case(Q3K_TINY, seed=5, tokens=20)
+    layer = make_layer(c, 20)
+    for T in (20, 12):
+        print("case q3k tiny chunked T", T, flush=True)
+        dev = "cuda"
+        x = torch.from_numpy(np.ascontiguousarray(c.x[:T])).to(dev)
+        y = torch.empty(T, c.w.hidden, device=dev)
+        dbg = dict(topk_idx=torch.empty(T, c.w.top_k, dtype=torch.int32, device=dev),
+                   topk_w=torch.empty(T, c.w.top_k, dtype=torch.float32, device=dev),
+                   latent=torch.full((T, c.w.n_groups, c.w.latent), float("nan"), device=dev))
+        layer.forward(x, y, debug=dbg)
+        torch.cuda.synchronize()
+        r = c.expect(T)
+        assert np.array_equal(dbg["topk_idx"].cpu().numpy(), r["idx"])
+        assert np.max(np.abs(dbg["topk_w"].cpu().numpy() - r["w"])) <= 1e-6
+        used = r["used"]
+        rel, _ = rel_errors(dbg["latent"].cpu().numpy()[used], r["xl"][used])
+        assert rel <= 1e-5, rel
+        got = y.cpu().numpy()
+        assert_close(got, r["y"], "y")
+        rel_r, _ = rel_errors(got - r["y_shared"], r["y_routed"])
+        assert rel_r <= 1e-4, rel_r
+    with pytest.raises(lmoe.LmoeError):
+        layer.forward(x, y, debug=dict(perm=torch.empty(12 * c.w.top_k, dtype=torch.int32, device="cuda")))
+    layer.close()
+
+
 def test_q3k_decode_activation_range():
     """Rows at 1e-3, 1e2, 1e-6 with every seventh element near 1e5, and 3e3
     through the Q3_K / IQ4_NL decoders (the token scales are undone on the
