@@ -560,6 +560,13 @@ __device__ __forceinline__ void tile_of(int L, int mtiles, int nquads, int& mt, 
   quad = (L % span) / gsz;
 }
 
+// the inverse: logical tile of (token tile mt, weight quad quad)
+__device__ __forceinline__ int tile_index(int mt, int quad, int mtiles, int nquads) {
+  constexpr int GM = 8;
+  const int first = (mt / GM) * GM, gsz = min(mtiles - first, GM);
+  return (mt / GM) * GM * nquads + quad * gsz + (mt - first);
+}
+
 // ---------------------------------------------------------------------------
 // LDS DMA.
 
@@ -2194,12 +2201,16 @@ __global__ __launch_bounds__(256) void k_dense16(Dense a) {
   __shared__ __align__(1024) uint8_t smem[kWgBuf * kWgStage];
   __shared__ int toks[GATHER ? kWgT : 1];
   const int nq = (a.ntiles + 3) / 4;
-  int mt, quad, g = 0, nrows;
+  int mt, quad, g = 0, nrows, sp = 0;
+  const int nsp = EPI == kEpiY ? a.nsplit : 1;
   const uint8_t* wbase = a.W.base;
   if constexpr (!GATHER) {
-    const int mtl = (a.T + kWgT - 1) / kWgT;
-    const int L = xcd_order(blockIdx.x, mtl * nq);
-    tile_of(L, mtl, nq, mt, quad);
+    // kEpiY: split sp of the stages (the slowest index, so that the tiles
+    // of one split that share rows sit together on an XCD)
+    const int mtl = (a.T + kWgT - 1) / kWgT, ntl = mtl * nq;
+    const int L0 = xcd_order(blockIdx.x, ntl * nsp);
+    sp = L0 / ntl;
+    tile_of(L0 % ntl, mtl, nq, mt, quad);
     nrows = min(kWgT, a.T - mt * kWgT);
   } else {
     // the grid is an upper bound; the work items (256-token tiles of the
@@ -2227,7 +2238,10 @@ __global__ __launch_bounds__(256) void k_dense16(Dense a) {
     __syncthreads();
   }
   const int lane = threadIdx.x & 63, wave = wave_id(), wm = wave & 1, wn = wave >> 1;
-  const int kmat = a.A.kmat, nst = kmat / kWgCols;
+  // stages: 32 columns of W's nmat matrices one after another (their
+  // activation columns contiguous), this block's share [st0, st1)
+  const int spm = a.A.kmat / kWgCols, nst = spm * a.W.nmat;
+  const int st0 = (int)((long long)nst * sp / nsp), st1 = (int)((long long)nst * (sp + 1) / nsp);
   // activation DMA: wave w stages rows 16 i .. + 15 for i = w + 4 j; lane l
   // the piece at position l % 4 of row 16 i + l / 4, which holds column
   // piece (l % 4) ^ ((row / 2) % 4). Rows past the tile's last read zeros.
@@ -2245,13 +2259,15 @@ __global__ __launch_bounds__(256) void k_dense16(Dense a) {
   }
   // weight DMA: wave w copies the 4 slots of stage s of tile 4 quad + w
   const int wt = 4 * quad + wave;
+  const size_t wspan = (size_t)(a.W.nmat - 1) * a.W.mat_bytes + (size_t)a.W.g.tile_slots * kSlot;
   const rsrc_t br = rsrc(wbase + (size_t)min(wt, a.ntiles - 1) * a.W.g.tile_slots * kSlot,
-                         wt < a.ntiles ? (uint32_t)(a.W.g.tile_slots * kSlot) : 0u);
+                         wt < a.ntiles ? (uint32_t)wspan : 0u);
   const uint32_t sbase = lds_off(smem);
   const auto issue = [&](int s) {
     const int b = s & (kWgBuf - 1);
-    const bool live = s < nst;
-    const uint32_t col = (uint32_t)(min(s, nst - 1) * kWgCols * 2);
+    const bool live = s < st1;
+    const int sc = min(s, st1 - 1), mat = sc / spm, sm = sc % spm;
+    const uint32_t col = (uint32_t)(sc * kWgCols * 2);
     const uint32_t st = sbase + b * kWgStage;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -2259,7 +2275,7 @@ __global__ __launch_bounds__(256) void k_dense16(Dense a) {
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg)
       dma16(live ? br : rsrc(a.W.base, 0u), st + kWgA + (wave * 4 + rg) * 1024, lane * 16,
-            (uint32_t)((4 * min(s, nst - 1) + rg) * kSlot));
+            (uint32_t)((size_t)mat * a.W.mat_bytes + (size_t)(4 * sm + rg) * kSlot));
   };
   f16v acc[4][4];
 #pragma unroll
@@ -2294,13 +2310,13 @@ __global__ __launch_bounds__(256) void k_dense16(Dense a) {
         acc[mb][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, af[mb]),
                                                             __builtin_bit_cast(half8, bf[j]), acc[mb][j], 0, 0, 0);
   };
-  issue(0);
-  issue(1);
-  issue(2);
-  __builtin_amdgcn_s_waitcnt(vmcnt_wait(16));             // this wave's stage 0
+  issue(st0);
+  issue(st0 + 1);
+  issue(st0 + 2);
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(16));             // this wave's first stage
   __syncthreads();
   uint4 a0[4], b0[4], a1[4], b1[4];
-  frags(0, 0, a0, b0);
+  frags(st0, 0, a0, b0);
   // stage s: second k-step's fragments read under the first's MFMAs; then
   // the wait for this wave's DMAs of stage s + 1 (those of s + 2, 8, may
   // stay in flight) and the barrier that makes every wave's visible and
@@ -2309,7 +2325,7 @@ __global__ __launch_bounds__(256) void k_dense16(Dense a) {
   // MFMAs (past the last stage they read a buffer of zeros, unused)
   // (scheduling barriers keep this order: the compiler would otherwise read
   // each fragment just before its MFMA and expose the LDS latency)
-  for (int s = 0; s < nst; ++s) {
+  for (int s = st0; s < st1; ++s) {
     frags(s, 1, a1, b1);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(a0, b0);
@@ -2333,12 +2349,27 @@ __global__ __launch_bounds__(256) void k_dense16(Dense a) {
       if (r >= nrows) continue;
       const size_t orow = GATHER ? (size_t)toks[r] * a.ostride + (size_t)g * a.gL
                                  : (size_t)(mt * kWgT + r) * a.ostride;
+      const int t = mt * kWgT + r;
+      // kEpiY: the 128-token half of the tile that holds row r, as a tile of
+      // the kEpiY partial layout (BM tokens x 256 columns)
+      const int L128 = EPI == kEpiY ? tile_index(2 * mt + wm, quad, a.mtiles, a.nquads) : 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int tile = 4 * quad + 2 * wn + (j >> 1);
         if (tile >= a.ntiles) continue;
         const int n = 64 * tile + 32 * (j & 1) + (lane & 31);
-        if constexpr (EPI == kEpiF16) ((_Float16*)a.out)[orow + n] = (_Float16)acc[mb][j][v];
+        if constexpr (EPI == kEpiF16) {
+          ((_Float16*)a.out)[orow + n] = (_Float16)acc[mb][j][v];
+        } else if constexpr (EPI == kEpiY) {
+          if (nsp > 1) {
+            const size_t jj = (size_t)sp * a.nrem + L128;
+            a.part[(jj * BM + (t - (2 * mt + wm) * BM)) * 256 + (n - 256 * quad)] = acc[mb][j][v];
+          } else {
+            // y holds the shared down projection and the residual already
+            const float ic = inv_pow2(a.xsc[t]);
+            ((float*)a.out)[orow + n] += acc[mb][j][v] * ic * ic;
+          }
+        }
       }
     }
 }
@@ -2482,6 +2513,21 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     if (ev) LMOE_HIP(hipEventRecord(h->phase_events[3], sd));
     return 0;
   };
+  // the shared down projection straight into y, with the token's range
+  // unscaling and the residual: y = c^-2 (Sd h) (+ x); U is added later. It
+  // follows the shared gate/up on that stream, unless phases are timed or y
+  // is x (the block forward in place: the routing still reads x), then it
+  // opens the U phase.
+  const bool early_sd = !ev && y != x;
+  auto shared_down = [&](hipStream_t sd) -> int {
+    Dense a{};
+    a.W = WMat{h->sdn, h->g_sdn, 0, 1};
+    a.A = AMat{p.hsb, (size_t)2 * Fs, Fs, Fs};
+    a.T = T; a.mtiles = mtiles; a.ntiles = h->g_sdn.tiles; a.nquads = (a.ntiles + NTW - 1) / NTW;
+    a.out = y; a.ostride = H; a.nvalid = H; a.res = norm ? x : nullptr; a.xsc = p.xsc;
+    a.nsplit = 1; a.nfull = mtiles * a.nquads; a.nrem = 0;
+    return launch_dense<kBF16, kEpiY>(a, sd);
+  };
   auto dense_front = [&](hipStream_t sd, bool d_part, bool s_part) -> int {
     if (d_part) {
       Dense a{};
@@ -2501,6 +2547,8 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
       a.xsc = p.xsc;
       if (int rc = launch_dense<kBF16, kEpiSwigluB2>(a, sd)) return rc;
       if (ev) LMOE_HIP(hipEventRecord(h->phase_events[4], sd));
+      else if (early_sd)
+        if (int rc = shared_down(sd)) return rc;
     }
     return 0;
   };
@@ -2619,47 +2667,46 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     LMOE_HIP(hipGetLastError());
   }
   if (ev) LMOE_HIP(hipEventRecord(h->phase_events[7], st));
-  // U over the concatenated groups, then the shared down projection
+  // U over the concatenated groups on k_dense16, split along k; the splits'
+  // partial sums (in the dead expert-output buffer) are added onto y, which
+  // holds the shared down projection and the residual already
   {
+    if (!early_sd)
+      if (int rc = shared_down(st)) return rc;
     Dense a{};
     a.W = WMat{h->umat16, h->g_u16, h->g_u16.bytes(), G};
     a.A = AMat{p.s, (size_t)G * L, 0, L};
-    a.W2 = WMat{h->sdn, h->g_sdn, 0, 1};
-    a.A2 = AMat{p.hsb, (size_t)2 * Fs, Fs, Fs};
-    a.T = T; a.mtiles = mtiles; a.ntiles = h->g_u16.tiles; a.nquads = (a.ntiles + NTW - 1) / NTW;
-    a.out = y; a.ostride = H; a.nvalid = H; a.res = norm ? x : nullptr; a.xsc = p.xsc;
-    // One block per CU at a time. Every tile is split along k into ns
-    // blocks, ns minimising rounds of the chip per split plus a small charge
-    // per split for writing and re-reading its partial sums (as many as the
-    // expert outputs' buffer, dead once combined, holds). Splitting every
-    // tile (rather than only those of a last, partial round) also evens out
-    // the blocks' run times, which memory contention spreads.
-    const int nblk0 = mtiles * a.nquads;
-    const size_t cap = (size_t)p.tmax * K * L / ((size_t)nblk0 * BM * 256);
+    a.T = T; a.mtiles = mtiles; a.ntiles = h->g_u16.tiles; a.nquads = (a.ntiles + 3) / 4;
+    a.out = y; a.ostride = H; a.nvalid = H; a.xsc = p.xsc;
+    // one 256 x 256 workgroup per CU at a time: the split minimising rounds
+    // of the chip per split plus a small charge per split for writing and
+    // re-reading its partial sums (as many as the buffer holds)
+    const int nt16 = ((T + kWgT - 1) / kWgT) * a.nquads;
+    a.nfull = 0;
+    a.nrem = mtiles * a.nquads;
+    const size_t cap = (size_t)p.tmax * K * L / ((size_t)a.nrem * BM * 256);
     const int smax = (int)std::max<size_t>(1, std::min<size_t>(8, cap));
     int ns = 1;
     double best = 1e30;
     for (int c = 1; c <= smax; ++c) {
-      const double rounds = (double)((nblk0 * c + h->ncu - 1) / h->ncu);
-      const double cost = rounds / c + 0.02 * c;
+      const double rounds = (double)((nt16 * c + h->ncu - 1) / h->ncu);
+      const double cost = rounds / c + 0.05 * (c > 1 ? c : 0);
       if (cost < best - 1e-9) { best = cost; ns = c; }
     }
     a.nsplit = ns;
-    a.nfull = ns == 1 ? nblk0 : 0;
-    a.nrem = ns == 1 ? 0 : nblk0;
     a.part = p.o;
-    if (int rc = launch_dense<kF16, kEpiY>(a, st)) return rc;
-    if (a.nsplit > 1) {
-      const float* res = norm ? x : nullptr;
+    hipLaunchKernelGGL((k_dense16<kEpiY, false>), dim3((unsigned)(nt16 * ns)), dim3(256), 0, st, a);
+    LMOE_HIP(hipGetLastError());
+    if (ns > 1) {
       const dim3 g(a.nrem * BM), b(256);
-      switch (a.nsplit) {
-        case 2: hipLaunchKernelGGL(k_ytiles<2>, g, b, 0, st, a, res); break;
-        case 3: hipLaunchKernelGGL(k_ytiles<3>, g, b, 0, st, a, res); break;
-        case 4: hipLaunchKernelGGL(k_ytiles<4>, g, b, 0, st, a, res); break;
-        case 5: hipLaunchKernelGGL(k_ytiles<5>, g, b, 0, st, a, res); break;
-        case 6: hipLaunchKernelGGL(k_ytiles<6>, g, b, 0, st, a, res); break;
-        case 7: hipLaunchKernelGGL(k_ytiles<7>, g, b, 0, st, a, res); break;
-        default: hipLaunchKernelGGL(k_ytiles<8>, g, b, 0, st, a, res); break;
+      switch (ns) {
+        case 2: hipLaunchKernelGGL(k_ytiles<2>, g, b, 0, st, a, (const float*)y); break;
+        case 3: hipLaunchKernelGGL(k_ytiles<3>, g, b, 0, st, a, (const float*)y); break;
+        case 4: hipLaunchKernelGGL(k_ytiles<4>, g, b, 0, st, a, (const float*)y); break;
+        case 5: hipLaunchKernelGGL(k_ytiles<5>, g, b, 0, st, a, (const float*)y); break;
+        case 6: hipLaunchKernelGGL(k_ytiles<6>, g, b, 0, st, a, (const float*)y); break;
+        case 7: hipLaunchKernelGGL(k_ytiles<7>, g, b, 0, st, a, (const float*)y); break;
+        default: hipLaunchKernelGGL(k_ytiles<8>, g, b, 0, st, a, (const float*)y); break;
       }
       LMOE_HIP(hipGetLastError());
     }
