@@ -49,7 +49,7 @@ PREFILL_KERNELS = ["k_prep + k_dense_dma<BF16,Logits> + k_select", "k_perm_*",
                    "k_dense_dma<BF16,SwigluB2> (shared gate/up)",
                    "k_grouped_dma<GateUp> (LDS DMA) + k_grouped_short<GateUp> (64- and 32-token pieces)",
                    "k_down_res (activations resident in LDS; 64- and 32-token blocks)", "k_combine",
-                   "k_dense_dma<F16,Y> (U + shared down, split along k; LDS DMA) + k_ytiles (split sums)"]
+                   "k_dense_dma<BF16,Y> (shared down into y) + k_dense16<Y> (U, split along k) + k_ytiles (split sums onto y)"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_145b_t4096_traffic.json")
 # kernel of each prefill phase as rocprofv3 names it (D and U on fp16 weights)
@@ -58,7 +58,7 @@ PREFILL_KERNEL_IDS = [["k_prep", "k_dense_dma<3, 0>", "k_select<5, 8>"],
                       "k_dense_dma<3, 2>",
                       ["k_grouped_dma<0>", "k_grouped_short<0, 2, 8>", "k_grouped_short<0, 1, 8>"],
                       ["k_down_res<8, 2>", "k_down_res<8, 1>"], "k_combine",
-                      ["k_dense_dma<5, 3>", "k_ytiles<4>"]]
+                      ["k_dense_dma<3, 3>", "k_dense16<3, false>", "k_ytiles<3>"]]
 
 
 def log(*a):
