@@ -203,11 +203,11 @@ def test_tiny_prefill_block():
 
 
 def test_prefill_u_split_along_k():
-    """latent 256 and top-8: the U + shared-down GEMM has 2 token tiles
-    (fewer than a round of the chip) and room for 6 partial sums per tile, so
-    it splits k six ways; the boundaries fall inside U, across the U /
-    shared-down seam and inside the shared down, and the last split has no U
-    stage at all. Every token is checked."""
+    """latent 256 and top-8: U has one 256-token tile (far less than a round
+    of the chip) and room for 6 partial sums per 128-token half, so it splits
+    k four ways (8 of its 32 stages each, across group boundaries), the
+    partials added onto the shared down projection already in y; T = 137
+    leaves the tile's second half mostly empty. Every token is checked."""
     w = wl.Workload("u_split", 256, 256, 32, 8, 4, 128, 192, 8, 200)
     c = Case(w, seed=11, tokens=200)
     layer = make_layer(c, 200)
