@@ -1611,11 +1611,12 @@ __device__ __forceinline__ double bf16_to_f64(uint32_t bits) {
   return (double)__uint_as_float(bits << 16);
 }
 
-// The x row of a token in the registers of a wave (in fp64, exact): lane l
-// holds columns 8 l + 512 j .. + 7 for j < NJ (H <= 512 NJ), zeros past H.
+// The x row of a token in the registers of a wave: lane l holds columns
+// 8 l + 512 j .. + 7 for j < NJ (H <= 512 NJ), zeros past H. Held in fp32
+// (half the registers of fp64) and widened exactly at each product.
 template <int NJ>
 struct XRow {
-  double v[NJ][8];   // the fp32 values, held converted for the fp64 products
+  float v[NJ][8];
 };
 
 template <int NJ>
@@ -1697,7 +1698,7 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // NJ: 512-column chunks of a row (H <= 512 NJ); EPL: experts per lane
 // (E <= 64 EPL), so the registers fit the layer
 template <int NJ, int EPL>
-__global__ __launch_bounds__(256) void k_select(Select a) {
+__global__ __launch_bounds__(256, 4) void k_select(Select a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   if (t >= a.T) return;
@@ -1787,14 +1788,22 @@ __global__ __launch_bounds__(256) void k_select(Select a) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const uint4 w = wc[j];
-      sd = fma(X.v[j][0], bf16_to_f64(w.x & 0xFFFFu), sd);
-      sd = fma(X.v[j][1], bf16_to_f64(w.x >> 16), sd);
-      sd = fma(X.v[j][2], bf16_to_f64(w.y & 0xFFFFu), sd);
-      sd = fma(X.v[j][3], bf16_to_f64(w.y >> 16), sd);
-      sd = fma(X.v[j][4], bf16_to_f64(w.z & 0xFFFFu), sd);
-      sd = fma(X.v[j][5], bf16_to_f64(w.z >> 16), sd);
-      sd = fma(X.v[j][6], bf16_to_f64(w.w & 0xFFFFu), sd);
-      sd = fma(X.v[j][7], bf16_to_f64(w.w >> 16), sd);
+      // widened here, per candidate (an empty asm keeps the compiler from
+      // hoisting the conversions and holding the row in fp64 registers)
+      float xv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        xv[k] = X.v[j][k];
+        asm volatile("" : "+v"(xv[k]));
+      }
+      sd = fma((double)xv[0], bf16_to_f64(w.x & 0xFFFFu), sd);
+      sd = fma((double)xv[1], bf16_to_f64(w.x >> 16), sd);
+      sd = fma((double)xv[2], bf16_to_f64(w.y & 0xFFFFu), sd);
+      sd = fma((double)xv[3], bf16_to_f64(w.y >> 16), sd);
+      sd = fma((double)xv[4], bf16_to_f64(w.z & 0xFFFFu), sd);
+      sd = fma((double)xv[5], bf16_to_f64(w.z >> 16), sd);
+      sd = fma((double)xv[6], bf16_to_f64(w.w & 0xFFFFu), sd);
+      sd = fma((double)xv[7], bf16_to_f64(w.w >> 16), sd);
     }
     const double l = wave_sum_f64(sd) * rt + (double)a.bias[e];
     nan_seen |= l != l;
