@@ -1519,6 +1519,7 @@ __device__ __forceinline__ float range_scale(float m) {
   return ldexpf(1.f, max(-60, min(60, 3 - ex)));
 }
 
+// Sum / maximum over the block (at most 8 waves), every thread gets it.
 __device__ __forceinline__ double block_sum(double v, double* red) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1529,53 +1530,60 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
   __syncthreads();
   return s;
 }
+__device__ __forceinline__ float block_max(float v, float* red) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float m = 0.f;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) m = fmaxf(m, red[i]);
+  return m;
+}
 
-// One block per token, 8 columns per thread and step (H is a multiple of 256).
-__global__ __launch_bounds__(256) void k_prep(Prep a) {
-  __shared__ double red[4];
-  const int t = blockIdx.x;
+// One block per token, one 8-column chunk per thread (blockDim = H / 8
+// rounded up to 64, H <= 4096): the row is read once and held in registers
+// for the second pass.
+__global__ __launch_bounds__(512) void k_prep(Prep a) {
+  __shared__ double red[8];
+  __shared__ float redm[8];
+  const int t = blockIdx.x, c = threadIdx.x;
   const float* xr = a.x + (size_t)t * a.H;
-  const int nc = a.H / 8;
-  __shared__ float redm[4];
+  const bool own = c < a.H / 8;
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (own) {
+    const float4 u0 = *(const float4*)(xr + 8 * c), u1 = *(const float4*)(xr + 8 * c + 4);
+    v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
+    v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+  }
   float r = 1.0f;
   double r64 = 1.0;
   double s = 0.0;
   float m = 0.f;
-  for (int c = threadIdx.x; c < nc; c += blockDim.x) {
-    const float4 u0 = *(const float4*)(xr + 8 * c), u1 = *(const float4*)(xr + 8 * c + 4);
-    const float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (a.norm) s += (double)v[j] * v[j];
-      m = fmaxf(m, fabsf(v[j]));
-    }
+  for (int j = 0; j < 8; ++j) {
+    if (a.norm) s += (double)v[j] * v[j];
+    m = fmaxf(m, fabsf(v[j]));
   }
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((threadIdx.x & 63) == 0) redm[threadIdx.x >> 6] = m;
+  m = block_max(m, redm);
   if (a.norm) {
     s = block_sum(s, red);
     r64 = 1.0 / sqrt(s / a.H + (double)a.eps);
     r = (float)r64;
-  } else {
-    __syncthreads();
   }
-  m = fmaxf(fmaxf(redm[0], redm[1]), fmaxf(redm[2], redm[3]));
   // the largest staged magnitude, up to rounding (enough to pick the scale)
   const float xs = range_scale(m * r);
   double s2 = 0.0;
-  for (int c = threadIdx.x; c < nc; c += blockDim.x) {
-    const float4 u0 = *(const float4*)(xr + 8 * c), u1 = *(const float4*)(xr + 8 * c + 4);
-    float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-    half8 h;
-    bf16x8 b0, b1;
+  half8 h;
+  bf16x8 b0, b1;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (a.norm) v[j] *= r;
-      h[j] = (_Float16)(v[j] * xs);
-      b0[j] = (__bf16)v[j];
-      b1[j] = (__bf16)(v[j] - (float)b0[j]);
-      s2 += (double)v[j] * v[j];
-    }
+  for (int j = 0; j < 8; ++j) {
+    if (a.norm) v[j] *= r;
+    h[j] = (_Float16)(v[j] * xs);
+    b0[j] = (__bf16)v[j];
+    b1[j] = (__bf16)(v[j] - (float)b0[j]);
+    s2 += (double)v[j] * v[j];
+  }
+  if (own) {
     *(half8*)(a.xh + (size_t)t * a.H + 8 * c) = h;
     *(bf16x8*)(a.xb + (size_t)t * 2 * a.H + 8 * c) = b0;
     *(bf16x8*)(a.xb + (size_t)t * 2 * a.H + a.H + 8 * c) = b1;
@@ -2162,24 +2170,45 @@ __global__ __launch_bounds__(1024) void k_router_wmax(const uint16_t* wr, int E,
 // tile b / BM, one column per thread; the NS loads are issued together.
 // Plain float accesses: y and the residual are caller pointers with no
 // alignment promise beyond float's.
+// Block = 4 rows of one split tile, a thread 4 consecutive columns of one
+// row (16-byte loads and stores); the partials are added in split order.
 template <int NS>
 __global__ __launch_bounds__(256) void k_ytiles(Dense a, const float* res) {
-  const int j = blockIdx.x / BM, r = blockIdx.x % BM, L = a.nfull + j;
+  constexpr int RPB = 4;                             // rows per block
+  const int j = blockIdx.x / (BM / RPB), r = (blockIdx.x % (BM / RPB)) * RPB + (threadIdx.x >> 6);
+  const int L = a.nfull + j, c = 4 * (threadIdx.x & 63);
   int mt, quad;
   tile_of(L, a.mtiles, a.nquads, mt, quad);
-  const int t = mt * BM + r, n = 256 * quad + threadIdx.x;
+  const int t = mt * BM + r, n = 256 * quad + c;
   if (t >= a.T || n >= a.nvalid) return;
-  const size_t tsz = (size_t)BM * 256, e = (size_t)r * 256 + threadIdx.x;
+  const size_t tsz = (size_t)BM * 256, e = (size_t)r * 256 + c;
   const size_t i = (size_t)t * a.ostride + n;
-  float p[NS];
-#pragma unroll
-  for (int k = 0; k < NS; ++k) p[k] = a.part[((size_t)k * a.nrem + j) * tsz + e];
-  float v = p[0];
-#pragma unroll
-  for (int k = 1; k < NS; ++k) v += p[k];
   const float ic = inv_pow2(a.xsc[t]);
-  v = v * ic * ic;
-  ((float*)a.out)[i] = res ? res[i] + v : v;
+  float* out = (float*)a.out;
+  if (n + 4 <= a.nvalid && (a.ostride & 3) == 0) {
+    float4 p[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) p[k] = *(const float4*)(a.part + ((size_t)k * a.nrem + j) * tsz + e);
+    float4 v = p[0];
+#pragma unroll
+    for (int k = 1; k < NS; ++k) {
+      v.x += p[k].x; v.y += p[k].y; v.z += p[k].z; v.w += p[k].w;
+    }
+    v.x = v.x * ic * ic; v.y = v.y * ic * ic; v.z = v.z * ic * ic; v.w = v.w * ic * ic;
+    if (res) {
+      const float4 q = *(const float4*)(res + i);
+      v.x = q.x + v.x; v.y = q.y + v.y; v.z = q.z + v.z; v.w = q.w + v.w;
+    }
+    *(float4*)(out + i) = v;
+    return;
+  }
+  for (int u = 0; u < 4 && n + u < a.nvalid; ++u) {
+    float v = a.part[((size_t)0 * a.nrem + j) * tsz + e + u];
+#pragma unroll
+    for (int k = 1; k < NS; ++k) v += a.part[((size_t)k * a.nrem + j) * tsz + e + u];
+    v = v * ic * ic;
+    out[i + u] = res ? res[i + u] + v : v;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -2493,7 +2522,7 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
   // staging
   {
     Prep a{x, T, H, norm ? 1 : 0, eps, (_Float16*)p.xh, (__bf16*)p.xb, p.xnorm, p.r, p.r64, p.xsc};
-    hipLaunchKernelGGL(k_prep, dim3(T), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_prep, dim3(T), dim3((H / 8 + 63) / 64 * 64), 0, st, a);
     LMOE_HIP(hipGetLastError());
   }
   // D and the shared gate/up need only the staged rows: D runs on the aux
@@ -2707,7 +2736,7 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     hipLaunchKernelGGL((k_dense16<kEpiY, false>), dim3((unsigned)(nt16 * ns)), dim3(256), 0, st, a);
     LMOE_HIP(hipGetLastError());
     if (ns > 1) {
-      const dim3 g(a.nrem * BM), b(256);
+      const dim3 g(a.nrem * (BM / 4)), b(256);
       switch (ns) {
         case 2: hipLaunchKernelGGL(k_ytiles<2>, g, b, 0, st, a, (const float*)y); break;
         case 3: hipLaunchKernelGGL(k_ytiles<3>, g, b, 0, st, a, (const float*)y); break;
