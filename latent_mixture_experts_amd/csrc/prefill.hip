@@ -1910,6 +1910,9 @@ struct Perm {
   int* inv;              // [T*K]
   const float* xsc;      // [T] range scale per token
   float* psc;            // [T*K] the same per sorted position
+  int* gl_tok;           // [G][gcap] each group's routed tokens, ascending
+  int* gl_cnt;           // [G]
+  int gcap;
 };
 
 __global__ __launch_bounds__(256) void k_perm_mask(Perm a) {
@@ -1936,7 +1939,7 @@ __global__ __launch_bounds__(256) void k_perm_mask(Perm a) {
 
 // one block of kMaxE threads: chunk prefixes, segment starts, group offsets
 // and the piece list of the grouped GEMMs
-__global__ __launch_bounds__(kMaxE) void k_perm_scan(Perm a) {
+__device__ __forceinline__ void perm_scan_block(const Perm& a) {
   __shared__ int sc[kMaxE];
   __shared__ int sp[kMaxE];
   __shared__ int sf[kMaxE];
@@ -2017,6 +2020,19 @@ __global__ __launch_bounds__(kMaxE) void k_perm_scan(Perm a) {
       a.npieces[2] = nmid;
     }
   }
+}
+
+// each group's routed tokens in ascending order (defined with the prefill
+// D over the routed pairs below)
+__device__ __forceinline__ void group_list_block(const unsigned long long* gmask, int nchunk, int G,
+                                                 int gcap, int* gl_tok, int* gl_cnt, int g);
+
+// Block 0: the scan above; blocks 1 .. G: group g - 1's token list (from
+// the per-chunk group bitmasks k_perm_mask wrote), which only the routed D
+// reads: one launch for both.
+__global__ __launch_bounds__(kMaxE) void k_perm_scan(Perm a) {
+  if (blockIdx.x == 0) perm_scan_block(a);
+  else group_list_block(a.gmask, a.nchunk, a.G, a.gcap, a.gl_tok, a.gl_cnt, (int)blockIdx.x - 1);
 }
 
 __global__ __launch_bounds__(256) void k_perm_scatter(Perm a) {
@@ -2417,12 +2433,12 @@ __global__ __launch_bounds__(256) void k_dense16(Dense a) {
 // per group, 1024 chunks of 64 tokens per pass; a block scan of the chunks'
 // popcounts gives each chunk's first position, then wave w writes the tokens
 // of chunks w, w + 16, ... (lane l: token 64 c + l).
-__global__ __launch_bounds__(1024) void k_group_lists(const unsigned long long* gmask, int nchunk, int G,
-                                                      int gcap, int* gl_tok, int* gl_cnt) {
+__device__ __forceinline__ void group_list_block(const unsigned long long* gmask, int nchunk, int G,
+                                                 int gcap, int* gl_tok, int* gl_cnt, int g) {
   __shared__ unsigned long long ms[1024];
   __shared__ int base[1024];
   __shared__ int wsum[16];
-  const int g = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int run = 0;
   for (int c0 = 0; c0 < nchunk; c0 += 1024) {
     const int c = c0 + tid;
@@ -2531,12 +2547,9 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
   // runs on the caller's stream in phase order, so that each phase is
   // measured alone.
   // D over the routed (token, group) pairs (the handle's prefill-D option):
-  // per-group token lists, then the gathered GEMM; it needs the routing
+  // the gathered GEMM over the per-group token lists the permutation wrote
   const bool routed = h->prefill_d_routed && (size_t)T * H * 2 < (1ull << 31);
   auto routed_d = [&](hipStream_t sd) -> int {
-    hipLaunchKernelGGL(k_group_lists, dim3(G), dim3(1024), 0, sd, (const unsigned long long*)p.gmask,
-                       prefill_chunks(T), G, p.tmax, p.gl_tok, p.gl_cnt);
-    LMOE_HIP(hipGetLastError());
     Dense a{};
     a.W = WMat{h->dmat16, h->g_d16, 0, 1};
     a.A = AMat{p.xh, (size_t)H, 0, H};
@@ -2653,9 +2666,11 @@ int forward_prefill(lmoe_t* h, const float* x, int T, float* y, bool norm, float
     a.labels = h->labels; a.seg_start = p.seg_start; a.expert_count = p.expert_count;
     a.group_off = p.group_off; a.pieces = (Piece*)p.pieces; a.npieces = p.npieces;
     a.perm = p.perm; a.inv = p.inv; a.xsc = p.xsc; a.psc = p.psc;
+    a.gl_tok = p.gl_tok; a.gl_cnt = p.gl_cnt; a.gcap = p.tmax;
     hipLaunchKernelGGL(k_perm_mask, dim3(a.nchunk), dim3(256), 0, st, a);
     LMOE_HIP(hipGetLastError());
-    hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(kMaxE), 0, st, a);
+    // the group lists' blocks only when the routed D reads them
+    hipLaunchKernelGGL(k_perm_scan, dim3(1 + (routed ? G : 0)), dim3(kMaxE), 0, st, a);
     LMOE_HIP(hipGetLastError());
     hipLaunchKernelGGL(k_perm_scatter, dim3((T * K + 255) / 256), dim3(256), 0, st, a);
     LMOE_HIP(hipGetLastError());
