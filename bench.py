@@ -44,8 +44,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 / bf16 matrix peak, published
 PREFILL_PHASES = ["route", "permute", "d", "shared_gate_up", "expert_gate_up", "expert_down",
                   "combine", "u_shared_down"]
-PREFILL_KERNELS = ["k_prep + k_dense_dma<BF16,Logits> + k_select", "k_perm_*",
-                   "k_group_lists + k_dense16<F16, gather> (D over the routed (t, g) pairs; 128 x 128 wave tiles, LDS DMA)",
+PREFILL_KERNELS = ["k_prep + k_dense_dma<BF16,Logits> + k_select", "k_perm_* (with the routed D's group lists)",
+                   "k_dense16<F16, gather> (D over the routed (t, g) pairs; 128 x 128 wave tiles, LDS DMA)",
                    "k_dense_dma<BF16,SwigluB2> (shared gate/up)",
                    "k_grouped_dma<GateUp> (LDS DMA) + k_grouped_short<GateUp> (64- and 32-token pieces)",
                    "k_down_res (activations resident in LDS; 64- and 32-token blocks)", "k_combine",
@@ -54,7 +54,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_145b_t4096_traffic.json")
 # kernel of each prefill phase as rocprofv3 names it (D and U on fp16 weights)
 PREFILL_KERNEL_IDS = [["k_prep", "k_dense_dma<3, 0>", "k_select<5, 8>"],
-                      ["k_perm_mask", "k_perm_scan", "k_perm_scatter"], ["k_group_lists", "k_dense16<1, true>"],
+                      ["k_perm_mask", "k_perm_scan", "k_perm_scatter"], ["k_dense16<1, true>"],
                       "k_dense_dma<3, 2>",
                       ["k_grouped_dma<0>", "k_grouped_short<0, 2, 8>", "k_grouped_short<0, 1, 8>"],
                       ["k_down_res<8, 2>", "k_down_res<8, 1>"], "k_combine",
