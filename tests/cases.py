@@ -7,7 +7,7 @@ import numpy as np
 import oracle
 from latent_mixture_experts_amd import workloads as wl
 
-# North-star parity bar on the layer output.
+# Parity bar on the layer output.
 REL_L2 = 1e-3
 MAX_ABS_OF_RMS = 1e-2
 

@@ -1,7 +1,7 @@
 """Parity of the HIP path (through the C ABI) with the fp64 oracle.
 
 Bit-exact: top-K indices, the group permutation, expert counts and group
-offsets. Within the spec bar: y (relative L2 <= 1e-3 and max-abs <=
+offsets. Within the parity bar: y (relative L2 <= 1e-3 and max-abs <=
 1e-2 * rms(y)); routing weights and latents are held to a far tighter bound
 because the path computes in fp32 / fp64 throughout."""
 

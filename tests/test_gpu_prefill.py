@@ -2,7 +2,7 @@
 assignments) with the fp64 oracle, through the C ABI.
 
 Bit-exact: top-K indices, the group permutation, expert counts and group
-offsets, for every token. Within the spec bar: y (relative L2 <= 1e-3,
+offsets, for every token. Within the parity bar: y (relative L2 <= 1e-3,
 max-abs <= 1e-2 * rms(y)). The path rounds its activations to fp16 five
 times (x, D x, h, the weighted expert outputs, the per-group sums) and the
 D/U weights q * d once; each rounding adds about 2e-4 relative error to the

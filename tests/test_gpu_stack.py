@@ -1,7 +1,7 @@
 """Parity of lmoe_forward_block (x += layer(RMSNorm(x))) with the oracle,
 layer by layer with teacher forcing: layer l of the oracle reads the GPU's
 own fp32 x_l, so rounding upstream cannot legitimately flip a near-tie
-downstream. Each layer's update x_{l+1} - x_l is held to the spec bar
+downstream. Each layer's update x_{l+1} - x_l is held to the parity bar
 and its routed part to 1e-4; the end-to-end drift against the oracle's own
 stack is printed, not gated."""
 
