@@ -123,12 +123,10 @@ size_t decode_ws_layout(const lmoe_t* h, int T, char* base, Workspace* out) {
   take(w.hsp, sizeof(float) * nss_s * T * 2 * Fs);
   take(w.hbuf, sizeof(float) * n * F);
   take(w.obuf, sizeof(float) * n * L);
-  take(w.s, sizeof(float) * T * G * L);
   // 2G + shared-down blocks (at most one per half-step)
   take(w.ypart, sizeof(float) * (2 * G + (Fs + 127) / 128) * T * H);
   take(w.ctr_router, sizeof(unsigned));
   take(w.ctr_y, sizeof(unsigned) * (H / 64));
-  take(w.ctr_g, sizeof(unsigned) * G * ((L + 63) / 64));
   if (out) *out = w;
   return (off + 255) / 256 * 256;
 }
@@ -221,7 +219,6 @@ int create_impl(lmoe_t* h) {
 #undef A
   LMOE_HIP(hipMemset(h->ws.ctr_router, 0, sizeof(unsigned)));
   LMOE_HIP(hipMemset(h->ws.ctr_y, 0, sizeof(unsigned) * (H / 64)));
-  LMOE_HIP(hipMemset(h->ws.ctr_g, 0, sizeof(unsigned) * G * ((L + 63) / 64)));
   LMOE_HIP(hipDeviceSynchronize());
   return 0;
 }
@@ -470,10 +467,9 @@ int lmoe_forward_noalloc(lmoe_t* h, const float* x, int32_t T, float* y, void* s
   hipStream_t st = (hipStream_t)stream;
   // the counters reset themselves at the end of a forward; clear them anyway,
   // in case another handle's forward on this device stopped short
-  const int nctr = h->d.hidden / 64, nctr_g = h->d.n_groups * ((h->d.latent + 63) / 64);
+  const int nctr = h->d.hidden / 64;
   hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(64), 0, st, ws.ctr_router, 1);
   hipLaunchKernelGGL(k_fill_zero, dim3((nctr + 255) / 256), dim3(256), 0, st, ws.ctr_y, nctr);
-  hipLaunchKernelGGL(k_fill_zero, dim3((nctr_g + 255) / 256), dim3(256), 0, st, ws.ctr_g, nctr_g);
   LMOE_HIP(hipGetLastError());
   return forward_decode(h, x, T, y, false, st, 0, &ws);
 }

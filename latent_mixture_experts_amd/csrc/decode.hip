@@ -347,10 +347,22 @@ __device__ __forceinline__ void wave_load(WRegs<FMT, NT, SL>& R, const uint8_t* 
 // vector i of the activations at byte offset xoff[i] of resource x. All
 // per-lane addresses are the one lane offset, which stays in a register
 // across items instead of one 64-bit address per load.
+// The weight half of wave_load_b: scales, then the code slots.
+template <int FMT, int NT, int SL>
+__device__ __forceinline__ void wave_load_wts(WRegs<FMT, NT, SL>& R, rsrc_t w, int ncs, int lane) {
+  const int tok = lane & 15;
+  if (FMT != kBF16) {
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) R.sc[rg] = ldb(w, 16 * tok, ncs * kSlot + rg * 256);
+  }
+#pragma unroll
+  for (int j = 0; j < SL; ++j)
+    if (j < ncs) R.q[j] = ldb<kAuxNT>(w, 16 * lane, j * kSlot);
+}
+
 template <int FMT, int NT, int SL>
 __device__ __forceinline__ void wave_load_b(WRegs<FMT, NT, SL>& R, rsrc_t w, int ncs, rsrc_t x,
                                             const int (&xoff)[NT], int n, int cols, int lane) {
-  const int tok = lane & 15;
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
     R.xr.v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -359,13 +371,7 @@ __device__ __forceinline__ void wave_load_b(WRegs<FMT, NT, SL>& R, rsrc_t w, int
       R.xr.v[i] = __builtin_bit_cast(float4, v);
     }
   }
-  if (FMT != kBF16) {
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) R.sc[rg] = ldb(w, 16 * tok, ncs * kSlot + rg * 256);
-  }
-#pragma unroll
-  for (int j = 0; j < SL; ++j)
-    if (j < ncs) R.q[j] = ldb<kAuxNT>(w, 16 * lane, j * kSlot);
+  wave_load_wts<FMT, NT, SL>(R, w, ncs, lane);
 }
 
 // The MFMAs of a loaded super-step (xs: this wave's staging area).
@@ -1200,14 +1206,13 @@ __global__ __launch_bounds__(1024) void k_phase2(P2 a) {
 }
 
 // ---------------------------------------------------------------------------
-// Phase 3: routed-expert down, scaled by the routing weight, and the
-// per-group sums s[t][g] = sum over token t's experts in group g, ascending k.
+// Phase 3: routed-expert down, scaled by the routing weight.
 //
 // One block per (slot, 64-row tile r of ell), one wave per super-step of the
 // ffn width, so that every block's loads are in flight at once and the
 // blocks spread over the whole chip whatever the group sizes. The weighted
-// outputs go to obuf with coherent stores; the last of group g's slots to
-// finish tile r adds, per token, the group's outputs in ascending k.
+// outputs go to obuf [sorted position][ell]; phase 4 forms the per-group
+// sums from them as it stages U's activations.
 
 constexpr size_t kLdsBytes = 160 * 1024;   // LDS of one CU
 
@@ -1227,7 +1232,6 @@ constexpr int phase3_waves(int nss) {
 template <int T, int W, int DN>
 __global__ __launch_bounds__(64 * W) void k_phase3(P3 a) {
   extern __shared__ __align__(16) char smem[];
-  __shared__ int flag;
   const Dims& d = a.d;
   const int tiles = a.gdn.tiles;                     // ell / 64
   const int j = blockIdx.x / tiles, r = blockIdx.x % tiles;
@@ -1238,7 +1242,6 @@ __global__ __launch_bounds__(64 * W) void k_phase3(P3 a) {
   if (j >= ci(a.ws.n_slots)[0]) return;
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6), nw = blockDim.x >> 6;
   ci_t perm = ci(a.ws.perm);
-  const int g = label_of(a.labels, e);
   const uint8_t* rec = a.experts + (size_t)e * a.stride;
   char* xs = smem + wave * stage_bytes_f16<T>();
   f4* red = (f4*)(smem + nw * stage_bytes_f16<T>());
@@ -1268,30 +1271,8 @@ __global__ __launch_bounds__(64 * W) void k_phase3(P3 a) {
         const int i = 4 * (lane >> 4) + v;
         const int row = r * 64 + rg * 16 + (lane & 15);
         if (i < cnt && row < d.L)
-          st_co(a.ws.obuf + (size_t)(start + i) * d.L + row, acc[rg][v] * ts[2] * a.ws.topk_w[perm[start + i]]);
+          a.ws.obuf[(size_t)(start + i) * d.L + row] = acc[rg][v] * ts[2] * a.ws.topk_w[perm[start + i]];
       }
-  }
-  ci_t gso = ci(a.ws.gslot_off);
-  if (!arrive_last(a.ws.ctr_g + g * tiles + r, (unsigned)(gso[g + 1] - gso[g]), &flag)) return;
-  // s[t][g][rows of r] for every token (0 where token t has no expert in g)
-  ci_t cnt_tab = ci(a.ws.tg_cnt);
-  ci_t pos_tab = ci(a.ws.tg_pos);
-  const int row = r * 64 + lane;
-  if (row >= d.L) return;
-  for (int t = wave; t < T; t += nw) {
-    const int q = t * d.G + g;
-    const int c = cnt_tab[q];
-    float v = 0.f;
-    for (int i0 = 0; i0 < c; i0 += 4) {               // four loads in flight, added in k order
-      float u[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        u[k] = i0 + k < c ? ld_co(a.ws.obuf + (size_t)pos_tab[q * d.K + i0 + k] * d.L + row) : 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (i0 + k < c) v += u[k];
-    }
-    a.ws.s[(size_t)q * d.L + row] = v;
   }
 }
 
@@ -1304,6 +1285,52 @@ __global__ __launch_bounds__(64 * W) void k_phase3(P3 a) {
 // round. Item (g, h) writes partial 2g + h of row tile r, shared down block
 // k partial 2G + k; the partials are added in that order, by k_ysum after
 // the kernel (SUMK) or by the last of a row tile's items to finish.
+
+// U's activations for group g, columns of super-step ss (lane l: 4 l ..
+// 4 l + 3): s[t][g] = the sum over token t's experts in group g of their
+// weighted outputs, added in ascending k (0 where t has none in g). Each
+// token's first kPreRows rows are loaded together (three at up to four
+// tokens, fewer beyond, for the registers); more are rare.
+template <int T>
+__device__ __forceinline__ void group_sums(const P4& a, int g, int ss, int lane, XRegs<T>& X) {
+  constexpr int kPreRows = T <= 4 ? 3 : T <= 6 ? 2 : 1;
+  const Dims& d = a.d;
+  ci_t cnt_tab = ci(a.ws.tg_cnt);
+  ci_t pos_tab = ci(a.ws.tg_pos);
+  const bool on = 4 * lane < ss_cols(a.gu, ss);
+  const float* ob = a.ws.obuf + ss * kSSCols + 4 * lane;
+  // the counts and the first positions in one round of scalar loads (the
+  // positions read whatever the count; entries past it are not used)
+  int c[T], pr[T][kPreRows];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int q = t * d.G + g;
+    c[t] = cnt_tab[q];
+#pragma unroll
+    for (int i = 0; i < kPreRows; ++i) pr[t][i] = i < d.K ? pos_tab[q * d.K + i] : 0;
+  }
+  float4 u[T][kPreRows];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int i = 0; i < kPreRows; ++i)
+      u[t][i] = on && i < c[t] ? *(const float4*)(ob + (size_t)pr[t][i] * d.L) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < kPreRows; ++i)
+      if (i < c[t]) {
+        v.x += u[t][i].x; v.y += u[t][i].y; v.z += u[t][i].z; v.w += u[t][i].w;
+      }
+    for (int i = kPreRows; i < c[t]; ++i) {
+      const float4 w = on ? *(const float4*)(ob + (size_t)pos_tab[(t * d.G + g) * d.K + i] * d.L)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    }
+    X.v[t] = v;
+  }
+}
 
 template <int T, int DU, int W, bool SUMK>
 __global__ __launch_bounds__(64 * W) void k_phase4(P4 a) {
@@ -1329,15 +1356,11 @@ __global__ __launch_bounds__(64 * W) void k_phase4(P4 a) {
     active = gso[g + 1] > gso[g];
     const int ss = h * a.hu + wave;
     if (active && wave < a.hu && ss < a.gu.nss) {
-      int xoff[T];
-#pragma unroll
-      for (int t = 0; t < T; ++t) xoff[t] = (int)(((t * d.G + g) * d.L + ss * kSSCols) * sizeof(float));
       const int ncs = ss_codes(DU, a.gu, ss);
       const uint8_t* p = ss_ptr(a.umat + (size_t)g * a.gu.bytes(), a.gu, r, ss);
       WRegs<DU, T> R;
-      wave_load_b<DU, T>(R, rsrc(p, (ncs + scale_slots(DU)) * kSlot), ncs,
-                         rsrc(a.ws.s, (uint32_t)((size_t)T * d.G * d.L * sizeof(float))), xoff, T,
-                         ss_cols(a.gu, ss), lane);
+      group_sums<T>(a, g, ss, lane, R.xr);
+      wave_load_wts<DU, T>(R, rsrc(p, (ncs + scale_slots(DU)) * kSlot), ncs, lane);
       wave_compute<DU, T>(R, ncs, T, xs, lane, acc);
     }
   } else {

@@ -132,11 +132,9 @@ struct Workspace {
   float* hsp = nullptr;          // [H/256][T][2 Fs] shared gate/up partials per super-step
   float* hbuf = nullptr;         // [T*K][F] expert hidden, sorted position order
   float* obuf = nullptr;         // [T*K][ell] weighted expert outputs, sorted position order
-  float* s = nullptr;            // [T][G][ell] per-group sums
   float* ypart = nullptr;        // [2G + shared-down blocks][T][H] phase-4 partials
   unsigned* ctr_router = nullptr;  // [1]
   unsigned* ctr_y = nullptr;       // [H/64]
-  unsigned* ctr_g = nullptr;       // [G][ell/64] phase-3 arrivals per (group, row tile)
   int nch = 0;                   // router column chunks
   int tmax = 0;                  // tokens the decode buffers hold
 };
