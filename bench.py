@@ -578,6 +578,11 @@ def bench_decode(lm, wl, w, args, torch, T=None, layers=None, steps=None, warmup
     gbps = step_bytes / (ms * 1e-3) / 1e9
     dom = int(np.argmax(pt))
     kern_us = float(pt[dom] * 1e3)
+    # phase 4 is two launches from four tokens on (its partials' ordered sum
+    # is a kernel of its own): its time and traffic are those of both
+    ysum = T >= 4
+    phase_names = ["k_phase1", "k_phase2", "k_phase3", "k_phase4 + k_ysum" if ysum else "k_phase4"]
+    phase_ids = ["k_phase1", "k_phase2", "k_phase3", ["k_phase4", "k_ysum"] if ysum else "k_phase4"]
     kbytes = float(pbytes[dom])
     log("%s T=%d: %.2f us/step (p10 %.2f, median %.2f, p90 %.2f us); %.0f GB/s over %.1f MB; "
         "%.1f distinct experts, %.1f groups used; kernels (us): %s; kernel GB/s: %s" % (
@@ -602,8 +607,8 @@ def bench_decode(lm, wl, w, args, torch, T=None, layers=None, steps=None, warmup
         "used_groups": mean["used_groups"],
         "roofline": {"bound": "hbm", "achieved": kbytes / (kern_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": kbytes / (kern_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("k_phase%d" % (dom + 1), "%s_t%d" % (w.name, T)),
-                     "kernel": "k_phase%d" % (dom + 1), "kernel_us": kern_us,
+                     "traffic": measured_traffic(phase_ids[dom], "%s_t%d" % (w.name, T)),
+                     "kernel": phase_names[dom], "kernel_us": kern_us,
                      "kernel_algorithmic_bytes": kbytes},
         "kernels_us": {"k_phase%d" % (k + 1): float(v * 1e3) for k, v in enumerate(pt)},
         "kernels_GBps": {"k_phase%d" % (k + 1): float(b / (v * 1e-3) / 1e9)
