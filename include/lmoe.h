@@ -191,9 +191,9 @@ int lmoe_forward_block(lmoe_t* h, float* x_inout_dev, int32_t T, float rms_eps,
  * events[0] on its stream before its first kernel and events[i] after its
  * i-th phase (hipEvent_t handles owned by the caller). Decode (T <= 8) has 4
  * phases: router + D + shared gate/up, expert gate/up, expert down,
- * combine + U + shared down (the per-group sums formed in U's staging). Prefill has 8: staging + router + top-K;
- * permutation; D; shared gate/up; expert gate/up; expert down; combine;
- * U + shared down. Forwards of the other path record nothing. NULL switches
+ * combine + U + shared down (the per-group sums formed in U's staging).
+ * Prefill has 8: staging + router + top-K; permutation; D; shared gate/up;
+ * expert gate/up; expert down; combine; U + shared down. Forwards of the other path record nothing. NULL switches
  * it off. EINVAL unless n is 5 or 9. */
 int lmoe_set_phase_events(lmoe_t* h, void* const* events, int32_t n);
 int32_t lmoe_phase_count(int32_t T);
